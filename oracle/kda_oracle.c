@@ -1,0 +1,339 @@
+/*
+ * kda_oracle.c -- plain, slow CPU oracle of the KDA decode update.
+ *
+ * TEST INFRASTRUCTURE ONLY (see kda_oracle.h): never linked into, loaded by
+ * or called from the product library.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * The loop is written in the order the update is defined, one operation at
+ * a time, with sequential sums and no blocking or reordering.
+ */
+#include "kda_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int g_mutation = 0;
+
+void kdao_set_mutation(int which) { g_mutation = which; }
+
+/* ------------------------------------------------------------------------ */
+/* binary16 conversions, from the IEEE 754 encoding definitions             */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  return u;
+}
+
+static float bits_f32(uint32_t u) {
+  float x;
+  memcpy(&x, &u, sizeof x);
+  return x;
+}
+
+/*
+ * Round to nearest, ties to even.  binary16: 1 sign bit, 5 exponent bits
+ * (bias 15), 10 fraction bits.  Largest finite 65504; smallest normal
+ * 2^-14; smallest subnormal 2^-24.
+ */
+uint16_t kdao_f32_to_f16_rne(float x) {
+  const uint32_t u = f32_bits(x);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t mag = u & 0x7fffffffu;
+
+  if (mag > 0x7f800000u) { /* NaN: keep it a NaN, make it quiet */
+    return (uint16_t)(sign | 0x7e00u | ((mag & 0x007fffffu) >> 13));
+  }
+  if (mag == 0x7f800000u) return (uint16_t)(sign | 0x7c00u); /* inf */
+
+  const int32_t e32 = (int32_t)(mag >> 23);     /* biased, 0..254 */
+  const int32_t e = e32 - 127;                   /* unbiased exponent */
+  uint32_t frac = mag & 0x007fffffu;
+
+  if (e >= -14) {
+    /* Normal range of binary16 (before rounding). */
+    uint32_t h = ((uint32_t)(e + 15) << 10) | (frac >> 13);
+    const uint32_t rest = frac & 0x1fffu; /* 13 dropped bits */
+    if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) h += 1u;
+    /* A carry out of the fraction bumps the exponent, which is the right
+     * encoding; reaching exponent 31 means overflow to infinity. */
+    if (h >= 0x7c00u) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | h);
+  }
+
+  /* Below the normal range: the result is a multiple of 2^-24. */
+  if (e32 == 0) return sign; /* binary32 subnormal: < 2^-126, rounds to 0 */
+  const uint32_t sig = frac | 0x00800000u;   /* value = sig * 2^(e - 23) */
+  const int32_t shift = -e - 1;              /* value / 2^-24 = sig >> shift */
+  if (shift > 24) return sign;               /* below half of 2^-24 */
+  uint32_t h = sig >> shift;
+  const uint32_t rest = sig & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rest > half || (rest == half && (h & 1u))) h += 1u;
+  return (uint16_t)(sign | h); /* h == 0x400 is the smallest normal: right */
+}
+
+float kdao_f16_to_f32(uint16_t hbits) {
+  const uint32_t sign = ((uint32_t)hbits & 0x8000u) << 16;
+  const uint32_t e = ((uint32_t)hbits >> 10) & 0x1fu;
+  const uint32_t frac = (uint32_t)hbits & 0x3ffu;
+  if (e == 0) {
+    /* zero or subnormal: frac * 2^-24, exact in binary32 */
+    const float m = (float)frac * 0x1p-24f;
+    return sign ? -m : m;
+  }
+  if (e == 31) return bits_f32(sign | 0x7f800000u | (frac << 13));
+  return bits_f32(sign | ((e - 15u + 127u) << 23) | (frac << 13));
+}
+
+void kdao_f32_to_f16_rne_array(const float* x, uint16_t* h, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) h[i] = kdao_f32_to_f16_rne(x[i]);
+}
+
+void kdao_f16_to_f32_array(const uint16_t* h, float* x, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) x[i] = kdao_f16_to_f32(h[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* argument checks shared by both precisions                                */
+/* ------------------------------------------------------------------------ */
+
+static int check_args(const void* pool, int32_t n_slots, int32_t H, int32_t K,
+                      int32_t V, const int32_t* slot_ids, int32_t n_req,
+                      int32_t n_rows, const void* q, const void* k,
+                      const void* v, const void* g, const void* b,
+                      const void* out) {
+  if (!pool || !slot_ids || !q || !k || !v || !g || !b || !out) return 0;
+  if (n_slots <= 0 || H <= 0 || K <= 0 || V <= 0 || n_req < 0 || n_rows <= 0)
+    return 0;
+  const int64_t R = (int64_t)n_req * n_rows;
+  for (int64_t i = 0; i < R; ++i)
+    if (slot_ids[i] < 0 || slot_ids[i] >= n_slots) return 0;
+  return 1;
+}
+
+/* Element offset of the [K, V] state of (slot, head) inside the pool. */
+static int64_t state_offset(int32_t slot, int32_t h, int32_t H, int32_t K,
+                            int32_t V) {
+  return ((int64_t)slot * H + h) * (int64_t)K * V;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp32 recurrence                                                          */
+/* ------------------------------------------------------------------------ */
+
+int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
+                  int32_t K, int32_t V, const int32_t* slot_ids,
+                  int32_t n_req, int32_t n_rows, const float* q,
+                  const float* k, const float* v, const float* g,
+                  const float* b, float scale, float* out) {
+  if (pool_kind != KDAO_POOL_F32 && pool_kind != KDAO_POOL_F16) return KDAO_EARG;
+  if (!check_args(pool, n_slots, H, K, V, slot_ids, n_req, n_rows, q, k, v, g,
+                  b, out))
+    return KDAO_EARG;
+
+  const float eps = 1e-6f;
+  float* S = (float*)malloc(sizeof(float) * (size_t)K * V);
+  float* qn = (float*)malloc(sizeof(float) * (size_t)K);
+  float* kn = (float*)malloc(sizeof(float) * (size_t)K);
+  float* a = (float*)malloc(sizeof(float) * (size_t)K);
+  float* w = (float*)malloc(sizeof(float) * (size_t)V);
+  float* u = (float*)malloc(sizeof(float) * (size_t)V);
+  if (!S || !qn || !kn || !a || !w || !u) {
+    free(S); free(qn); free(kn); free(a); free(w); free(u);
+    return KDAO_EARG;
+  }
+  float* pf = (float*)pool;
+  uint16_t* ph = (uint16_t*)pool;
+
+  for (int32_t r = 0; r < n_req; ++r) {
+    for (int32_t h = 0; h < H; ++h) {
+      /* initial state: the request's row-0 slot, widened exactly */
+      const int64_t off0 = state_offset(slot_ids[(int64_t)r * n_rows], h, H, K, V);
+      for (int64_t e = 0; e < (int64_t)K * V; ++e)
+        S[e] = pool_kind == KDAO_POOL_F32 ? pf[off0 + e] : kdao_f16_to_f32(ph[off0 + e]);
+
+      for (int32_t t = 0; t < n_rows; ++t) {
+        const int64_t rho = (int64_t)r * n_rows + t;
+        if (g_mutation == 9 && t > 0) { /* planted: chain not carried */
+          for (int64_t e = 0; e < (int64_t)K * V; ++e)
+            S[e] = pool_kind == KDAO_POOL_F32 ? pf[off0 + e] : kdao_f16_to_f32(ph[off0 + e]);
+        }
+        const float* qv = q + (rho * H + h) * K;
+        const float* kv = k + (rho * H + h) * K;
+        const float* gv = g + (rho * H + h) * K;
+        const float* vv = v + (rho * H + h) * V;
+        const float bv = b[rho * H + h];
+        float* ov = out + (rho * H + h) * V;
+
+        /* L2 normalisation of q and k */
+        float sq = 0.0f, sk = 0.0f;
+        for (int32_t i = 0; i < K; ++i) sq = sq + qv[i] * qv[i];
+        for (int32_t i = 0; i < K; ++i) sk = sk + kv[i] * kv[i];
+        const float rq = g_mutation == 6 ? 1.0f / (sq + eps) : 1.0f / sqrtf(sq + eps);
+        const float rk = 1.0f / sqrtf(sk + eps);
+        for (int32_t i = 0; i < K; ++i) qn[i] = qv[i] * rq;
+        for (int32_t i = 0; i < K; ++i) kn[i] = kv[i] * rk;
+
+        /* per-key-channel decay and sigmoid gate */
+        for (int32_t i = 0; i < K; ++i)
+          a[i] = g_mutation == 1 ? 1.0f : (g_mutation == 8 ? expf(-gv[i]) : expf(gv[i]));
+        const float beta = g_mutation == 11 ? 1.0f / (1.0f + expf(bv))
+                                            : 1.0f / (1.0f + expf(-bv));
+
+        /* S' = diag(a) S */
+        for (int32_t i = 0; i < K; ++i)
+          for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
+
+        if (g_mutation == 4) { /* planted: read-out before the update */
+          for (int32_t j = 0; j < V; ++j) {
+            float acc = 0.0f;
+            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
+            ov[j] = scale * acc;
+          }
+        }
+
+        /* w = S'^T kn ; u = v - w */
+        for (int32_t j = 0; j < V; ++j) {
+          float acc = 0.0f;
+          for (int32_t i = 0; i < K; ++i) {
+            const float s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
+            acc = acc + kn[i] * s;
+          }
+          w[j] = acc;
+        }
+        for (int32_t j = 0; j < V; ++j) u[j] = g_mutation == 2 ? vv[j] + w[j] : vv[j] - w[j];
+
+        /* S = S' + (beta kn) u^T */
+        for (int32_t i = 0; i < K; ++i) {
+          const float bk = g_mutation == 5 ? kn[i] : beta * kn[i];
+          for (int32_t j = 0; j < V; ++j)
+            S[(int64_t)i * V + j] = S[(int64_t)i * V + j] + bk * u[j];
+        }
+
+        /* o = scale * S^T qn (post-update state) */
+        if (g_mutation != 4) {
+          for (int32_t j = 0; j < V; ++j) {
+            float acc = 0.0f;
+            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
+            ov[j] = (g_mutation == 7 ? scale * scale : scale) * acc;
+          }
+        }
+
+        /* store this token's state to its snapshot slot */
+        const int32_t dst_slot = g_mutation == 10 ? slot_ids[(int64_t)r * n_rows] : slot_ids[rho];
+        const int64_t offt = state_offset(dst_slot, h, H, K, V);
+        for (int64_t e = 0; e < (int64_t)K * V; ++e) {
+          if (pool_kind == KDAO_POOL_F32)
+            pf[offt + e] = S[e];
+          else
+            ph[offt + e] = kdao_f32_to_f16_rne(S[e]);
+        }
+      }
+    }
+  }
+  free(S); free(qn); free(kn); free(a); free(w); free(u);
+  return KDAO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp64 twin of the same loop                                               */
+/* ------------------------------------------------------------------------ */
+
+int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
+                  int32_t V, const int32_t* slot_ids, int32_t n_req,
+                  int32_t n_rows, const float* q, const float* k,
+                  const float* v, const float* g, const float* b,
+                  double scale, double* out) {
+  if (!check_args(pool, n_slots, H, K, V, slot_ids, n_req, n_rows, q, k, v, g,
+                  b, out))
+    return KDAO_EARG;
+
+  const double eps = 1e-6;
+  double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
+  double* qn = (double*)malloc(sizeof(double) * (size_t)K);
+  double* kn = (double*)malloc(sizeof(double) * (size_t)K);
+  double* a = (double*)malloc(sizeof(double) * (size_t)K);
+  double* w = (double*)malloc(sizeof(double) * (size_t)V);
+  double* u = (double*)malloc(sizeof(double) * (size_t)V);
+  if (!S || !qn || !kn || !a || !w || !u) {
+    free(S); free(qn); free(kn); free(a); free(w); free(u);
+    return KDAO_EARG;
+  }
+
+  for (int32_t r = 0; r < n_req; ++r) {
+    for (int32_t h = 0; h < H; ++h) {
+      const int64_t off0 = state_offset(slot_ids[(int64_t)r * n_rows], h, H, K, V);
+      for (int64_t e = 0; e < (int64_t)K * V; ++e) S[e] = pool[off0 + e];
+
+      for (int32_t t = 0; t < n_rows; ++t) {
+        const int64_t rho = (int64_t)r * n_rows + t;
+        if (g_mutation == 9 && t > 0)
+          for (int64_t e = 0; e < (int64_t)K * V; ++e) S[e] = pool[off0 + e];
+        const float* qv = q + (rho * H + h) * K;
+        const float* kv = k + (rho * H + h) * K;
+        const float* gv = g + (rho * H + h) * K;
+        const float* vv = v + (rho * H + h) * V;
+        const double bv = (double)b[rho * H + h];
+        double* ov = out + (rho * H + h) * V;
+
+        double sq = 0.0, sk = 0.0;
+        for (int32_t i = 0; i < K; ++i) sq = sq + (double)qv[i] * (double)qv[i];
+        for (int32_t i = 0; i < K; ++i) sk = sk + (double)kv[i] * (double)kv[i];
+        const double rq = g_mutation == 6 ? 1.0 / (sq + eps) : 1.0 / sqrt(sq + eps);
+        const double rk = 1.0 / sqrt(sk + eps);
+        for (int32_t i = 0; i < K; ++i) qn[i] = (double)qv[i] * rq;
+        for (int32_t i = 0; i < K; ++i) kn[i] = (double)kv[i] * rk;
+
+        for (int32_t i = 0; i < K; ++i)
+          a[i] = g_mutation == 1 ? 1.0 : (g_mutation == 8 ? exp(-(double)gv[i]) : exp((double)gv[i]));
+        const double beta = g_mutation == 11 ? 1.0 / (1.0 + exp(bv)) : 1.0 / (1.0 + exp(-bv));
+
+        for (int32_t i = 0; i < K; ++i)
+          for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
+
+        if (g_mutation == 4) {
+          for (int32_t j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
+            ov[j] = scale * acc;
+          }
+        }
+
+        for (int32_t j = 0; j < V; ++j) {
+          double acc = 0.0;
+          for (int32_t i = 0; i < K; ++i) {
+            const double s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
+            acc = acc + kn[i] * s;
+          }
+          w[j] = acc;
+        }
+        for (int32_t j = 0; j < V; ++j)
+          u[j] = g_mutation == 2 ? (double)vv[j] + w[j] : (double)vv[j] - w[j];
+
+        for (int32_t i = 0; i < K; ++i) {
+          const double bk = g_mutation == 5 ? kn[i] : beta * kn[i];
+          for (int32_t j = 0; j < V; ++j)
+            S[(int64_t)i * V + j] = S[(int64_t)i * V + j] + bk * u[j];
+        }
+
+        if (g_mutation != 4) {
+          for (int32_t j = 0; j < V; ++j) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
+            ov[j] = (g_mutation == 7 ? scale * scale : scale) * acc;
+          }
+        }
+
+        const int32_t dst_slot = g_mutation == 10 ? slot_ids[(int64_t)r * n_rows] : slot_ids[rho];
+        const int64_t offt = state_offset(dst_slot, h, H, K, V);
+        for (int64_t e = 0; e < (int64_t)K * V; ++e) pool[offt + e] = S[e];
+      }
+    }
+  }
+  free(S); free(qn); free(kn); free(a); free(w); free(u);
+  return KDAO_OK;
+}

@@ -1,0 +1,115 @@
+/*
+ * kda_oracle.h -- CPU oracle for the KDA (Kimi Delta Attention) recurrent
+ * decode update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this code: only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark use it.  It shares no source, header, table
+ * or helper with the HIP library; both sides meet only through the seeded
+ * inputs that the test harness hands to each.
+ *
+ * What it computes (one decode launch over a host copy of the state pool):
+ *
+ *   for each request r and head h:
+ *     S = widen(pool[slot(r, 0)][h])                  -- exact widening
+ *     for each of the request's rows t (tokens, in order):
+ *       qn = q / sqrt(sum q^2 + eps), kn likewise      -- in-kernel L2 norm
+ *       a_i = exp(g_i), beta = 1 / (1 + exp(-b))      -- decay, sigmoid gate
+ *       S'  = diag(a) S
+ *       u   = v - S'^T kn
+ *       S   = S' + beta kn u^T
+ *       o   = scale * S^T qn                           -- post-update state
+ *       pool[slot(r, t)][h] = narrow(S)                -- identity or RNE fp16
+ *
+ * Sources (page title, then section):
+ *  - ROCm/ATOM PR #2945 (gfx950 mono K1 on an fp16 KDA state pool),
+ *    Summary and Changes: every loaded state is widened to fp32, the
+ *    recurrence runs in fp32, every stored state is rounded to fp16 to
+ *    nearest even; one address function serves the initial state and each
+ *    token's snapshot slot.  Limitations: k is L2-normalised, beta lies in
+ *    (0, 1), the decay is at most 1.
+ *  - ROCm/ATOM PR #2130 "perf(kimi-k3): make the KDA temporal state dtype
+ *    configurable", What: a [12, 128, 128] state per layer per token; q and
+ *    k are L2-normalised in-kernel; the recurrence accumulates in fp32
+ *    whatever the pool stores.  Copilot review: the fused sigmoid gating
+ *    kernel takes the pool as its initial state.
+ * The equations themselves (decay, delta correction, read-out after the
+ * update) are the standard KDA / gated-delta-rule decode step that these
+ * pages build on; the pages corroborate each ingredient but print none.
+ *
+ * Readings where the pages are silent: eps = 1e-6 added to the sum of
+ * squares; the read-out uses the post-update state; beta is one scalar per
+ * (row, head); a multi-row request chains its tokens through the fp32 state
+ * and rounds only the stores; the initial state comes from the request's
+ * row-0 slot.
+ *
+ * Precision: the pages fix the recurrence at fp32, so kdao_step_f32 is the
+ * pages' precision (sequential sums, no fused multiply-add: build with
+ * -ffp-contract=off).  kdao_step_f64 is the same loop in fp64, used as the
+ * near-exact reference and for drift reports.
+ */
+#ifndef KDA_ORACLE_H
+#define KDA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Pool element kinds understood by the oracle (its own numbering). */
+#define KDAO_POOL_F32 0
+#define KDAO_POOL_F16 1
+
+/* Return codes. */
+#define KDAO_OK 0
+#define KDAO_EARG 1 /* bad argument (null pointer, bad size, bad slot id) */
+
+/* IEEE 754 binary32 -> binary16, round to nearest, ties to even.  Overflow
+ * gives +-inf, NaN stays NaN (quiet, payload truncated), subnormal results
+ * are produced, never flushed. */
+uint16_t kdao_f32_to_f16_rne(float x);
+/* IEEE 754 binary16 -> binary32, exact. */
+float kdao_f16_to_f32(uint16_t h);
+void kdao_f32_to_f16_rne_array(const float* x, uint16_t* h, int64_t n);
+void kdao_f16_to_f32_array(const uint16_t* h, float* x, int64_t n);
+
+/*
+ * One decode launch, fp32 recurrence.
+ *   pool       host pool [n_slots, H, K, V] (V fastest), element kind
+ *              pool_kind (float for F32, uint16_t fp16 bits for F16).
+ *              Updated in place: row t of request r writes its post-update
+ *              state to slot slot_ids[r * n_rows + t]; the initial state is
+ *              read from slot slot_ids[r * n_rows].  Slots not named are
+ *              untouched.
+ *   slot_ids   [n_req * n_rows], distinct, each in [0, n_slots).
+ *   q, k, g    [n_req * n_rows, H, K]; v [.., H, V]; b [.., H]; fp32.
+ *   out        [n_req * n_rows, H, V] fp32.
+ * Returns KDAO_OK or KDAO_EARG (no partial writes on KDAO_EARG).
+ */
+int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
+                  int32_t K, int32_t V, const int32_t* slot_ids,
+                  int32_t n_req, int32_t n_rows, const float* q,
+                  const float* k, const float* v, const float* g,
+                  const float* b, float scale, float* out);
+
+/* The same loop carried out in fp64 on an fp64 pool (inputs widened). */
+int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
+                  int32_t V, const int32_t* slot_ids, int32_t n_req,
+                  int32_t n_rows, const float* q, const float* k,
+                  const float* v, const float* g, const float* b,
+                  double scale, double* out);
+
+/*
+ * Planted-mistake switch, for the tests that show the pins catch a wrong
+ * oracle.  0 = none (default).  Any other value changes one term of
+ * kdao_step_f32 / kdao_step_f64 (see kda_oracle.c).  Never set outside those
+ * tests.
+ */
+void kdao_set_mutation(int which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_ORACLE_H */

@@ -1,0 +1,149 @@
+"""ctypes front end of the C oracle (oracle/kda_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Every function works on host NumPy arrays; the
+pool arrays are updated in place exactly as one decode launch would update
+the device pool.  What the loop computes, and which page passage each step
+follows, is written out in kda_oracle.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+POOL_F32 = 0
+POOL_F16 = 1
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load oracle/libkda_oracle.so, compiling it first if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    c_f = ctypes.POINTER(ctypes.c_float)
+    c_d = ctypes.POINTER(ctypes.c_double)
+    c_i = ctypes.POINTER(ctypes.c_int32)
+    c_u16 = ctypes.POINTER(ctypes.c_uint16)
+    L.kdao_f32_to_f16_rne.argtypes = [ctypes.c_float]
+    L.kdao_f32_to_f16_rne.restype = ctypes.c_uint16
+    L.kdao_f16_to_f32.argtypes = [ctypes.c_uint16]
+    L.kdao_f16_to_f32.restype = ctypes.c_float
+    L.kdao_f32_to_f16_rne_array.argtypes = [c_f, c_u16, ctypes.c_int64]
+    L.kdao_f32_to_f16_rne_array.restype = None
+    L.kdao_f16_to_f32_array.argtypes = [c_u16, c_f, ctypes.c_int64]
+    L.kdao_f16_to_f32_array.restype = None
+    i32 = ctypes.c_int32
+    L.kdao_step_f32.argtypes = [ctypes.c_void_p, ctypes.c_int, i32, i32, i32, i32,
+                                c_i, i32, i32, c_f, c_f, c_f, c_f, c_f,
+                                ctypes.c_float, c_f]
+    L.kdao_step_f32.restype = ctypes.c_int
+    L.kdao_step_f64.argtypes = [c_d, i32, i32, i32, i32, c_i, i32, i32,
+                                c_f, c_f, c_f, c_f, c_f, ctypes.c_double, c_d]
+    L.kdao_step_f64.restype = ctypes.c_int
+    L.kdao_set_mutation.argtypes = [ctypes.c_int]
+    L.kdao_set_mutation.restype = None
+    _lib = L
+    return L
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def f32_to_f16_rne(x: np.ndarray) -> np.ndarray:
+    """binary32 -> binary16 bits (uint16), round to nearest even."""
+    x = _f32(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().kdao_f32_to_f16_rne_array(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def f16_to_f32(h: np.ndarray) -> np.ndarray:
+    """binary16 bits (uint16) -> binary32, exact."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().kdao_f16_to_f32_array(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_float), h.size)
+    return out
+
+
+def _check_inputs(pool, slot_ids, q, k, v, g, b, n_rows):
+    n_slots, H, K, V = pool.shape
+    slot_ids = np.ascontiguousarray(slot_ids, dtype=np.int32).reshape(-1)
+    R = slot_ids.size
+    if R % n_rows:
+        raise ValueError("slot_ids length %d is not a multiple of n_rows %d" % (R, n_rows))
+    q, k, v, g, b = (_f32(x) for x in (q, k, v, g, b))
+    if q.shape != (R, H, K) or k.shape != (R, H, K) or g.shape != (R, H, K):
+        raise ValueError("q, k, g must be [R, H, K]")
+    if v.shape != (R, H, V):
+        raise ValueError("v must be [R, H, V]")
+    if b.shape != (R, H):
+        raise ValueError("b must be [R, H]")
+    return (n_slots, H, K, V), slot_ids, q, k, v, g, b
+
+
+def step_f32(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
+             scale: float | None = None) -> np.ndarray:
+    """One decode launch in fp32 on a host pool (float32 or uint16 fp16 bits,
+    shape [n_slots, H, K, V]), updated in place.  Returns out [R, H, V]."""
+    if not pool.flags["C_CONTIGUOUS"]:
+        raise ValueError("pool must be C-contiguous")
+    if pool.dtype == np.float32:
+        kind = POOL_F32
+    elif pool.dtype == np.uint16:
+        kind = POOL_F16
+    else:
+        raise TypeError("oracle pool must be float32 or uint16 (fp16 bits)")
+    (n_slots, H, K, V), slot_ids, q, k, v, g, b = _check_inputs(pool, slot_ids, q, k, v, g, b, n_rows)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    R = slot_ids.size
+    out = np.zeros((R, H, V), dtype=np.float32)
+    rc = lib().kdao_step_f32(pool.ctypes.data, kind, n_slots, H, K, V,
+                             _ptr(slot_ids, ctypes.c_int32), R // n_rows, n_rows,
+                             _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                             _ptr(v, ctypes.c_float), _ptr(g, ctypes.c_float),
+                             _ptr(b, ctypes.c_float), float(scale),
+                             _ptr(out, ctypes.c_float))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (code %d)" % rc)
+    return out
+
+
+def step_f64(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
+             scale: float | None = None) -> np.ndarray:
+    """The same launch in fp64 on a float64 host pool, updated in place."""
+    if pool.dtype != np.float64 or not pool.flags["C_CONTIGUOUS"]:
+        raise TypeError("fp64 oracle pool must be a C-contiguous float64 array")
+    (n_slots, H, K, V), slot_ids, q, k, v, g, b = _check_inputs(pool, slot_ids, q, k, v, g, b, n_rows)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    R = slot_ids.size
+    out = np.zeros((R, H, V), dtype=np.float64)
+    rc = lib().kdao_step_f64(_ptr(pool, ctypes.c_double), n_slots, H, K, V,
+                             _ptr(slot_ids, ctypes.c_int32), R // n_rows, n_rows,
+                             _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                             _ptr(v, ctypes.c_float), _ptr(g, ctypes.c_float),
+                             _ptr(b, ctypes.c_float), float(scale),
+                             _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (code %d)" % rc)
+    return out
+
+
+def set_mutation(which: int) -> None:
+    """Plant one mistake in the oracle (tests of the pins only); 0 clears."""
+    lib().kdao_set_mutation(int(which))
