@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--dtype f32|f16]
+                    [--no-extras] [--no-cpu-baseline]
+
+A step is one decode launch over the batched workload: 64 request slots
+gathered by a random permutation from a 96-slot pool, one token each, H = 12
+heads of K = V = 128 (fp32 pool by default, fp16 with --dtype f16).  Every
+step's state is read from and written back to the pool in HBM.  Successive
+steps rotate over enough distinct pool copies (>= 1 GiB in all) that the
+256 MB last-level cache cannot hold the state between visits, as in a model
+whose 69 KDA layers each stream their own pool.
+
+Prints ONE JSON line.  value = state GB/s (state bytes read + written per
+step / wall time per step, timed region bracketed by synchronisations);
+roofline = algorithmic bytes of one launch / its average duration measured
+with HIP events on the launch stream, against the 8 TB/s HBM peak; traffic =
+hardware byte counters of the committed rocprofv3 summary when it was taken
+on this kernel source, else null; cpu_baseline = the CPU oracle timed on a
+bounded sample of the same workload.  Extra keys report the other workloads
+(fp16 pool, 8 x 8 speculative rows, a 69-layer step) and a plain-copy
+bandwidth probe.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # AMD MI355X published HBM3E bandwidth
+PEAK_SOURCE = "AMD MI355X spec: 8 TB/s HBM3E"
+# The pages' production kernel on this workload (fp32 state, H=12, K=V=128,
+# N=64, at its fp32 V-block cap of 32): 24.6 us, i.e. 4092 GB/s of state.
+PAGES_FP32_US = 24.6
+PAGES_FP16_US = 16.1
+KERNEL_SRC = os.path.join(ROOT, "kda_gated_delta_decode_amd", "csrc", "kda_decode.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_decode_tile_pmc_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--dtype", choices=["f32", "f16"], default="f32")
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Workload:
+    """Device buffers for one decode workload, with rotating pool copies."""
+
+    def __init__(self, inp, min_rotation_bytes: int, torch):
+        self.inp = inp
+        dev = torch.device("cuda", 0)
+        import numpy as np
+        host_pool = inp.pool if inp.dtype == "f32" else inp.pool.view(np.float16)
+        pool_bytes = host_pool.nbytes
+        n_copies = max(1, math.ceil(min_rotation_bytes / pool_bytes))
+        first = torch.from_numpy(host_pool).to(dev)
+        self.pools = [first] + [first.clone() for _ in range(n_copies - 1)]
+        self.ids = torch.from_numpy(inp.slot_ids).to(dev)
+        self.q, self.k, self.v, self.g, self.b = (torch.from_numpy(getattr(inp, n)).to(dev)
+                                                  for n in ("q", "k", "v", "g", "b"))
+        R, H, V = inp.slot_ids.size, inp.pool.shape[1], inp.pool.shape[3]
+        self.out = torch.empty((R, H, V), dtype=torch.float32, device=dev)
+        self.rotation_bytes = pool_bytes * n_copies
+
+    def launch(self, i: int, B):
+        B.kda_decode_step(self.pools[i % len(self.pools)], self.ids, self.q, self.k, self.v,
+                          self.g, self.b, self.out, n_rows_per_slot=self.inp.n_rows,
+                          scale=self.inp.scale)
+
+
+def time_launches(fn, steps: int, warmup: int, torch):
+    """Wall time per step over `steps` back-to-back launches, and the mean
+    of per-launch HIP-event durations (events on the launch stream)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    region_ms = start.elapsed_time(end)
+    # per-launch durations, a second pass bracketed the same way
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record()
+        fn(warmup + steps + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) for a, b in evs)
+    return {
+        "ms_per_step": region_ms / steps,
+        "host_ms_per_step": wall_ms / steps,
+        "launch_ms_mean": sum(durs) / len(durs),
+        "launch_ms_p10": durs[len(durs) // 10],
+        "launch_ms_p50": durs[len(durs) // 2],
+        "launch_ms_p90": durs[(9 * len(durs)) // 10],
+    }
+
+
+def pmc_traffic(expected_launch_key: str):
+    """Traffic from the committed counter summary, if it was taken on the
+    current kernel source for this launch; else None."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = s.get("launches", {}).get(expected_launch_key)
+    if entry is None or s.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, seconds: float):
+    """Time the CPU oracle (fp32 loop, one thread) on a bounded sample of the
+    workload: whole oracle launches over the first 8 requests, repeated until
+    `seconds` have passed."""
+    from oracle import kda_oracle
+    n_req = min(8, inp.n_req)
+    rows = n_req * inp.n_rows
+    sel = slice(0, rows)
+    pool = inp.pool.copy()
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        kda_oracle.step_f32(pool, inp.slot_ids[sel], inp.q[sel], inp.k[sel], inp.v[sel],
+                            inp.g[sel], inp.b[sel], n_rows=inp.n_rows, scale=inp.scale)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    H, K, V = inp.pool.shape[1:]
+    elem = 4 if inp.dtype == "f32" else 2
+    state_bytes = calls * n_req * H * K * V * elem * (1 + inp.n_rows)
+    return {
+        "value": state_bytes / el / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d oracle launches of %d of the %d requests x %d heads (%s pool, %d row(s)), %.1f s"
+                  % (calls, n_req, inp.n_req, H, inp.dtype, inp.n_rows, el),
+        "us_per_full_step": el / calls * (inp.n_req / n_req) * 1e6,
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path has no cross-GPU exchange and this build "
+              "runs on a single MI355X; --gpus %d is not supported (use --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import kda_inputs
+    from kda_gated_delta_decode_amd import binding as B
+
+    B.library()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+
+    ROT = 1 << 30
+    main_inp = kda_inputs.batched_f32(0) if args.dtype == "f32" else kda_inputs.batched_f16(0)
+    wl = Workload(main_inp, ROT, torch)
+    log("workload:", main_inp.name, "rotation copies:", len(wl.pools))
+    t = time_launches(lambda i: wl.launch(i, B), args.steps, args.warmup, torch)
+    state_bytes = main_inp.state_bytes()
+    alg_bytes = state_bytes + main_inp.io_bytes()
+    value = state_bytes / (t["ms_per_step"] * 1e-3) / 1e9
+    achieved = alg_bytes / (t["launch_ms_mean"] * 1e-3) / 1e9
+    desc = B.kda_describe_launch(main_inp.n_req, main_inp.n_rows, main_inp.pool.shape[1], main_inp.dtype)
+    launch_key = "%s_n%d_rows%d" % (main_inp.dtype, main_inp.n_req, main_inp.n_rows)
+    pages_us = PAGES_FP32_US if args.dtype == "f32" else PAGES_FP16_US
+    pages_gbs = state_bytes / (pages_us * 1e-6) / 1e9
+
+    rec = {
+        "metric": "KDA decode state GB/s (% of HBM peak) + us/step, H=12 K=V=128 N=64 fp16/fp32",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / pages_gbs, 3),
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": "batched KDA decode: 64 of 96 slots, 1 token each, H=12, K=V=128, %s state pool, "
+                        "pools rotated over %.2f GiB" % ("fp32" if args.dtype == "f32" else "fp16",
+                                                          wl.rotation_bytes / 2 ** 30),
+            "n_req": main_inp.n_req, "rows_per_req": main_inp.n_rows, "heads": 12, "K": 128, "V": 128,
+            "pool_slots": int(main_inp.pool.shape[0]), "state_dtype": args.dtype,
+            "launch": desc,
+        },
+        "us_per_step": round(t["ms_per_step"] * 1e3, 3),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "updates_per_s": main_inp.n_req * main_inp.n_rows * 12 / (t["ms_per_step"] * 1e-3),
+        "vs_baseline_basis": "the pages' production fused gating kernel at this workload: %.1f us "
+                             "(%.0f GB/s of state), MI355X context" % (pages_us, pages_gbs),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": pmc_traffic(launch_key),
+            "kernel": "kda_decode_tile",
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "launch_us_mean": round(t["launch_ms_mean"] * 1e3, 3),
+            "launch_us_p10_p50_p90": [round(t[k] * 1e3, 3) for k in ("launch_ms_p10", "launch_ms_p50", "launch_ms_p90")],
+            "peak_source": PEAK_SOURCE,
+        },
+        "device": dev_name,
+    }
+
+    if not args.no_extras:
+        extras = {}
+        # plain copy: the achievable streaming bandwidth, 1 GiB each way
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        tc = time_launches(lambda i: B.kda_copy_probe(dst, src), 20, 3, torch)
+        extras["copy_probe_1GiB"] = {"GB/s_read_plus_write": round(2 * n / (tc["launch_ms_mean"] * 1e-3) / 1e9, 1),
+                                     "us": round(tc["launch_ms_mean"] * 1e3, 2)}
+        del src, dst
+        rec["pct_of_copy_bandwidth"] = round(100.0 * achieved / extras["copy_probe_1GiB"]["GB/s_read_plus_write"], 2)
+        for name, fn in (("batched_f16" if args.dtype == "f32" else "batched_f32",
+                          kda_inputs.batched_f16 if args.dtype == "f32" else kda_inputs.batched_f32),
+                         ("spec_verify_f16", kda_inputs.spec_verify_f16)):
+            inp = fn(0)
+            w = Workload(inp, ROT, torch)
+            tt = time_launches(lambda i: w.launch(i, B), max(50, args.steps // 2), 10, torch)
+            sb, ab = inp.state_bytes(), inp.state_bytes() + inp.io_bytes()
+            extras[name] = {
+                "workload": inp.name, "us_per_step": round(tt["ms_per_step"] * 1e3, 3),
+                "launch_us_mean": round(tt["launch_ms_mean"] * 1e3, 3),
+                "state_GB/s": round(sb / (tt["ms_per_step"] * 1e-3) / 1e9, 1),
+                "algorithmic_GB/s_per_launch": round(ab / (tt["launch_ms_mean"] * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(ab / (tt["launch_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            del w
+        # a 69-layer decode step: 69 independent 64-slot pools, one launch each
+        for dt in ("f32", "f16"):
+            extras["layers69_" + dt] = layers69(dt, B, torch, steps=10, warmup=2)
+        rec["extras"] = extras
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(main_inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def layers69(dtype, B, torch, steps, warmup, n_layers=69):
+    """Time 69 back-to-back launches (one per layer pool of 64 slots, one
+    token each) as one decode step."""
+    import kda_inputs
+    H, n = 12, 64
+    tdt = torch.float32 if dtype == "f32" else torch.float16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    pools = []
+    for _ in range(n_layers):
+        p = torch.randn((n, H, 128, 128), generator=gen, device="cuda", dtype=torch.float32)
+        pools.append((p * 0.05).to(tdt))
+        del p
+    inp = kda_inputs.make_inputs("row inputs", n, n, 1, "f32", H=1, seed=0)  # only for ids
+    ids = torch.from_numpy(inp.slot_ids).cuda()
+    q = torch.randn((n, H, 128), generator=gen, device="cuda")
+    k = torch.randn((n, H, 128), generator=gen, device="cuda")
+    v = torch.randn((n, H, 128), generator=gen, device="cuda")
+    g = -torch.nn.functional.softplus(torch.randn((n, H, 128), generator=gen, device="cuda"))
+    b = torch.randn((n, H), generator=gen, device="cuda")
+    out = torch.empty((n, H, 128), device="cuda")
+
+    def one_step(_i):
+        for p in pools:
+            B.kda_decode_step(p, ids, q, k, v, g, b, out)
+    tt = time_launches(one_step, steps, warmup, torch)
+    elem = 4 if dtype == "f32" else 2
+    state = n_layers * n * H * 128 * 128 * elem * 2
+    io = n_layers * n * H * (3 * 128 + 2 * 128 + 1) * 4
+    res = {"us_per_step": round(tt["ms_per_step"] * 1e3, 1),
+           "state_GB/s": round(state / (tt["ms_per_step"] * 1e-3) / 1e9, 1),
+           "algorithmic_bytes": state + io,
+           "frac_of_peak": round((state + io) / (tt["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del pools
+    torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()

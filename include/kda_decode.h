@@ -1,0 +1,239 @@
+/*
+ * kda_decode.h -- C ABI of the MI355X (gfx950) KDA recurrent decode library.
+ *
+ * The operation (Kimi Delta Attention decode, one launch):
+ *   for each request r, head h, and each of the request's rows t in order,
+ *   with the state S of (r, h) held in fp32 between rows:
+ *     qn = q / sqrt(|q|^2 + 1e-6),  kn = k / sqrt(|k|^2 + 1e-6)
+ *     a  = exp(g)  (per key channel),  beta = 1 / (1 + exp(-b))
+ *     S' = diag(a) S;  u = v - S'^T kn;  S = S' + beta kn u^T
+ *     o  = scale * S^T qn
+ *     state_at(r, t) <- S   (fp32 as is, or fp16 rounded to nearest even)
+ *   The first row's initial state is read from state_at(r, 0).
+ *
+ * Passages this follows (page title, then section):
+ *  - ROCm/ATOM PR #2945 (gfx950 mono K1 takes an fp16 KDA state pool),
+ *    Summary and Changes: the pool's dtype is a build constant of the
+ *    kernel; each loaded state is widened to fp32, the recurrence runs in
+ *    fp32, each stored state is rounded to fp16 to nearest even; one address
+ *    function, state_at, serves the request's initial state and every
+ *    token's snapshot slot; a pool of the other dtype is refused (it would
+ *    be read at the wrong element size); bf16 is refused, not reinterpreted.
+ *    Limitations: k is unit after normalisation, beta in (0, 1), decay <= 1.
+ *  - ROCm/ATOM PR #2130 "perf(kimi-k3): make the KDA temporal state dtype
+ *    configurable", What: a [12, 128, 128] state per layer streams through
+ *    HBM every decode token (state-bandwidth bound); q and k are
+ *    L2-normalised in-kernel; the recurrence accumulates in fp32 whatever
+ *    the pool stores.  Copilot review: the initial state must be validated
+ *    early instead of being dereferenced when absent.
+ *
+ * Conventions for every function:
+ *  - Return value: KDA_OK (0) or a kda_status code; kda_strerror() names it.
+ *    Functions returning a size or offset return a negative kda_status on
+ *    error instead.
+ *  - Arguments are validated on the host before any HIP call; a refused call
+ *    changes nothing and launches nothing.
+ *  - The caller owns every buffer.  The library allocates no memory, never
+ *    synchronises, and enqueues its work on the caller's stream (a
+ *    hipStream_t passed as void*, NULL = the null stream).  A device fault
+ *    surfaces at the caller's next synchronisation.
+ */
+#ifndef KDA_DECODE_H
+#define KDA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
+#define KDA_HEAD_K 128
+#define KDA_HEAD_V 128
+/* Rows (tokens) one request may chain in one launch: 1 + up to 7 drafts. */
+#define KDA_MAX_ROWS 8
+
+/* Element type of a state pool. */
+typedef enum kda_dtype {
+  KDA_F32 = 0,
+  KDA_F16 = 1,
+  KDA_BF16 = 2 /* named only to be refused */
+} kda_dtype;
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,           /* a required pointer is NULL */
+  KDA_ERR_DTYPE_REFUSED = 2,  /* bf16 or an unknown dtype */
+  KDA_ERR_DTYPE_MISMATCH = 3, /* state_dtype differs from the pool's dtype */
+  KDA_ERR_SHAPE = 4,          /* K or V != 128, H < 1, n_slots < 1 */
+  KDA_ERR_ROWS = 5,           /* rows per request outside [1, KDA_MAX_ROWS] */
+  KDA_ERR_SLOT = 6,           /* slot id out of range or repeated, or more
+                                 rows than slots */
+  KDA_ERR_ALIGN = 7,          /* a device pointer is not 16-byte aligned */
+  KDA_ERR_ARG = 8,            /* other bad argument (negative count, index
+                                 out of range, non-finite scale) */
+  KDA_ERR_LAUNCH = 9          /* the HIP runtime reported a launch error */
+} kda_status;
+
+/*
+ * A state pool: device memory holding [n_slots, H, K, V] elements of dtype,
+ * row-major with V fastest, i.e. slot s, head h, key row i, value column j
+ * lives at element ((s * H + h) * K + i) * V + j.  base must be 16-byte
+ * aligned.  The caller allocates, owns and frees it.
+ */
+typedef struct kda_pool {
+  void* base;
+  int32_t n_slots;
+  int32_t H;
+  int32_t K;
+  int32_t V;
+  kda_dtype dtype;
+} kda_pool;
+
+/*
+ * kda_decode_step -- one decode launch over n_req requests of
+ * n_rows_per_slot rows each (R = n_req * n_rows_per_slot rows in all).
+ *
+ *  pool        the state pool (dtype F32 or F16), updated in place.
+ *  slot_ids    device int32 [R]: row t of request r uses slot
+ *              slot_ids[r * n_rows_per_slot + t] (see kda_state_at).  The
+ *              ids of one launch must be distinct and in [0, n_slots):
+ *              kda_validate checks a host copy.  On the device, a request
+ *              with any id out of range is skipped: its out rows are set to
+ *              NaN and no state is read or written.  Repeated ids are not
+ *              detected on the device and give an unspecified result.
+ *  q, k, g     device fp32 [R, H, 128]; v: device fp32 [R, H, 128];
+ *  b           device fp32 [R, H]; rows of one request are adjacent.
+ *              g is the log-decay (a = exp(g)); callers keep g <= 0.
+ *  out         device fp32 [R, H, 128], written.
+ *  state_dtype the dtype the caller built for; must equal pool->dtype.
+ *  scale       read-out scale, usually 1/sqrt(128).  Must be finite.
+ *  stream      hipStream_t as void*, NULL for the null stream.
+ *
+ * All device pointers must be 16-byte aligned (slot_ids and b: 4-byte).
+ * n_req == 0 is a valid no-op, and then only the pool must be non-NULL.
+ * Checks run in the order: pool NULL, DTYPE_REFUSED, DTYPE_MISMATCH,
+ * SHAPE, ROWS, ARG (counts), SLOT, then the row buffers' NULL, ARG (scale,
+ * opts), ALIGN.  Errors: KDA_ERR_NULL, KDA_ERR_DTYPE_REFUSED,
+ * KDA_ERR_DTYPE_MISMATCH, KDA_ERR_SHAPE, KDA_ERR_ROWS, KDA_ERR_SLOT (more
+ * rows than slots), KDA_ERR_ALIGN, KDA_ERR_ARG, KDA_ERR_LAUNCH.
+ */
+int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
+                    const float* q, const float* k, const float* v,
+                    const float* g, const float* b, float* out, int32_t n_req,
+                    int32_t n_rows_per_slot, kda_dtype state_dtype,
+                    float scale, void* stream);
+
+/*
+ * Launch options of kda_decode_step_ex.  Zero-initialise for the library's
+ * defaults.  waves_per_tile: wavefronts that split one tile's 128 key rows,
+ * 0 (the library's choice) or 1, 2, 4, 8.  The choice changes the order of
+ * the fp32 column sums (so results may differ in the last bits), never the
+ * operation; fixing it fixes every result bit for given inputs.
+ */
+typedef struct kda_launch_opts {
+  int32_t waves_per_tile;
+} kda_launch_opts;
+
+/*
+ * kda_decode_step_ex -- kda_decode_step with launch options (opts may be
+ * NULL for the defaults).  For tests that must hold the summation order
+ * fixed across launches and for tuning sweeps.  Additional error:
+ * KDA_ERR_ARG for a waves_per_tile outside {0, 1, 2, 4, 8}.
+ */
+int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
+                       const float* q, const float* k, const float* v,
+                       const float* g, const float* b, float* out,
+                       int32_t n_req, int32_t n_rows_per_slot,
+                       kda_dtype state_dtype, float scale,
+                       const kda_launch_opts* opts, void* stream);
+
+/*
+ * kda_validate -- host-side check of a launch's arguments and slot table
+ * (ROCm/ATOM PR #2945, Changes: the step checks the pool's dtype against
+ * the build; anything but fp32 or fp16 is refused).  slot_ids_host is a
+ * HOST copy of the slot table [n_req * n_rows]; every id must lie in
+ * [0, n_slots) and appear once.  Touches no device memory.  Returns KDA_OK
+ * or the first error found, in the order: NULL, DTYPE_REFUSED,
+ * DTYPE_MISMATCH, SHAPE, ROWS, ARG, SLOT.
+ */
+int kda_validate(const kda_pool* pool, const int32_t* slot_ids_host,
+                 int32_t n_req, int32_t n_rows, kda_dtype state_dtype);
+
+/*
+ * kda_state_at -- element offset, from pool->base, of the [H, K, V] block
+ * that row `row` of request `req` reads or writes (ROCm/ATOM PR #2945,
+ * Changes: one address function for the initial state and every token's
+ * snapshot slot).  Head h's [K, V] state follows at + h * K * V.  Row 0's
+ * block is also the request's initial state.  slot_ids_host is a host copy
+ * of the slot table.  Returns a negative kda_status on error.
+ */
+int64_t kda_state_at(const kda_pool* pool, const int32_t* slot_ids_host,
+                     int32_t n_rows, int32_t req, int32_t row);
+
+/*
+ * kda_pool_bytes -- bytes of a pool of n_slots slots of [H, K, V] elements
+ * of dtype: every size derives from the one dtype decision (ROCm/ATOM PR
+ * #2130, What and Memory).  Returns 0 for a refused dtype or a bad size.
+ */
+size_t kda_pool_bytes(int32_t n_slots, int32_t H, int32_t K, int32_t V,
+                      kda_dtype dtype);
+
+/*
+ * kda_tile_bv -- value columns per state tile for a pool dtype: 32 for a
+ * 4-byte state, 64 for a 2-byte one, so that a tile row is one 128-byte line
+ * whatever the element size (compare ROCm/ATOM PR #2130, What and Copilot
+ * review: a 2-byte state wants twice the V per block to keep the same bytes
+ * in flight).  Returns a negative kda_status for a refused dtype.
+ */
+int32_t kda_tile_bv(kda_dtype dtype);
+
+/* Launch shape kda_decode_step uses for a given problem (host only). */
+typedef struct kda_launch_desc {
+  int32_t bv;              /* value columns per tile */
+  int32_t waves_per_tile;  /* wavefronts that split one tile's K rows */
+  int32_t threads;         /* threads per workgroup */
+  int32_t tiles;           /* n_req * H * (V / bv) */
+  int32_t blocks;          /* workgroups launched */
+  int32_t lds_bytes;       /* static LDS per workgroup */
+  const char* kernel;      /* kernel symbol family name */
+} kda_launch_desc;
+
+/* Fills *desc for (n_req, n_rows, H, dtype) under opts (NULL = defaults).
+ * Errors: KDA_ERR_NULL, KDA_ERR_DTYPE_REFUSED, KDA_ERR_SHAPE (H < 1),
+ * KDA_ERR_ROWS, KDA_ERR_ARG. */
+int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H,
+                        kda_dtype dtype, const kda_launch_opts* opts,
+                        kda_launch_desc* desc);
+
+/*
+ * kda_tile_of_block -- the tile a workgroup processes.  Workgroups are
+ * handed to the 8 XCDs of the chip round-robin; this maps them so that the
+ * workgroups one XCD runs hold consecutive tiles (the tiles of one
+ * (request, head) share that XCD's L2 for q, k, g).  A bijection of
+ * [0, n_blocks).  Returns -1 for block out of range.
+ */
+int32_t kda_tile_of_block(int32_t block, int32_t n_blocks);
+
+/*
+ * kda_copy_probe -- measurement helper: copies `bytes` (a multiple of 16)
+ * from src to dst with a plain streaming kernel of the same load/store
+ * width as the decode kernel, on `stream`.  Used to calibrate achievable
+ * bandwidth and hardware byte counters.  Both pointers 16-byte aligned.
+ */
+int kda_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Message for a kda_status code (static string, never NULL). */
+const char* kda_strerror(int code);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_DECODE_H */

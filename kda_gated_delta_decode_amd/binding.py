@@ -1,0 +1,257 @@
+"""Python binding of the KDA decode C ABI (include/kda_decode.h).
+
+Argument marshalling only: every entry point here turns torch tensors (for
+device buffers), NumPy arrays (for host tables) and Python numbers into the
+C call of the same name, and raises KdaError on a non-zero status.  All
+arithmetic of the decode update runs in the library's gfx950 kernels; there
+is no fallback path.  If libkda_decode.so has not been built, the first call
+raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda_decode.so")
+
+# kda_dtype
+KDA_F32 = 0
+KDA_F16 = 1
+KDA_BF16 = 2
+_UNKNOWN_DTYPE = 99  # what a dtype the ABI does not name is passed as
+
+# kda_status
+KDA_OK = 0
+KDA_ERR_NULL = 1
+KDA_ERR_DTYPE_REFUSED = 2
+KDA_ERR_DTYPE_MISMATCH = 3
+KDA_ERR_SHAPE = 4
+KDA_ERR_ROWS = 5
+KDA_ERR_SLOT = 6
+KDA_ERR_ALIGN = 7
+KDA_ERR_ARG = 8
+KDA_ERR_LAUNCH = 9
+
+KDA_HEAD_K = 128
+KDA_HEAD_V = 128
+KDA_MAX_ROWS = 8
+
+
+class kda_pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("n_slots", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class kda_launch_opts(ctypes.Structure):
+    _fields_ = [("waves_per_tile", ctypes.c_int32)]
+
+
+class kda_launch_desc(ctypes.Structure):
+    _fields_ = [("bv", ctypes.c_int32), ("waves_per_tile", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("tiles", ctypes.c_int32),
+                ("blocks", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("kernel", ctypes.c_char_p)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        super().__init__("%s: %s (code %d)" % (where, kda_strerror(code), code))
+
+
+# The C symbols and their signatures, as include/kda_decode.h declares them.
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+SIGNATURES = {
+    "kda_decode_step": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P,
+                                       _I32, _I32, ctypes.c_int, ctypes.c_float, _P]),
+    "kda_decode_step_ex": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P,
+                                          _I32, _I32, ctypes.c_int, ctypes.c_float,
+                                          ctypes.POINTER(kda_launch_opts), _P]),
+    "kda_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _I32, _I32, ctypes.c_int]),
+    "kda_state_at": (ctypes.c_int64, [ctypes.POINTER(kda_pool), _P, _I32, _I32, _I32]),
+    "kda_pool_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, ctypes.c_int]),
+    "kda_tile_bv": (_I32, [ctypes.c_int]),
+    "kda_describe_launch": (ctypes.c_int, [_I32, _I32, _I32, ctypes.c_int,
+                                           ctypes.POINTER(kda_launch_opts),
+                                           ctypes.POINTER(kda_launch_desc)]),
+    "kda_tile_of_block": (_I32, [_I32, _I32]),
+    "kda_copy_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "kda_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "kda_abi_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libkda_decode.so (ImportError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libkda_decode.so is not built at %s; build it with "
+                          "`python -m kda_gated_delta_decode_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    if torch_dtype == torch.float32:
+        return KDA_F32
+    if torch_dtype == torch.float16:
+        return KDA_F16
+    if torch_dtype == torch.bfloat16:
+        return KDA_BF16
+    return _UNKNOWN_DTYPE
+
+
+def _dtype_arg(d) -> int:
+    if isinstance(d, (int, np.integer)):
+        return int(d)
+    if isinstance(d, str):
+        return {"f32": KDA_F32, "fp32": KDA_F32, "float32": KDA_F32, "f16": KDA_F16,
+                "fp16": KDA_F16, "float16": KDA_F16, "bf16": KDA_BF16,
+                "bfloat16": KDA_BF16}.get(d, _UNKNOWN_DTYPE)
+    return dtype_code(d)
+
+
+def make_pool(pool, dtype=None) -> kda_pool:
+    """kda_pool describing a device tensor [n_slots, H, K, V] (contiguous).
+    `dtype` overrides the element type the struct declares (default: the
+    tensor's own)."""
+    if not pool.is_contiguous():
+        raise ValueError("pool must be contiguous [n_slots, H, K, V]")
+    if pool.dim() != 4:
+        raise ValueError("pool must be 4-D [n_slots, H, K, V]")
+    n_slots, H, K, V = pool.shape
+    code = dtype_code(pool.dtype) if dtype is None else _dtype_arg(dtype)
+    return kda_pool(ctypes.c_void_p(pool.data_ptr()), n_slots, H, K, V, code)
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(code: int, where: str) -> None:
+    if code != KDA_OK:
+        raise KdaError(code, where)
+
+
+# ---------------------------------------------------------------------------
+# the entry points
+# ---------------------------------------------------------------------------
+
+def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1,
+                    state_dtype=None, scale: float | None = None, stream=None,
+                    waves_per_tile: int = 0, pool_dtype=None) -> None:
+    """One decode launch (see kda_decode_step in include/kda_decode.h).
+
+    pool: device tensor [n_slots, H, 128, 128], float32 or float16, updated
+    in place.  slot_ids: device int32 [R]; q, k, g: device float32 [R, H, 128];
+    v, out: [R, H, 128]; b: [R, H].  state_dtype defaults to the pool's
+    dtype; pool_dtype overrides what the pool struct declares (tests of the
+    refusals).  waves_per_tile != 0 selects kda_decode_step_ex."""
+    import torch
+    P = make_pool(pool, pool_dtype)
+    sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
+    R = slot_ids.numel()
+    if R % n_rows_per_slot != 0:
+        raise ValueError("slot_ids holds %d rows, not a multiple of %d" % (R, n_rows_per_slot))
+    n_req = R // n_rows_per_slot
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.shape[2])
+    args = (ctypes.byref(P), _dev(slot_ids, "slot_ids", torch.int32),
+            _dev(q, "q", torch.float32), _dev(k, "k", torch.float32), _dev(v, "v", torch.float32),
+            _dev(g, "g", torch.float32), _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
+            n_req, n_rows_per_slot, sd, float(scale))
+    if waves_per_tile:
+        opts = kda_launch_opts(int(waves_per_tile))
+        rc = library().kda_decode_step_ex(*args, ctypes.byref(opts), _stream_ptr(stream))
+        _check(rc, "kda_decode_step_ex")
+    else:
+        rc = library().kda_decode_step(*args, _stream_ptr(stream))
+        _check(rc, "kda_decode_step")
+
+
+def kda_validate(pool_desc: kda_pool, slot_ids_host, n_req: int, n_rows: int, state_dtype) -> int:
+    """Host-side validation; returns the kda_status code (0 = OK)."""
+    ids = np.ascontiguousarray(slot_ids_host, dtype=np.int32)
+    return int(library().kda_validate(ctypes.byref(pool_desc), ids.ctypes.data_as(ctypes.c_void_p),
+                                      n_req, n_rows, _dtype_arg(state_dtype)))
+
+
+def kda_state_at(pool_desc: kda_pool, slot_ids_host, n_rows: int, req: int, row: int) -> int:
+    """Element offset of the [H, K, V] block of (req, row); negative status on error."""
+    ids = np.ascontiguousarray(slot_ids_host, dtype=np.int32)
+    return int(library().kda_state_at(ctypes.byref(pool_desc), ids.ctypes.data_as(ctypes.c_void_p),
+                                      n_rows, req, row))
+
+
+def kda_pool_bytes(n_slots: int, H: int, K: int, V: int, dtype) -> int:
+    return int(library().kda_pool_bytes(n_slots, H, K, V, _dtype_arg(dtype)))
+
+
+def kda_tile_bv(dtype) -> int:
+    return int(library().kda_tile_bv(_dtype_arg(dtype)))
+
+
+def kda_describe_launch(n_req: int, n_rows: int, H: int, dtype, waves_per_tile: int = 0) -> dict:
+    d = kda_launch_desc()
+    opts = kda_launch_opts(int(waves_per_tile))
+    _check(library().kda_describe_launch(n_req, n_rows, H, _dtype_arg(dtype), ctypes.byref(opts),
+                                         ctypes.byref(d)), "kda_describe_launch")
+    return {"bv": d.bv, "waves_per_tile": d.waves_per_tile, "threads": d.threads,
+            "tiles": d.tiles, "blocks": d.blocks, "lds_bytes": d.lds_bytes,
+            "kernel": d.kernel.decode()}
+
+
+def kda_tile_of_block(block: int, n_blocks: int) -> int:
+    return int(library().kda_tile_of_block(block, n_blocks))
+
+
+def kda_copy_probe(dst, src, nbytes: int | None = None, stream=None) -> None:
+    """Device-to-device streaming copy of nbytes (default: all of src)."""
+    nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(library().kda_copy_probe(_dev(dst, "dst"), _dev(src, "src"), nb, _stream_ptr(stream)),
+           "kda_copy_probe")
+
+
+def kda_strerror(code: int) -> str:
+    return library().kda_strerror(int(code)).decode()
+
+
+def kda_abi_version() -> int:
+    return int(library().kda_abi_version())

@@ -1,0 +1,75 @@
+"""Build the KDA decode C-ABI library (libkda_decode.so) in-tree for gfx950.
+
+    python -m kda_gated_delta_decode_amd.build [-v]
+
+Compiles csrc/kda_decode.hip (kernels and launch entry points) and
+csrc/kda_host.cpp (validation, addressing, sizing) with hipcc into
+kda_gated_delta_decode_amd/libkda_decode.so.  Flags:
+  --offload-arch=gfx950          MI355X only
+  -ffp-contract=off              no implicit multiply-add fusion: every fused
+                                 multiply-add in the kernels is an explicit
+                                 fmaf, so fp32 and fp16 builds do identical
+                                 arithmetic
+  -target-feature -packed-fp32-ops   keep the compiler from forming packed
+                                 fp32 instructions
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkda_decode.so")
+SOURCES = [os.path.join(CSRC, "kda_decode.hip"), os.path.join(CSRC, "kda_host.cpp")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the KDA decode library needs ROCm's hipcc")
+
+
+def flags() -> list[str]:
+    return [
+        "--offload-arch=" + ARCH,
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        "-ffp-contract=off",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall",
+        "-I", INCLUDE,
+        "-I", CSRC,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always; a build check must compile).  Returns the
+    path of the .so.  The output is written atomically."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *flags(), *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so;
+    # that notice is expected and is filtered out of the log.
+    noise = ("packed-fp32-ops' is not a recognized feature", "argument unused during compilation")
+    log = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if not any(n in l for n in noise))
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, log))
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,518 @@
+// kda_decode.hip -- gfx950 (MI355X) kernels and launch entry points of the
+// KDA recurrent decode library.
+//
+// The update (one decode row of one request, per head; the state S is a
+// [K=128, V=128] fp32 matrix while it is in registers):
+//   S' = diag(exp(g)) S,  u = v - S'^T kn,  S = S' + beta kn u^T,
+//   o = scale * S^T qn,   with qn, kn the L2-normalised q, k and
+//   beta = sigmoid(b).
+// Pool handling follows ROCm/ATOM PR #2945 (Summary, Changes): the pool's
+// dtype is a build constant, loads widen to fp32, the recurrence is fp32,
+// fp16 stores round to nearest even, and one address function (state_at)
+// locates the initial state and every row's snapshot.  ROCm/ATOM PR #2130
+// (What) places the normalisation of q and k inside the kernel.
+//
+// Work decomposition.  A tile is (request, head, V-tile): all 128 key rows
+// by BV value columns, BV chosen so a tile row is one 128-byte line (32 fp32
+// or 64 fp16 columns).  Value columns are independent, so a tile needs no
+// data from any other tile.  Inside a wavefront, 8 lanes cover one tile row
+// with 16-byte loads; the 8 row groups of a wave each own a contiguous run
+// of rows.  Column sums over K are an in-lane sum over the lane's rows, then
+// an exchange across the row groups (lane bits 3..5: DPP row_ror:8, then the
+// gfx950 permlane16/permlane32 swaps), which leaves the same bits in every
+// lane.  With NW > 1 waves per tile the per-wave sums meet in LDS.
+//
+// The read-out uses o_j = scale * (qn . s'_j + beta (qn . kn) u_j), the same
+// quantity as scale * qn . s_j after the update (s_j = s'_j + beta kn u_j),
+// so one pass over S' gives both column sums and the stores need not wait
+// for a second reduction.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "kda_decode.h"
+#include "kda_internal.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+struct Args {
+  void* pool;
+  const int32_t* slot_ids;
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* g;
+  const float* b;
+  float* out;
+  int32_t n_slots;
+  int32_t H;
+  int32_t n_rows;
+  int32_t n_vt;  // V-tiles per head
+  float scale;
+};
+
+using f2 = float __attribute__((ext_vector_type(2)));
+using f4 = float __attribute__((ext_vector_type(4)));
+using h8 = _Float16 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums.  Each returns x_i + x_(i xor m) in lane i: the same two
+// operands in every lane of a pair, so all lanes of a group end with
+// identical bits after the full butterfly.
+// ---------------------------------------------------------------------------
+
+// DPP controls (GCN/CDNA encoding): quad_perm selectors, row_half_mirror,
+// row_ror:8 (a rotate by 8 inside a 16-lane row is the xor-8 partner).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor3 = 0x1B;     // quad_perm [3,2,1,0]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float sum_xor1(float x) { return x + dpp<kDppQuadXor1>(x); }
+__device__ __forceinline__ float sum_xor2(float x) { return x + dpp<kDppQuadXor2>(x); }
+// half-row mirror sends lane i to i^7 (within 8 lanes); a quad xor-3 of that
+// is i^4.
+__device__ __forceinline__ float sum_xor4(float x) {
+  return x + dpp<kDppQuadXor3>(dpp<kDppRowHalfMirror>(x));
+}
+__device__ __forceinline__ float sum_xor8(float x) { return x + dpp<kDppRowRor8>(x); }
+// permlane16_swap(x, x) returns rows (0,0,2,2) and (1,1,3,3) of x.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// permlane32_swap(x, x) returns halves (lo,lo) and (hi,hi) of x.
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  return sum_xor32(sum_xor16(sum_xor8(sum_xor4(sum_xor2(sum_xor1(x))))));
+}
+// Sum over the 8 row groups of a wave (lane bits 3, 4, 5).
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  return sum_xor32(sum_xor16(sum_xor8(x)));
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte state vectors: 4 fp32 or 8 fp16 columns of one tile row.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Lane16;
+
+template <>
+struct Lane16<float> {
+  using vec = f4;
+  static constexpr int kCols = 4;
+  __device__ __forceinline__ static void widen(const vec& r, float* s) {
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) s[c] = r[c];
+  }
+  __device__ __forceinline__ static vec narrow(const float* s) {
+    vec r;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) r[c] = s[c];
+    return r;
+  }
+};
+
+template <>
+struct Lane16<_Float16> {
+  using vec = h8;
+  static constexpr int kCols = 8;
+  // fp16 -> fp32 is exact.
+  __device__ __forceinline__ static void widen(const vec& r, float* s) {
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) s[c] = static_cast<float>(r[c]);
+  }
+  // fp32 -> fp16 under the default round-to-nearest-even mode
+  // (v_cvt_pk_f16_f32).  The empty asm pins each value as a rounded fp32
+  // register first: otherwise the backend may fold the fp32 fma that made
+  // it and this narrowing into one mixed-precision fma, which rounds once,
+  // straight to fp16, instead of storing the rounded fp32 state's RNE.
+  __device__ __forceinline__ static vec narrow(const float* s) {
+    vec r;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      float x = s[c];
+      asm("" : "+v"(x));
+      r[c] = static_cast<_Float16>(x);
+    }
+    return r;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Reads of N consecutive fp32 values from LDS (N a multiple of 2; 16-byte
+// reads where N is a multiple of 4).
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void lds_rows(const float* src, float (&dst)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int m = 0; m < N; m += 4) {
+      const f4 x = *reinterpret_cast<const f4*>(src + m);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[m + e] = x[e];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < N; m += 2) {
+      const f2 x = *reinterpret_cast<const f2*>(src + m);
+      dst[m] = x[0];
+      dst[m + 1] = x[1];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The decode kernel.  One workgroup = one tile = NW wavefronts splitting the
+// 128 key rows.  MULTI selects the chained-rows variant (the fp32 state stays
+// in registers across the request's rows); otherwise the request has one row
+// and the tile stays packed in its storage type, widened where it is used.
+// ---------------------------------------------------------------------------
+template <typename T, int NW, bool MULTI>
+__global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
+  using L = Lane16<T>;
+  using vec = typename L::vec;
+  constexpr int CPL = L::kCols;         // columns per lane
+  constexpr int LPR = 8;                // lanes per tile row (8 x 16 B = 128 B)
+  constexpr int BV = LPR * CPL;         // columns per tile
+  constexpr int GROUPS = kWave / LPR;   // row groups per wave
+  constexpr int RPW = kHeadK / NW;      // rows per wave
+  constexpr int RPL = RPW / GROUPS;     // rows per lane
+  constexpr int TMAX = MULTI ? KDA_MAX_ROWS : 1;
+  constexpr int TPW = (TMAX + NW - 1) / NW;  // prologue rows per wave
+  static_assert(RPL % 2 == 0, "rows per lane must be even");
+
+  // Per-row vectors staged once: normalised q and k, decay a = exp(g), the
+  // tile's columns of v, and the scalars beta and qn . kn.
+  // (16-byte aligned: they are read and written with 8- and 16-byte ops)
+  __shared__ __attribute__((aligned(16))) float s_qn[TMAX][kHeadK];
+  __shared__ __attribute__((aligned(16))) float s_kn[TMAX][kHeadK];
+  __shared__ __attribute__((aligned(16))) float s_a[TMAX][kHeadK];
+  __shared__ __attribute__((aligned(16))) float s_v[TMAX][BV];
+  __shared__ float s_beta[TMAX];
+  __shared__ float s_qk[TMAX];
+  __shared__ __attribute__((aligned(16))) float s_red[NW > 1 ? 2 : 1][NW > 1 ? NW : 1][2][BV];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int cg = lane % LPR;
+  const int rg = lane / LPR;
+  const int row0 = wave * RPW + rg * RPL;
+
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int vt = tile % a.n_vt;
+  const int rh = tile / a.n_vt;
+  const int h = rh % a.H;
+  const int r = rh / a.H;
+  const int n_rows = MULTI ? a.n_rows : 1;
+  const int col0 = vt * BV + cg * CPL;
+  const bool writer = (wave == 0) && (rg == 0);  // lanes that write `out`
+
+  // Slot ids of this request (wave-uniform).  A request with an id out of
+  // range is skipped: its out rows become NaN, the pool is not touched.
+  const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
+  bool ids_ok = true;
+  for (int t = 0; t < n_rows; ++t) {
+    const int32_t s = ids[t];
+    ids_ok = ids_ok && s >= 0 && s < a.n_slots;
+  }
+  if (!ids_ok) {
+    if (writer) {
+      for (int t = 0; t < n_rows; ++t) {
+        const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+        float* op = a.out + (rho * a.H + h) * kHeadV + col0;
+#pragma unroll
+        for (int c = 0; c < CPL; c += 4) *reinterpret_cast<f4*>(op + c) = f4{NAN, NAN, NAN, NAN};
+      }
+    }
+    return;
+  }
+
+  // -- prologue loads: each wave takes rows wave, wave + NW, ... ------------
+  f2 q2[TPW], k2[TPW], g2[TPW];
+  f4 v4[TPW];
+  float braw[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + j * NW;
+    if (t < n_rows) {
+      const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+      const int64_t voff = (rho * a.H + h) * kHeadK;
+      q2[j] = reinterpret_cast<const f2*>(a.q + voff)[lane];
+      k2[j] = reinterpret_cast<const f2*>(a.k + voff)[lane];
+      g2[j] = reinterpret_cast<const f2*>(a.g + voff)[lane];
+      if (lane < BV / 4)
+        v4[j] = *reinterpret_cast<const f4*>(a.v + (rho * a.H + h) * kHeadV + vt * BV + 4 * lane);
+      braw[j] = a.b[rho * a.H + h];
+    }
+  }
+
+  // -- the state tile: RPL rows x 16 bytes per lane --------------------------
+  const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
+  const int64_t slot_elems = static_cast<int64_t>(a.H) * head_elems;
+  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + col0;
+  T* const pool = static_cast<T*>(a.pool);
+  vec raw[RPL];
+  {
+    const T* src = pool + static_cast<int64_t>(ids[0]) * slot_elems + lane_off;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) raw[m] = *reinterpret_cast<const vec*>(src + m * kHeadV);
+  }
+
+  // -- prologue compute: norms over all 128 entries (lane holds 2), stage ----
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + j * NW;
+    if (t < n_rows) {
+      const float sq = wave_sum(fmaf(q2[j][1], q2[j][1], q2[j][0] * q2[j][0]));
+      const float sk = wave_sum(fmaf(k2[j][1], k2[j][1], k2[j][0] * k2[j][0]));
+      const float sqk = wave_sum(fmaf(q2[j][1], k2[j][1], q2[j][0] * k2[j][0]));
+      const float rq = 1.0f / sqrtf(sq + 1e-6f);
+      const float rk = 1.0f / sqrtf(sk + 1e-6f);
+      *reinterpret_cast<f2*>(&s_qn[t][2 * lane]) = f2{q2[j][0] * rq, q2[j][1] * rq};
+      *reinterpret_cast<f2*>(&s_kn[t][2 * lane]) = f2{k2[j][0] * rk, k2[j][1] * rk};
+      *reinterpret_cast<f2*>(&s_a[t][2 * lane]) = f2{expf(g2[j][0]), expf(g2[j][1])};
+      if (lane < BV / 4) *reinterpret_cast<f4*>(&s_v[t][4 * lane]) = v4[j];
+      if (lane == 0) {
+        s_beta[t] = 1.0f / (1.0f + expf(-braw[j]));
+        s_qk[t] = (sqk * rq) * rk;
+      }
+    }
+  }
+  __syncthreads();
+
+  // fp32 state kept across rows (chained variant only)
+  float S[MULTI ? RPL : 1][CPL];
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) L::widen(raw[m], S[m]);
+  }
+
+  for (int t = 0; t < n_rows; ++t) {
+    const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+    float qn[RPL], kn[RPL], am[RPL];
+    lds_rows<RPL>(&s_qn[t][row0], qn);
+    lds_rows<RPL>(&s_kn[t][row0], kn);
+    lds_rows<RPL>(&s_a[t][row0], am);
+
+    // Decay, then both column sums over this lane's rows.
+    float w[CPL], p[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      w[c] = 0.0f;
+      p[c] = 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      float sp[CPL];
+      if constexpr (MULTI) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sp[c] = S[m][c];
+      } else {
+        L::widen(raw[m], sp);
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        sp[c] = am[m] * sp[c];
+        w[c] = fmaf(kn[m], sp[c], w[c]);
+        p[c] = fmaf(qn[m], sp[c], p[c]);
+      }
+      if constexpr (MULTI) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) S[m][c] = sp[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      w[c] = rowgroup_sum(w[c]);
+      p[c] = rowgroup_sum(p[c]);
+    }
+    if constexpr (NW > 1) {
+      const int par = t & 1;
+      if (rg == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          s_red[par][wave][0][cg * CPL + c] = w[c];
+          s_red[par][wave][1][cg * CPL + c] = p[c];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        float ws = s_red[par][0][0][cg * CPL + c];
+        float ps = s_red[par][0][1][cg * CPL + c];
+#pragma unroll
+        for (int x = 1; x < NW; ++x) {
+          ws += s_red[par][x][0][cg * CPL + c];
+          ps += s_red[par][x][1][cg * CPL + c];
+        }
+        w[c] = ws;
+        p[c] = ps;
+      }
+    }
+
+    const float beta = s_beta[t];
+    float u[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) u[c] = s_v[t][cg * CPL + c] - w[c];
+
+    // Rank-1 correction and this row's snapshot store.
+    T* dst = pool + static_cast<int64_t>(ids[t]) * slot_elems + lane_off;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      const float bk = beta * kn[m];
+      float s1[CPL];
+      if constexpr (MULTI) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) s1[c] = fmaf(bk, u[c], S[m][c]);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) S[m][c] = s1[c];
+      } else {
+        // S' recomputed from the packed tile: the same product as above
+        L::widen(raw[m], s1);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) s1[c] = fmaf(bk, u[c], am[m] * s1[c]);
+      }
+      *reinterpret_cast<vec*>(dst + m * kHeadV) = L::narrow(s1);
+    }
+
+    if (writer) {
+      const float bqk = beta * s_qk[t];
+      float* op = a.out + (rho * a.H + h) * kHeadV + col0;
+#pragma unroll
+      for (int c = 0; c < CPL; c += 4) {
+        f4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = a.scale * fmaf(bqk, u[c + e], p[c + e]);
+        *reinterpret_cast<f4*>(op + c) = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming copy used to calibrate bandwidth and byte counters.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kda_copy_probe_kernel(const f4* __restrict__ src,
+                                                             f4* __restrict__ dst, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const f4 x0 = src[i];
+    const f4 x1 = src[i + stride];
+    const f4 x2 = src[i + 2 * stride];
+    const f4 x3 = src[i + 3 * stride];
+    dst[i] = x0;
+    dst[i + stride] = x1;
+    dst[i + 2 * stride] = x2;
+    dst[i + 3 * stride] = x3;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+template <typename T, int NW, bool MULTI>
+static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((kda_decode_tile<T, NW, MULTI>), dim3(blocks), dim3(kWave * NW), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch(const Args& a, int32_t nw, int32_t blocks, hipStream_t s) {
+  if (a.n_rows == 1) {
+    switch (nw) {
+      case 1: return launch_tile<T, 1, false>(a, blocks, s);
+      case 2: return launch_tile<T, 2, false>(a, blocks, s);
+      case 4: return launch_tile<T, 4, false>(a, blocks, s);
+      default: return launch_tile<T, 8, false>(a, blocks, s);
+    }
+  }
+  switch (nw) {
+    case 1: return launch_tile<T, 1, true>(a, blocks, s);
+    case 2: return launch_tile<T, 2, true>(a, blocks, s);
+    case 4: return launch_tile<T, 4, true>(a, blocks, s);
+    default: return launch_tile<T, 8, true>(a, blocks, s);
+  }
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids, const float* q,
+                                  const float* k, const float* v, const float* g, const float* b,
+                                  float* out, int32_t n_req, int32_t n_rows_per_slot,
+                                  kda_dtype state_dtype, float scale, const kda_launch_opts* opts,
+                                  void* stream) {
+  const int rc = check_common(pool, n_req, n_rows_per_slot, state_dtype);
+  if (rc != KDA_OK) return rc;
+  if (n_req == 0) return KDA_OK;  // empty launch: the row buffers may be NULL
+  if (slot_ids == nullptr || q == nullptr || k == nullptr || v == nullptr || g == nullptr ||
+      b == nullptr || out == nullptr)
+    return KDA_ERR_NULL;
+  if (!std::isfinite(scale)) return KDA_ERR_ARG;
+  if (opts != nullptr && !waves_allowed(opts->waves_per_tile)) return KDA_ERR_ARG;
+  if (!aligned16(pool->base) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(g) || !aligned16(out) || !aligned4(b) || !aligned4(slot_ids))
+    return KDA_ERR_ALIGN;
+
+  const int32_t bv = tile_bv(state_dtype);
+  const int32_t nw = waves_per_tile(state_dtype, n_rows_per_slot, opts);
+  Args a;
+  a.pool = pool->base;
+  a.slot_ids = slot_ids;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.b = b;
+  a.out = out;
+  a.n_slots = pool->n_slots;
+  a.H = pool->H;
+  a.n_rows = n_rows_per_slot;
+  a.n_vt = kHeadV / bv;
+  a.scale = scale;
+  const int32_t blocks = n_req * pool->H * a.n_vt;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const hipError_t err = state_dtype == KDA_F32 ? dispatch<float>(a, nw, blocks, s)
+                                                : dispatch<_Float16>(a, nw, blocks, s);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+extern "C" int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids, const float* q,
+                               const float* k, const float* v, const float* g, const float* b,
+                               float* out, int32_t n_req, int32_t n_rows_per_slot,
+                               kda_dtype state_dtype, float scale, void* stream) {
+  return kda_decode_step_ex(pool, slot_ids, q, k, v, g, b, out, n_req, n_rows_per_slot,
+                            state_dtype, scale, nullptr, stream);
+}
+
+extern "C" int kda_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {
+  if (dst == nullptr || src == nullptr) return KDA_ERR_NULL;
+  if (!aligned16(dst) || !aligned16(src)) return KDA_ERR_ALIGN;
+  if (bytes % 16 != 0) return KDA_ERR_ARG;
+  if (bytes == 0) return KDA_OK;
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  const int64_t want = (n + 1023) / 1024;  // about 4 vectors per thread
+  const int32_t blocks = static_cast<int32_t>(want < 16384 ? (want < 1 ? 1 : want) : 16384);
+  hipLaunchKernelGGL(kda_copy_probe_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const f4*>(src),
+                     static_cast<f4*>(dst), n);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}

@@ -1,0 +1,127 @@
+// kda_host.cpp -- host half of the KDA decode C ABI: argument validation,
+// addressing (state_at), pool sizing, launch description and error strings.
+// Makes no HIP call, so every refusal can be exercised without a GPU.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <unordered_set>
+
+#include "kda_decode.h"
+#include "kda_internal.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+static bool dtype_known(int dt) { return dt == KDA_F32 || dt == KDA_F16; }
+
+// The checks every entry point shares, in the documented order (ROCm/ATOM
+// PR #2945, Changes: refuse anything but fp32 or fp16 rather than
+// reinterpret it; refuse a pool of the other dtype, which would be read at
+// the wrong element size).
+int check_common(const kda_pool* pool, int32_t n_req, int32_t n_rows,
+                 kda_dtype state_dtype) {
+  if (pool == nullptr || pool->base == nullptr) return KDA_ERR_NULL;
+  if (!dtype_known(state_dtype) || !dtype_known(pool->dtype)) return KDA_ERR_DTYPE_REFUSED;
+  if (state_dtype != pool->dtype) return KDA_ERR_DTYPE_MISMATCH;
+  if (pool->K != kHeadK || pool->V != kHeadV || pool->H < 1 || pool->n_slots < 1)
+    return KDA_ERR_SHAPE;
+  if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
+  if (n_req < 0) return KDA_ERR_ARG;
+  if (static_cast<int64_t>(n_req) * n_rows > pool->n_slots) return KDA_ERR_SLOT;
+  // grid size: n_req * H * (V / bv) workgroups must fit in int32
+  const int64_t tiles = static_cast<int64_t>(n_req) * pool->H * (kHeadV / tile_bv(state_dtype));
+  if (tiles > INT32_MAX) return KDA_ERR_ARG;
+  return KDA_OK;
+}
+
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+int kda_validate(const kda_pool* pool, const int32_t* slot_ids_host, int32_t n_req,
+                 int32_t n_rows, kda_dtype state_dtype) {
+  if (slot_ids_host == nullptr) return KDA_ERR_NULL;
+  const int rc = check_common(pool, n_req, n_rows, state_dtype);
+  if (rc != KDA_OK) return rc;
+  const int64_t R = static_cast<int64_t>(n_req) * n_rows;
+  std::unordered_set<int32_t> seen;
+  seen.reserve(static_cast<size_t>(R));
+  for (int64_t i = 0; i < R; ++i) {
+    const int32_t s = slot_ids_host[i];
+    if (s < 0 || s >= pool->n_slots) return KDA_ERR_SLOT;
+    if (!seen.insert(s).second) return KDA_ERR_SLOT;
+  }
+  return KDA_OK;
+}
+
+int64_t kda_state_at(const kda_pool* pool, const int32_t* slot_ids_host, int32_t n_rows,
+                     int32_t req, int32_t row) {
+  if (pool == nullptr || slot_ids_host == nullptr) return -KDA_ERR_NULL;
+  if (!dtype_known(pool->dtype)) return -KDA_ERR_DTYPE_REFUSED;
+  if (pool->K < 1 || pool->V < 1 || pool->H < 1 || pool->n_slots < 1) return -KDA_ERR_SHAPE;
+  if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return -KDA_ERR_ROWS;
+  if (req < 0 || row < 0 || row >= n_rows) return -KDA_ERR_ARG;
+  const int32_t s = slot_ids_host[static_cast<int64_t>(req) * n_rows + row];
+  if (s < 0 || s >= pool->n_slots) return -KDA_ERR_SLOT;
+  return static_cast<int64_t>(s) * pool->H * pool->K * pool->V;
+}
+
+size_t kda_pool_bytes(int32_t n_slots, int32_t H, int32_t K, int32_t V, kda_dtype dtype) {
+  if (!dtype_known(dtype) || n_slots < 0 || H < 0 || K < 0 || V < 0) return 0;
+  const size_t elem = dtype == KDA_F32 ? 4 : 2;
+  return static_cast<size_t>(n_slots) * H * K * V * elem;
+}
+
+int32_t kda_tile_bv(kda_dtype dtype) {
+  if (!dtype_known(dtype)) return -KDA_ERR_DTYPE_REFUSED;
+  return tile_bv(dtype);
+}
+
+int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtype,
+                        const kda_launch_opts* opts, kda_launch_desc* desc) {
+  if (desc == nullptr) return KDA_ERR_NULL;
+  if (!dtype_known(dtype)) return KDA_ERR_DTYPE_REFUSED;
+  if (H < 1) return KDA_ERR_SHAPE;
+  if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
+  if (n_req < 0) return KDA_ERR_ARG;
+  if (opts != nullptr && !waves_allowed(opts->waves_per_tile)) return KDA_ERR_ARG;
+  const int32_t bv = tile_bv(dtype);
+  const int32_t nw = waves_per_tile(dtype, n_rows, opts);
+  const int64_t tiles = static_cast<int64_t>(n_req) * H * (kHeadV / bv);
+  if (tiles > INT32_MAX) return KDA_ERR_ARG;
+  desc->bv = bv;
+  desc->waves_per_tile = nw;
+  desc->threads = nw * kWave;
+  desc->tiles = static_cast<int32_t>(tiles);
+  desc->blocks = static_cast<int32_t>(tiles);
+  desc->lds_bytes = lds_bytes(bv, nw, n_rows);
+  desc->kernel = "kda_decode_tile";
+  return KDA_OK;
+}
+
+int32_t kda_tile_of_block(int32_t block, int32_t n_blocks) {
+  if (n_blocks < 1 || block < 0 || block >= n_blocks) return -1;
+  return tile_of_block(block, n_blocks);
+}
+
+const char* kda_strerror(int code) {
+  switch (code) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_DTYPE_REFUSED: return "state dtype refused: only fp32 and fp16 pools are supported (bf16 is refused, not reinterpreted)";
+    case KDA_ERR_DTYPE_MISMATCH: return "state dtype does not match the pool's dtype (it would be read at the wrong element size)";
+    case KDA_ERR_SHAPE: return "unsupported shape: K and V must be 128, H and n_slots at least 1";
+    case KDA_ERR_ROWS: return "rows per request must be in [1, 8]";
+    case KDA_ERR_SLOT: return "slot id out of range or repeated, or more rows than slots";
+    case KDA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case KDA_ERR_ARG: return "bad argument (negative count, index out of range or non-finite scale)";
+    case KDA_ERR_LAUNCH: return "the HIP runtime reported a kernel launch error";
+    default: return "unknown kda status code";
+  }
+}
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/kda_decode.h declares, and refuses bad calls on the host before any
+HIP call (ROCm/ATOM PR #2945, Changes and Testing: bf16 refused, a pool of
+the other dtype refused, every build key carries the dtype)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda_decode.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+K = pytest.importorskip("kda_gated_delta_decode_amd")
+from kda_gated_delta_decode_amd import binding as B  # noqa: E402
+
+FAKE = 0x10000   # an aligned non-null address: only ever passed to calls that
+                 # the host validation refuses, so it is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(kda_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for expected in ["kda_decode_step", "kda_decode_step_ex", "kda_validate", "kda_state_at",
+                     "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
+                     "kda_copy_probe", "kda_strerror", "kda_abi_version"]:
+        assert expected in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
+    assert B.kda_abi_version() == 1
+
+
+def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
+    return B.kda_pool(ctypes.c_void_p(base), n_slots, H, Kd, V, dtype)
+
+
+def step(P, n_req=4, n_rows=1, state_dtype=None, scale=0.0883883, ptrs=None, opts=None):
+    p = [FAKE] * 7 if ptrs is None else ptrs
+    sd = P.dtype if state_dtype is None else state_dtype
+    args = (ctypes.byref(P), *[ctypes.c_void_p(x) for x in p], n_req, n_rows, sd, scale)
+    if opts is None:
+        return B.library().kda_decode_step(*args, None)
+    return B.library().kda_decode_step_ex(*args, ctypes.byref(opts), None)
+
+
+def test_refusals_before_any_hip_call():
+    assert step(pool(dtype=B.KDA_BF16)) == B.KDA_ERR_DTYPE_REFUSED
+    assert step(pool(dtype=7)) == B.KDA_ERR_DTYPE_REFUSED
+    assert step(pool(dtype=B.KDA_F16), state_dtype=B.KDA_F32) == B.KDA_ERR_DTYPE_MISMATCH
+    assert step(pool(dtype=B.KDA_F32), state_dtype=B.KDA_F16) == B.KDA_ERR_DTYPE_MISMATCH
+    assert step(pool(Kd=64)) == B.KDA_ERR_SHAPE
+    assert step(pool(V=256)) == B.KDA_ERR_SHAPE
+    assert step(pool(H=0)) == B.KDA_ERR_SHAPE
+    assert step(pool(), n_rows=0) == B.KDA_ERR_ROWS
+    assert step(pool(), n_rows=9) == B.KDA_ERR_ROWS
+    assert step(pool(), n_req=-1) == B.KDA_ERR_ARG
+    assert step(pool(n_slots=10), n_req=3, n_rows=4) == B.KDA_ERR_SLOT
+    assert step(pool(), scale=float("nan")) == B.KDA_ERR_ARG
+    assert step(pool(), scale=float("inf")) == B.KDA_ERR_ARG
+    assert step(pool(), opts=B.kda_launch_opts(3)) == B.KDA_ERR_ARG
+    assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
+    assert step(pool(), ptrs=[FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]) == B.KDA_ERR_ALIGN
+    assert step(pool(), ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE]) == B.KDA_ERR_ALIGN
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_null_pointers_refused(which):
+    ptrs = [FAKE] * 7
+    ptrs[which] = 0
+    assert step(pool(), ptrs=ptrs) == B.KDA_ERR_NULL
+    assert step(pool(base=0)) == B.KDA_ERR_NULL
+    assert B.library().kda_decode_step(None, *[ctypes.c_void_p(FAKE)] * 7, 1, 1, 0, 0.1, None) == B.KDA_ERR_NULL
+
+
+def test_empty_launch_is_a_no_op():
+    # n_req == 0 passes validation and returns before any HIP call; the row
+    # buffers of an empty launch may be NULL
+    assert step(pool(), n_req=0) == B.KDA_OK
+    assert step(pool(dtype=B.KDA_F16), n_req=0, n_rows=8) == B.KDA_OK
+    assert step(pool(), n_req=0, ptrs=[0] * 7) == B.KDA_OK
+    assert step(pool(base=0), n_req=0) == B.KDA_ERR_NULL
+
+
+def test_validate_slot_table():
+    P = pool(n_slots=10)
+    ok = np.array([3, 1, 4, 0, 9, 2], dtype=np.int32)
+    assert B.kda_validate(P, ok, 3, 2, B.KDA_F32) == B.KDA_OK
+    assert B.kda_validate(P, np.array([3, 1, 3, 0], np.int32), 2, 2, B.KDA_F32) == B.KDA_ERR_SLOT
+    assert B.kda_validate(P, np.array([3, 10], np.int32), 2, 1, B.KDA_F32) == B.KDA_ERR_SLOT
+    assert B.kda_validate(P, np.array([-1, 2], np.int32), 2, 1, B.KDA_F32) == B.KDA_ERR_SLOT
+    assert B.kda_validate(P, ok, 3, 2, B.KDA_BF16) == B.KDA_ERR_DTYPE_REFUSED
+    assert B.kda_validate(P, ok, 3, 2, B.KDA_F16) == B.KDA_ERR_DTYPE_MISMATCH
+    assert B.library().kda_validate(ctypes.byref(P), None, 3, 2, 0) == B.KDA_ERR_NULL
+
+
+def test_state_at_addresses_initial_and_snapshot_slots():
+    # ROCm/ATOM PR #2945, Changes: one address function for the initial
+    # state (row 0) and every row's snapshot slot.
+    P = pool(n_slots=96, H=12)
+    ids = np.arange(64, dtype=np.int32)[::-1].copy()   # 8 requests x 8 rows
+    block = 12 * 128 * 128
+    for req in range(8):
+        for row in range(8):
+            assert B.kda_state_at(P, ids, 8, req, row) == int(ids[req * 8 + row]) * block
+    assert B.kda_state_at(P, ids, 8, 0, 8) == -B.KDA_ERR_ARG
+    assert B.kda_state_at(P, ids, 9, 0, 0) == -B.KDA_ERR_ROWS
+    bad = ids.copy()
+    bad[5] = 96
+    assert B.kda_state_at(P, bad, 8, 0, 5) == -B.KDA_ERR_SLOT
+
+
+def test_pool_sizing_matches_the_pages_memory_table():
+    gold = json.load(open(os.path.join(GOLDEN, "pages_memory_table.json")))
+    L, H, Kd, V = gold["layers"], gold["H"], gold["K"], gold["V"]
+    f32 = L * B.kda_pool_bytes(1, H, Kd, V, "f32")
+    f16 = L * B.kda_pool_bytes(1, H, Kd, V, "f16")
+    diff_mb = gold["state_per_slot_MB"]["f32"] - gold["state_per_slot_MB"]["f16"]
+    assert abs((f32 - f16) / 1e6 - diff_mb) <= 2 * gold["printed_precision_MB"]
+    # what is left is the same for both dtypes (the conv state)
+    rest32 = gold["state_per_slot_MB"]["f32"] - f32 / 1e6
+    rest16 = gold["state_per_slot_MB"]["f16"] - f16 / 1e6
+    assert abs(rest32 - rest16) <= 2 * gold["printed_precision_MB"]
+    # 64-slot pools, in GiB
+    for dt in ("f32", "f16"):
+        gib = 64 * gold["state_per_slot_MB"][dt] * 1e6 / 2 ** 30
+        assert abs(gib - gold["state_pool_64_slots_GB"][dt]) < 0.006
+    assert B.kda_pool_bytes(64, 12, 128, 128, "bf16") == 0
+    assert B.kda_pool_bytes(-1, 12, 128, 128, "f32") == 0
+
+
+def test_tile_width_follows_the_pages_cap():
+    gold = json.load(open(os.path.join(GOLDEN, "pages_tiling.json")))
+    assert B.kda_tile_bv("f16") == gold["bv_cap"]["f16"]
+    assert B.kda_tile_bv("f32") == gold["bv_cap"]["f32"]
+    assert B.kda_tile_bv("bf16") == -B.KDA_ERR_DTYPE_REFUSED
+    # a tile row is one 128-byte line either way
+    assert B.kda_tile_bv("f16") * 2 == B.kda_tile_bv("f32") * 4 == 128
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 96, 192, 1536, 3072, 3073, 12345])
+def test_block_to_tile_map_is_a_bijection(n):
+    tiles = [B.kda_tile_of_block(b, n) for b in range(n)]
+    assert sorted(tiles) == list(range(n))
+    # the blocks of one XCD (b % 8 equal) hold consecutive tiles
+    for x in range(min(8, n)):
+        mine = [tiles[b] for b in range(x, n, 8)]
+        assert mine == list(range(mine[0], mine[0] + len(mine)))
+    assert B.kda_tile_of_block(n, n) == -1
+
+
+def test_describe_launch():
+    d = B.kda_describe_launch(64, 1, 12, "f32")
+    assert (d["bv"], d["tiles"], d["blocks"]) == (32, 64 * 12 * 4, 64 * 12 * 4)
+    d = B.kda_describe_launch(64, 1, 12, "f16")
+    assert (d["bv"], d["tiles"]) == (64, 64 * 12 * 2)
+    d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8)
+    assert (d["waves_per_tile"], d["threads"]) == (8, 512)
+    with pytest.raises(B.KdaError):
+        B.kda_describe_launch(8, 9, 12, "f16")
+    with pytest.raises(B.KdaError):
+        B.kda_describe_launch(8, 1, 12, "bf16")
+
+
+def test_strerror_names_every_code():
+    msgs = {c: B.kda_strerror(c) for c in range(10)}
+    assert len(set(msgs.values())) == 10
+    assert "bf16" in msgs[B.KDA_ERR_DTYPE_REFUSED]
+    assert B.kda_strerror(1234) == "unknown kda status code"
