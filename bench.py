@@ -15,7 +15,8 @@ whose 69 KDA layers each stream their own pool.
 Prints ONE JSON line.  value = state GB/s (state bytes read + written per
 step / wall time per step, timed region bracketed by synchronisations);
 roofline = algorithmic bytes of one launch / its average duration measured
-with HIP events on the launch stream, against the 8 TB/s HBM peak; traffic =
+with HIP events on the launch stream (the timed launches are replayed from
+one HIP graph, back to back), against the 8 TB/s HBM peak; traffic =
 hardware byte counters of the committed rocprofv3 summary when it was taken
 on this kernel source, else null; cpu_baseline = the CPU oracle timed on a
 bounded sample of the same workload.  Extra keys report the other workloads
@@ -43,7 +44,7 @@ PEAK_SOURCE = "AMD MI355X spec: 8 TB/s HBM3E"
 PAGES_FP32_US = 24.6
 PAGES_FP16_US = 16.1
 KERNEL_SRC = os.path.join(ROOT, "kda_gated_delta_decode_amd", "csrc", "kda_decode.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_decode_tile_pmc_traffic.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_decode_tile_pmc_traffic.txt")
 
 
 def log(*a):
@@ -62,6 +63,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--dtype", choices=["f32", "f16"], default="f32")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
+    ap.add_argument("--extras", choices=["all", "copy"], default="all",
+                    help="'copy' runs only the plain-copy probe after the main workload")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch eagerly instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
@@ -92,40 +97,59 @@ class Workload:
                           scale=self.inp.scale)
 
 
+EAGER = False
+
+
 def time_launches(fn, steps: int, warmup: int, torch):
-    """Wall time per step over `steps` back-to-back launches, and the mean
-    of per-launch HIP-event durations (events on the launch stream)."""
-    for i in range(warmup):
-        fn(i)
+    """Time `steps` calls of fn(i) (each enqueues one step on the current
+    stream) replayed from a HIP graph, after `warmup` calls replayed the same
+    way.  Graph replay is how a serving step is launched; it takes the
+    Python binding's per-call overhead off the GPU's timeline, so the event
+    region measures the kernels back to back.  Returns per-step times."""
+    if EAGER:
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            fn(warmup + i)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        return {"ms_per_step": ms / steps, "host_ms_per_step": ms / steps, "launch_ms_mean": ms / steps}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)                       # one eager call before capture
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    g_warm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        for i in range(warmup):
+            fn(i)
+    g_timed = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_timed):
+        for i in range(steps):
+            fn(warmup + i)
+    g_warm.replay()
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     start.record()
-    for i in range(steps):
-        fn(warmup + i)
+    g_timed.replay()
     end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     region_ms = start.elapsed_time(end)
-    # per-launch durations, a second pass bracketed the same way
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        evs[i][0].record()
-        fn(warmup + steps + i)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    durs = sorted(a.elapsed_time(b) for a, b in evs)
-    return {
-        "ms_per_step": region_ms / steps,
-        "host_ms_per_step": wall_ms / steps,
-        "launch_ms_mean": sum(durs) / len(durs),
-        "launch_ms_p10": durs[len(durs) // 10],
-        "launch_ms_p50": durs[len(durs) // 2],
-        "launch_ms_p90": durs[(9 * len(durs)) // 10],
-    }
+    del g_warm, g_timed
+    # Graph-replayed launches run back to back, so the event region divided
+    # by the step count is the mean step (and, at one launch per step, the
+    # mean launch) duration.
+    return {"ms_per_step": region_ms / steps, "host_ms_per_step": wall_ms / steps,
+            "launch_ms_mean": region_ms / steps}
 
 
 def pmc_traffic(expected_launch_key: str):
@@ -177,6 +201,8 @@ def cpu_baseline(inp, seconds: float):
 
 def main():
     args = parse()
+    global EAGER
+    EAGER = args.eager
     if args.gpus != 1:
         print("bench.py measures one GPU: this path has no cross-GPU exchange and this build "
               "runs on a single MI355X; --gpus %d is not supported (use --gpus 1)" % args.gpus,
@@ -246,7 +272,8 @@ def main():
             "kernel": "kda_decode_tile",
             "algorithmic_bytes_per_launch": alg_bytes,
             "launch_us_mean": round(t["launch_ms_mean"] * 1e3, 3),
-            "launch_us_p10_p50_p90": [round(t[k] * 1e3, 3) for k in ("launch_ms_p10", "launch_ms_p50", "launch_ms_p90")],
+            "timing": ("HIP events around %d eager launches" % args.steps) if args.eager else
+                      ("HIP events around one HIP-graph replay of the %d launches" % args.steps),
             "peak_source": PEAK_SOURCE,
         },
         "device": dev_name,
@@ -254,19 +281,24 @@ def main():
 
     if not args.no_extras:
         extras = {}
-        # plain copy: the achievable streaming bandwidth, 1 GiB each way
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
-        src.fill_(1)
-        tc = time_launches(lambda i: B.kda_copy_probe(dst, src), 20, 3, torch)
-        extras["copy_probe_1GiB"] = {"GB/s_read_plus_write": round(2 * n / (tc["launch_ms_mean"] * 1e-3) / 1e9, 1),
-                                     "us": round(tc["launch_ms_mean"] * 1e3, 2)}
-        del src, dst
+        # plain copies: the achievable streaming read+write bandwidth at
+        # 1 GiB, and a copy moving the same bytes as one decode step
+        for label, nbytes in (("copy_probe_1GiB", 1 << 30),
+                              ("copy_probe_same_bytes", (state_bytes // 2) // 16 * 16)):
+            src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            src.fill_(1)
+            tc = time_launches(lambda i: B.kda_copy_probe(dst, src), 20, 3, torch)
+            extras[label] = {"bytes_copied": nbytes,
+                             "GB/s_read_plus_write": round(2 * nbytes / (tc["launch_ms_mean"] * 1e-3) / 1e9, 1),
+                             "us": round(tc["launch_ms_mean"] * 1e3, 2)}
+            del src, dst
         rec["pct_of_copy_bandwidth"] = round(100.0 * achieved / extras["copy_probe_1GiB"]["GB/s_read_plus_write"], 2)
-        for name, fn in (("batched_f16" if args.dtype == "f32" else "batched_f32",
+        other = () if args.extras == "copy" else (
+                        ("batched_f16" if args.dtype == "f32" else "batched_f32",
                           kda_inputs.batched_f16 if args.dtype == "f32" else kda_inputs.batched_f32),
-                         ("spec_verify_f16", kda_inputs.spec_verify_f16)):
+                         ("spec_verify_f16", kda_inputs.spec_verify_f16))
+        for name, fn in other:
             inp = fn(0)
             w = Workload(inp, ROT, torch)
             tt = time_launches(lambda i: w.launch(i, B), max(50, args.steps // 2), 10, torch)
@@ -280,7 +312,7 @@ def main():
             }
             del w
         # a 69-layer decode step: 69 independent 64-slot pools, one launch each
-        for dt in ("f32", "f16"):
+        for dt in (("f32", "f16") if args.extras == "all" else ()):
             extras["layers69_" + dt] = layers69(dt, B, torch, steps=10, warmup=2)
         rec["extras"] = extras
         torch.cuda.empty_cache()

@@ -129,20 +129,25 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
 
 /*
  * Launch options of kda_decode_step_ex.  Zero-initialise for the library's
- * defaults.  waves_per_tile: wavefronts that split one tile's 128 key rows,
- * 0 (the library's choice) or 1, 2, 4, 8.  The choice changes the order of
- * the fp32 column sums (so results may differ in the last bits), never the
+ * defaults; each non-zero field overrides one choice.
+ *  waves_per_tile  wavefronts that split one tile's 128 key rows: 1, 2, 4, 8.
+ *  bv              value columns per tile: 32, 64 or 128 for fp32 pools
+ *                  (8, 16, 32 lanes per tile row), 64 or 128 for fp16.
+ * Supported combinations keep 2..32 key rows per lane (rows per lane =
+ * 2 * lanes per row / waves).  The shape changes the order of the fp32
+ * column sums over K (so results may differ in the last bits), never the
  * operation; fixing it fixes every result bit for given inputs.
  */
 typedef struct kda_launch_opts {
   int32_t waves_per_tile;
+  int32_t bv;
 } kda_launch_opts;
 
 /*
  * kda_decode_step_ex -- kda_decode_step with launch options (opts may be
  * NULL for the defaults).  For tests that must hold the summation order
  * fixed across launches and for tuning sweeps.  Additional error:
- * KDA_ERR_ARG for a waves_per_tile outside {0, 1, 2, 4, 8}.
+ * KDA_ERR_ARG for a shape that is not supported (see kda_launch_opts).
  */
 int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
                        const float* q, const float* k, const float* v,
@@ -183,11 +188,12 @@ size_t kda_pool_bytes(int32_t n_slots, int32_t H, int32_t K, int32_t V,
                       kda_dtype dtype);
 
 /*
- * kda_tile_bv -- value columns per state tile for a pool dtype: 32 for a
- * 4-byte state, 64 for a 2-byte one, so that a tile row is one 128-byte line
- * whatever the element size (compare ROCm/ATOM PR #2130, What and Copilot
- * review: a 2-byte state wants twice the V per block to keep the same bytes
- * in flight).  Returns a negative kda_status for a refused dtype.
+ * kda_tile_bv -- value columns per state tile that single-row launches use
+ * by default (128 for both dtypes: whole state rows per wave instruction).
+ * Narrower tiles (32 fp32 / 64 fp16 columns, the V-block cap of the pages'
+ * portable kernel, ROCm/ATOM PR #2130, Copilot review) remain available
+ * through kda_launch_opts.  Returns a negative kda_status for a refused
+ * dtype.
  */
 int32_t kda_tile_bv(kda_dtype dtype);
 

@@ -47,7 +47,7 @@ class kda_pool(ctypes.Structure):
 
 
 class kda_launch_opts(ctypes.Structure):
-    _fields_ = [("waves_per_tile", ctypes.c_int32)]
+    _fields_ = [("waves_per_tile", ctypes.c_int32), ("bv", ctypes.c_int32)]
 
 
 class kda_launch_desc(ctypes.Structure):
@@ -176,14 +176,15 @@ def _check(code: int, where: str) -> None:
 
 def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1,
                     state_dtype=None, scale: float | None = None, stream=None,
-                    waves_per_tile: int = 0, pool_dtype=None) -> None:
+                    waves_per_tile: int = 0, bv: int = 0, pool_dtype=None) -> None:
     """One decode launch (see kda_decode_step in include/kda_decode.h).
 
     pool: device tensor [n_slots, H, 128, 128], float32 or float16, updated
     in place.  slot_ids: device int32 [R]; q, k, g: device float32 [R, H, 128];
     v, out: [R, H, 128]; b: [R, H].  state_dtype defaults to the pool's
     dtype; pool_dtype overrides what the pool struct declares (tests of the
-    refusals).  waves_per_tile != 0 selects kda_decode_step_ex."""
+    refusals).  A non-zero waves_per_tile or bv selects kda_decode_step_ex
+    with those launch options."""
     import torch
     P = make_pool(pool, pool_dtype)
     sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
@@ -197,8 +198,8 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
             _dev(q, "q", torch.float32), _dev(k, "k", torch.float32), _dev(v, "v", torch.float32),
             _dev(g, "g", torch.float32), _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
             n_req, n_rows_per_slot, sd, float(scale))
-    if waves_per_tile:
-        opts = kda_launch_opts(int(waves_per_tile))
+    if waves_per_tile or bv:
+        opts = kda_launch_opts(int(waves_per_tile), int(bv))
         rc = library().kda_decode_step_ex(*args, ctypes.byref(opts), _stream_ptr(stream))
         _check(rc, "kda_decode_step_ex")
     else:
@@ -228,9 +229,10 @@ def kda_tile_bv(dtype) -> int:
     return int(library().kda_tile_bv(_dtype_arg(dtype)))
 
 
-def kda_describe_launch(n_req: int, n_rows: int, H: int, dtype, waves_per_tile: int = 0) -> dict:
+def kda_describe_launch(n_req: int, n_rows: int, H: int, dtype, waves_per_tile: int = 0,
+                        bv: int = 0) -> dict:
     d = kda_launch_desc()
-    opts = kda_launch_opts(int(waves_per_tile))
+    opts = kda_launch_opts(int(waves_per_tile), int(bv))
     _check(library().kda_describe_launch(n_req, n_rows, H, _dtype_arg(dtype), ctypes.byref(opts),
                                          ctypes.byref(d)), "kda_describe_launch")
     return {"bv": d.bv, "waves_per_tile": d.waves_per_tile, "threads": d.threads,

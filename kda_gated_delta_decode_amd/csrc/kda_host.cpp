@@ -28,8 +28,9 @@ int check_common(const kda_pool* pool, int32_t n_req, int32_t n_rows,
   if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
   if (n_req < 0) return KDA_ERR_ARG;
   if (static_cast<int64_t>(n_req) * n_rows > pool->n_slots) return KDA_ERR_SLOT;
-  // grid size: n_req * H * (V / bv) workgroups must fit in int32
-  const int64_t tiles = static_cast<int64_t>(n_req) * pool->H * (kHeadV / tile_bv(state_dtype));
+  // grid size: n_req * H * (V / bv) workgroups must fit in int32 for the
+  // narrowest tile any launch shape uses (bv = 32)
+  const int64_t tiles = static_cast<int64_t>(n_req) * pool->H * (kHeadV / 32);
   if (tiles > INT32_MAX) return KDA_ERR_ARG;
   return KDA_OK;
 }
@@ -86,9 +87,10 @@ int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtyp
   if (H < 1) return KDA_ERR_SHAPE;
   if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
   if (n_req < 0) return KDA_ERR_ARG;
-  if (opts != nullptr && !waves_allowed(opts->waves_per_tile)) return KDA_ERR_ARG;
-  const int32_t bv = tile_bv(dtype);
-  const int32_t nw = waves_per_tile(dtype, n_rows, opts);
+  Shape shape;
+  if (!resolve_shape(dtype, n_rows, opts, &shape)) return KDA_ERR_ARG;
+  const int32_t bv = shape.bv;
+  const int32_t nw = shape.nw;
   const int64_t tiles = static_cast<int64_t>(n_req) * H * (kHeadV / bv);
   if (tiles > INT32_MAX) return KDA_ERR_ARG;
   desc->bv = bv;

@@ -21,25 +21,58 @@ constexpr int kNumXcd = 8;     // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kHeadK = KDA_HEAD_K;
 constexpr int kHeadV = KDA_HEAD_V;
 
-// Value columns per tile: one 128-byte line per tile row, i.e. 32 fp32 or
-// 64 fp16 columns; a wavefront then spans 8 lanes x 16 bytes per row.
-inline int32_t tile_bv(kda_dtype dt) { return dt == KDA_F32 ? 32 : 64; }
+// Columns one lane holds: a 16-byte vector of the pool's element type.
+inline int32_t cols_per_lane(kda_dtype dt) { return dt == KDA_F32 ? 4 : 8; }
 
-// Wavefronts splitting the K rows of one tile.  One wave per tile when each
-// request has one row: no LDS, no barrier, 16 rows per lane.  Chained rows
-// (speculative verify) have few tiles and write one snapshot per row, so K
-// is split over more waves to spread the fp32 work and the stores over the
-// chip; the partial column sums then meet in LDS once per row.
-inline int32_t default_waves_per_tile(kda_dtype /*dt*/, int32_t n_rows) {
-  return n_rows == 1 ? 1 : 4;
+// Default launch shape, chosen by measurement on MI355X (graph-replayed
+// launches, 1 GiB of rotating pools, nontemporal state traffic):
+//  - one row per request: whole 128-column tile rows, so every wave
+//    instruction reads or writes whole 512-byte (fp32) / 256-byte (fp16)
+//    state rows; K split over 2 (fp32) or 4 (fp16) waves.  At 64 requests x
+//    12 heads: fp32 17.9 us, fp16 9.7 us, against 20-21 us and 10-14 us for
+//    the narrow 32/64-column tiles.
+//  - chained rows: 64-column tiles with K over 8 (fp32) or 4 (fp16) waves:
+//    few tiles exist, so K is spread over more waves and each row's partial
+//    column sums meet in LDS.
+inline int32_t default_bv(kda_dtype /*dt*/, int32_t n_rows) { return n_rows == 1 ? 128 : 64; }
+inline int32_t default_waves_per_tile(kda_dtype dt, int32_t n_rows) {
+  if (n_rows == 1) return dt == KDA_F32 ? 2 : 4;
+  return dt == KDA_F32 ? 8 : 4;
 }
 
-inline bool waves_allowed(int32_t nw) { return nw == 0 || nw == 1 || nw == 2 || nw == 4 || nw == 8; }
+// The single-row default tile width (what kda_tile_bv reports).
+inline int32_t tile_bv(kda_dtype dt) { return default_bv(dt, 1); }
 
-// The wave count a launch uses: the option if set, else the default.
-inline int32_t waves_per_tile(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts) {
-  if (opts != nullptr && opts->waves_per_tile != 0) return opts->waves_per_tile;
-  return default_waves_per_tile(dt, n_rows);
+// The (bv, waves) shapes the kernels are instantiated for: 8, 16 or 32
+// lanes per tile row (bv = lanes x columns per lane, at most 128), 1, 2, 4
+// or 8 waves, at least 2 rows per lane (rows per lane = 2 * lanes / waves)
+// and at most 128 state elements per lane, which keeps every variant free of
+// register spills.
+inline bool shape_supported(kda_dtype dt, int32_t bv, int32_t nw) {
+  const int32_t cpl = cols_per_lane(dt);
+  if (bv <= 0 || bv % cpl != 0 || kHeadV % bv != 0) return false;
+  const int32_t lpr = bv / cpl;
+  if (lpr != 8 && lpr != 16 && lpr != 32) return false;
+  if (nw != 1 && nw != 2 && nw != 4 && nw != 8) return false;
+  const int32_t rpl = 2 * lpr / nw;
+  return rpl >= 2 && rpl * cpl <= 128;
+}
+
+struct Shape {
+  int32_t bv;  // value columns per tile
+  int32_t nw;  // waves per tile
+};
+
+// The shape a launch uses: each option field that is set overrides the
+// default.  Returns false if the result is not an instantiated shape.
+inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts, Shape* out) {
+  Shape s{default_bv(dt, n_rows), default_waves_per_tile(dt, n_rows)};
+  if (opts != nullptr) {
+    if (opts->bv != 0) s.bv = opts->bv;
+    if (opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
+  }
+  *out = s;
+  return shape_supported(dt, s.bv, s.nw);
 }
 
 // Bytes of static LDS per workgroup: the staged per-row vectors (normalised

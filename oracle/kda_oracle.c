@@ -189,22 +189,21 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
           for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
 
         if (g_mutation == 4) { /* planted: read-out before the update */
-          for (int32_t j = 0; j < V; ++j) {
-            float acc = 0.0f;
-            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
-            ov[j] = scale * acc;
-          }
+          for (int32_t j = 0; j < V; ++j) ov[j] = 0.0f;
+          for (int32_t i = 0; i < K; ++i)
+            for (int32_t j = 0; j < V; ++j) ov[j] = ov[j] + qn[i] * S[(int64_t)i * V + j];
+          for (int32_t j = 0; j < V; ++j) ov[j] = scale * ov[j];
         }
 
-        /* w = S'^T kn ; u = v - w */
-        for (int32_t j = 0; j < V; ++j) {
-          float acc = 0.0f;
-          for (int32_t i = 0; i < K; ++i) {
+        /* w = S'^T kn ; u = v - w.  Each w_j is the sum over i = 0..K-1 in
+         * order; the loops run i-outer only so that rows are read
+         * contiguously. */
+        for (int32_t j = 0; j < V; ++j) w[j] = 0.0f;
+        for (int32_t i = 0; i < K; ++i)
+          for (int32_t j = 0; j < V; ++j) {
             const float s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
-            acc = acc + kn[i] * s;
+            w[j] = w[j] + kn[i] * s;
           }
-          w[j] = acc;
-        }
         for (int32_t j = 0; j < V; ++j) u[j] = g_mutation == 2 ? vv[j] + w[j] : vv[j] - w[j];
 
         /* S = S' + (beta kn) u^T */
@@ -214,13 +213,12 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
             S[(int64_t)i * V + j] = S[(int64_t)i * V + j] + bk * u[j];
         }
 
-        /* o = scale * S^T qn (post-update state) */
+        /* o = scale * S^T qn (post-update state), sums in i order */
         if (g_mutation != 4) {
-          for (int32_t j = 0; j < V; ++j) {
-            float acc = 0.0f;
-            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
-            ov[j] = (g_mutation == 7 ? scale * scale : scale) * acc;
-          }
+          for (int32_t j = 0; j < V; ++j) w[j] = 0.0f;
+          for (int32_t i = 0; i < K; ++i)
+            for (int32_t j = 0; j < V; ++j) w[j] = w[j] + qn[i] * S[(int64_t)i * V + j];
+          for (int32_t j = 0; j < V; ++j) ov[j] = (g_mutation == 7 ? scale * scale : scale) * w[j];
         }
 
         /* store this token's state to its snapshot slot */
@@ -296,21 +294,18 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
           for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
 
         if (g_mutation == 4) {
-          for (int32_t j = 0; j < V; ++j) {
-            double acc = 0.0;
-            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
-            ov[j] = scale * acc;
-          }
+          for (int32_t j = 0; j < V; ++j) ov[j] = 0.0;
+          for (int32_t i = 0; i < K; ++i)
+            for (int32_t j = 0; j < V; ++j) ov[j] = ov[j] + qn[i] * S[(int64_t)i * V + j];
+          for (int32_t j = 0; j < V; ++j) ov[j] = scale * ov[j];
         }
 
-        for (int32_t j = 0; j < V; ++j) {
-          double acc = 0.0;
-          for (int32_t i = 0; i < K; ++i) {
+        for (int32_t j = 0; j < V; ++j) w[j] = 0.0;
+        for (int32_t i = 0; i < K; ++i)
+          for (int32_t j = 0; j < V; ++j) {
             const double s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
-            acc = acc + kn[i] * s;
+            w[j] = w[j] + kn[i] * s;
           }
-          w[j] = acc;
-        }
         for (int32_t j = 0; j < V; ++j)
           u[j] = g_mutation == 2 ? (double)vv[j] + w[j] : (double)vv[j] - w[j];
 
@@ -321,11 +316,10 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
         }
 
         if (g_mutation != 4) {
-          for (int32_t j = 0; j < V; ++j) {
-            double acc = 0.0;
-            for (int32_t i = 0; i < K; ++i) acc = acc + qn[i] * S[(int64_t)i * V + j];
-            ov[j] = (g_mutation == 7 ? scale * scale : scale) * acc;
-          }
+          for (int32_t j = 0; j < V; ++j) w[j] = 0.0;
+          for (int32_t i = 0; i < K; ++i)
+            for (int32_t j = 0; j < V; ++j) w[j] = w[j] + qn[i] * S[(int64_t)i * V + j];
+          for (int32_t j = 0; j < V; ++j) ov[j] = (g_mutation == 7 ? scale * scale : scale) * w[j];
         }
 
         const int32_t dst_slot = g_mutation == 10 ? slot_ids[(int64_t)r * n_rows] : slot_ids[rho];

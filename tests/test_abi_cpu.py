@@ -71,7 +71,10 @@ def test_refusals_before_any_hip_call():
     assert step(pool(n_slots=10), n_req=3, n_rows=4) == B.KDA_ERR_SLOT
     assert step(pool(), scale=float("nan")) == B.KDA_ERR_ARG
     assert step(pool(), scale=float("inf")) == B.KDA_ERR_ARG
-    assert step(pool(), opts=B.kda_launch_opts(3)) == B.KDA_ERR_ARG
+    assert step(pool(), opts=B.kda_launch_opts(3, 0)) == B.KDA_ERR_ARG
+    assert step(pool(), opts=B.kda_launch_opts(0, 48)) == B.KDA_ERR_ARG
+    assert step(pool(dtype=B.KDA_F16), opts=B.kda_launch_opts(0, 32)) == B.KDA_ERR_ARG
+    assert step(pool(dtype=B.KDA_F16), opts=B.kda_launch_opts(1, 128)) == B.KDA_ERR_ARG  # spills
     assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE]) == B.KDA_ERR_ALIGN
@@ -142,13 +145,18 @@ def test_pool_sizing_matches_the_pages_memory_table():
     assert B.kda_pool_bytes(-1, 12, 128, 128, "f32") == 0
 
 
-def test_tile_width_follows_the_pages_cap():
+def test_pages_tile_widths_are_supported_shapes():
+    # The pages' portable kernel caps the V block at 32 columns for a 4-byte
+    # state and 64 for a 2-byte one; both widths are launchable here (their
+    # tile row is one 128-byte line), though the default tile is wider.
     gold = json.load(open(os.path.join(GOLDEN, "pages_tiling.json")))
-    assert B.kda_tile_bv("f16") == gold["bv_cap"]["f16"]
-    assert B.kda_tile_bv("f32") == gold["bv_cap"]["f32"]
+    for dt in ("f32", "f16"):
+        bv = gold["bv_cap"][dt]
+        d = B.kda_describe_launch(64, 1, 12, dt, waves_per_tile=1, bv=bv)
+        assert d["bv"] == bv and d["tiles"] == 64 * 12 * (128 // bv)
+        assert bv * (4 if dt == "f32" else 2) == 128
+    assert B.kda_tile_bv("f32") == B.kda_tile_bv("f16") == 128
     assert B.kda_tile_bv("bf16") == -B.KDA_ERR_DTYPE_REFUSED
-    # a tile row is one 128-byte line either way
-    assert B.kda_tile_bv("f16") * 2 == B.kda_tile_bv("f32") * 4 == 128
 
 
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 96, 192, 1536, 3072, 3073, 12345])
@@ -162,11 +170,34 @@ def test_block_to_tile_map_is_a_bijection(n):
     assert B.kda_tile_of_block(n, n) == -1
 
 
+SHAPES_F32 = {(32, 1), (32, 2), (32, 4), (32, 8), (64, 1), (64, 2), (64, 4), (64, 8),
+              (128, 2), (128, 4), (128, 8)}
+SHAPES_F16 = {(64, 1), (64, 2), (64, 4), (64, 8), (128, 2), (128, 4), (128, 8)}
+
+
+@pytest.mark.parametrize("dtype,shapes", [("f32", SHAPES_F32), ("f16", SHAPES_F16)])
+def test_supported_launch_shapes(dtype, shapes):
+    got = set()
+    for bv in (16, 32, 48, 64, 128, 256):
+        for w in (1, 2, 3, 4, 8, 16):
+            try:
+                d = B.kda_describe_launch(64, 1, 12, dtype, waves_per_tile=w, bv=bv)
+            except B.KdaError as e:
+                assert e.code == B.KDA_ERR_ARG
+                continue
+            assert (d["bv"], d["waves_per_tile"]) == (bv, w)
+            assert d["tiles"] == 64 * 12 * (128 // bv)
+            got.add((bv, w))
+    assert got == shapes
+
+
 def test_describe_launch():
     d = B.kda_describe_launch(64, 1, 12, "f32")
-    assert (d["bv"], d["tiles"], d["blocks"]) == (32, 64 * 12 * 4, 64 * 12 * 4)
+    assert (d["bv"], d["waves_per_tile"], d["tiles"], d["blocks"]) == (128, 2, 768, 768)
     d = B.kda_describe_launch(64, 1, 12, "f16")
-    assert (d["bv"], d["tiles"]) == (64, 64 * 12 * 2)
+    assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (128, 4, 768)
+    d = B.kda_describe_launch(8, 8, 12, "f16")
+    assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 4, 8 * 12 * 2)
     d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8)
     assert (d["waves_per_tile"], d["threads"]) == (8, 512)
     with pytest.raises(B.KdaError):

@@ -55,15 +55,21 @@ def test_full_size_other_dtype_and_rows(oracle, dtype):
 SHAPES = [(1, 1, 1), (3, 1, 1), (5, 2, 1), (2, 12, 1), (1, 1, 8), (3, 2, 3), (2, 5, 8), (4, 3, 7)]
 
 
-@pytest.mark.parametrize("waves", [1, 2, 4, 8])
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
+LAUNCH_SHAPES = [("f32", bv, w) for bv, w in [(32, 1), (32, 2), (32, 4), (32, 8), (64, 1), (64, 2),
+                                              (64, 4), (64, 8), (128, 2), (128, 4), (128, 8)]] + \
+                [("f16", bv, w) for bv, w in [(64, 1), (64, 2), (64, 4), (64, 8), (128, 2), (128, 4),
+                                              (128, 8)]]
+
+
+@pytest.mark.parametrize("dtype,bv,waves", LAUNCH_SHAPES)
 @pytest.mark.parametrize("n_req,H,n_rows", SHAPES)
-def test_small_shapes_every_wave_layout(oracle, waves, dtype, n_req, H, n_rows):
+def test_small_shapes_every_launch_shape(oracle, dtype, bv, waves, n_req, H, n_rows):
     n_slots = n_req * n_rows + 3
     inp = kda_inputs.make_inputs("small", n_slots, n_req, n_rows, dtype, H=H,
                                  seed=1000 + 7 * n_req + 31 * H + n_rows)
-    gp, go = run_gpu(inp, waves_per_tile=waves)
-    check_parity(oracle, inp, gp, go, label="small %s w%d %dx%dx%d" % (dtype, waves, n_req, H, n_rows))
+    gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv)
+    check_parity(oracle, inp, gp, go,
+                 label="small %s bv%d w%d %dx%dx%d" % (dtype, bv, waves, n_req, H, n_rows))
 
 
 # --- edge cases -----------------------------------------------------------
@@ -113,10 +119,14 @@ def test_identity_gate_keeps_state_bits(oracle, dtype, n_rows):
     inp.g[:] = 0.0
     inp.b[:] = -1e4
     gp, go = run_gpu(inp)
+    # unchanged in value: a -0 may come back as +0 ((-0) + (+0) * u = +0),
+    # exactly as the oracle computes it
+    as_float = (lambda x: x) if dtype == "f32" else (lambda x: x.view(np.float16))
     for r in range(3):
         s0 = inp.slot_ids[r * n_rows]
         for t in range(n_rows):
-            np.testing.assert_array_equal(gp[inp.slot_ids[r * n_rows + t]], inp.pool[s0])
+            got, want = as_float(gp[inp.slot_ids[r * n_rows + t]]), as_float(inp.pool[s0])
+            assert np.array_equal(got, want)
     check_parity(oracle, inp, gp, go, label="identity")
 
 
@@ -174,26 +184,37 @@ def test_64bit_pool_offsets(oracle):
 
 # --- structure ------------------------------------------------------------
 
+# Lane layouts (lanes per tile row, waves per tile) that both dtypes build:
+# an fp16 tile of 8 * lanes columns and an fp32 tile of 4 * lanes columns
+# put the same rows in the same lanes, so their column sums are identical.
+TWIN_LAYOUTS = [(8, 1), (8, 2), (8, 4), (8, 8), (16, 2), (16, 4), (16, 8)]
+
+
 @pytest.mark.parametrize("n_rows", [1, 8])
-@pytest.mark.parametrize("waves", [1, 4])
-def test_fp32_twin_of_fp16_launch(n_rows, waves):
-    """fp16 launch vs the same launch on the exactly widened fp32 pool:
-    outputs bit-equal; each fp16 snapshot = RNE(fp32 snapshot)."""
+@pytest.mark.parametrize("lanes,waves", TWIN_LAYOUTS)
+def test_fp32_twin_of_fp16_launch(n_rows, lanes, waves):
+    """fp16 launch vs the same launch on the exactly widened fp32 pool, same
+    lane layout: outputs bit-equal; each fp16 snapshot = RNE(fp32 snapshot)
+    (ROCm/ATOM PR #2945, Testing)."""
     inp16 = kda_inputs.make_inputs("twin", 96, 64 // n_rows, n_rows, "f16", seed=23)
     inp32 = kda_inputs.DecodeInputs("twin32", "f32", inp16.pool.view(np.float16).astype(np.float32),
                                     inp16.slot_ids, inp16.q, inp16.k, inp16.v, inp16.g, inp16.b,
                                     n_rows, inp16.scale)
-    p16, o16 = run_gpu(inp16, waves_per_tile=waves)
-    p32, o32 = run_gpu(inp32, waves_per_tile=waves)
+    p16, o16 = run_gpu(inp16, waves_per_tile=waves, bv=8 * lanes)
+    p32, o32 = run_gpu(inp32, waves_per_tile=waves, bv=4 * lanes)
     np.testing.assert_array_equal(o16.view(np.uint32), o32.view(np.uint32))
     np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
 
 
-@pytest.mark.parametrize("waves", [1, 2, 4, 8])
-def test_chained_rows_equal_single_row_launches_fp32(waves):
+F32_SHAPES = [(32, 1), (32, 2), (32, 4), (32, 8), (64, 1), (64, 2), (64, 4), (64, 8),
+              (128, 2), (128, 4), (128, 8)]
+
+
+@pytest.mark.parametrize("bv,waves", F32_SHAPES)
+def test_chained_rows_equal_single_row_launches_fp32(bv, waves):
     n_req, n = 4, 6
     inp = kda_inputs.make_inputs("chain", 40, n_req, n, "f32", seed=29)
-    pm, om = run_gpu(inp, waves_per_tile=waves)
+    pm, om = run_gpu(inp, waves_per_tile=waves, bv=bv)
     pool, ids, t, out = device_inputs(inp)
     for step in range(n):
         rows = torch.arange(n_req, device="cuda") * n + step
@@ -204,7 +225,7 @@ def test_chained_rows_equal_single_row_launches_fp32(waves):
         B.kda_decode_step(pool, ids[rows].contiguous(), t["q"][rows].contiguous(),
                           t["k"][rows].contiguous(), t["v"][rows].contiguous(),
                           t["g"][rows].contiguous(), t["b"][rows].contiguous(), sub_out,
-                          n_rows_per_slot=1, waves_per_tile=waves)
+                          n_rows_per_slot=1, waves_per_tile=waves, bv=bv)
         out[rows] = sub_out
     torch.cuda.synchronize()
     np.testing.assert_array_equal(pool_to_host(pool).view(np.uint32), pm.view(np.uint32))
@@ -226,9 +247,9 @@ def test_permutation_equivariance_and_determinism(dtype):
     np.testing.assert_array_equal(o2.view(np.uint32), o1[perm].view(np.uint32))
 
 
-def test_wave_layouts_agree_within_rounding():
+def test_launch_shapes_agree_within_rounding():
     inp = kda_inputs.make_inputs("layouts", 96, 64, 1, "f32", seed=37)
-    res = [run_gpu(inp, waves_per_tile=w) for w in (1, 2, 4, 8)]
+    res = [run_gpu(inp, waves_per_tile=w, bv=bv) for bv, w in F32_SHAPES]
     for p, o in res[1:]:
         assert np.max(np.abs(p - res[0][0])) <= 1e-6
         assert out_rel_err(o, res[0][1]) <= OUT_REL
