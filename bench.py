@@ -282,17 +282,21 @@ def main():
     if not args.no_extras:
         extras = {}
         # plain copies: the achievable streaming read+write bandwidth at
-        # 1 GiB, and a copy moving the same bytes as one decode step
+        # 1 GiB, and a copy moving the same bytes as one decode step; the
+        # latter rotates over >= 1 GiB of buffer pairs like the decode pools
         for label, nbytes in (("copy_probe_1GiB", 1 << 30),
                               ("copy_probe_same_bytes", (state_bytes // 2) // 16 * 16)):
-            src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-            dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-            src.fill_(1)
-            tc = time_launches(lambda i: B.kda_copy_probe(dst, src), 20, 3, torch)
-            extras[label] = {"bytes_copied": nbytes,
+            pairs = max(1, math.ceil((1 << 30) / (2 * nbytes)))
+            bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+                     torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(pairs)]
+            for src, _ in bufs:
+                src.fill_(1)
+            tc = time_launches(lambda i: B.kda_copy_probe(bufs[i % pairs][1], bufs[i % pairs][0]),
+                               max(20, 2 * pairs), 3, torch)
+            extras[label] = {"bytes_copied": nbytes, "buffer_pairs_rotated": pairs,
                              "GB/s_read_plus_write": round(2 * nbytes / (tc["launch_ms_mean"] * 1e-3) / 1e9, 1),
                              "us": round(tc["launch_ms_mean"] * 1e3, 2)}
-            del src, dst
+            del bufs
         rec["pct_of_copy_bandwidth"] = round(100.0 * achieved / extras["copy_probe_1GiB"]["GB/s_read_plus_write"], 2)
         other = () if args.extras == "copy" else (
                         ("batched_f16" if args.dtype == "f32" else "batched_f32",

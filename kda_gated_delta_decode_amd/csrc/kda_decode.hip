@@ -230,13 +230,17 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   const int col0 = vt * BV + cg * CPL;
   const bool writer = (wave == 0) && (rg == 0);  // lanes that write `out`
 
-  // Slot ids of this request (wave-uniform).  A request with an id out of
-  // range is skipped: its out rows become NaN, the pool is not touched.
+  // Slot ids of this request, read once into wave-uniform registers before
+  // any store (a re-read after the snapshot stores would be a vector load
+  // that waits for every earlier store to retire).  A request with an id out
+  // of range is skipped: its out rows become NaN, the pool is not touched.
   const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
+  int32_t sid[TMAX];
   bool ids_ok = true;
-  for (int t = 0; t < n_rows; ++t) {
-    const int32_t s = ids[t];
-    ids_ok = ids_ok && s >= 0 && s < a.n_slots;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    sid[t] = t < n_rows ? ids[t] : 0;
+    ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
   }
   if (!ids_ok) {
     if (writer) {
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   T* const pool = static_cast<T*>(a.pool);
   vec raw[RPL];
   {
-    const T* src = pool + static_cast<int64_t>(ids[0]) * slot_elems + lane_off;
+    const T* src = pool + static_cast<int64_t>(sid[0]) * slot_elems + lane_off;
 #pragma unroll
     for (int m = 0; m < RPL; ++m)
       raw[m] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(src + m * kHeadV));
@@ -311,7 +315,10 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
     for (int m = 0; m < RPL; ++m) L::widen(raw[m], S[m]);
   }
 
-  for (int t = 0; t < n_rows; ++t) {
+  // Rows unrolled: every LDS index and slot id below is static.
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if (t >= n_rows) break;
     const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
     float qn[RPL], kn[RPL], am[RPL];
     lds_rows<RPL>(&s_qn[t][row0], qn);
@@ -380,7 +387,7 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
     for (int c = 0; c < CPL; ++c) u[c] = s_v[t][cg * CPL + c] - w[c];
 
     // Rank-1 correction and this row's snapshot store.
-    T* dst = pool + static_cast<int64_t>(ids[t]) * slot_elems + lane_off;
+    T* dst = pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off;
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
       const float bk = beta * kn[m];
