@@ -209,7 +209,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
+    import numpy as np
     import torch
 
     import kda_inputs
@@ -306,14 +306,23 @@ def main():
             inp = fn(0)
             w = Workload(inp, ROT, torch)
             tt = time_launches(lambda i: w.launch(i, B), max(50, args.steps // 2), 10, torch)
-            sb, ab = inp.state_bytes(), inp.state_bytes() + inp.io_bytes()
-            extras[name] = {
-                "workload": inp.name, "us_per_step": round(tt["ms_per_step"] * 1e3, 3),
-                "launch_us_mean": round(tt["launch_ms_mean"] * 1e3, 3),
-                "state_GB/s": round(sb / (tt["ms_per_step"] * 1e-3) / 1e9, 1),
-                "algorithmic_GB/s_per_launch": round(ab / (tt["launch_ms_mean"] * 1e-3) / 1e9, 1),
-                "frac_of_peak": round(ab / (tt["launch_ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            }
+            extras[name] = summarize(inp, tt)
+            del w
+        if args.extras == "all":
+            # the same batched step out of place: each request reads slot A
+            # and writes slot B of a 128-slot pool (init_slot_ids), as a
+            # runtime that ping-pongs two slots per request would
+            inp = kda_inputs.make_inputs("batched decode N=64, out of place (128-slot pool), %s pool"
+                                         % args.dtype, 128, 64, 1, args.dtype, seed=0)
+            inp.slot_ids[:] = np.arange(64, 128, dtype=np.int32)
+            w = Workload(inp, ROT, torch)
+            init_d = torch.arange(64, dtype=torch.int32, device="cuda")
+
+            def pingpong(i):
+                B.kda_decode_step(w.pools[i % len(w.pools)], w.ids, w.q, w.k, w.v, w.g, w.b, w.out,
+                                  scale=inp.scale, init_slot_ids=init_d)
+            tt = time_launches(pingpong, max(50, args.steps // 2), 10, torch)
+            extras["batched_%s_out_of_place" % args.dtype] = summarize(inp, tt)
             del w
         # a 69-layer decode step: 69 independent 64-slot pools, one launch each
         for dt in (("f32", "f16") if args.extras == "all" else ()):
@@ -324,6 +333,15 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(main_inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def summarize(inp, tt):
+    sb, ab = inp.state_bytes(), inp.state_bytes() + inp.io_bytes()
+    us = tt["ms_per_step"] * 1e3
+    return {"workload": inp.name, "us_per_step": round(us, 3),
+            "state_GB/s": round(sb / us / 1e3, 1),
+            "algorithmic_GB/s": round(ab / us / 1e3, 1),
+            "frac_of_peak": round(ab / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def layers69(dtype, B, torch, steps, warmup, n_layers=69):

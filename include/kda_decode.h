@@ -144,12 +144,31 @@ typedef struct kda_launch_opts {
 } kda_launch_opts;
 
 /*
- * kda_decode_step_ex -- kda_decode_step with launch options (opts may be
- * NULL for the defaults).  For tests that must hold the summation order
- * fixed across launches and for tuning sweeps.  Additional error:
- * KDA_ERR_ARG for a shape that is not supported (see kda_launch_opts).
+ * kda_decode_step_ex -- kda_decode_step with a separate initial-state slot
+ * per request and launch options.
+ *
+ *  init_slot_ids  NULL, or device int32 [n_req]: request r reads its initial
+ *                 state from slot init_slot_ids[r] instead of its row-0 slot
+ *                 slot_ids[r * n_rows_per_slot].  This is how a speculative
+ *                 step resumes from the snapshot of its last accepted token,
+ *                 and how a checkpointed state is loaded (ROCm/ATOM PR #2945,
+ *                 Changes: one address function serves the initial state,
+ *                 every token's snapshot slot, and the checkpoint load and
+ *                 flush).  An initial slot may be one of its own request's
+ *                 snapshot slots (it is read before any store) but must not
+ *                 be written by another request of the launch; kda_validate
+ *                 checks a host copy.  With one row per request and
+ *                 init_slot_ids[r] != slot_ids[r], the update is out of
+ *                 place (ping-pong between two slots).
+ *  opts           NULL for the defaults (see kda_launch_opts): for tests
+ *                 that must hold the summation order fixed across launches
+ *                 and for tuning sweeps.
+ * Additional errors: KDA_ERR_ARG for a shape that is not supported; a request
+ * whose initial slot is out of range is skipped on the device like one with
+ * a bad snapshot slot (out rows NaN, nothing stored).
  */
 int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
+                       const int32_t* init_slot_ids,
                        const float* q, const float* k, const float* v,
                        const float* g, const float* b, float* out,
                        int32_t n_req, int32_t n_rows_per_slot,
@@ -157,16 +176,36 @@ int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
                        const kda_launch_opts* opts, void* stream);
 
 /*
- * kda_validate -- host-side check of a launch's arguments and slot table
+ * kda_validate -- host-side check of a launch's arguments and slot tables
  * (ROCm/ATOM PR #2945, Changes: the step checks the pool's dtype against
  * the build; anything but fp32 or fp16 is refused).  slot_ids_host is a
  * HOST copy of the slot table [n_req * n_rows]; every id must lie in
- * [0, n_slots) and appear once.  Touches no device memory.  Returns KDA_OK
- * or the first error found, in the order: NULL, DTYPE_REFUSED,
- * DTYPE_MISMATCH, SHAPE, ROWS, ARG, SLOT.
+ * [0, n_slots) and appear once.  init_slot_ids_host is NULL or a host copy
+ * of the initial slots [n_req]: each in range and not among another
+ * request's snapshot slots.  Touches no device memory.  Returns KDA_OK or
+ * the first error found, in the order: NULL, DTYPE_REFUSED, DTYPE_MISMATCH,
+ * SHAPE, ROWS, ARG, SLOT.
  */
 int kda_validate(const kda_pool* pool, const int32_t* slot_ids_host,
-                 int32_t n_req, int32_t n_rows, kda_dtype state_dtype);
+                 const int32_t* init_slot_ids_host, int32_t n_req,
+                 int32_t n_rows, kda_dtype state_dtype);
+
+/*
+ * kda_state_copy -- copy whole slots of a pool: for i in [0, n), the
+ * [H, K, V] block of slot dst_slot_ids[i] becomes that of src_slot_ids[i]
+ * (every head).  The ReplaySSM-style checkpoint flush (a chosen snapshot
+ * into a checkpoint slot) and load (back into a working slot) through the
+ * same slot addressing as the decode (ROCm/ATOM PR #2945, Changes).
+ * src_slot_ids, dst_slot_ids: device int32 [n].  dst ids must be distinct
+ * and no dst may be another pair's src (caller contract).  A pair with an
+ * id out of range is skipped on the device.  Bytes are copied as they are:
+ * the pool keeps its dtype.  Errors: KDA_ERR_NULL, KDA_ERR_DTYPE_REFUSED,
+ * KDA_ERR_DTYPE_MISMATCH, KDA_ERR_SHAPE, KDA_ERR_ARG (n < 0 or n > 65535),
+ * KDA_ERR_ALIGN, KDA_ERR_LAUNCH.  n == 0 is a no-op.
+ */
+int kda_state_copy(const kda_pool* pool, const int32_t* src_slot_ids,
+                   const int32_t* dst_slot_ids, int32_t n, kda_dtype state_dtype,
+                   void* stream);
 
 /*
  * kda_state_at -- element offset, from pool->base, of the [H, K, V] block

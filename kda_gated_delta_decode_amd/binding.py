@@ -70,9 +70,10 @@ SIGNATURES = {
     "kda_decode_step": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P,
                                        _I32, _I32, ctypes.c_int, ctypes.c_float, _P]),
     "kda_decode_step_ex": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P,
-                                          _I32, _I32, ctypes.c_int, ctypes.c_float,
+                                          _P, _I32, _I32, ctypes.c_int, ctypes.c_float,
                                           ctypes.POINTER(kda_launch_opts), _P]),
-    "kda_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _I32, _I32, ctypes.c_int]),
+    "kda_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, ctypes.c_int]),
+    "kda_state_copy": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, ctypes.c_int, _P]),
     "kda_state_at": (ctypes.c_int64, [ctypes.POINTER(kda_pool), _P, _I32, _I32, _I32]),
     "kda_pool_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, ctypes.c_int]),
     "kda_tile_bv": (_I32, [ctypes.c_int]),
@@ -176,15 +177,17 @@ def _check(code: int, where: str) -> None:
 
 def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1,
                     state_dtype=None, scale: float | None = None, stream=None,
-                    waves_per_tile: int = 0, bv: int = 0, pool_dtype=None) -> None:
+                    waves_per_tile: int = 0, bv: int = 0, pool_dtype=None,
+                    init_slot_ids=None) -> None:
     """One decode launch (see kda_decode_step in include/kda_decode.h).
 
     pool: device tensor [n_slots, H, 128, 128], float32 or float16, updated
     in place.  slot_ids: device int32 [R]; q, k, g: device float32 [R, H, 128];
     v, out: [R, H, 128]; b: [R, H].  state_dtype defaults to the pool's
     dtype; pool_dtype overrides what the pool struct declares (tests of the
-    refusals).  A non-zero waves_per_tile or bv selects kda_decode_step_ex
-    with those launch options."""
+    refusals).  init_slot_ids (device int32 [n_req]) reads each request's
+    initial state from that slot; it, or a non-zero waves_per_tile or bv,
+    selects kda_decode_step_ex."""
     import torch
     P = make_pool(pool, pool_dtype)
     sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
@@ -194,24 +197,44 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
     n_req = R // n_rows_per_slot
     if scale is None:
         scale = 1.0 / math.sqrt(pool.shape[2])
-    args = (ctypes.byref(P), _dev(slot_ids, "slot_ids", torch.int32),
-            _dev(q, "q", torch.float32), _dev(k, "k", torch.float32), _dev(v, "v", torch.float32),
+    rows = (_dev(q, "q", torch.float32), _dev(k, "k", torch.float32), _dev(v, "v", torch.float32),
             _dev(g, "g", torch.float32), _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
             n_req, n_rows_per_slot, sd, float(scale))
-    if waves_per_tile or bv:
+    ids = _dev(slot_ids, "slot_ids", torch.int32)
+    if waves_per_tile or bv or init_slot_ids is not None:
+        if init_slot_ids is not None and init_slot_ids.numel() != n_req:
+            raise ValueError("init_slot_ids needs one entry per request")
         opts = kda_launch_opts(int(waves_per_tile), int(bv))
-        rc = library().kda_decode_step_ex(*args, ctypes.byref(opts), _stream_ptr(stream))
+        rc = library().kda_decode_step_ex(ctypes.byref(P), ids,
+                                          _dev(init_slot_ids, "init_slot_ids", torch.int32), *rows,
+                                          ctypes.byref(opts), _stream_ptr(stream))
         _check(rc, "kda_decode_step_ex")
     else:
-        rc = library().kda_decode_step(*args, _stream_ptr(stream))
+        rc = library().kda_decode_step(ctypes.byref(P), ids, *rows, _stream_ptr(stream))
         _check(rc, "kda_decode_step")
 
 
-def kda_validate(pool_desc: kda_pool, slot_ids_host, n_req: int, n_rows: int, state_dtype) -> int:
+def kda_validate(pool_desc: kda_pool, slot_ids_host, n_req: int, n_rows: int, state_dtype,
+                 init_slot_ids_host=None) -> int:
     """Host-side validation; returns the kda_status code (0 = OK)."""
     ids = np.ascontiguousarray(slot_ids_host, dtype=np.int32)
+    init = None if init_slot_ids_host is None else np.ascontiguousarray(init_slot_ids_host, dtype=np.int32)
     return int(library().kda_validate(ctypes.byref(pool_desc), ids.ctypes.data_as(ctypes.c_void_p),
+                                      None if init is None else init.ctypes.data_as(ctypes.c_void_p),
                                       n_req, n_rows, _dtype_arg(state_dtype)))
+
+
+def kda_state_copy(pool, src_slot_ids, dst_slot_ids, state_dtype=None, stream=None) -> None:
+    """Copy whole slots: pool[dst[i]] = pool[src[i]] (device int32 id tensors)."""
+    import torch
+    P = make_pool(pool)
+    sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
+    n = src_slot_ids.numel()
+    if dst_slot_ids.numel() != n:
+        raise ValueError("src and dst slot tables differ in length")
+    _check(library().kda_state_copy(ctypes.byref(P), _dev(src_slot_ids, "src_slot_ids", torch.int32),
+                                    _dev(dst_slot_ids, "dst_slot_ids", torch.int32), n, sd,
+                                    _stream_ptr(stream)), "kda_state_copy")
 
 
 def kda_state_at(pool_desc: kda_pool, slot_ids_host, n_rows: int, req: int, row: int) -> int:

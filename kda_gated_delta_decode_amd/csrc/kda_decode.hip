@@ -45,6 +45,7 @@ namespace kda {
 struct Args {
   void* pool;
   const int32_t* slot_ids;
+  const int32_t* init_slot_ids;  // nullable: per-request initial-state slot
   const float* q;
   const float* k;
   const float* v;
@@ -242,6 +243,8 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
     sid[t] = t < n_rows ? ids[t] : 0;
     ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
   }
+  const int32_t init_slot = a.init_slot_ids != nullptr ? a.init_slot_ids[r] : sid[0];
+  ids_ok = ids_ok && init_slot >= 0 && init_slot < a.n_slots;
   if (!ids_ok) {
     if (writer) {
       for (int t = 0; t < n_rows; ++t) {
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   T* const pool = static_cast<T*>(a.pool);
   vec raw[RPL];
   {
-    const T* src = pool + static_cast<int64_t>(sid[0]) * slot_elems + lane_off;
+    const T* src = pool + static_cast<int64_t>(init_slot) * slot_elems + lane_off;
 #pragma unroll
     for (int m = 0; m < RPL; ++m)
       raw[m] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(src + m * kHeadV));
@@ -431,6 +434,23 @@ __global__ __launch_bounds__(256) void kda_copy_probe_kernel(const f4* __restric
   if (i < n) dst[i] = src[i];
 }
 
+// ---------------------------------------------------------------------------
+// Whole-slot copies (checkpoint flush / load): grid.y = pair, grid.x covers
+// the slot's bytes, one 16-byte vector per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kda_state_copy_kernel(
+    char* __restrict__ pool, const int32_t* __restrict__ src_ids, const int32_t* __restrict__ dst_ids,
+    int32_t n_slots, int64_t slot_vecs) {
+  const int32_t s = src_ids[blockIdx.y];
+  const int32_t d = dst_ids[blockIdx.y];
+  if (s < 0 || s >= n_slots || d < 0 || d >= n_slots) return;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= slot_vecs) return;
+  const f4* src = reinterpret_cast<const f4*>(pool) + s * slot_vecs;
+  f4* dst = reinterpret_cast<f4*>(pool) + d * slot_vecs;
+  __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 template <typename T, int LPR, int NW>
 static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream) {
   if (a.n_rows == 1)
@@ -475,11 +495,11 @@ static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3
 
 using namespace kda;
 
-extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids, const float* q,
-                                  const float* k, const float* v, const float* g, const float* b,
-                                  float* out, int32_t n_req, int32_t n_rows_per_slot,
-                                  kda_dtype state_dtype, float scale, const kda_launch_opts* opts,
-                                  void* stream) {
+extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
+                                  const int32_t* init_slot_ids, const float* q, const float* k,
+                                  const float* v, const float* g, const float* b, float* out,
+                                  int32_t n_req, int32_t n_rows_per_slot, kda_dtype state_dtype,
+                                  float scale, const kda_launch_opts* opts, void* stream) {
   const int rc = check_common(pool, n_req, n_rows_per_slot, state_dtype);
   if (rc != KDA_OK) return rc;
   if (n_req == 0) return KDA_OK;  // empty launch: the row buffers may be NULL
@@ -490,12 +510,14 @@ extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
   Shape shape;
   if (!resolve_shape(state_dtype, n_rows_per_slot, opts, &shape)) return KDA_ERR_ARG;
   if (!aligned16(pool->base) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
-      !aligned16(g) || !aligned16(out) || !aligned4(b) || !aligned4(slot_ids))
+      !aligned16(g) || !aligned16(out) || !aligned4(b) || !aligned4(slot_ids) ||
+      !aligned4(init_slot_ids))
     return KDA_ERR_ALIGN;
 
   Args a;
   a.pool = pool->base;
   a.slot_ids = slot_ids;
+  a.init_slot_ids = init_slot_ids;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -519,8 +541,28 @@ extern "C" int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids, co
                                const float* k, const float* v, const float* g, const float* b,
                                float* out, int32_t n_req, int32_t n_rows_per_slot,
                                kda_dtype state_dtype, float scale, void* stream) {
-  return kda_decode_step_ex(pool, slot_ids, q, k, v, g, b, out, n_req, n_rows_per_slot,
+  return kda_decode_step_ex(pool, slot_ids, nullptr, q, k, v, g, b, out, n_req, n_rows_per_slot,
                             state_dtype, scale, nullptr, stream);
+}
+
+extern "C" int kda_state_copy(const kda_pool* pool, const int32_t* src_slot_ids,
+                              const int32_t* dst_slot_ids, int32_t n, kda_dtype state_dtype,
+                              void* stream) {
+  const int rc = check_common(pool, 0, 1, state_dtype);
+  if (rc != KDA_OK) return rc;
+  if (n < 0) return KDA_ERR_ARG;
+  if (n == 0) return KDA_OK;
+  if (src_slot_ids == nullptr || dst_slot_ids == nullptr) return KDA_ERR_NULL;
+  if (!aligned16(pool->base) || !aligned4(src_slot_ids) || !aligned4(dst_slot_ids))
+    return KDA_ERR_ALIGN;
+  const int64_t elem = state_dtype == KDA_F32 ? 4 : 2;
+  const int64_t slot_vecs = static_cast<int64_t>(pool->H) * kHeadK * kHeadV * elem / 16;
+  const int64_t bx = (slot_vecs + 255) / 256;
+  if (bx > INT32_MAX || n > 65535) return KDA_ERR_ARG;
+  hipLaunchKernelGGL(kda_state_copy_kernel, dim3(static_cast<uint32_t>(bx), static_cast<uint32_t>(n)),
+                     dim3(256), 0, static_cast<hipStream_t>(stream), static_cast<char*>(pool->base),
+                     src_slot_ids, dst_slot_ids, pool->n_slots, slot_vecs);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 extern "C" int kda_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {

@@ -4,7 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <unordered_set>
+#include <unordered_map>
 
 #include "kda_decode.h"
 #include "kda_internal.h"
@@ -41,18 +41,27 @@ using namespace kda;
 
 extern "C" {
 
-int kda_validate(const kda_pool* pool, const int32_t* slot_ids_host, int32_t n_req,
-                 int32_t n_rows, kda_dtype state_dtype) {
+int kda_validate(const kda_pool* pool, const int32_t* slot_ids_host,
+                 const int32_t* init_slot_ids_host, int32_t n_req, int32_t n_rows,
+                 kda_dtype state_dtype) {
   if (slot_ids_host == nullptr) return KDA_ERR_NULL;
   const int rc = check_common(pool, n_req, n_rows, state_dtype);
   if (rc != KDA_OK) return rc;
   const int64_t R = static_cast<int64_t>(n_req) * n_rows;
-  std::unordered_set<int32_t> seen;
-  seen.reserve(static_cast<size_t>(R));
+  std::unordered_map<int32_t, int32_t> owner;  // snapshot slot -> request
+  owner.reserve(static_cast<size_t>(R));
   for (int64_t i = 0; i < R; ++i) {
     const int32_t s = slot_ids_host[i];
     if (s < 0 || s >= pool->n_slots) return KDA_ERR_SLOT;
-    if (!seen.insert(s).second) return KDA_ERR_SLOT;
+    if (!owner.emplace(s, static_cast<int32_t>(i / n_rows)).second) return KDA_ERR_SLOT;
+  }
+  if (init_slot_ids_host != nullptr) {
+    for (int32_t r = 0; r < n_req; ++r) {
+      const int32_t s = init_slot_ids_host[r];
+      if (s < 0 || s >= pool->n_slots) return KDA_ERR_SLOT;
+      const auto it = owner.find(s);
+      if (it != owner.end() && it->second != r) return KDA_ERR_SLOT;  // another request writes it
+    }
   }
   return KDA_OK;
 }

@@ -39,10 +39,11 @@ def dense_token(S0: np.ndarray, q, k, v, g, b, scale: float):
 
 
 def dense_launch(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
-                 scale: float | None = None) -> np.ndarray:
+                 scale: float | None = None, init_slot_ids=None) -> np.ndarray:
     """A whole launch on an fp64 pool [n_slots, H, K, V], updated in place:
-    request r chains its n_rows tokens starting from slot slot_ids[r*n_rows]
-    and writes token t's state to slot slot_ids[r*n_rows + t]."""
+    request r chains its n_rows tokens starting from slot init_slot_ids[r]
+    (default slot_ids[r*n_rows]) and writes token t's state to slot
+    slot_ids[r*n_rows + t]."""
     n_slots, H, K, V = pool.shape
     if scale is None:
         scale = 1.0 / np.sqrt(K)
@@ -51,7 +52,8 @@ def dense_launch(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
     out = np.zeros((R, H, V), dtype=np.float64)
     for r in range(R // n_rows):
         for h in range(H):
-            S = pool[slot_ids[r * n_rows], h].astype(np.float64).copy()
+            s0 = slot_ids[r * n_rows] if init_slot_ids is None else init_slot_ids[r]
+            S = pool[s0, h].astype(np.float64).copy()
             for t in range(n_rows):
                 rho = r * n_rows + t
                 S, out[rho, h] = dense_token(S, q[rho, h], k[rho, h], v[rho, h],

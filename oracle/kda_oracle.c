@@ -97,13 +97,46 @@ void kdao_f16_to_f32_array(const uint16_t* h, float* x, int64_t n) {
   for (int64_t i = 0; i < n; ++i) x[i] = kdao_f16_to_f32(h[i]);
 }
 
+/* bfloat16 keeps binary32's sign and 8-bit exponent and the top 7 fraction
+ * bits; narrowing rounds the dropped 16 bits to nearest, ties to even (a
+ * carry into the exponent is the right encoding, up to infinity). */
+uint16_t kdao_f32_to_bf16_rne(float x) {
+  const uint32_t u = f32_bits(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u); /* quiet NaN */
+  const uint32_t rest = u & 0xffffu;
+  uint32_t hi = u >> 16;
+  if (rest > 0x8000u || (rest == 0x8000u && (hi & 1u))) hi += 1u;
+  return (uint16_t)hi;
+}
+
+float kdao_bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+void kdao_f32_to_bf16_rne_array(const float* x, uint16_t* h, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) h[i] = kdao_f32_to_bf16_rne(x[i]);
+}
+
+static float widen_any(const void* pool, int kind, int64_t i) {
+  if (kind == KDAO_POOL_F32) return ((const float*)pool)[i];
+  const uint16_t h = ((const uint16_t*)pool)[i];
+  return kind == KDAO_POOL_F16 ? kdao_f16_to_f32(h) : kdao_bf16_to_f32(h);
+}
+
+static void narrow_any(void* pool, int kind, int64_t i, float x) {
+  if (kind == KDAO_POOL_F32)
+    ((float*)pool)[i] = x;
+  else if (kind == KDAO_POOL_F16)
+    ((uint16_t*)pool)[i] = kdao_f32_to_f16_rne(x);
+  else
+    ((uint16_t*)pool)[i] = kdao_f32_to_bf16_rne(x);
+}
+
 /* ------------------------------------------------------------------------ */
 /* argument checks shared by both precisions                                */
 /* ------------------------------------------------------------------------ */
 
 static int check_args(const void* pool, int32_t n_slots, int32_t H, int32_t K,
-                      int32_t V, const int32_t* slot_ids, int32_t n_req,
-                      int32_t n_rows, const void* q, const void* k,
+                      int32_t V, const int32_t* slot_ids, const int32_t* init_slot_ids,
+                      int32_t n_req, int32_t n_rows, const void* q, const void* k,
                       const void* v, const void* g, const void* b,
                       const void* out) {
   if (!pool || !slot_ids || !q || !k || !v || !g || !b || !out) return 0;
@@ -112,6 +145,9 @@ static int check_args(const void* pool, int32_t n_slots, int32_t H, int32_t K,
   const int64_t R = (int64_t)n_req * n_rows;
   for (int64_t i = 0; i < R; ++i)
     if (slot_ids[i] < 0 || slot_ids[i] >= n_slots) return 0;
+  if (init_slot_ids)
+    for (int32_t r = 0; r < n_req; ++r)
+      if (init_slot_ids[r] < 0 || init_slot_ids[r] >= n_slots) return 0;
   return 1;
 }
 
@@ -127,11 +163,12 @@ static int64_t state_offset(int32_t slot, int32_t h, int32_t H, int32_t K,
 
 int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
                   int32_t K, int32_t V, const int32_t* slot_ids,
-                  int32_t n_req, int32_t n_rows, const float* q,
+                  const int32_t* init_slot_ids, int32_t n_req, int32_t n_rows, const float* q,
                   const float* k, const float* v, const float* g,
                   const float* b, float scale, float* out) {
-  if (pool_kind != KDAO_POOL_F32 && pool_kind != KDAO_POOL_F16) return KDAO_EARG;
-  if (!check_args(pool, n_slots, H, K, V, slot_ids, n_req, n_rows, q, k, v, g,
+  if (pool_kind != KDAO_POOL_F32 && pool_kind != KDAO_POOL_F16 && pool_kind != KDAO_POOL_BF16)
+    return KDAO_EARG;
+  if (!check_args(pool, n_slots, H, K, V, slot_ids, init_slot_ids, n_req, n_rows, q, k, v, g,
                   b, out))
     return KDAO_EARG;
 
@@ -146,21 +183,21 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
     free(S); free(qn); free(kn); free(a); free(w); free(u);
     return KDAO_EARG;
   }
-  float* pf = (float*)pool;
-  uint16_t* ph = (uint16_t*)pool;
 
   for (int32_t r = 0; r < n_req; ++r) {
     for (int32_t h = 0; h < H; ++h) {
-      /* initial state: the request's row-0 slot, widened exactly */
-      const int64_t off0 = state_offset(slot_ids[(int64_t)r * n_rows], h, H, K, V);
+      /* initial state: the request's initial slot if given, else its row-0
+       * slot; widened exactly */
+      const int32_t s0 = init_slot_ids ? init_slot_ids[r] : slot_ids[(int64_t)r * n_rows];
+      const int64_t off0 = state_offset(s0, h, H, K, V);
       for (int64_t e = 0; e < (int64_t)K * V; ++e)
-        S[e] = pool_kind == KDAO_POOL_F32 ? pf[off0 + e] : kdao_f16_to_f32(ph[off0 + e]);
+        S[e] = widen_any(pool, pool_kind, off0 + e);
 
       for (int32_t t = 0; t < n_rows; ++t) {
         const int64_t rho = (int64_t)r * n_rows + t;
         if (g_mutation == 9 && t > 0) { /* planted: chain not carried */
           for (int64_t e = 0; e < (int64_t)K * V; ++e)
-            S[e] = pool_kind == KDAO_POOL_F32 ? pf[off0 + e] : kdao_f16_to_f32(ph[off0 + e]);
+            S[e] = widen_any(pool, pool_kind, off0 + e);
         }
         const float* qv = q + (rho * H + h) * K;
         const float* kv = k + (rho * H + h) * K;
@@ -224,12 +261,7 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
         /* store this token's state to its snapshot slot */
         const int32_t dst_slot = g_mutation == 10 ? slot_ids[(int64_t)r * n_rows] : slot_ids[rho];
         const int64_t offt = state_offset(dst_slot, h, H, K, V);
-        for (int64_t e = 0; e < (int64_t)K * V; ++e) {
-          if (pool_kind == KDAO_POOL_F32)
-            pf[offt + e] = S[e];
-          else
-            ph[offt + e] = kdao_f32_to_f16_rne(S[e]);
-        }
+        for (int64_t e = 0; e < (int64_t)K * V; ++e) narrow_any(pool, pool_kind, offt + e, S[e]);
       }
     }
   }
@@ -242,11 +274,11 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
 /* ------------------------------------------------------------------------ */
 
 int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
-                  int32_t V, const int32_t* slot_ids, int32_t n_req,
+                  int32_t V, const int32_t* slot_ids, const int32_t* init_slot_ids, int32_t n_req,
                   int32_t n_rows, const float* q, const float* k,
                   const float* v, const float* g, const float* b,
                   double scale, double* out) {
-  if (!check_args(pool, n_slots, H, K, V, slot_ids, n_req, n_rows, q, k, v, g,
+  if (!check_args(pool, n_slots, H, K, V, slot_ids, init_slot_ids, n_req, n_rows, q, k, v, g,
                   b, out))
     return KDAO_EARG;
 
@@ -264,7 +296,8 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
 
   for (int32_t r = 0; r < n_req; ++r) {
     for (int32_t h = 0; h < H; ++h) {
-      const int64_t off0 = state_offset(slot_ids[(int64_t)r * n_rows], h, H, K, V);
+      const int32_t s0 = init_slot_ids ? init_slot_ids[r] : slot_ids[(int64_t)r * n_rows];
+      const int64_t off0 = state_offset(s0, h, H, K, V);
       for (int64_t e = 0; e < (int64_t)K * V; ++e) S[e] = pool[off0 + e];
 
       for (int32_t t = 0; t < n_rows; ++t) {

@@ -60,6 +60,7 @@ extern "C" {
 /* Pool element kinds understood by the oracle (its own numbering). */
 #define KDAO_POOL_F32 0
 #define KDAO_POOL_F16 1
+#define KDAO_POOL_BF16 2 /* error studies only: the library refuses bf16 pools */
 
 /* Return codes. */
 #define KDAO_OK 0
@@ -74,28 +75,42 @@ float kdao_f16_to_f32(uint16_t h);
 void kdao_f32_to_f16_rne_array(const float* x, uint16_t* h, int64_t n);
 void kdao_f16_to_f32_array(const uint16_t* h, float* x, int64_t n);
 
+/* bfloat16 (the top 16 bits of binary32): RNE narrowing, exact widening.
+ * Used only to measure what a bf16 pool would cost in accuracy (ROCm/ATOM
+ * PR #2130, What: bf16's 3 fewer mantissa bits cost roughly 8x the error). */
+uint16_t kdao_f32_to_bf16_rne(float x);
+float kdao_bf16_to_f32(uint16_t h);
+void kdao_f32_to_bf16_rne_array(const float* x, uint16_t* h, int64_t n);
+
 /*
  * One decode launch, fp32 recurrence.
  *   pool       host pool [n_slots, H, K, V] (V fastest), element kind
- *              pool_kind (float for F32, uint16_t fp16 bits for F16).
+ *              pool_kind (float for F32, uint16_t fp16 bits for F16,
+ *              uint16_t bf16 bits for BF16).
  *              Updated in place: row t of request r writes its post-update
  *              state to slot slot_ids[r * n_rows + t]; the initial state is
- *              read from slot slot_ids[r * n_rows].  Slots not named are
+ *              read from slot init_slot_ids[r] if init_slot_ids is not NULL,
+ *              else from slot slot_ids[r * n_rows].  Slots not named are
  *              untouched.
  *   slot_ids   [n_req * n_rows], distinct, each in [0, n_slots).
+ *   init_slot_ids  NULL or [n_req], each in [0, n_slots): where each
+ *              request's initial state is read (an earlier step's accepted
+ *              snapshot, or a checkpoint slot; ROCm/ATOM PR #2945, Changes:
+ *              the same address function serves the initial state, the
+ *              snapshots, and the checkpoint load).
  *   q, k, g    [n_req * n_rows, H, K]; v [.., H, V]; b [.., H]; fp32.
  *   out        [n_req * n_rows, H, V] fp32.
  * Returns KDAO_OK or KDAO_EARG (no partial writes on KDAO_EARG).
  */
 int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
                   int32_t K, int32_t V, const int32_t* slot_ids,
-                  int32_t n_req, int32_t n_rows, const float* q,
+                  const int32_t* init_slot_ids, int32_t n_req, int32_t n_rows, const float* q,
                   const float* k, const float* v, const float* g,
                   const float* b, float scale, float* out);
 
 /* The same loop carried out in fp64 on an fp64 pool (inputs widened). */
 int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
-                  int32_t V, const int32_t* slot_ids, int32_t n_req,
+                  int32_t V, const int32_t* slot_ids, const int32_t* init_slot_ids, int32_t n_req,
                   int32_t n_rows, const float* q, const float* k,
                   const float* v, const float* g, const float* b,
                   double scale, double* out);

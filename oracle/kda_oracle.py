@@ -16,6 +16,7 @@ from . import build as _build
 
 POOL_F32 = 0
 POOL_F16 = 1
+POOL_BF16 = 2
 
 _lib = None
 
@@ -40,12 +41,14 @@ def lib() -> ctypes.CDLL:
     L.kdao_f32_to_f16_rne_array.restype = None
     L.kdao_f16_to_f32_array.argtypes = [c_u16, c_f, ctypes.c_int64]
     L.kdao_f16_to_f32_array.restype = None
+    L.kdao_f32_to_bf16_rne_array.argtypes = [c_f, c_u16, ctypes.c_int64]
+    L.kdao_f32_to_bf16_rne_array.restype = None
     i32 = ctypes.c_int32
     L.kdao_step_f32.argtypes = [ctypes.c_void_p, ctypes.c_int, i32, i32, i32, i32,
-                                c_i, i32, i32, c_f, c_f, c_f, c_f, c_f,
+                                c_i, c_i, i32, i32, c_f, c_f, c_f, c_f, c_f,
                                 ctypes.c_float, c_f]
     L.kdao_step_f32.restype = ctypes.c_int
-    L.kdao_step_f64.argtypes = [c_d, i32, i32, i32, i32, c_i, i32, i32,
+    L.kdao_step_f64.argtypes = [c_d, i32, i32, i32, i32, c_i, c_i, i32, i32,
                                 c_f, c_f, c_f, c_f, c_f, ctypes.c_double, c_d]
     L.kdao_step_f64.restype = ctypes.c_int
     L.kdao_set_mutation.argtypes = [ctypes.c_int]
@@ -79,6 +82,24 @@ def f16_to_f32(h: np.ndarray) -> np.ndarray:
     return out
 
 
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """binary32 -> bfloat16 bits (uint16), round to nearest even."""
+    x = _f32(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().kdao_f32_to_bf16_rne_array(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def _init_ptr(init_slot_ids, n_req):
+    """(array kept alive, pointer) for an optional per-request initial slot table."""
+    if init_slot_ids is None:
+        return None, None
+    arr = np.ascontiguousarray(init_slot_ids, dtype=np.int32).reshape(-1)
+    if arr.size != n_req:
+        raise ValueError("init_slot_ids needs one entry per request")
+    return arr, _ptr(arr, ctypes.c_int32)
+
+
 def _check_inputs(pool, slot_ids, q, k, v, g, b, n_rows):
     n_slots, H, K, V = pool.shape
     slot_ids = np.ascontiguousarray(slot_ids, dtype=np.int32).reshape(-1)
@@ -96,15 +117,18 @@ def _check_inputs(pool, slot_ids, q, k, v, g, b, n_rows):
 
 
 def step_f32(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
-             scale: float | None = None) -> np.ndarray:
+             scale: float | None = None, init_slot_ids=None, bf16: bool = False) -> np.ndarray:
     """One decode launch in fp32 on a host pool (float32 or uint16 fp16 bits,
-    shape [n_slots, H, K, V]), updated in place.  Returns out [R, H, V]."""
+    shape [n_slots, H, K, V]), updated in place.  Returns out [R, H, V].
+    init_slot_ids: optional [n_req] slots holding each request's initial
+    state (default: each request's row-0 slot).  bf16=True reads a uint16
+    pool as bfloat16 bits (error studies only)."""
     if not pool.flags["C_CONTIGUOUS"]:
         raise ValueError("pool must be C-contiguous")
     if pool.dtype == np.float32:
         kind = POOL_F32
     elif pool.dtype == np.uint16:
-        kind = POOL_F16
+        kind = POOL_BF16 if bf16 else POOL_F16
     else:
         raise TypeError("oracle pool must be float32 or uint16 (fp16 bits)")
     (n_slots, H, K, V), slot_ids, q, k, v, g, b = _check_inputs(pool, slot_ids, q, k, v, g, b, n_rows)
@@ -112,8 +136,9 @@ def step_f32(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
         scale = 1.0 / np.sqrt(K)
     R = slot_ids.size
     out = np.zeros((R, H, V), dtype=np.float32)
+    keep, init_p = _init_ptr(init_slot_ids, R // n_rows)
     rc = lib().kdao_step_f32(pool.ctypes.data, kind, n_slots, H, K, V,
-                             _ptr(slot_ids, ctypes.c_int32), R // n_rows, n_rows,
+                             _ptr(slot_ids, ctypes.c_int32), init_p, R // n_rows, n_rows,
                              _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
                              _ptr(v, ctypes.c_float), _ptr(g, ctypes.c_float),
                              _ptr(b, ctypes.c_float), float(scale),
@@ -124,7 +149,7 @@ def step_f32(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
 
 
 def step_f64(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
-             scale: float | None = None) -> np.ndarray:
+             scale: float | None = None, init_slot_ids=None) -> np.ndarray:
     """The same launch in fp64 on a float64 host pool, updated in place."""
     if pool.dtype != np.float64 or not pool.flags["C_CONTIGUOUS"]:
         raise TypeError("fp64 oracle pool must be a C-contiguous float64 array")
@@ -133,8 +158,9 @@ def step_f64(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
         scale = 1.0 / np.sqrt(K)
     R = slot_ids.size
     out = np.zeros((R, H, V), dtype=np.float64)
+    keep, init_p = _init_ptr(init_slot_ids, R // n_rows)
     rc = lib().kdao_step_f64(_ptr(pool, ctypes.c_double), n_slots, H, K, V,
-                             _ptr(slot_ids, ctypes.c_int32), R // n_rows, n_rows,
+                             _ptr(slot_ids, ctypes.c_int32), init_p, R // n_rows, n_rows,
                              _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
                              _ptr(v, ctypes.c_float), _ptr(g, ctypes.c_float),
                              _ptr(b, ctypes.c_float), float(scale),

@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for expected in ["kda_decode_step", "kda_decode_step_ex", "kda_validate", "kda_state_at",
+                     "kda_state_copy",
                      "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
                      "kda_copy_probe", "kda_strerror", "kda_abi_version"]:
         assert expected in names
@@ -48,13 +49,15 @@ def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
     return B.kda_pool(ctypes.c_void_p(base), n_slots, H, Kd, V, dtype)
 
 
-def step(P, n_req=4, n_rows=1, state_dtype=None, scale=0.0883883, ptrs=None, opts=None):
+def step(P, n_req=4, n_rows=1, state_dtype=None, scale=0.0883883, ptrs=None, opts=None, init=None):
     p = [FAKE] * 7 if ptrs is None else ptrs
     sd = P.dtype if state_dtype is None else state_dtype
-    args = (ctypes.byref(P), *[ctypes.c_void_p(x) for x in p], n_req, n_rows, sd, scale)
-    if opts is None:
+    if opts is None and init is None:
+        args = (ctypes.byref(P), *[ctypes.c_void_p(x) for x in p], n_req, n_rows, sd, scale)
         return B.library().kda_decode_step(*args, None)
-    return B.library().kda_decode_step_ex(*args, ctypes.byref(opts), None)
+    args = (ctypes.byref(P), ctypes.c_void_p(p[0]), ctypes.c_void_p(init),
+            *[ctypes.c_void_p(x) for x in p[1:]], n_req, n_rows, sd, scale)
+    return B.library().kda_decode_step_ex(*args, None if opts is None else ctypes.byref(opts), None)
 
 
 def test_refusals_before_any_hip_call():
@@ -78,6 +81,8 @@ def test_refusals_before_any_hip_call():
     assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE]) == B.KDA_ERR_ALIGN
+    assert step(pool(), init=FAKE + 2) == B.KDA_ERR_ALIGN
+    assert step(pool(dtype=B.KDA_BF16), init=FAKE) == B.KDA_ERR_DTYPE_REFUSED
 
 
 @pytest.mark.parametrize("which", range(7))
@@ -98,6 +103,34 @@ def test_empty_launch_is_a_no_op():
     assert step(pool(base=0), n_req=0) == B.KDA_ERR_NULL
 
 
+def test_validate_initial_slots():
+    P = pool(n_slots=10)
+    ids = np.array([3, 1, 4, 0, 9, 2], dtype=np.int32)    # 3 requests x 2 rows
+    assert B.kda_validate(P, ids, 3, 2, B.KDA_F32, init_slot_ids_host=[5, 6, 7]) == B.KDA_OK
+    # a request may resume from one of its own snapshot slots ...
+    assert B.kda_validate(P, ids, 3, 2, B.KDA_F32, init_slot_ids_host=[1, 4, 2]) == B.KDA_OK
+    # ... and requests may share a read-only initial slot ...
+    assert B.kda_validate(P, ids, 3, 2, B.KDA_F32, init_slot_ids_host=[5, 5, 5]) == B.KDA_OK
+    # ... but not read a slot another request writes
+    assert B.kda_validate(P, ids, 3, 2, B.KDA_F32, init_slot_ids_host=[4, 6, 7]) == B.KDA_ERR_SLOT
+    assert B.kda_validate(P, ids, 3, 2, B.KDA_F32, init_slot_ids_host=[5, 6, 10]) == B.KDA_ERR_SLOT
+    assert B.kda_validate(P, ids, 3, 2, B.KDA_F32, init_slot_ids_host=[-1, 6, 7]) == B.KDA_ERR_SLOT
+
+
+def test_state_copy_refusals():
+    L = B.library()
+    P = pool(n_slots=10)
+    f = ctypes.c_void_p(FAKE)
+    assert L.kda_state_copy(ctypes.byref(P), f, f, 0, B.KDA_F32, None) == B.KDA_OK
+    assert L.kda_state_copy(ctypes.byref(P), f, f, -1, B.KDA_F32, None) == B.KDA_ERR_ARG
+    assert L.kda_state_copy(ctypes.byref(P), f, f, 70000, B.KDA_F32, None) == B.KDA_ERR_ARG
+    assert L.kda_state_copy(ctypes.byref(P), None, f, 2, B.KDA_F32, None) == B.KDA_ERR_NULL
+    assert L.kda_state_copy(ctypes.byref(P), f, f, 2, B.KDA_F16, None) == B.KDA_ERR_DTYPE_MISMATCH
+    P16 = pool(n_slots=10, dtype=B.KDA_BF16)
+    assert L.kda_state_copy(ctypes.byref(P16), f, f, 2, B.KDA_BF16, None) == B.KDA_ERR_DTYPE_REFUSED
+    assert L.kda_state_copy(ctypes.byref(P), ctypes.c_void_p(FAKE + 1), f, 2, B.KDA_F32, None) == B.KDA_ERR_ALIGN
+
+
 def test_validate_slot_table():
     P = pool(n_slots=10)
     ok = np.array([3, 1, 4, 0, 9, 2], dtype=np.int32)
@@ -107,7 +140,7 @@ def test_validate_slot_table():
     assert B.kda_validate(P, np.array([-1, 2], np.int32), 2, 1, B.KDA_F32) == B.KDA_ERR_SLOT
     assert B.kda_validate(P, ok, 3, 2, B.KDA_BF16) == B.KDA_ERR_DTYPE_REFUSED
     assert B.kda_validate(P, ok, 3, 2, B.KDA_F16) == B.KDA_ERR_DTYPE_MISMATCH
-    assert B.library().kda_validate(ctypes.byref(P), None, 3, 2, 0) == B.KDA_ERR_NULL
+    assert B.library().kda_validate(ctypes.byref(P), None, None, 3, 2, 0) == B.KDA_ERR_NULL
 
 
 def test_state_at_addresses_initial_and_snapshot_slots():

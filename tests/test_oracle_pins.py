@@ -357,3 +357,58 @@ def test_planted_mistakes_are_caught(oracle, mutation):
     finally:
         oracle.set_mutation(0)
     assert caught, "planted mistake %d passed every pin" % mutation
+
+
+# ---------------------------------------------------------------------------
+# initial state read from a separate slot (accepted-count / checkpoint load)
+# ---------------------------------------------------------------------------
+
+def test_init_slot_equal_to_row0_slot_changes_nothing(oracle):
+    inp = kda_inputs.make_inputs("init same", 20, 3, 4, "f16", seed=51)
+    p1, o1 = run_f32(oracle, inp)
+    p2 = inp.pool.copy()
+    o2 = oracle.step_f32(p2, inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b, n_rows=4,
+                         scale=inp.scale, init_slot_ids=inp.slot_ids[::4])
+    np.testing.assert_array_equal(p1, p2)
+    np.testing.assert_array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_init_slot_is_copy_then_launch(oracle, dtype):
+    # reading the initial state from slot i is the same as first copying
+    # slot i into the request's row-0 slot (NumPy copy) and launching as usual
+    inp = kda_inputs.make_inputs("init other", 24, 3, 2, dtype, seed=53)
+    free = np.setdiff1d(np.arange(24), inp.slot_ids)
+    init = free[:3].astype(np.int32)
+    p_init = inp.pool.copy()
+    o_init = oracle.step_f32(p_init, inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b, n_rows=2,
+                             scale=inp.scale, init_slot_ids=init)
+    p_copy = inp.pool.copy()
+    for r in range(3):
+        p_copy[inp.slot_ids[2 * r]] = p_copy[init[r]]
+    o_copy = oracle.step_f32(p_copy, inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b, n_rows=2,
+                             scale=inp.scale)
+    np.testing.assert_array_equal(p_init, p_copy)
+    np.testing.assert_array_equal(o_init.view(np.uint32), o_copy.view(np.uint32))
+    # and the init slots themselves are only read
+    np.testing.assert_array_equal(p_init[init], inp.pool[init])
+
+
+def test_init_slot_loop_matches_dense(oracle):
+    inp = small(n_slots=12, n_req=3, n_rows=3, K=8, V=8, seed=57)
+    init = np.array([11, 10, 9], dtype=np.int32)
+    pool = f64_pool(inp)
+    o_loop = oracle.step_f64(pool, inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b, n_rows=3,
+                             scale=inp.scale, init_slot_ids=init)
+    pd = f64_pool(inp)
+    o_dense = dense.dense_launch(pd, inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b, n_rows=3,
+                                 scale=inp.scale, init_slot_ids=init)
+    np.testing.assert_allclose(pool, pd, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(o_loop, o_dense, rtol=1e-12, atol=1e-14)
+
+
+def test_oracle_rejects_bad_init_slot(oracle):
+    inp = small()
+    with pytest.raises(ValueError):
+        oracle.step_f32(inp.pool.copy(), inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b,
+                        init_slot_ids=np.array([0, 6], dtype=np.int32))
