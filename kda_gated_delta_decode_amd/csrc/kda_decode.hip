@@ -114,6 +114,53 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
   return sum_xor32(x);
 }
 
+// Reduce-scatter over the row groups, for tiles whose per-wave sums then
+// meet in LDS.  The gfx950 permlane swaps exchange halves of TWO registers,
+// so one swap and one add reduce two values at once: after the swap over
+// lane bit 5 (and bit 4, unless LPR == 32) each lane quadrant q holds the
+// full sums of orig[q * M + j], j < M, in out[j].  With LPR == 8 the lanes
+// are first all-reduced over bit 3 (DPP), which leaves duplicates that only
+// the bit-3-clear lanes store.  Orig is laid out so each quadrant's values
+// are contiguous.
+template <int LPR>
+constexpr int rs_quadrants() { return LPR == 32 ? 2 : 4; }
+
+template <int LPR, int N>
+__device__ __forceinline__ void rowgroup_reduce_scatter(const float (&orig)[N],
+                                                        float (&out)[N / rs_quadrants<LPR>()]) {
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "8, 16 or 32 lanes per row");
+  constexpr int Q = rs_quadrants<LPR>();
+  constexpr int M = N / Q;
+  float x[N];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      float v = orig[q * M + j];
+      if constexpr (LPR == 8) v = sum_xor8(v);
+      x[Q * j + q] = v;
+    }
+  }
+  float y[N / 2];
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[2 * i]),
+                                                    __float_as_uint(x[2 * i + 1]), false, false);
+    y[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (Q == 2) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) out[i] = y[i];
+  } else {
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[2 * j]),
+                                                      __float_as_uint(y[2 * j + 1]), false, false);
+      out[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 16-byte state vectors: 4 fp32 or 8 fp16 columns of one tile row.
 // ---------------------------------------------------------------------------
@@ -355,32 +402,55 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
         for (int c = 0; c < CPL; ++c) S[m][c] = sp[c];
       }
     }
+    if constexpr (NW == 1) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      w[c] = rowgroup_sum<LPR>(w[c]);
-      p[c] = rowgroup_sum<LPR>(p[c]);
-    }
-    if constexpr (NW > 1) {
+      for (int c = 0; c < CPL; ++c) {
+        w[c] = rowgroup_sum<LPR>(w[c]);
+        p[c] = rowgroup_sum<LPR>(p[c]);
+      }
+    } else {
+      // reduce-scatter inside the wave, then the waves' sums meet in LDS
+      constexpr int Q = rs_quadrants<LPR>();
+      constexpr int M = 2 * CPL / Q;
+      float wp[2 * CPL], part[M];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        wp[c] = w[c];
+        wp[CPL + c] = p[c];
+      }
+      rowgroup_reduce_scatter<LPR>(wp, part);
+      const int quad = Q == 2 ? (lane >> 5) : ((lane >> 4) & 1) * 2 + (lane >> 5);
+      const int qty = (quad * M) / CPL;        // 0: w, 1: p
+      const int off = (quad * M) % CPL;        // first column of the quadrant
       const int par = t & 1;
-      if (rg == 0) {
+      if (LPR != 8 || (lane & 8) == 0) {
+        float* dstp = &s_red[par][wave][qty][cg * CPL + off];
+        if constexpr (M == 4) {
+          *reinterpret_cast<f4*>(dstp) = f4{part[0], part[1], part[2], part[3]};
+        } else {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          s_red[par][wave][0][cg * CPL + c] = w[c];
-          s_red[par][wave][1][cg * CPL + c] = p[c];
+          for (int m = 0; m < M; m += 2) *reinterpret_cast<f2*>(dstp + m) = f2{part[m], part[m + 1]};
         }
       }
       __syncthreads();
+      float tw[CPL], tp[CPL];
+      lds_rows<CPL>(&s_red[par][0][0][cg * CPL], tw);
+      lds_rows<CPL>(&s_red[par][0][1][cg * CPL], tp);
+#pragma unroll
+      for (int x = 1; x < NW; ++x) {
+        float xw[CPL], xp[CPL];
+        lds_rows<CPL>(&s_red[par][x][0][cg * CPL], xw);
+        lds_rows<CPL>(&s_red[par][x][1][cg * CPL], xp);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          tw[c] += xw[c];
+          tp[c] += xp[c];
+        }
+      }
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        float ws = s_red[par][0][0][cg * CPL + c];
-        float ps = s_red[par][0][1][cg * CPL + c];
-#pragma unroll
-        for (int x = 1; x < NW; ++x) {
-          ws += s_red[par][x][0][cg * CPL + c];
-          ps += s_red[par][x][1][cg * CPL + c];
-        }
-        w[c] = ws;
-        p[c] = ps;
+        w[c] = tw[c];
+        p[c] = tp[c];
       }
     }
 
