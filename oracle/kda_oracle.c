@@ -364,3 +364,54 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
   free(S); free(qn); free(kn); free(a); free(w); free(u);
   return KDAO_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* short causal convolution (see kda_oracle.h)                              */
+/* ------------------------------------------------------------------------ */
+
+int kdao_conv_f32(uint16_t* conv_pool, int32_t n_slots, int32_t C,
+                  const int32_t* slot_ids, const int32_t* init_slot_ids,
+                  int32_t n_req, int32_t n_rows, const float* x, const float* w,
+                  float* y) {
+  if (!conv_pool || !slot_ids || !x || !w || !y) return KDAO_EARG;
+  if (n_slots <= 0 || C <= 0 || n_req < 0 || n_rows <= 0) return KDAO_EARG;
+  const int64_t R = (int64_t)n_req * n_rows;
+  for (int64_t i = 0; i < R; ++i)
+    if (slot_ids[i] < 0 || slot_ids[i] >= n_slots) return KDAO_EARG;
+  if (init_slot_ids)
+    for (int32_t r = 0; r < n_req; ++r)
+      if (init_slot_ids[r] < 0 || init_slot_ids[r] >= n_slots) return KDAO_EARG;
+
+  const int32_t HIST = 3, TAPS = 4;
+  float* win = (float*)malloc(sizeof(float) * (size_t)(HIST + n_rows));
+  uint16_t* snap = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)R * HIST * C);
+  if (!win || !snap) {
+    free(win); free(snap);
+    return KDAO_EARG;
+  }
+  /* all reads of a launch see the pool as it was before the launch: the
+   * snapshots are staged and written at the end */
+  for (int32_t r = 0; r < n_req; ++r) {
+    const int32_t s0 = init_slot_ids ? init_slot_ids[r] : slot_ids[(int64_t)r * n_rows];
+    for (int32_t c = 0; c < C; ++c) {
+      for (int32_t e = 0; e < HIST; ++e)
+        win[e] = kdao_bf16_to_f32(conv_pool[((int64_t)s0 * HIST + e) * C + c]);
+      for (int32_t t = 0; t < n_rows; ++t) win[HIST + t] = x[((int64_t)r * n_rows + t) * C + c];
+      for (int32_t t = 0; t < n_rows; ++t) {
+        const int64_t rho = (int64_t)r * n_rows + t;
+        float acc = 0.0f;
+        for (int32_t j = 0; j < TAPS; ++j) acc = acc + w[(int64_t)c * TAPS + j] * win[t + j];
+        y[rho * C + c] = g_mutation == 12 ? acc : acc / (1.0f + expf(-acc));
+        for (int32_t e = 0; e < HIST; ++e)
+          snap[(rho * HIST + e) * C + c] = kdao_f32_to_bf16_rne(win[t + 1 + e]);
+      }
+    }
+  }
+  for (int64_t rho = 0; rho < R; ++rho)
+    for (int32_t e = 0; e < HIST; ++e)
+      for (int32_t c = 0; c < C; ++c)
+        conv_pool[((int64_t)slot_ids[rho] * HIST + e) * C + c] = snap[(rho * HIST + e) * C + c];
+  free(win);
+  free(snap);
+  return KDAO_OK;
+}

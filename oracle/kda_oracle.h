@@ -116,6 +116,33 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
                   double scale, double* out);
 
 /*
+ * Short causal convolution in front of the recurrence (q, k and v each pass
+ * a depthwise causal convolution of 4 taps, then SiLU).  The conv state of a
+ * slot holds the last 3 raw inputs of every channel in bfloat16: ROCm/ATOM
+ * PR #2130, Memory: the per-slot remainder that does not follow the state
+ * dtype is 1.91 MB over 69 layers = 3 entries x (3 x 12 x 128) channels x 2
+ * bytes; ROCm/ATOM PR #2894 (the two-node trial): the conv reads a 3-entry
+ * history, then writes back the old entries followed by the step's inputs.
+ *
+ *   conv_pool  [n_slots, 3, C] uint16 bf16 bits (entry 0 oldest), updated:
+ *              row t of request r writes its history after token t -- the
+ *              last 3 entries of (history, x_0 .. x_t) -- rounded to bf16
+ *              to nearest even, to slot slot_ids[r * n_rows + t].
+ *   slot_ids / init_slot_ids as in kdao_step_f32 (init NULL: the history is
+ *              read from the row-0 slot).
+ *   x          [n_req * n_rows, C] fp32 raw inputs; the rows of one launch use
+ *              their fp32 inputs directly, only the stored history rounds.
+ *   w          [C, 4] fp32 taps, w[c][3] multiplies the newest input.
+ *   y          [n_req * n_rows, C] fp32 outputs:
+ *              y_t = silu(sum_j w[j] * win[t + j]),  win = (hist, x_0 .. x_t),
+ *              silu(s) = s / (1 + exp(-s)), the sum taken j = 0..3 in order.
+ */
+int kdao_conv_f32(uint16_t* conv_pool, int32_t n_slots, int32_t C,
+                  const int32_t* slot_ids, const int32_t* init_slot_ids,
+                  int32_t n_req, int32_t n_rows, const float* x, const float* w,
+                  float* y);
+
+/*
  * Planted-mistake switch, for the tests that show the pins catch a wrong
  * oracle.  0 = none (default).  Any other value changes one term of
  * kdao_step_f32 / kdao_step_f64 (see kda_oracle.c).  Never set outside those

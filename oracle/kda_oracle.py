@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.kdao_step_f64.argtypes = [c_d, i32, i32, i32, i32, c_i, c_i, i32, i32,
                                 c_f, c_f, c_f, c_f, c_f, ctypes.c_double, c_d]
     L.kdao_step_f64.restype = ctypes.c_int
+    L.kdao_conv_f32.argtypes = [c_u16, i32, i32, c_i, c_i, i32, i32, c_f, c_f, c_f]
+    L.kdao_conv_f32.restype = ctypes.c_int
     L.kdao_set_mutation.argtypes = [ctypes.c_int]
     L.kdao_set_mutation.restype = None
     _lib = L
@@ -168,6 +170,29 @@ def step_f64(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
     return out
+
+
+def conv_f32(conv_pool: np.ndarray, slot_ids, x, w, n_rows: int = 1,
+             init_slot_ids=None) -> np.ndarray:
+    """Short causal convolution + SiLU over a host conv pool [n_slots, 3, C]
+    of bfloat16 bits (uint16), updated in place with each row's history
+    snapshot.  x: [R, C] fp32, w: [C, 4] fp32.  Returns y [R, C] fp32."""
+    if conv_pool.dtype != np.uint16 or conv_pool.ndim != 3 or conv_pool.shape[1] != 3 \
+            or not conv_pool.flags["C_CONTIGUOUS"]:
+        raise TypeError("conv pool must be a C-contiguous uint16 [n_slots, 3, C] array")
+    n_slots, _, C = conv_pool.shape
+    slot_ids = np.ascontiguousarray(slot_ids, dtype=np.int32).reshape(-1)
+    R = slot_ids.size
+    x = _f32(x).reshape(R, C)
+    w = _f32(w).reshape(C, 4)
+    y = np.zeros((R, C), dtype=np.float32)
+    keep, init_p = _init_ptr(init_slot_ids, R // n_rows)
+    rc = lib().kdao_conv_f32(_ptr(conv_pool, ctypes.c_uint16), n_slots, C,
+                             _ptr(slot_ids, ctypes.c_int32), init_p, R // n_rows, n_rows,
+                             _ptr(x, ctypes.c_float), _ptr(w, ctypes.c_float), _ptr(y, ctypes.c_float))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (code %d)" % rc)
+    return y
 
 
 def set_mutation(which: int) -> None:
