@@ -98,6 +98,7 @@ class Workload:
 
 
 EAGER = False
+ROT = 1 << 30  # bytes of pool copies each timed workload rotates over (> the 256 MiB MALL)
 
 
 def time_launches(fn, steps: int, warmup: int, torch):
@@ -222,7 +223,6 @@ def main():
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
 
-    ROT = 1 << 30
     main_inp = kda_inputs.batched_f32(0) if args.dtype == "f32" else kda_inputs.batched_f16(0)
     wl = Workload(main_inp, ROT, torch)
     log("workload:", main_inp.name, "rotation copies:", len(wl.pools))
@@ -324,6 +324,10 @@ def main():
             tt = time_launches(pingpong, max(50, args.steps // 2), 10, torch)
             extras["batched_%s_out_of_place" % args.dtype] = summarize(inp, tt)
             del w
+        if args.extras == "all":
+            for name, (n_req, n_rows, dt) in (("batched_%s_fused_conv" % args.dtype, (64, 1, args.dtype)),
+                                              ("spec_verify_f16_fused_conv", (8, 8, "f16"))):
+                extras[name] = fused_conv(n_req, n_rows, dt, B, torch, max(50, args.steps // 2))
         # a 69-layer decode step: 69 independent 64-slot pools, one launch each
         for dt in (("f32", "f16") if args.extras == "all" else ()):
             extras["layers69_" + dt] = layers69(dt, B, torch, steps=10, warmup=2)
@@ -340,6 +344,38 @@ def summarize(inp, tt):
     us = tt["ms_per_step"] * 1e3
     return {"workload": inp.name, "us_per_step": round(us, 3),
             "state_GB/s": round(sb / us / 1e3, 1),
+            "algorithmic_GB/s": round(ab / us / 1e3, 1),
+            "frac_of_peak": round(ab / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def fused_conv(n_req, n_rows, dtype, B, torch, steps):
+    """Time the decode step with the short convolution fused in front
+    (kda_decode_step_conv) on a 96-slot pool; state pools and conv pools both
+    rotate over >= 1 GiB.  Algorithmic bytes add to the plain step's the raw
+    q|k|v rows, the taps, and the conv history (3 bf16 entries of 3*H*128
+    channels) read once per request and written once per row."""
+    import kda_inputs
+    ci = kda_inputs.make_conv_inputs("fused conv + decode, %d req x %d rows, %s pool, H=12"
+                                     % (n_req, n_rows, dtype), 96, n_req, n_rows, dtype, seed=0)
+    inp = ci.dec
+    w = Workload(inp, ROT, torch)
+    conv0 = torch.from_numpy(ci.conv).cuda().view(torch.bfloat16)
+    convs = [conv0] + [conv0.clone() for _ in range(len(w.pools) - 1)]
+    x = torch.from_numpy(ci.x).cuda()
+    cw = torch.from_numpy(ci.w).cuda()
+
+    def step(i):
+        B.kda_decode_step_conv(w.pools[i % len(w.pools)], convs[i % len(convs)], w.ids, x, cw,
+                               w.g, w.b, w.out, n_rows_per_slot=n_rows, scale=inp.scale)
+    tt = time_launches(step, steps, 10, torch)
+    R, H = inp.slot_ids.size, inp.pool.shape[1]
+    hist = 3 * 3 * H * 128 * 2
+    extra = R * 3 * H * 128 * 4 + 3 * H * 128 * 4 * 4 + hist * (n_req + R) \
+        - R * H * 128 * 3 * 4  # x replaces q, k, v
+    us = tt["ms_per_step"] * 1e3
+    ab = inp.state_bytes() + inp.io_bytes() + extra
+    del w, convs
+    return {"workload": inp.name, "us_per_step": round(us, 3),
             "algorithmic_GB/s": round(ab / us / 1e3, 1),
             "frac_of_peak": round(ab / us / 1e3 / HBM_PEAK_GBS, 4)}
 

@@ -176,6 +176,50 @@ int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
                        const kda_launch_opts* opts, void* stream);
 
 /*
+ * A short-convolution history pool: device memory holding [n_slots, 3, C]
+ * bfloat16 values, C = 3 * H * 128 channels ordered (q | k | v) x H x 128,
+ * entry 0 the oldest of the last 3 raw inputs of each channel.  Slot s of
+ * the conv pool belongs with slot s of the state pool (one slot id addresses
+ * both).  2 bytes x 3 entries x 4608 channels = 27,648 bytes per slot per
+ * layer at H = 12: the part of the pages' per-slot memory that does not
+ * follow the state dtype (ROCm/ATOM PR #2130, Memory).  base 16-byte aligned.
+ */
+typedef struct kda_conv_pool {
+  void* base;
+  int32_t n_slots;
+  int32_t H;
+} kda_conv_pool;
+
+/*
+ * kda_decode_step_conv -- the decode step with the short causal convolution
+ * fused in front (q, k and v each pass a 4-tap depthwise causal convolution,
+ * then SiLU; ROCm/ATOM PR #2894, the two-node trial: a 3-entry history is
+ * read, then the old entries and the step's inputs are written back).
+ *
+ *  conv        the history pool (n_slots and H equal to the state pool's).
+ *  x           device fp32 [R, 3, H, 128]: the raw q, k, v inputs (before
+ *              the convolution) of every row.
+ *  conv_w      device fp32 [3, H, 128, 4]: per-channel taps, tap 3 on the
+ *              newest input.  No bias.
+ *  g, b, out, slot_ids, init_slot_ids, n_req, n_rows_per_slot,
+ *  state_dtype, scale, opts, stream: as in kda_decode_step_ex.
+ * For row t of request r: q, k, v = silu(sum_j w_j win[t + j]) over the
+ * window win = (history of the initial slot, raw rows 0..t of the request),
+ * then the decode update.  Row t's snapshot slot receives both the state and
+ * the history after row t (its last 3 raw inputs, rounded to bfloat16 to
+ * nearest even); rows of one launch use their fp32 inputs directly.
+ * Launch shapes: whole heads only (opts->bv 0 or 128; waves 2, 4 or 8).
+ * Errors: as kda_decode_step_ex, plus KDA_ERR_NULL for a missing conv pool,
+ * x or conv_w, KDA_ERR_SHAPE if the pools' n_slots or H differ.
+ */
+int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
+                         const int32_t* slot_ids, const int32_t* init_slot_ids,
+                         const float* x, const float* conv_w, const float* g,
+                         const float* b, float* out, int32_t n_req,
+                         int32_t n_rows_per_slot, kda_dtype state_dtype,
+                         float scale, const kda_launch_opts* opts, void* stream);
+
+/*
  * kda_validate -- host-side check of a launch's arguments and slot tables
  * (ROCm/ATOM PR #2945, Changes: the step checks the pool's dtype against
  * the build; anything but fp32 or fp16 is refused).  slot_ids_host is a

@@ -46,6 +46,10 @@ class kda_pool(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int)]
 
 
+class kda_conv_pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("n_slots", ctypes.c_int32), ("H", ctypes.c_int32)]
+
+
 class kda_launch_opts(ctypes.Structure):
     _fields_ = [("waves_per_tile", ctypes.c_int32), ("bv", ctypes.c_int32)]
 
@@ -72,6 +76,9 @@ SIGNATURES = {
     "kda_decode_step_ex": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P,
                                           _P, _I32, _I32, ctypes.c_int, ctypes.c_float,
                                           ctypes.POINTER(kda_launch_opts), _P]),
+    "kda_decode_step_conv": (ctypes.c_int, [ctypes.POINTER(kda_pool), ctypes.POINTER(kda_conv_pool),
+                                            _P, _P, _P, _P, _P, _P, _P, _I32, _I32, ctypes.c_int,
+                                            ctypes.c_float, ctypes.POINTER(kda_launch_opts), _P]),
     "kda_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, ctypes.c_int]),
     "kda_state_copy": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, ctypes.c_int, _P]),
     "kda_state_at": (ctypes.c_int64, [ctypes.POINTER(kda_pool), _P, _I32, _I32, _I32]),
@@ -157,6 +164,13 @@ def _dev(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need_numel(t, name, n):
+    """The library cannot see tensor sizes: refuse a tensor that holds fewer
+    (or more) elements than the launch will address."""
+    if t is not None and t.numel() != n:
+        raise ValueError("%s holds %d elements, the launch addresses %d" % (name, t.numel(), n))
+
+
 def _stream_ptr(stream):
     import torch
     if stream is None:
@@ -197,6 +211,11 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
     n_req = R // n_rows_per_slot
     if scale is None:
         scale = 1.0 / math.sqrt(pool.shape[2])
+    H = pool.shape[1]
+    for t, name, n in ((q, "q", R * H * pool.shape[2]), (k, "k", R * H * pool.shape[2]),
+                       (g, "g", R * H * pool.shape[2]), (v, "v", R * H * pool.shape[3]),
+                       (out, "out", R * H * pool.shape[3]), (b, "b", R * H)):
+        _need_numel(t, name, n)
     rows = (_dev(q, "q", torch.float32), _dev(k, "k", torch.float32), _dev(v, "v", torch.float32),
             _dev(g, "g", torch.float32), _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
             n_req, n_rows_per_slot, sd, float(scale))
@@ -212,6 +231,48 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
     else:
         rc = library().kda_decode_step(ctypes.byref(P), ids, *rows, _stream_ptr(stream))
         _check(rc, "kda_decode_step")
+
+
+def make_conv_pool(conv) -> kda_conv_pool:
+    """kda_conv_pool describing a device tensor [n_slots, 3, 3, H, 128] of
+    bfloat16 (the history of q | k | v)."""
+    import torch
+    if conv.dtype != torch.bfloat16 or not conv.is_contiguous() or conv.dim() != 5 \
+            or tuple(conv.shape[1:3]) != (3, 3) or conv.shape[4] != KDA_HEAD_K:
+        raise ValueError("conv pool must be a contiguous bfloat16 [n_slots, 3, 3, H, 128] tensor")
+    return kda_conv_pool(ctypes.c_void_p(conv.data_ptr()), conv.shape[0], conv.shape[3])
+
+
+def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot: int = 1,
+                         state_dtype=None, scale: float | None = None, stream=None,
+                         init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0) -> None:
+    """Decode step with the short causal convolution fused in front (see
+    kda_decode_step_conv in include/kda_decode.h).  conv: bfloat16 history
+    [n_slots, 3, 3, H, 128]; x: fp32 raw q|k|v [R, 3, H, 128]; conv_w: fp32
+    taps [3, H, 128, 4]; the other arguments as kda_decode_step."""
+    import torch
+    P = make_pool(pool)
+    Cv = make_conv_pool(conv)
+    sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
+    R = slot_ids.numel()
+    if R % n_rows_per_slot != 0:
+        raise ValueError("slot_ids holds %d rows, not a multiple of %d" % (R, n_rows_per_slot))
+    n_req = R // n_rows_per_slot
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.shape[2])
+    H = pool.shape[1]
+    for t, name, n in ((x, "x", R * 3 * H * KDA_HEAD_K), (conv_w, "conv_w", 3 * H * KDA_HEAD_K * 4),
+                       (g, "g", R * H * KDA_HEAD_K), (out, "out", R * H * KDA_HEAD_K),
+                       (b, "b", R * H), (init_slot_ids, "init_slot_ids", n_req)):
+        _need_numel(t, name, n)
+    opts = kda_launch_opts(int(waves_per_tile), int(bv))
+    rc = library().kda_decode_step_conv(
+        ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32),
+        _dev(init_slot_ids, "init_slot_ids", torch.int32), _dev(x, "x", torch.float32),
+        _dev(conv_w, "conv_w", torch.float32), _dev(g, "g", torch.float32),
+        _dev(b, "b", torch.float32), _dev(out, "out", torch.float32), n_req, n_rows_per_slot, sd,
+        float(scale), ctypes.byref(opts), _stream_ptr(stream))
+    _check(rc, "kda_decode_step_conv")
 
 
 def kda_validate(pool_desc: kda_pool, slot_ids_host, n_req: int, n_rows: int, state_dtype,

@@ -52,6 +52,10 @@ struct Args {
   const float* g;
   const float* b;
   float* out;
+  // fused short convolution (CONV kernels only)
+  const float* x;          // raw q|k|v inputs [R, 3, H, 128]
+  const float* conv_w;     // taps [3, H, 128, 4], tap 3 on the newest input
+  uint16_t* conv_pool;     // bf16 history [n_slots, 3, 3 * H * 128], entry 0 oldest
   int32_t n_slots;
   int32_t H;
   int32_t n_rows;
@@ -210,6 +214,19 @@ struct Lane16<_Float16> {
 };
 
 // ---------------------------------------------------------------------------
+// bfloat16 history entries of the short convolution: widening is exact (the
+// top half of a binary32); narrowing rounds to nearest even (v_cvt_pk_bf16_f32).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
+  const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+  const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float silu(float s) { return s / (1.0f + expf(-s)); }
+
+// ---------------------------------------------------------------------------
 // Reads of N consecutive fp32 values from LDS (N a multiple of 2; 16-byte
 // reads where N is a multiple of 4).
 // ---------------------------------------------------------------------------
@@ -238,7 +255,7 @@ __device__ __forceinline__ void lds_rows(const float* src, float (&dst)[N]) {
 // in registers across the request's rows); otherwise the request has one row
 // and the tile stays packed in its storage type, widened where it is used.
 // ---------------------------------------------------------------------------
-template <typename T, int LPR, int NW, bool MULTI>
+template <typename T, int LPR, int NW, bool MULTI, bool CONV>
 __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   using L = Lane16<T>;
   using vec = typename L::vec;
@@ -251,6 +268,9 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   constexpr int TPW = (TMAX + NW - 1) / NW;  // prologue rows per wave
   static_assert(RPL % 2 == 0 && RPL >= 2 && RPL * CPL <= 128, "2+ rows, <= 128 elements per lane");
   static_assert(BV <= kHeadV && kHeadV % BV == 0, "tiles must divide V");
+  // the fused convolution needs every channel of a head in one workgroup:
+  // its history reads and snapshot writes are then ordered by a barrier
+  static_assert(!CONV || BV == kHeadV, "the fused convolution takes whole heads");
 
   // Per-row vectors staged once: normalised q and k, decay a = exp(g), the
   // tile's columns of v, and the scalars beta and qn . kn.
@@ -308,17 +328,86 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   f2 q2[TPW], k2[TPW], g2[TPW];
   f4 v4[TPW];
   float braw[TPW];
+  // fused convolution: the history each row's snapshot keeps (window
+  // entries t+1 .. t+3) for this lane's 2 q, 2 k and 4 v channels
+  constexpr int TC = CONV ? TPW : 1;
+  f2 hq[TC][3], hk[TC][3];
+  f4 hv[TC][3];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     const int t = wave + j * NW;
     if (t < n_rows) {
       const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
       const int64_t voff = (rho * a.H + h) * kHeadK;
-      q2[j] = reinterpret_cast<const f2*>(a.q + voff)[lane];
-      k2[j] = reinterpret_cast<const f2*>(a.k + voff)[lane];
+      if constexpr (CONV) {
+        // y_t = silu(sum_j w_j win[t + j]), win = (3-entry history, rows of
+        // this request); the history comes from the initial slot
+        const int64_t C = static_cast<int64_t>(3) * a.H * kHeadK;
+        const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
+        const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
+        const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
+        const bool vl = lane < BV / 4;
+        f2 eq[4], ek[4];
+        f4 ev[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int pos = t + m;              // window index
+          if (pos < 3) {
+            const uint16_t* hb = a.conv_pool + (static_cast<int64_t>(init_slot) * 3 + pos) * C;
+            const uint32_t pq = *reinterpret_cast<const uint32_t*>(hb + chq);
+            const uint32_t pk = *reinterpret_cast<const uint32_t*>(hb + chk);
+            eq[m] = f2{bf16_lo(pq), bf16_hi(pq)};
+            ek[m] = f2{bf16_lo(pk), bf16_hi(pk)};
+            if (vl) {
+              const uint2 pv = *reinterpret_cast<const uint2*>(hb + chv);
+              ev[m] = f4{bf16_lo(pv.x), bf16_hi(pv.x), bf16_lo(pv.y), bf16_hi(pv.y)};
+            }
+          } else {
+            const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * C;
+            eq[m] = *reinterpret_cast<const f2*>(xr + chq);
+            ek[m] = *reinterpret_cast<const f2*>(xr + chk);
+            if (vl) ev[m] = *reinterpret_cast<const f4*>(xr + chv);
+          }
+        }
+        const f4 wq0 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4);
+        const f4 wq1 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4 + 4);
+        const f4 wk0 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4);
+        const f4 wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
+        float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          sq0 = fmaf(wq0[m], eq[m][0], sq0);
+          sq1 = fmaf(wq1[m], eq[m][1], sq1);
+          sk0 = fmaf(wk0[m], ek[m][0], sk0);
+          sk1 = fmaf(wk1[m], ek[m][1], sk1);
+        }
+        q2[j] = f2{silu(sq0), silu(sq1)};
+        k2[j] = f2{silu(sk0), silu(sk1)};
+        if (vl) {
+          f4 yv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f4 wv = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
+            float sv = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sv = fmaf(wv[m], ev[m][e], sv);
+            yv[e] = silu(sv);
+          }
+          v4[j] = yv;
+        }
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+          hq[j][e] = eq[e + 1];
+          hk[j][e] = ek[e + 1];
+          hv[j][e] = ev[e + 1];
+        }
+      } else {
+        q2[j] = reinterpret_cast<const f2*>(a.q + voff)[lane];
+        k2[j] = reinterpret_cast<const f2*>(a.k + voff)[lane];
+        if (lane < BV / 4)
+          v4[j] = *reinterpret_cast<const f4*>(a.v + (rho * a.H + h) * kHeadV + vt * BV + 4 * lane);
+      }
       g2[j] = reinterpret_cast<const f2*>(a.g + voff)[lane];
-      if (lane < BV / 4)
-        v4[j] = *reinterpret_cast<const f4*>(a.v + (rho * a.H + h) * kHeadV + vt * BV + 4 * lane);
       braw[j] = a.b[rho * a.H + h];
     }
   }
@@ -357,6 +446,34 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
     }
   }
   __syncthreads();
+
+  if constexpr (CONV) {
+    // every wave has read the history: the rows' snapshots may now overwrite
+    // it (row 0's slot is the initial slot of an in-place launch)
+    const int64_t C = static_cast<int64_t>(3) * a.H * kHeadK;
+    const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
+    const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
+    const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + j * NW;
+      if (t < n_rows) {
+        int32_t st = sid[0];
+#pragma unroll
+        for (int u = 1; u < TMAX; ++u)
+          if (u == t) st = sid[u];
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+          uint16_t* hb = a.conv_pool + (static_cast<int64_t>(st) * 3 + e) * C;
+          *reinterpret_cast<uint32_t*>(hb + chq) = bf16_pack(hq[j][e][0], hq[j][e][1]);
+          *reinterpret_cast<uint32_t*>(hb + chk) = bf16_pack(hk[j][e][0], hk[j][e][1]);
+          if (lane < BV / 4)
+            *reinterpret_cast<uint2*>(hb + chv) = uint2{bf16_pack(hv[j][e][0], hv[j][e][1]),
+                                                         bf16_pack(hv[j][e][2], hv[j][e][3])};
+        }
+      }
+    }
+  }
 
   // fp32 state kept across rows (chained variant only)
   float S[MULTI ? RPL : 1][CPL];
@@ -524,12 +641,36 @@ __global__ __launch_bounds__(256) void kda_state_copy_kernel(
 template <typename T, int LPR, int NW>
 static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream) {
   if (a.n_rows == 1)
-    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false>), dim3(blocks), dim3(kWave * NW), 0,
-                       stream, a);
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, false>), dim3(blocks), dim3(kWave * NW),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true>), dim3(blocks), dim3(kWave * NW), 0,
-                       stream, a);
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false>), dim3(blocks), dim3(kWave * NW),
+                       0, stream, a);
   return hipGetLastError();
+}
+
+// Fused-convolution launches: whole-head tiles (32 fp32 / 16 fp16 lanes per
+// row), 2, 4 or 8 waves.
+template <typename T, int LPR, int NW>
+static hipError_t launch_conv(const Args& a, int32_t blocks, hipStream_t stream) {
+  if (a.n_rows == 1)
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, true>), dim3(blocks), dim3(kWave * NW),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, true>), dim3(blocks), dim3(kWave * NW),
+                       0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dispatch_conv(const Args& a, int32_t nw, int32_t blocks, hipStream_t s) {
+  constexpr int LPR = kHeadV / Lane16<T>::kCols;
+  switch (nw) {
+    case 2: return launch_conv<T, LPR, 2>(a, blocks, s);
+    case 4: return launch_conv<T, LPR, 4>(a, blocks, s);
+    case 8: return launch_conv<T, LPR, 8>(a, blocks, s);
+    default: return hipErrorInvalidValue;  // unreachable: checked on the host
+  }
 }
 
 // One instantiation per shape that shape_supported() admits.
@@ -588,6 +729,9 @@ extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
   a.pool = pool->base;
   a.slot_ids = slot_ids;
   a.init_slot_ids = init_slot_ids;
+  a.x = nullptr;
+  a.conv_w = nullptr;
+  a.conv_pool = nullptr;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -613,6 +757,52 @@ extern "C" int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids, co
                                kda_dtype state_dtype, float scale, void* stream) {
   return kda_decode_step_ex(pool, slot_ids, nullptr, q, k, v, g, b, out, n_req, n_rows_per_slot,
                             state_dtype, scale, nullptr, stream);
+}
+
+extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
+                                    const int32_t* slot_ids, const int32_t* init_slot_ids,
+                                    const float* x, const float* conv_w, const float* g,
+                                    const float* b, float* out, int32_t n_req,
+                                    int32_t n_rows_per_slot, kda_dtype state_dtype, float scale,
+                                    const kda_launch_opts* opts, void* stream) {
+  const int rc = check_common(pool, n_req, n_rows_per_slot, state_dtype);
+  if (rc != KDA_OK) return rc;
+  if (conv == nullptr || conv->base == nullptr) return KDA_ERR_NULL;
+  if (conv->n_slots != pool->n_slots || conv->H != pool->H) return KDA_ERR_SHAPE;
+  if (n_req == 0) return KDA_OK;
+  if (slot_ids == nullptr || x == nullptr || conv_w == nullptr || g == nullptr || b == nullptr ||
+      out == nullptr)
+    return KDA_ERR_NULL;
+  if (!std::isfinite(scale)) return KDA_ERR_ARG;
+  Shape shape;
+  if (!resolve_conv_shape(state_dtype, n_rows_per_slot, opts, &shape)) return KDA_ERR_ARG;
+  if (!aligned16(pool->base) || !aligned16(conv->base) || !aligned16(x) || !aligned16(conv_w) ||
+      !aligned16(g) || !aligned16(out) || !aligned4(b) || !aligned4(slot_ids) ||
+      !aligned4(init_slot_ids))
+    return KDA_ERR_ALIGN;
+  Args a;
+  a.pool = pool->base;
+  a.slot_ids = slot_ids;
+  a.init_slot_ids = init_slot_ids;
+  a.q = nullptr;
+  a.k = nullptr;
+  a.v = nullptr;
+  a.g = g;
+  a.b = b;
+  a.out = out;
+  a.x = x;
+  a.conv_w = conv_w;
+  a.conv_pool = static_cast<uint16_t*>(conv->base);
+  a.n_slots = pool->n_slots;
+  a.H = pool->H;
+  a.n_rows = n_rows_per_slot;
+  a.n_vt = 1;
+  a.scale = scale;
+  const int32_t blocks = n_req * pool->H;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err = state_dtype == KDA_F32 ? dispatch_conv<float>(a, shape.nw, blocks, s)
+                                                : dispatch_conv<_Float16>(a, shape.nw, blocks, s);
+  return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 extern "C" int kda_state_copy(const kda_pool* pool, const int32_t* src_slot_ids,

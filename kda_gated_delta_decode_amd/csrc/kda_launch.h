@@ -86,6 +86,21 @@ inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows) {
   return 4 * (staged + red);
 }
 
+// Fused-convolution launches take whole heads (bv = 128) so that a head's
+// convolution history is read and rewritten inside one workgroup; waves per
+// tile 2, 4 or 8 (default: 2 fp32 / 4 fp16 for one row, 8 / 4 for chained
+// rows).  A bv option other than 0 or 128 is refused.
+inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts,
+                               Shape* out) {
+  Shape s{kHeadV, n_rows == 1 ? (dt == KDA_F32 ? 2 : 4) : (dt == KDA_F32 ? 8 : 4)};
+  if (opts != nullptr) {
+    if (opts->bv != 0 && opts->bv != kHeadV) return false;
+    if (opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
+  }
+  *out = s;
+  return s.nw == 2 || s.nw == 4 || s.nw == 8;
+}
+
 // XCD-aware block -> tile map.  The dispatcher sends block b to XCD b % 8;
 // give XCD x the x-th contiguous range of tiles, so the V-tiles of one
 // (request, head) run on one XCD and share its L2.  A bijection of [0, n).

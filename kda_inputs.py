@@ -152,3 +152,31 @@ WORKLOADS = {
     "batched_f16": batched_f16,
     "spec_verify_f16": spec_verify_f16,
 }
+
+
+@dataclass
+class ConvInputs:
+    """Inputs of a decode launch with the short convolution fused in front:
+    the decode inputs (q, k, v unused) plus the conv history pool (bfloat16
+    bits [n_slots, 3, 3, H, 128]), the raw q|k|v rows x [R, 3, H, 128] and the
+    taps w [3, H, 128, 4]."""
+    dec: DecodeInputs
+    conv: np.ndarray
+    x: np.ndarray
+    w: np.ndarray
+
+
+def make_conv_inputs(name: str, n_slots: int, n_req: int, n_rows: int, dtype: str = "f32",
+                     H: int = H_DEFAULT, seed: int = 0) -> ConvInputs:
+    """Recipe: the decode draws of make_inputs(seed), then from
+    default_rng(seed + 10**6): the conv history ~ N(0, 1) cut to bfloat16 (the
+    top 16 bits of the fp32 draw: any bfloat16 value is a valid history), the
+    raw rows x ~ N(0, 1), the taps w ~ N(0, 0.5^2)."""
+    dec = make_inputs(name, n_slots, n_req, n_rows, dtype, H=H, seed=seed)
+    rng = np.random.default_rng(seed + 10 ** 6)
+    hist = rng.standard_normal((n_slots, 3, 3, H, K_DEFAULT), dtype=np.float32)
+    conv = (hist.view(np.uint32) >> 16).astype(np.uint16)
+    R = n_req * n_rows
+    x = rng.standard_normal((R, 3, H, K_DEFAULT), dtype=np.float32)
+    w = rng.standard_normal((3, H, K_DEFAULT, 4), dtype=np.float32) * np.float32(0.5)
+    return ConvInputs(dec, conv, x, w)

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for expected in ["kda_decode_step", "kda_decode_step_ex", "kda_validate", "kda_state_at",
-                     "kda_state_copy",
+                     "kda_state_copy", "kda_decode_step_conv",
                      "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
                      "kda_copy_probe", "kda_strerror", "kda_abi_version"]:
         assert expected in names
@@ -244,3 +244,32 @@ def test_strerror_names_every_code():
     assert len(set(msgs.values())) == 10
     assert "bf16" in msgs[B.KDA_ERR_DTYPE_REFUSED]
     assert B.kda_strerror(1234) == "unknown kda status code"
+
+
+def conv_step(P, conv, n_req=4, n_rows=1, ptrs=None, opts=None, scale=0.0883883):
+    p = [FAKE] * 7 if ptrs is None else ptrs     # slot_ids, x, conv_w, g, b, out, init
+    f = [ctypes.c_void_p(v) for v in p]
+    return B.library().kda_decode_step_conv(
+        ctypes.byref(P), None if conv is None else ctypes.byref(conv), f[0], f[6], f[1], f[2],
+        f[3], f[4], f[5], n_req, n_rows, P.dtype, scale,
+        None if opts is None else ctypes.byref(opts), None)
+
+
+def test_conv_step_refusals():
+    P = pool(n_slots=16)
+    Cv = B.kda_conv_pool(ctypes.c_void_p(FAKE), 16, 12)
+    assert conv_step(P, None) == B.KDA_ERR_NULL
+    assert conv_step(P, B.kda_conv_pool(None, 16, 12)) == B.KDA_ERR_NULL
+    assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE), 15, 12)) == B.KDA_ERR_SHAPE
+    assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE), 16, 8)) == B.KDA_ERR_SHAPE
+    assert conv_step(pool(n_slots=16, dtype=B.KDA_BF16), Cv) == B.KDA_ERR_DTYPE_REFUSED
+    assert conv_step(P, Cv, n_rows=9) == B.KDA_ERR_ROWS
+    assert conv_step(P, Cv, n_req=0) == B.KDA_OK
+    for which in range(6):
+        ptrs = [FAKE] * 7
+        ptrs[which] = 0
+        assert conv_step(P, Cv, ptrs=ptrs) == B.KDA_ERR_NULL
+    assert conv_step(P, Cv, opts=B.kda_launch_opts(0, 64)) == B.KDA_ERR_ARG   # whole heads only
+    assert conv_step(P, Cv, opts=B.kda_launch_opts(1, 0)) == B.KDA_ERR_ARG
+    assert conv_step(P, Cv, scale=float("nan")) == B.KDA_ERR_ARG
+    assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE + 8), 16, 12)) == B.KDA_ERR_ALIGN

@@ -1,0 +1,108 @@
+"""GPU parity of the decode step with the short causal convolution fused in
+front (kda_decode_step_conv) against the oracle's composition: the
+convolution (oracle.conv_f32) and then the decode (oracle.step_f32).
+
+State and outputs to the decode tolerances; the convolution histories the
+launch writes (RNE bfloat16 of raw inputs) bit for bit; slots not named
+untouched in both pools."""
+import numpy as np
+import pytest
+
+import kda_inputs
+from gpu_helpers import (B, F16_ULP, OUT_REL, STATE_ABS_F32, f16_ulp_distance, need_gpu,
+                         out_rel_err, pool_to_host, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def gpu_conv(ci, init=None, waves=0):
+    d = ci.dec
+    dev = torch.device("cuda", 0)
+    pool = torch.from_numpy(d.pool if d.dtype == "f32" else d.pool.view(np.float16)).to(dev)
+    conv = torch.from_numpy(ci.conv).to(dev).view(torch.bfloat16)
+    ids = torch.from_numpy(d.slot_ids).to(dev)
+    x = torch.from_numpy(ci.x).to(dev)
+    w = torch.from_numpy(ci.w).to(dev)
+    g = torch.from_numpy(d.g).to(dev)
+    b = torch.from_numpy(d.b).to(dev)
+    out = torch.full((d.slot_ids.size, d.pool.shape[1], 128), float("nan"), device=dev)
+    init_d = None if init is None else torch.from_numpy(np.asarray(init, np.int32)).to(dev)
+    B.kda_decode_step_conv(pool, conv, ids, x, w, g, b, out, n_rows_per_slot=d.n_rows,
+                           scale=d.scale, init_slot_ids=init_d, waves_per_tile=waves)
+    torch.cuda.synchronize()
+    return pool_to_host(pool), conv.view(torch.int16).cpu().numpy().view(np.uint16), out.cpu().numpy()
+
+
+def oracle_conv(oracle, ci, init=None):
+    d = ci.dec
+    n_slots, H = d.pool.shape[0], d.pool.shape[1]
+    C = 3 * H * 128
+    conv = ci.conv.reshape(n_slots, 3, C).copy()
+    R = d.slot_ids.size
+    y = oracle.conv_f32(conv, d.slot_ids, ci.x.reshape(R, C), ci.w.reshape(C, 4),
+                        n_rows=d.n_rows, init_slot_ids=init).reshape(R, 3, H, 128)
+    pool = d.pool.copy()
+    out = oracle.step_f32(pool, d.slot_ids, np.ascontiguousarray(y[:, 0]), np.ascontiguousarray(y[:, 1]),
+                          np.ascontiguousarray(y[:, 2]), d.g, d.b, n_rows=d.n_rows, scale=d.scale,
+                          init_slot_ids=init)
+    return pool, conv.reshape(ci.conv.shape), out
+
+
+def check(oracle, ci, init=None, waves=0):
+    gp, gc, go = gpu_conv(ci, init, waves)
+    op, oc, oo = oracle_conv(oracle, ci, init)
+    d = ci.dec
+    if d.dtype == "f32":
+        assert np.max(np.abs(gp - op)) <= STATE_ABS_F32
+    else:
+        assert f16_ulp_distance(gp, op).max() <= F16_ULP
+    assert out_rel_err(go, oo) <= OUT_REL
+    np.testing.assert_array_equal(gc, oc)
+    untouched = np.setdiff1d(np.arange(d.pool.shape[0]), np.concatenate(
+        [d.slot_ids, [] if init is None else np.asarray(init)]).astype(int))
+    np.testing.assert_array_equal(gc[untouched], ci.conv[untouched])
+    np.testing.assert_array_equal(gp[untouched], d.pool[untouched])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("n_req,n_rows", [(64, 1), (8, 8), (3, 5)])
+def test_fused_conv_parity(oracle, dtype, n_req, n_rows):
+    ci = kda_inputs.make_conv_inputs("conv", 96, n_req, n_rows, dtype, seed=101 + n_rows)
+    check(oracle, ci)
+
+
+@pytest.mark.parametrize("waves", [2, 4, 8])
+@pytest.mark.parametrize("n_rows", [1, 6])
+def test_fused_conv_every_wave_count(oracle, waves, n_rows):
+    ci = kda_inputs.make_conv_inputs("conv waves", 40, 4, n_rows, "f16", H=3, seed=131 + waves)
+    check(oracle, ci, waves=waves)
+
+
+@pytest.mark.parametrize("n_rows", [1, 4])
+def test_fused_conv_initial_slots(oracle, n_rows):
+    ci = kda_inputs.make_conv_inputs("conv init", 64, 6, n_rows, "f32", seed=141)
+    free = np.setdiff1d(np.arange(64), ci.dec.slot_ids)
+    init = np.random.default_rng(3).permutation(free)[:6].astype(np.int32)
+    check(oracle, ci, init=init)
+
+
+def test_fused_conv_identity_taps_equal_plain_decode_of_silu(oracle):
+    # taps (0, 0, 0, 1): q, k, v = silu(x); the state update must then equal
+    # the plain decode launched on silu(x) (same kernels downstream)
+    ci = kda_inputs.make_conv_inputs("conv id", 32, 8, 1, "f32", seed=151)
+    ci.w[:] = 0.0
+    ci.w[..., 3] = 1.0
+    gp, gc, go = gpu_conv(ci)
+    d = ci.dec
+    xs = ci.x.astype(np.float64)
+    y = (xs / (1.0 + np.exp(-xs))).astype(np.float32)
+    op = d.pool.copy()
+    oo = oracle.step_f32(op, d.slot_ids, np.ascontiguousarray(y[:, 0]), np.ascontiguousarray(y[:, 1]),
+                         np.ascontiguousarray(y[:, 2]), d.g, d.b, n_rows=1, scale=d.scale)
+    assert np.max(np.abs(gp - op)) <= STATE_ABS_F32
+    assert out_rel_err(go, oo) <= OUT_REL
