@@ -1,0 +1,179 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the
+benchmark (kernel durations, HBM traffic per launch).
+
+    python -m kda_gated_delta_decode_amd.profiling trace --stats S.csv --trace T.csv \
+        --kernel SUBSTR --timed N --command "..." --title "..." --out FILE.md
+    python -m kda_gated_delta_decode_amd.profiling pmc --run LABEL FETCH.csv WRITE.csv \
+        [--run ...] --command "..." --out FILE.json
+
+`pmc` calibrates the counters on the plain copy kernel of the same runs:
+kda_copy_probe_kernel copies one 16-byte vector per thread, so a dispatch of
+grid G work-items reads and writes 16 G bytes.  FETCH_SIZE and WRITE_SIZE
+(KiB per dispatch) are scaled by (16 G) / (1024 * counter) averaged over the
+copy dispatches, then applied to the decode kernel's mean per dispatch.
+
+Reads only the CSV files it is given; runs nothing on the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(HERE, "csrc", "kda_decode.hip")
+COPY_KERNEL = "kda_copy_probe_kernel"
+DECODE_KERNEL = "kda_decode_tile"
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_by_dispatch(path, counter):
+    """{kernel name: [(grid size, value), ...]} for one counter, one entry per
+    dispatch (values of several agents / dimensions of a dispatch summed)."""
+    per = defaultdict(float)
+    meta = {}
+    for r in _rows(path):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        per[key] += float(r["Counter_Value"])
+        meta[key] = (r["Kernel_Name"], int(r["Grid_Size"]))
+    out = defaultdict(list)
+    for key in sorted(per):
+        name, grid = meta[key]
+        out[name].append((grid, per[key]))
+    return out
+
+
+def pmc(args):
+    import kda_inputs
+    runs = {}
+    fetch_factors, write_factors, calib = [], [], {}
+    for label, fpath, wpath in args.run:
+        fe = _counter_by_dispatch(fpath, "FETCH_SIZE")
+        wr = _counter_by_dispatch(wpath, "WRITE_SIZE")
+        for name in fe:
+            if COPY_KERNEL not in name:
+                continue
+            by_bytes_f, by_bytes_w = defaultdict(list), defaultdict(list)
+            for grid, v in fe[name]:
+                by_bytes_f[16 * grid].append(v)
+            for grid, v in wr.get(name, []):
+                by_bytes_w[16 * grid].append(v)
+            for nbytes in sorted(by_bytes_f):
+                ff = nbytes / (statistics.mean(by_bytes_f[nbytes]) * 1024)
+                wf = nbytes / (statistics.mean(by_bytes_w[nbytes]) * 1024)
+                fetch_factors.append(ff)
+                write_factors.append(wf)
+                calib["%s/%d" % (label, nbytes)] = {
+                    "bytes_copied": nbytes,
+                    "FETCH_SIZE_KiB": round(statistics.mean(by_bytes_f[nbytes]), 1),
+                    "WRITE_SIZE_KiB": round(statistics.mean(by_bytes_w[nbytes]), 1),
+                    "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}
+        dec = [n for n in fe if DECODE_KERNEL in n]
+        if len(dec) != 1:
+            raise SystemExit("run %s: expected one decode kernel, found %r" % (label, dec))
+        runs[label] = (dec[0], fe[dec[0]], wr[dec[0]])
+    ff = statistics.mean(fetch_factors)
+    wf = statistics.mean(write_factors)
+    launches = {}
+    for label, (name, fe, wr) in runs.items():
+        dtype = label.split("_")[0]
+        inp = kda_inputs.batched_f32(0) if dtype == "f32" else kda_inputs.batched_f16(0)
+        fk = statistics.mean(v for _, v in fe)
+        wk = statistics.mean(v for _, v in wr)
+        rd, wt = fk * 1024 * ff, wk * 1024 * wf
+        alg = inp.state_bytes() + inp.io_bytes()
+        launches[label] = {"kernel": name, "dispatches": len(fe),
+                           "FETCH_SIZE_KiB": round(fk, 1), "WRITE_SIZE_KiB": round(wk, 1),
+                           "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wt),
+                           "hbm_bytes_per_launch": int(rd + wt),
+                           "algorithmic_bytes_per_launch": alg,
+                           "hbm_over_algorithmic": round((rd + wt) / alg, 4)}
+    doc = {"what": "HBM traffic of the decode kernel from rocprofv3 --pmc FETCH_SIZE and "
+                   "WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the same "
+                   "counter to the known bytes of the plain copy kernel in the same runs",
+           "commands": args.command, "kernel_source_sha256_16": kernel_hash(),
+           "calibration_copy_probe": calib, "fetch_factor": round(ff, 4),
+           "write_factor": round(wf, 4), "launches": launches}
+    with open(args.out, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+
+
+def trace(args):
+    stats = _rows(args.stats)
+    lines = ["# %s" % args.title, "",
+             "Command (from the repository root, `TMPDIR=/tmp`):", "", "```"]
+    lines += args.command + ["```", "",
+                             "Kernel source sha256[:16] at the time: `%s`." % kernel_hash(), "",
+                             "## rocprofv3 kernel stats (all dispatches of the run)", "",
+                             "| Kernel | Calls | Average µs | Min µs | Max µs |", "|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"][:100]
+        lines.append("| `%s` | %s | %.3f | %.3f | %.3f |" % (
+            name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3))
+    tr = [r for r in _rows(args.trace) if args.kernel in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = sorted({r["Kernel_Name"] for r in tr})
+    timed = tr[-args.timed:]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+    span = (int(timed[-1]["End_Timestamp"]) - int(timed[0]["Start_Timestamp"])) / 1e3
+    gaps = [(int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3
+            for a, b in zip(timed, timed[1:])]
+    q = statistics.quantiles(dur, n=10)
+    lines += ["", "## The timed launches (the last %d dispatches of `%s`)" % (args.timed, args.kernel), "",
+              "- kernel(s): %s" % ", ".join("`%s`" % n for n in names),
+              "- kernel duration mean %.3f µs, median %.3f µs, p10 %.3f µs, p90 %.3f µs" % (
+                  statistics.mean(dur), statistics.median(dur), q[0], q[-1]),
+              "- first start to last end / %d = %.3f µs; median gap between launches %.3f µs" % (
+                  args.timed, span / args.timed, statistics.median(gaps) if gaps else 0.0)]
+    if args.algorithmic_bytes:
+        m = statistics.mean(dur)
+        lines.append("- %d algorithmic bytes / %.3f µs = %.0f GB/s = %.1f%% of 8 TB/s" % (
+            args.algorithmic_bytes, m, args.algorithmic_bytes / m / 1e3,
+            100 * args.algorithmic_bytes / m / 1e3 / 8000))
+    for note in args.note or []:
+        lines += ["", note]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("--run", nargs=3, action="append", required=True,
+                   metavar=("LABEL", "FETCH_CSV", "WRITE_CSV"))
+    p.add_argument("--command", action="append", required=True)
+    p.add_argument("--out", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--stats", required=True)
+    t.add_argument("--trace", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--timed", type=int, required=True)
+    t.add_argument("--algorithmic-bytes", type=int, default=0)
+    t.add_argument("--command", action="append", required=True)
+    t.add_argument("--title", required=True)
+    t.add_argument("--note", action="append")
+    t.add_argument("--out", required=True)
+    a = ap.parse_args()
+    (pmc if a.cmd == "pmc" else trace)(a)
+
+
+if __name__ == "__main__":
+    main()
