@@ -180,3 +180,74 @@ def make_conv_inputs(name: str, n_slots: int, n_req: int, n_rows: int, dtype: st
     x = rng.standard_normal((R, 3, H, K_DEFAULT), dtype=np.float32)
     w = rng.standard_normal((3, H, K_DEFAULT, 4), dtype=np.float32) * np.float32(0.5)
     return ConvInputs(dec, conv, x, w)
+
+
+@dataclass
+class PrefillInputs:
+    """Inputs of one prefill launch: n_seq sequences packed along the token
+    axis (cu_seqlens), each starting from its initial slot of the pool and
+    storing its final state to its destination slot."""
+    name: str
+    dtype: str
+    pool: np.ndarray           # [n_slots, H, K, V] float32, or uint16 fp16 bits
+    init_slot_ids: np.ndarray  # int32 [n_seq]
+    dst_slot_ids: np.ndarray   # int32 [n_seq]
+    cu_seqlens: np.ndarray     # int32 [n_seq + 1]
+    q: np.ndarray              # float32 [T, H, K]
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    b: np.ndarray              # float32 [T, H]
+    scale: float
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def io_bytes(self) -> int:
+        """Algorithmic bytes: q, k, v, g, out (fp32) and b per token-head,
+        each sequence's state read once and written once, the id tables."""
+        _, H, K, V = self.pool.shape
+        elem = 4 if self.dtype == "f32" else 2
+        n_seq = self.init_slot_ids.size
+        return (self.n_tokens * H * (3 * K + 2 * V + 1) * 4 + 2 * n_seq * H * K * V * elem
+                + 4 * (3 * n_seq + 1))
+
+
+def make_prefill_inputs(name: str, lengths, n_slots: int, dtype: str = "f32", H: int = H_DEFAULT,
+                        K: int = K_DEFAULT, V: int = V_DEFAULT, seed: int = 0,
+                        in_place: bool = True) -> PrefillInputs:
+    """Recipe: default_rng(seed) draws the pool S0 ~ N(0, 0.05^2), then the
+    rows q, k, v, g, b of all T = sum(lengths) tokens as for decode, then a
+    permutation of the pool's slots: the first n_seq are the initial slots,
+    the next n_seq the destination slots (unless in_place)."""
+    lengths = [int(x) for x in lengths]
+    n_seq = len(lengths)
+    if n_seq * (1 if in_place else 2) > n_slots:
+        raise ValueError("not enough slots")
+    rng = np.random.default_rng(seed)
+    pool = draw_pool(rng, n_slots, H, K, V, dtype)
+    T = sum(lengths)
+    q, k, v, g, b = draw_rows(rng, T, H, K, V)
+    perm = rng.permutation(n_slots).astype(np.int32)
+    init = perm[:n_seq].copy()
+    dst = init.copy() if in_place else perm[n_seq:2 * n_seq].copy()
+    cu = np.zeros(n_seq + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return PrefillInputs(name=name, dtype=dtype, pool=pool, init_slot_ids=init, dst_slot_ids=dst,
+                         cu_seqlens=cu, q=q, k=k, v=v, g=g, b=b, scale=float(1.0 / np.sqrt(K)))
+
+
+def prefill_lengths(n_seq: int, mean: int, seed: int) -> list:
+    """A ragged length mix: uniform on [mean/4, 7*mean/4], so the total is
+    about n_seq * mean and the lengths mostly fall between chunk boundaries."""
+    rng = np.random.default_rng(seed + 7)
+    return [int(x) for x in rng.integers(max(1, mean // 4), 7 * mean // 4 + 1, size=n_seq)]
+
+
+def prefill_batch(dtype: str, seed: int = 0) -> PrefillInputs:
+    """The prefill workload: 32 prompts of ragged length (mean 1024 tokens,
+    about 32K tokens in all), H = 12, K = V = 128, each from its own slot of
+    a 64-slot pool, final state stored in place."""
+    return make_prefill_inputs("prefill 32 prompts x ~1K tokens (ragged), %s pool, H=12 K=V=128"
+                               % dtype, prefill_lengths(32, 1024, seed), 64, dtype, seed=seed)

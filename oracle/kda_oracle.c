@@ -161,6 +161,68 @@ static int64_t state_offset(int32_t slot, int32_t h, int32_t H, int32_t K,
 /* fp32 recurrence                                                          */
 /* ------------------------------------------------------------------------ */
 
+/* One token of the recurrence on one head, fp32 (the order of the update's
+ * definition: normalise, gate, decay, delta correction, rank-1 update, read
+ * out the post-update state).  S [K, V] is updated in place; qn, kn, a, w, u
+ * are work arrays; ov receives the V outputs. */
+static void token_f32(float* S, int32_t K, int32_t V, const float* qv, const float* kv,
+                      const float* gv, const float* vv, float bv, float scale, float* qn,
+                      float* kn, float* a, float* w, float* u, float* ov) {
+  const float eps = 1e-6f;
+
+  /* L2 normalisation of q and k */
+  float sq = 0.0f, sk = 0.0f;
+  for (int32_t i = 0; i < K; ++i) sq = sq + qv[i] * qv[i];
+  for (int32_t i = 0; i < K; ++i) sk = sk + kv[i] * kv[i];
+  const float rq = g_mutation == 6 ? 1.0f / (sq + eps) : 1.0f / sqrtf(sq + eps);
+  const float rk = 1.0f / sqrtf(sk + eps);
+  for (int32_t i = 0; i < K; ++i) qn[i] = qv[i] * rq;
+  for (int32_t i = 0; i < K; ++i) kn[i] = kv[i] * rk;
+
+  /* per-key-channel decay and sigmoid gate */
+  for (int32_t i = 0; i < K; ++i)
+    a[i] = g_mutation == 1 ? 1.0f : (g_mutation == 8 ? expf(-gv[i]) : expf(gv[i]));
+  const float beta = g_mutation == 11 ? 1.0f / (1.0f + expf(bv))
+                                      : 1.0f / (1.0f + expf(-bv));
+
+  /* S' = diag(a) S */
+  for (int32_t i = 0; i < K; ++i)
+    for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
+
+  if (g_mutation == 4) { /* planted: read-out before the update */
+    for (int32_t j = 0; j < V; ++j) ov[j] = 0.0f;
+    for (int32_t i = 0; i < K; ++i)
+      for (int32_t j = 0; j < V; ++j) ov[j] = ov[j] + qn[i] * S[(int64_t)i * V + j];
+    for (int32_t j = 0; j < V; ++j) ov[j] = scale * ov[j];
+  }
+
+  /* w = S'^T kn ; u = v - w.  Each w_j is the sum over i = 0..K-1 in
+   * order; the loops run i-outer only so that rows are read
+   * contiguously. */
+  for (int32_t j = 0; j < V; ++j) w[j] = 0.0f;
+  for (int32_t i = 0; i < K; ++i)
+    for (int32_t j = 0; j < V; ++j) {
+      const float s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
+      w[j] = w[j] + kn[i] * s;
+    }
+  for (int32_t j = 0; j < V; ++j) u[j] = g_mutation == 2 ? vv[j] + w[j] : vv[j] - w[j];
+
+  /* S = S' + (beta kn) u^T */
+  for (int32_t i = 0; i < K; ++i) {
+    const float bk = g_mutation == 5 ? kn[i] : beta * kn[i];
+    for (int32_t j = 0; j < V; ++j)
+      S[(int64_t)i * V + j] = S[(int64_t)i * V + j] + bk * u[j];
+  }
+
+  /* o = scale * S^T qn (post-update state), sums in i order */
+  if (g_mutation != 4) {
+    for (int32_t j = 0; j < V; ++j) w[j] = 0.0f;
+    for (int32_t i = 0; i < K; ++i)
+      for (int32_t j = 0; j < V; ++j) w[j] = w[j] + qn[i] * S[(int64_t)i * V + j];
+    for (int32_t j = 0; j < V; ++j) ov[j] = (g_mutation == 7 ? scale * scale : scale) * w[j];
+  }
+}
+
 int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
                   int32_t K, int32_t V, const int32_t* slot_ids,
                   const int32_t* init_slot_ids, int32_t n_req, int32_t n_rows, const float* q,
@@ -172,7 +234,6 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
                   b, out))
     return KDAO_EARG;
 
-  const float eps = 1e-6f;
   float* S = (float*)malloc(sizeof(float) * (size_t)K * V);
   float* qn = (float*)malloc(sizeof(float) * (size_t)K);
   float* kn = (float*)malloc(sizeof(float) * (size_t)K);
@@ -199,64 +260,9 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
           for (int64_t e = 0; e < (int64_t)K * V; ++e)
             S[e] = widen_any(pool, pool_kind, off0 + e);
         }
-        const float* qv = q + (rho * H + h) * K;
-        const float* kv = k + (rho * H + h) * K;
-        const float* gv = g + (rho * H + h) * K;
-        const float* vv = v + (rho * H + h) * V;
-        const float bv = b[rho * H + h];
-        float* ov = out + (rho * H + h) * V;
-
-        /* L2 normalisation of q and k */
-        float sq = 0.0f, sk = 0.0f;
-        for (int32_t i = 0; i < K; ++i) sq = sq + qv[i] * qv[i];
-        for (int32_t i = 0; i < K; ++i) sk = sk + kv[i] * kv[i];
-        const float rq = g_mutation == 6 ? 1.0f / (sq + eps) : 1.0f / sqrtf(sq + eps);
-        const float rk = 1.0f / sqrtf(sk + eps);
-        for (int32_t i = 0; i < K; ++i) qn[i] = qv[i] * rq;
-        for (int32_t i = 0; i < K; ++i) kn[i] = kv[i] * rk;
-
-        /* per-key-channel decay and sigmoid gate */
-        for (int32_t i = 0; i < K; ++i)
-          a[i] = g_mutation == 1 ? 1.0f : (g_mutation == 8 ? expf(-gv[i]) : expf(gv[i]));
-        const float beta = g_mutation == 11 ? 1.0f / (1.0f + expf(bv))
-                                            : 1.0f / (1.0f + expf(-bv));
-
-        /* S' = diag(a) S */
-        for (int32_t i = 0; i < K; ++i)
-          for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
-
-        if (g_mutation == 4) { /* planted: read-out before the update */
-          for (int32_t j = 0; j < V; ++j) ov[j] = 0.0f;
-          for (int32_t i = 0; i < K; ++i)
-            for (int32_t j = 0; j < V; ++j) ov[j] = ov[j] + qn[i] * S[(int64_t)i * V + j];
-          for (int32_t j = 0; j < V; ++j) ov[j] = scale * ov[j];
-        }
-
-        /* w = S'^T kn ; u = v - w.  Each w_j is the sum over i = 0..K-1 in
-         * order; the loops run i-outer only so that rows are read
-         * contiguously. */
-        for (int32_t j = 0; j < V; ++j) w[j] = 0.0f;
-        for (int32_t i = 0; i < K; ++i)
-          for (int32_t j = 0; j < V; ++j) {
-            const float s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
-            w[j] = w[j] + kn[i] * s;
-          }
-        for (int32_t j = 0; j < V; ++j) u[j] = g_mutation == 2 ? vv[j] + w[j] : vv[j] - w[j];
-
-        /* S = S' + (beta kn) u^T */
-        for (int32_t i = 0; i < K; ++i) {
-          const float bk = g_mutation == 5 ? kn[i] : beta * kn[i];
-          for (int32_t j = 0; j < V; ++j)
-            S[(int64_t)i * V + j] = S[(int64_t)i * V + j] + bk * u[j];
-        }
-
-        /* o = scale * S^T qn (post-update state), sums in i order */
-        if (g_mutation != 4) {
-          for (int32_t j = 0; j < V; ++j) w[j] = 0.0f;
-          for (int32_t i = 0; i < K; ++i)
-            for (int32_t j = 0; j < V; ++j) w[j] = w[j] + qn[i] * S[(int64_t)i * V + j];
-          for (int32_t j = 0; j < V; ++j) ov[j] = (g_mutation == 7 ? scale * scale : scale) * w[j];
-        }
+        token_f32(S, K, V, q + (rho * H + h) * K, k + (rho * H + h) * K, g + (rho * H + h) * K,
+                  v + (rho * H + h) * V, b[rho * H + h], scale, qn, kn, a, w, u,
+                  out + (rho * H + h) * V);
 
         /* store this token's state to its snapshot slot */
         const int32_t dst_slot = g_mutation == 10 ? slot_ids[(int64_t)r * n_rows] : slot_ids[rho];
@@ -273,6 +279,58 @@ int kdao_step_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H,
 /* fp64 twin of the same loop                                               */
 /* ------------------------------------------------------------------------ */
 
+/* The same token in fp64 (inputs widened exactly). */
+static void token_f64(double* S, int32_t K, int32_t V, const float* qv, const float* kv,
+                      const float* gv, const float* vv, float b32, double scale, double* qn,
+                      double* kn, double* a, double* w, double* u, double* ov) {
+  const double eps = 1e-6;
+  const double bv = (double)b32;
+
+  double sq = 0.0, sk = 0.0;
+  for (int32_t i = 0; i < K; ++i) sq = sq + (double)qv[i] * (double)qv[i];
+  for (int32_t i = 0; i < K; ++i) sk = sk + (double)kv[i] * (double)kv[i];
+  const double rq = g_mutation == 6 ? 1.0 / (sq + eps) : 1.0 / sqrt(sq + eps);
+  const double rk = 1.0 / sqrt(sk + eps);
+  for (int32_t i = 0; i < K; ++i) qn[i] = (double)qv[i] * rq;
+  for (int32_t i = 0; i < K; ++i) kn[i] = (double)kv[i] * rk;
+
+  for (int32_t i = 0; i < K; ++i)
+    a[i] = g_mutation == 1 ? 1.0 : (g_mutation == 8 ? exp(-(double)gv[i]) : exp((double)gv[i]));
+  const double beta = g_mutation == 11 ? 1.0 / (1.0 + exp(bv)) : 1.0 / (1.0 + exp(-bv));
+
+  for (int32_t i = 0; i < K; ++i)
+    for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
+
+  if (g_mutation == 4) {
+    for (int32_t j = 0; j < V; ++j) ov[j] = 0.0;
+    for (int32_t i = 0; i < K; ++i)
+      for (int32_t j = 0; j < V; ++j) ov[j] = ov[j] + qn[i] * S[(int64_t)i * V + j];
+    for (int32_t j = 0; j < V; ++j) ov[j] = scale * ov[j];
+  }
+
+  for (int32_t j = 0; j < V; ++j) w[j] = 0.0;
+  for (int32_t i = 0; i < K; ++i)
+    for (int32_t j = 0; j < V; ++j) {
+      const double s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
+      w[j] = w[j] + kn[i] * s;
+    }
+  for (int32_t j = 0; j < V; ++j)
+    u[j] = g_mutation == 2 ? (double)vv[j] + w[j] : (double)vv[j] - w[j];
+
+  for (int32_t i = 0; i < K; ++i) {
+    const double bk = g_mutation == 5 ? kn[i] : beta * kn[i];
+    for (int32_t j = 0; j < V; ++j)
+      S[(int64_t)i * V + j] = S[(int64_t)i * V + j] + bk * u[j];
+  }
+
+  if (g_mutation != 4) {
+    for (int32_t j = 0; j < V; ++j) w[j] = 0.0;
+    for (int32_t i = 0; i < K; ++i)
+      for (int32_t j = 0; j < V; ++j) w[j] = w[j] + qn[i] * S[(int64_t)i * V + j];
+    for (int32_t j = 0; j < V; ++j) ov[j] = (g_mutation == 7 ? scale * scale : scale) * w[j];
+  }
+}
+
 int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
                   int32_t V, const int32_t* slot_ids, const int32_t* init_slot_ids, int32_t n_req,
                   int32_t n_rows, const float* q, const float* k,
@@ -282,7 +340,6 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
                   b, out))
     return KDAO_EARG;
 
-  const double eps = 1e-6;
   double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
   double* qn = (double*)malloc(sizeof(double) * (size_t)K);
   double* kn = (double*)malloc(sizeof(double) * (size_t)K);
@@ -304,61 +361,117 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
         const int64_t rho = (int64_t)r * n_rows + t;
         if (g_mutation == 9 && t > 0)
           for (int64_t e = 0; e < (int64_t)K * V; ++e) S[e] = pool[off0 + e];
-        const float* qv = q + (rho * H + h) * K;
-        const float* kv = k + (rho * H + h) * K;
-        const float* gv = g + (rho * H + h) * K;
-        const float* vv = v + (rho * H + h) * V;
-        const double bv = (double)b[rho * H + h];
-        double* ov = out + (rho * H + h) * V;
-
-        double sq = 0.0, sk = 0.0;
-        for (int32_t i = 0; i < K; ++i) sq = sq + (double)qv[i] * (double)qv[i];
-        for (int32_t i = 0; i < K; ++i) sk = sk + (double)kv[i] * (double)kv[i];
-        const double rq = g_mutation == 6 ? 1.0 / (sq + eps) : 1.0 / sqrt(sq + eps);
-        const double rk = 1.0 / sqrt(sk + eps);
-        for (int32_t i = 0; i < K; ++i) qn[i] = (double)qv[i] * rq;
-        for (int32_t i = 0; i < K; ++i) kn[i] = (double)kv[i] * rk;
-
-        for (int32_t i = 0; i < K; ++i)
-          a[i] = g_mutation == 1 ? 1.0 : (g_mutation == 8 ? exp(-(double)gv[i]) : exp((double)gv[i]));
-        const double beta = g_mutation == 11 ? 1.0 / (1.0 + exp(bv)) : 1.0 / (1.0 + exp(-bv));
-
-        for (int32_t i = 0; i < K; ++i)
-          for (int32_t j = 0; j < V; ++j) S[(int64_t)i * V + j] = a[i] * S[(int64_t)i * V + j];
-
-        if (g_mutation == 4) {
-          for (int32_t j = 0; j < V; ++j) ov[j] = 0.0;
-          for (int32_t i = 0; i < K; ++i)
-            for (int32_t j = 0; j < V; ++j) ov[j] = ov[j] + qn[i] * S[(int64_t)i * V + j];
-          for (int32_t j = 0; j < V; ++j) ov[j] = scale * ov[j];
-        }
-
-        for (int32_t j = 0; j < V; ++j) w[j] = 0.0;
-        for (int32_t i = 0; i < K; ++i)
-          for (int32_t j = 0; j < V; ++j) {
-            const double s = g_mutation == 3 ? S[(int64_t)j * V + i] : S[(int64_t)i * V + j];
-            w[j] = w[j] + kn[i] * s;
-          }
-        for (int32_t j = 0; j < V; ++j)
-          u[j] = g_mutation == 2 ? (double)vv[j] + w[j] : (double)vv[j] - w[j];
-
-        for (int32_t i = 0; i < K; ++i) {
-          const double bk = g_mutation == 5 ? kn[i] : beta * kn[i];
-          for (int32_t j = 0; j < V; ++j)
-            S[(int64_t)i * V + j] = S[(int64_t)i * V + j] + bk * u[j];
-        }
-
-        if (g_mutation != 4) {
-          for (int32_t j = 0; j < V; ++j) w[j] = 0.0;
-          for (int32_t i = 0; i < K; ++i)
-            for (int32_t j = 0; j < V; ++j) w[j] = w[j] + qn[i] * S[(int64_t)i * V + j];
-          for (int32_t j = 0; j < V; ++j) ov[j] = (g_mutation == 7 ? scale * scale : scale) * w[j];
-        }
+        token_f64(S, K, V, q + (rho * H + h) * K, k + (rho * H + h) * K, g + (rho * H + h) * K,
+                  v + (rho * H + h) * V, b[rho * H + h], scale, qn, kn, a, w, u,
+                  out + (rho * H + h) * V);
 
         const int32_t dst_slot = g_mutation == 10 ? slot_ids[(int64_t)r * n_rows] : slot_ids[rho];
         const int64_t offt = state_offset(dst_slot, h, H, K, V);
         for (int64_t e = 0; e < (int64_t)K * V; ++e) pool[offt + e] = S[e];
       }
+    }
+  }
+  free(S); free(qn); free(kn); free(a); free(w); free(u);
+  return KDAO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* prefill: whole sequences through the same per-token recurrence           */
+/* ------------------------------------------------------------------------ */
+
+static int check_prefill(const void* pool, int32_t n_slots, int32_t H, int32_t K, int32_t V,
+                         const int32_t* init_slot_ids, const int32_t* dst_slot_ids,
+                         const int32_t* cu_seqlens, int32_t n_seq, const void* q,
+                         const void* k, const void* v, const void* g, const void* b,
+                         const void* out) {
+  if (!pool || !init_slot_ids || !cu_seqlens || !q || !k || !v || !g || !b || !out) return 0;
+  if (n_slots <= 0 || H <= 0 || K <= 0 || V <= 0 || n_seq < 0) return 0;
+  if (n_seq > 0 && cu_seqlens[0] < 0) return 0;
+  for (int32_t s = 0; s < n_seq; ++s) {
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return 0;
+    if (init_slot_ids[s] < 0 || init_slot_ids[s] >= n_slots) return 0;
+    const int32_t d = dst_slot_ids ? dst_slot_ids[s] : init_slot_ids[s];
+    if (d < 0 || d >= n_slots) return 0;
+  }
+  /* a destination slot is written by one sequence only and is no other
+   * sequence's initial slot: then every sequence reads the pool as it was
+   * before the launch, whatever the order of the sequences */
+  for (int32_t s = 0; s < n_seq; ++s) {
+    const int32_t d = dst_slot_ids ? dst_slot_ids[s] : init_slot_ids[s];
+    for (int32_t u = 0; u < n_seq; ++u) {
+      if (u == s) continue;
+      const int32_t du = dst_slot_ids ? dst_slot_ids[u] : init_slot_ids[u];
+      if (du == d || init_slot_ids[u] == d) return 0;
+    }
+  }
+  return 1;
+}
+
+int kdao_prefill_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H, int32_t K,
+                     int32_t V, const int32_t* init_slot_ids, const int32_t* dst_slot_ids,
+                     const int32_t* cu_seqlens, int32_t n_seq, const float* q, const float* k,
+                     const float* v, const float* g, const float* b, float scale, float* out) {
+  if (pool_kind != KDAO_POOL_F32 && pool_kind != KDAO_POOL_F16 && pool_kind != KDAO_POOL_BF16)
+    return KDAO_EARG;
+  if (!check_prefill(pool, n_slots, H, K, V, init_slot_ids, dst_slot_ids, cu_seqlens, n_seq, q,
+                     k, v, g, b, out))
+    return KDAO_EARG;
+  float* S = (float*)malloc(sizeof(float) * (size_t)K * V);
+  float* qn = (float*)malloc(sizeof(float) * (size_t)K);
+  float* kn = (float*)malloc(sizeof(float) * (size_t)K);
+  float* a = (float*)malloc(sizeof(float) * (size_t)K);
+  float* w = (float*)malloc(sizeof(float) * (size_t)V);
+  float* u = (float*)malloc(sizeof(float) * (size_t)V);
+  if (!S || !qn || !kn || !a || !w || !u) {
+    free(S); free(qn); free(kn); free(a); free(w); free(u);
+    return KDAO_EARG;
+  }
+  for (int32_t sq = 0; sq < n_seq; ++sq) {
+    for (int32_t h = 0; h < H; ++h) {
+      const int64_t off0 = state_offset(init_slot_ids[sq], h, H, K, V);
+      for (int64_t e = 0; e < (int64_t)K * V; ++e) S[e] = widen_any(pool, pool_kind, off0 + e);
+      for (int64_t t = cu_seqlens[sq]; t < cu_seqlens[sq + 1]; ++t)
+        token_f32(S, K, V, q + (t * H + h) * K, k + (t * H + h) * K, g + (t * H + h) * K,
+                  v + (t * H + h) * V, b[t * H + h], scale, qn, kn, a, w, u,
+                  out + (t * H + h) * V);
+      const int32_t d = dst_slot_ids ? dst_slot_ids[sq] : init_slot_ids[sq];
+      const int64_t offd = state_offset(d, h, H, K, V);
+      for (int64_t e = 0; e < (int64_t)K * V; ++e) narrow_any(pool, pool_kind, offd + e, S[e]);
+    }
+  }
+  free(S); free(qn); free(kn); free(a); free(w); free(u);
+  return KDAO_OK;
+}
+
+int kdao_prefill_f64(double* pool, int32_t n_slots, int32_t H, int32_t K, int32_t V,
+                     const int32_t* init_slot_ids, const int32_t* dst_slot_ids,
+                     const int32_t* cu_seqlens, int32_t n_seq, const float* q, const float* k,
+                     const float* v, const float* g, const float* b, double scale,
+                     double* out) {
+  if (!check_prefill(pool, n_slots, H, K, V, init_slot_ids, dst_slot_ids, cu_seqlens, n_seq, q,
+                     k, v, g, b, out))
+    return KDAO_EARG;
+  double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
+  double* qn = (double*)malloc(sizeof(double) * (size_t)K);
+  double* kn = (double*)malloc(sizeof(double) * (size_t)K);
+  double* a = (double*)malloc(sizeof(double) * (size_t)K);
+  double* w = (double*)malloc(sizeof(double) * (size_t)V);
+  double* u = (double*)malloc(sizeof(double) * (size_t)V);
+  if (!S || !qn || !kn || !a || !w || !u) {
+    free(S); free(qn); free(kn); free(a); free(w); free(u);
+    return KDAO_EARG;
+  }
+  for (int32_t sq = 0; sq < n_seq; ++sq) {
+    for (int32_t h = 0; h < H; ++h) {
+      const int64_t off0 = state_offset(init_slot_ids[sq], h, H, K, V);
+      for (int64_t e = 0; e < (int64_t)K * V; ++e) S[e] = pool[off0 + e];
+      for (int64_t t = cu_seqlens[sq]; t < cu_seqlens[sq + 1]; ++t)
+        token_f64(S, K, V, q + (t * H + h) * K, k + (t * H + h) * K, g + (t * H + h) * K,
+                  v + (t * H + h) * V, b[t * H + h], scale, qn, kn, a, w, u,
+                  out + (t * H + h) * V);
+      const int32_t d = dst_slot_ids ? dst_slot_ids[sq] : init_slot_ids[sq];
+      const int64_t offd = state_offset(d, h, H, K, V);
+      for (int64_t e = 0; e < (int64_t)K * V; ++e) pool[offd + e] = S[e];
     }
   }
   free(S); free(qn); free(kn); free(a); free(w); free(u);

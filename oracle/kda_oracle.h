@@ -116,6 +116,33 @@ int kdao_step_f64(double* pool, int32_t n_slots, int32_t H, int32_t K,
                   double scale, double* out);
 
 /*
+ * Prefill: whole sequences through the same recurrence, token by token
+ * (ROCm/ATOM PR #2130, What and Depends on: the prefill kernel reads its
+ * initial state from the pool in the pool's dtype and writes the final state
+ * back; the recurrence is the decode step's, applied to every token of the
+ * prompt in order).
+ *   init_slot_ids  [n_seq]: slot of each sequence's initial state (widened).
+ *   dst_slot_ids   NULL (= init_slot_ids) or [n_seq]: where the final state is
+ *                  stored (narrowed).  Distinct, and none is another
+ *                  sequence's initial slot.
+ *   cu_seqlens     [n_seq + 1] non-decreasing token offsets: sequence s owns
+ *                  tokens cu_seqlens[s] .. cu_seqlens[s + 1] - 1 of q, k, v,
+ *                  g [T, H, K|V], b [T, H] and out [T, H, V].  Empty
+ *                  sequences copy their state (widened, then narrowed).
+ * Only the final state of each sequence is stored; out holds every token's
+ * read-out.
+ */
+int kdao_prefill_f32(void* pool, int pool_kind, int32_t n_slots, int32_t H, int32_t K,
+                     int32_t V, const int32_t* init_slot_ids, const int32_t* dst_slot_ids,
+                     const int32_t* cu_seqlens, int32_t n_seq, const float* q, const float* k,
+                     const float* v, const float* g, const float* b, float scale, float* out);
+int kdao_prefill_f64(double* pool, int32_t n_slots, int32_t H, int32_t K, int32_t V,
+                     const int32_t* init_slot_ids, const int32_t* dst_slot_ids,
+                     const int32_t* cu_seqlens, int32_t n_seq, const float* q, const float* k,
+                     const float* v, const float* g, const float* b, double scale,
+                     double* out);
+
+/*
  * Short causal convolution in front of the recurrence (q, k and v each pass
  * a depthwise causal convolution of 4 taps, then SiLU).  The conv state of a
  * slot holds the last 3 raw inputs of every channel in bfloat16: ROCm/ATOM

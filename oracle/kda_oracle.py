@@ -51,6 +51,12 @@ def lib() -> ctypes.CDLL:
     L.kdao_step_f64.argtypes = [c_d, i32, i32, i32, i32, c_i, c_i, i32, i32,
                                 c_f, c_f, c_f, c_f, c_f, ctypes.c_double, c_d]
     L.kdao_step_f64.restype = ctypes.c_int
+    L.kdao_prefill_f32.argtypes = [ctypes.c_void_p, ctypes.c_int, i32, i32, i32, i32, c_i, c_i, c_i,
+                                   i32, c_f, c_f, c_f, c_f, c_f, ctypes.c_float, c_f]
+    L.kdao_prefill_f32.restype = ctypes.c_int
+    L.kdao_prefill_f64.argtypes = [c_d, i32, i32, i32, i32, c_i, c_i, c_i, i32,
+                                   c_f, c_f, c_f, c_f, c_f, ctypes.c_double, c_d]
+    L.kdao_prefill_f64.restype = ctypes.c_int
     L.kdao_conv_f32.argtypes = [c_u16, i32, i32, c_i, c_i, i32, i32, c_f, c_f, c_f]
     L.kdao_conv_f32.restype = ctypes.c_int
     L.kdao_set_mutation.argtypes = [ctypes.c_int]
@@ -167,6 +173,74 @@ def step_f64(pool: np.ndarray, slot_ids, q, k, v, g, b, n_rows: int = 1,
                              _ptr(v, ctypes.c_float), _ptr(g, ctypes.c_float),
                              _ptr(b, ctypes.c_float), float(scale),
                              _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (code %d)" % rc)
+    return out
+
+
+def _prefill_args(pool, init_slot_ids, dst_slot_ids, cu_seqlens, q, k, v, g, b):
+    n_slots, H, K, V = pool.shape
+    init = np.ascontiguousarray(init_slot_ids, dtype=np.int32).reshape(-1)
+    n_seq = init.size
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32).reshape(-1)
+    if cu.size != n_seq + 1:
+        raise ValueError("cu_seqlens needs n_seq + 1 entries")
+    dst = None if dst_slot_ids is None else np.ascontiguousarray(dst_slot_ids, dtype=np.int32).reshape(-1)
+    if dst is not None and dst.size != n_seq:
+        raise ValueError("dst_slot_ids needs one entry per sequence")
+    T = int(cu[-1]) if n_seq else 0
+    q, k, v, g, b = (_f32(x) for x in (q, k, v, g, b))
+    if q.shape[0] < T or k.shape[0] < T or v.shape[0] < T or g.shape[0] < T or b.shape[0] < T:
+        raise ValueError("q, k, v, g, b hold fewer tokens than cu_seqlens addresses")
+    if q.shape[1:] != (H, K) or k.shape[1:] != (H, K) or g.shape[1:] != (H, K) \
+            or v.shape[1:] != (H, V) or b.shape[1:] != (H,):
+        raise ValueError("q, k, g [T, H, K]; v [T, H, V]; b [T, H]")
+    return (n_slots, H, K, V), init, dst, cu, n_seq, q, k, v, g, b
+
+
+def prefill_f32(pool: np.ndarray, init_slot_ids, cu_seqlens, q, k, v, g, b, dst_slot_ids=None,
+                scale: float | None = None, bf16: bool = False) -> np.ndarray:
+    """Prefill in fp32 on a host pool (float32, or uint16 fp16 / bf16 bits),
+    updated in place with each sequence's final state.  Returns out [T, H, V]
+    (rows past cu_seqlens[-1], if any, stay zero)."""
+    if not pool.flags["C_CONTIGUOUS"]:
+        raise ValueError("pool must be C-contiguous")
+    kind = POOL_F32 if pool.dtype == np.float32 else (POOL_BF16 if bf16 else POOL_F16)
+    if pool.dtype not in (np.float32, np.uint16):
+        raise TypeError("oracle pool must be float32 or uint16")
+    (n_slots, H, K, V), init, dst, cu, n_seq, q, k, v, g, b = _prefill_args(
+        pool, init_slot_ids, dst_slot_ids, cu_seqlens, q, k, v, g, b)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    out = np.zeros((q.shape[0], H, V), dtype=np.float32)
+    rc = lib().kdao_prefill_f32(pool.ctypes.data, kind, n_slots, H, K, V, _ptr(init, ctypes.c_int32),
+                                None if dst is None else _ptr(dst, ctypes.c_int32),
+                                _ptr(cu, ctypes.c_int32), n_seq, _ptr(q, ctypes.c_float),
+                                _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+                                _ptr(g, ctypes.c_float), _ptr(b, ctypes.c_float), float(scale),
+                                _ptr(out, ctypes.c_float))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (code %d)" % rc)
+    return out
+
+
+def prefill_f64(pool: np.ndarray, init_slot_ids, cu_seqlens, q, k, v, g, b, dst_slot_ids=None,
+                scale: float | None = None) -> np.ndarray:
+    """The same prefill in fp64 on a float64 host pool, updated in place."""
+    if pool.dtype != np.float64 or not pool.flags["C_CONTIGUOUS"]:
+        raise TypeError("fp64 oracle pool must be a C-contiguous float64 array")
+    (n_slots, H, K, V), init, dst, cu, n_seq, q, k, v, g, b = _prefill_args(
+        pool, init_slot_ids, dst_slot_ids, cu_seqlens, q, k, v, g, b)
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    out = np.zeros((q.shape[0], H, V), dtype=np.float64)
+    rc = lib().kdao_prefill_f64(_ptr(pool, ctypes.c_double), n_slots, H, K, V,
+                                _ptr(init, ctypes.c_int32),
+                                None if dst is None else _ptr(dst, ctypes.c_int32),
+                                _ptr(cu, ctypes.c_int32), n_seq, _ptr(q, ctypes.c_float),
+                                _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+                                _ptr(g, ctypes.c_float), _ptr(b, ctypes.c_float), float(scale),
+                                _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
     return out
