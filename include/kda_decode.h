@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -279,6 +279,60 @@ size_t kda_pool_bytes(int32_t n_slots, int32_t H, int32_t K, int32_t V,
  * dtype.
  */
 int32_t kda_tile_bv(kda_dtype dtype);
+
+/*
+ * kda_prefill -- chunked prefill: whole prompts through the same recurrence
+ * as kda_decode_step (ROCm/ATOM PR #2130, What and Depends on: every path,
+ * prefill included, reads and writes the state in the pool's dtype while
+ * the recurrence runs in fp32; the prefill kernel takes its initial state
+ * from the pool, fp16 included).
+ *
+ * Sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s + 1] - 1.  Its state
+ * starts from slot init_slot_ids[s] (widened exactly), every token t is
+ * applied in order, out[t] receives scale * S_t^T qn_t, and only the final
+ * state is stored, to slot dst_slot_ids[s] (NULL: back to init_slot_ids[s];
+ * fp16 pools round to nearest even).  An empty sequence copies its state.
+ *
+ *  pool           device pool [n_slots, H, 128, 128] of state_dtype.
+ *  init_slot_ids  device int32 [n_seq].
+ *  dst_slot_ids   NULL or device int32 [n_seq]: distinct, and none is
+ *                 another sequence's initial slot (kda_prefill_validate
+ *                 checks host copies).
+ *  cu_seqlens     device int32 [n_seq + 1], non-decreasing, cu_seqlens[0]
+ *                 >= 0, cu_seqlens[n_seq] <= n_tokens.
+ *  q, k, g        device fp32 [n_tokens, H, 128], 16-byte aligned; v, out
+ *                 device fp32 [n_tokens, H, 128]; b device fp32 [n_tokens, H].
+ *  n_seq          sequences (<= n_slots); n_tokens: rows of the token arrays.
+ *  opts           NULL or kda_prefill_opts (chunk: 0 = default 64, or 32/64
+ *                 tokens per chunk; the chunk changes the rounding order,
+ *                 never the operation).
+ * The chunked form (per-channel cumulative decay, a unit lower-triangular
+ * solve per chunk, matrix-core products) equals the token-by-token
+ * recurrence up to rounding.  Device-side, a sequence whose table entries
+ * are out of range is skipped (nothing written for it).
+ * Errors: as kda_decode_step (KDA_ERR_SLOT: n_seq > n_slots), KDA_ERR_ARG
+ * (bad chunk, n_tokens < 0, non-finite scale).  Asynchronous on stream.
+ */
+typedef struct kda_prefill_opts {
+  int32_t chunk;
+} kda_prefill_opts;
+
+int kda_prefill(const kda_pool* pool, const int32_t* init_slot_ids,
+                const int32_t* dst_slot_ids, const int32_t* cu_seqlens, const float* q,
+                const float* k, const float* v, const float* g, const float* b, float* out,
+                int32_t n_seq, int64_t n_tokens, kda_dtype state_dtype, float scale,
+                const kda_prefill_opts* opts, void* stream);
+
+/*
+ * kda_prefill_validate -- host-side check of a prefill's tables (host
+ * copies): KDA_ERR_NULL, KDA_ERR_ARG (cu_seqlens not non-decreasing from
+ * >= 0 to <= n_tokens), KDA_ERR_SLOT (an id out of range, two sequences
+ * storing to one slot, or a destination that is another sequence's initial
+ * slot), plus the pool checks of kda_validate.  CPU only.
+ */
+int kda_prefill_validate(const kda_pool* pool, const int32_t* init_slot_ids_host,
+                         const int32_t* dst_slot_ids_host, const int32_t* cu_seqlens_host,
+                         int32_t n_seq, int64_t n_tokens, kda_dtype state_dtype);
 
 /* Launch shape kda_decode_step uses for a given problem (host only). */
 typedef struct kda_launch_desc {

@@ -8,6 +8,6 @@ the C names and only marshal arguments.
 """
 from .binding import (  # noqa: F401
     KDA_BF16, KDA_F16, KDA_F32, KDA_MAX_ROWS, KdaError, kda_abi_version, kda_copy_probe,
-    kda_decode_step, kda_decode_step_conv, kda_describe_launch, kda_pool_bytes, kda_state_at, kda_state_copy, kda_strerror,
-    kda_tile_bv, kda_tile_of_block, kda_validate, library, make_conv_pool, make_pool,
+    kda_decode_step, kda_decode_step_conv, kda_describe_launch, kda_pool_bytes, kda_prefill,
+    kda_prefill_validate, kda_state_at, kda_state_copy, kda_strerror, kda_tile_bv, kda_tile_of_block, kda_validate, library, make_conv_pool, make_pool,
 )

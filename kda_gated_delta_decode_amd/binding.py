@@ -54,6 +54,10 @@ class kda_launch_opts(ctypes.Structure):
     _fields_ = [("waves_per_tile", ctypes.c_int32), ("bv", ctypes.c_int32)]
 
 
+class kda_prefill_opts(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32)]
+
+
 class kda_launch_desc(ctypes.Structure):
     _fields_ = [("bv", ctypes.c_int32), ("waves_per_tile", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("tiles", ctypes.c_int32),
@@ -81,6 +85,11 @@ SIGNATURES = {
                                             ctypes.c_float, ctypes.POINTER(kda_launch_opts), _P]),
     "kda_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, ctypes.c_int]),
     "kda_state_copy": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, ctypes.c_int, _P]),
+    "kda_prefill": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _I32, ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                                   ctypes.POINTER(kda_prefill_opts), _P]),
+    "kda_prefill_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _I32,
+                                            ctypes.c_int64, ctypes.c_int]),
     "kda_state_at": (ctypes.c_int64, [ctypes.POINTER(kda_pool), _P, _I32, _I32, _I32]),
     "kda_pool_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, ctypes.c_int]),
     "kda_tile_bv": (_I32, [ctypes.c_int]),
@@ -273,6 +282,50 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
         _dev(b, "b", torch.float32), _dev(out, "out", torch.float32), n_req, n_rows_per_slot, sd,
         float(scale), ctypes.byref(opts), _stream_ptr(stream))
     _check(rc, "kda_decode_step_conv")
+
+
+def kda_prefill(pool, init_slot_ids, cu_seqlens, q, k, v, g, b, out, dst_slot_ids=None,
+                state_dtype=None, scale: float | None = None, chunk: int = 0, stream=None) -> None:
+    """Chunked prefill (see kda_prefill in include/kda_decode.h).  pool: device
+    tensor [n_slots, H, 128, 128]; init_slot_ids, dst_slot_ids (optional):
+    device int32 [n_seq]; cu_seqlens: device int32 [n_seq + 1]; q, k, g, v,
+    out: device float32 [T, H, 128]; b: [T, H]."""
+    import torch
+    P = make_pool(pool)
+    sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
+    n_seq = init_slot_ids.numel()
+    H = pool.shape[1]
+    T = q.shape[0]
+    for t, name, n in ((cu_seqlens, "cu_seqlens", n_seq + 1), (dst_slot_ids, "dst_slot_ids", n_seq),
+                       (q, "q", T * H * KDA_HEAD_K), (k, "k", T * H * KDA_HEAD_K),
+                       (g, "g", T * H * KDA_HEAD_K), (v, "v", T * H * KDA_HEAD_V),
+                       (out, "out", T * H * KDA_HEAD_V), (b, "b", T * H)):
+        _need_numel(t, name, n)
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.shape[2])
+    opts = kda_prefill_opts(int(chunk))
+    rc = library().kda_prefill(ctypes.byref(P), _dev(init_slot_ids, "init_slot_ids", torch.int32),
+                               _dev(dst_slot_ids, "dst_slot_ids", torch.int32),
+                               _dev(cu_seqlens, "cu_seqlens", torch.int32),
+                               _dev(q, "q", torch.float32), _dev(k, "k", torch.float32),
+                               _dev(v, "v", torch.float32), _dev(g, "g", torch.float32),
+                               _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
+                               n_seq, T, sd, float(scale), ctypes.byref(opts), _stream_ptr(stream))
+    _check(rc, "kda_prefill")
+
+
+def kda_prefill_validate(pool_desc: kda_pool, init_slot_ids_host, cu_seqlens_host, n_tokens: int,
+                         state_dtype, dst_slot_ids_host=None) -> int:
+    """Host-side check of a prefill's tables; returns the kda_status code."""
+    init = np.ascontiguousarray(init_slot_ids_host, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    dst = None if dst_slot_ids_host is None else np.ascontiguousarray(dst_slot_ids_host, dtype=np.int32)
+    if cu.size != init.size + 1 or (dst is not None and dst.size != init.size):
+        raise ValueError("cu_seqlens needs n_seq + 1 entries, dst_slot_ids n_seq")
+    return int(library().kda_prefill_validate(
+        ctypes.byref(pool_desc), init.ctypes.data_as(ctypes.c_void_p),
+        None if dst is None else dst.ctypes.data_as(ctypes.c_void_p),
+        cu.ctypes.data_as(ctypes.c_void_p), init.size, int(n_tokens), _dtype_arg(state_dtype)))
 
 
 def kda_validate(pool_desc: kda_pool, slot_ids_host, n_req: int, n_rows: int, state_dtype,

@@ -66,6 +66,33 @@ int kda_validate(const kda_pool* pool, const int32_t* slot_ids_host,
   return KDA_OK;
 }
 
+int kda_prefill_validate(const kda_pool* pool, const int32_t* init_slot_ids_host,
+                         const int32_t* dst_slot_ids_host, const int32_t* cu_seqlens_host,
+                         int32_t n_seq, int64_t n_tokens, kda_dtype state_dtype) {
+  const int rc = check_common(pool, n_seq, 1, state_dtype);
+  if (rc != KDA_OK) return rc;
+  if (n_tokens < 0) return KDA_ERR_ARG;
+  if (n_seq == 0) return KDA_OK;
+  if (init_slot_ids_host == nullptr || cu_seqlens_host == nullptr) return KDA_ERR_NULL;
+  if (cu_seqlens_host[0] < 0) return KDA_ERR_ARG;
+  for (int32_t s = 0; s < n_seq; ++s)
+    if (cu_seqlens_host[s + 1] < cu_seqlens_host[s]) return KDA_ERR_ARG;
+  if (cu_seqlens_host[n_seq] > n_tokens) return KDA_ERR_ARG;
+  std::unordered_map<int32_t, int32_t> writer;  // destination slot -> sequence
+  writer.reserve(static_cast<size_t>(n_seq));
+  for (int32_t s = 0; s < n_seq; ++s) {
+    const int32_t i = init_slot_ids_host[s];
+    const int32_t d = dst_slot_ids_host != nullptr ? dst_slot_ids_host[s] : i;
+    if (i < 0 || i >= pool->n_slots || d < 0 || d >= pool->n_slots) return KDA_ERR_SLOT;
+    if (!writer.emplace(d, s).second) return KDA_ERR_SLOT;
+  }
+  for (int32_t s = 0; s < n_seq; ++s) {
+    const auto it = writer.find(init_slot_ids_host[s]);
+    if (it != writer.end() && it->second != s) return KDA_ERR_SLOT;  // another sequence writes it
+  }
+  return KDA_OK;
+}
+
 int64_t kda_state_at(const kda_pool* pool, const int32_t* slot_ids_host, int32_t n_rows,
                      int32_t req, int32_t row) {
   if (pool == nullptr || slot_ids_host == nullptr) return -KDA_ERR_NULL;

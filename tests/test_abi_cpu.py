@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for expected in ["kda_decode_step", "kda_decode_step_ex", "kda_validate", "kda_state_at",
-                     "kda_state_copy", "kda_decode_step_conv",
+                     "kda_state_copy", "kda_decode_step_conv", "kda_prefill",
+                     "kda_prefill_validate",
                      "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
                      "kda_copy_probe", "kda_strerror", "kda_abi_version"]:
         assert expected in names
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 1
+    assert B.kda_abi_version() == 2
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -273,3 +274,47 @@ def test_conv_step_refusals():
     assert conv_step(P, Cv, opts=B.kda_launch_opts(1, 0)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, scale=float("nan")) == B.KDA_ERR_ARG
     assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE + 8), 16, 12)) == B.KDA_ERR_ALIGN
+
+
+def prefill(P, n_seq=4, n_tokens=100, ptrs=None, chunk=0, scale=0.0883883, dtype=None):
+    p = [FAKE] * 9 if ptrs is None else ptrs     # init, cu, q, k, v, g, b, out, dst
+    f = [ctypes.c_void_p(v) for v in p]
+    return B.library().kda_prefill(
+        ctypes.byref(P), f[0], f[8], f[1], f[2], f[3], f[4], f[5], f[6], f[7], n_seq, n_tokens,
+        P.dtype if dtype is None else dtype, scale, ctypes.byref(B.kda_prefill_opts(chunk)), None)
+
+
+def test_prefill_refusals():
+    P = pool(n_slots=16)
+    assert prefill(pool(n_slots=16, base=0)) == B.KDA_ERR_NULL
+    assert prefill(pool(n_slots=16, dtype=B.KDA_BF16)) == B.KDA_ERR_DTYPE_REFUSED
+    assert prefill(P, dtype=B.KDA_F16) == B.KDA_ERR_DTYPE_MISMATCH
+    assert prefill(pool(n_slots=16, Kd=64)) == B.KDA_ERR_SHAPE
+    assert prefill(P, n_seq=17) == B.KDA_ERR_SLOT          # more sequences than slots
+    assert prefill(P, n_seq=-1) == B.KDA_ERR_ARG
+    assert prefill(P, n_tokens=-1) == B.KDA_ERR_ARG
+    assert prefill(P, chunk=48) == B.KDA_ERR_ARG
+    assert prefill(P, scale=float("inf")) == B.KDA_ERR_ARG
+    assert prefill(P, n_seq=0) == B.KDA_OK
+    for which in range(8):
+        ptrs = [FAKE] * 9
+        ptrs[which] = 0
+        assert prefill(P, ptrs=ptrs) == B.KDA_ERR_NULL, which
+    ptrs = [FAKE] * 9
+    ptrs[2] = FAKE + 4                                     # q must be 16-byte aligned
+    assert prefill(P, ptrs=ptrs) == B.KDA_ERR_ALIGN
+
+
+@pytest.mark.parametrize("init,dst,cu,n_tokens,code", [
+    ([0, 1], [2, 3], [0, 3, 7], 7, 0),
+    ([0, 1], None, [0, 0, 0], 0, 0),                        # empty sequences, in place
+    ([0, 1], [2, 2], [0, 3, 7], 7, B.KDA_ERR_SLOT),         # one slot stored twice
+    ([0, 1], [1, 3], [0, 3, 7], 7, B.KDA_ERR_SLOT),         # destination is another's initial slot
+    ([0, 16], None, [0, 3, 7], 7, B.KDA_ERR_SLOT),          # slot out of range
+    ([0, 1], None, [0, 5, 3], 7, B.KDA_ERR_ARG),            # cu_seqlens decreasing
+    ([0, 1], None, [0, 3, 8], 7, B.KDA_ERR_ARG),            # past the token arrays
+    ([0, 1], None, [-1, 3, 7], 7, B.KDA_ERR_ARG),
+])
+def test_prefill_validate(init, dst, cu, n_tokens, code):
+    assert B.kda_prefill_validate(pool(n_slots=16), init, cu, n_tokens, B.KDA_F32,
+                                  dst_slot_ids_host=dst) == code

@@ -1,0 +1,160 @@
+"""GPU parity of the chunked prefill (kda_prefill) against the oracle's
+token-by-token prefill (oracle.prefill_f32, fp32, sequential sums).
+
+Tolerances.  The chunked kernel reassociates the recurrence (per-channel
+cumulative decays, a triangular solve per chunk, matrix-core sums), so its
+rounding differs from the oracle's by more than one decode step's.  The
+bounds are the decode ones carried over: fp32 pools, max abs state error
+<= 1e-6 over every stored state and per (token, head) ||o - o_ref|| /
+||o_ref|| <= 1e-5.  fp16 pools: every stored element must be the RNE of some
+fp32 value within 1e-6 of the oracle's fp32 state (the fp32 bound, then the
+store's rounding), which for states of ordinary size is "within 1 fp16
+ulp".  The strong-decay stress case is graded against the fp64 oracle with
+a 1e-4 output bound: there the fp32 oracle itself is 2e-5 from fp64
+(outputs are a small difference of large terms)."""
+import numpy as np
+import pytest
+
+import kda_inputs
+from gpu_helpers import B, need_gpu, pool_to_host, torch
+
+pytestmark = pytest.mark.gpu
+
+STATE_ABS = 1e-6
+OUT_REL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def run_gpu(inp, chunk=0, dst=True):
+    dev = torch.device("cuda", 0)
+    pool = torch.from_numpy(inp.pool if inp.dtype == "f32" else inp.pool.view(np.float16)).to(dev)
+    t = {n: torch.from_numpy(getattr(inp, n)).to(dev) for n in ("q", "k", "v", "g", "b")}
+    init = torch.from_numpy(inp.init_slot_ids).to(dev)
+    dst_d = torch.from_numpy(inp.dst_slot_ids).to(dev) if dst else None
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    out = torch.full((inp.q.shape[0], inp.pool.shape[1], inp.pool.shape[3]), float("nan"),
+                     device=dev)
+    B.kda_prefill(pool, init, cu, t["q"], t["k"], t["v"], t["g"], t["b"], out, dst_slot_ids=dst_d,
+                  scale=inp.scale, chunk=chunk)
+    torch.cuda.synchronize()
+    return pool_to_host(pool), out.cpu().numpy()
+
+
+def ordered(bits):
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def check_state(oracle, inp, gpu_pool, ref_pool32, slots):
+    """ref_pool32: the oracle's fp32 final states (an fp32 pool run on the
+    widened initial states)."""
+    for s in slots:
+        ref = ref_pool32[s]
+        if inp.dtype == "f32":
+            err = np.max(np.abs(gpu_pool[s] - ref))
+            assert err <= STATE_ABS, "slot %d: state error %.3e" % (s, err)
+        else:
+            lo = ordered(oracle.f32_to_f16_rne(ref - np.float32(STATE_ABS)))
+            hi = ordered(oracle.f32_to_f16_rne(ref + np.float32(STATE_ABS)))
+            got = ordered(gpu_pool[s])
+            bad = (got < lo) | (got > hi)
+            assert not bad.any(), "slot %d: %d fp16 elements outside RNE([x - 1e-6, x + 1e-6])" % (
+                s, int(bad.sum()))
+
+
+def out_rel(go, oo):
+    num = np.linalg.norm(go - oo, axis=-1)
+    den = np.linalg.norm(oo, axis=-1)
+    return float(np.max(num / np.maximum(den, 1e-30))) if num.size else 0.0
+
+
+def oracle_f32_states(oracle, inp, seqs=None):
+    """The oracle on the widened initial states (fp32 pool), so the final
+    states come back before any rounding; restricted to `seqs` if given."""
+    pool32 = inp.pool.copy() if inp.dtype == "f32" else oracle.f16_to_f32(inp.pool)
+    init, dst, cu = inp.init_slot_ids, inp.dst_slot_ids, inp.cu_seqlens
+    if seqs is not None:
+        seqs = list(seqs)
+        init, dst = init[seqs], dst[seqs]
+        lens = np.diff(cu)[seqs]
+        starts = cu[seqs]
+        idx = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, lens)]).astype(np.int64)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        rows = [getattr(inp, n)[idx] for n in ("q", "k", "v", "g", "b")]
+    else:
+        idx = None
+        rows = [inp.q, inp.k, inp.v, inp.g, inp.b]
+    out = oracle.prefill_f32(pool32, init, cu, *rows, dst_slot_ids=dst, scale=inp.scale)
+    return pool32, out, idx
+
+
+LENGTHS = [0, 1, 15, 16, 17, 63, 64, 65, 130, 200]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("chunk", [64, 32])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_prefill_parity(oracle, dtype, chunk, in_place):
+    inp = kda_inputs.make_prefill_inputs("prefill parity", LENGTHS, 24, dtype, H=2, seed=11,
+                                         in_place=in_place)
+    gp, go = run_gpu(inp, chunk)
+    ref32, oo, _ = oracle_f32_states(oracle, inp)
+    check_state(oracle, inp, gp, ref32, inp.dst_slot_ids)
+    T = inp.n_tokens
+    assert out_rel(go[:T], oo[:T]) <= OUT_REL
+    named = set(inp.dst_slot_ids.tolist())
+    for s in range(24):
+        if s not in named:
+            np.testing.assert_array_equal(gp[s], inp.pool[s])
+
+
+def test_prefill_without_dst_table_stores_in_place(oracle):
+    inp = kda_inputs.make_prefill_inputs("prefill in place", [40, 70], 6, "f32", H=3, seed=13)
+    gp, go = run_gpu(inp, dst=False)
+    ref32, oo, _ = oracle_f32_states(oracle, inp)
+    check_state(oracle, inp, gp, ref32, inp.init_slot_ids)
+    assert out_rel(go, oo) <= OUT_REL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_prefill_empty_sequences_copy_the_state(dtype):
+    inp = kda_inputs.make_prefill_inputs("prefill empty", [0, 0, 5], 8, dtype, H=2, seed=14,
+                                         in_place=False)
+    gp, _ = run_gpu(inp)
+    for s in (0, 1):
+        np.testing.assert_array_equal(gp[inp.dst_slot_ids[s]], inp.pool[inp.init_slot_ids[s]])
+
+
+def test_prefill_strong_decay_takes_the_exact_path(oracle):
+    # log-decays of -3 .. -8 per token: the in-block decay passes e^80, so
+    # the diagonal blocks go pair by pair; results stay finite and accurate
+    inp = kda_inputs.make_prefill_inputs("prefill strong decay", [130, 40], 8, "f32", H=2, seed=12)
+    inp.g[:] = -np.random.default_rng(0).uniform(3.0, 8.0, inp.g.shape).astype(np.float32)
+    gp, go = run_gpu(inp)
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gp))
+    p64 = inp.pool.astype(np.float64)
+    o64 = oracle.prefill_f64(p64, inp.init_slot_ids, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.g,
+                             inp.b, scale=inp.scale)
+    for s in inp.init_slot_ids:
+        assert np.max(np.abs(gp[s] - p64[s])) <= STATE_ABS
+    assert out_rel(go, o64) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_prefill_full_batch_sampled(oracle, dtype):
+    """The bench's workload (32 ragged prompts, ~34K tokens, H = 12) in the
+    launch configuration the bench times; the oracle recomputes the three
+    shortest prompts (all heads) and every output must be finite."""
+    inp = kda_inputs.prefill_batch(dtype)
+    gp, go = run_gpu(inp)
+    T = inp.n_tokens
+    assert np.all(np.isfinite(go[:T]))
+    lens = np.diff(inp.cu_seqlens)
+    seqs = [int(s) for s in np.argsort(lens, kind="stable")[:3]]
+    ref32, oo, idx = oracle_f32_states(oracle, inp, seqs)
+    check_state(oracle, inp, gp, ref32, inp.dst_slot_ids[seqs])
+    assert out_rel(go[idx], oo) <= OUT_REL
