@@ -303,7 +303,7 @@ int32_t kda_tile_bv(kda_dtype dtype);
  *  q, k, g        device fp32 [n_tokens, H, 128], 16-byte aligned; v, out
  *                 device fp32 [n_tokens, H, 128]; b device fp32 [n_tokens, H].
  *  n_seq          sequences (<= n_slots); n_tokens: rows of the token arrays.
- *  opts           NULL or kda_prefill_opts (chunk: 0 = default 64, or 32/64
+ *  opts           NULL or kda_prefill_opts (chunk: 0 = default 32, or 32/64
  *                 tokens per chunk; the chunk changes the rounding order,
  *                 never the operation).
  * The chunked form (per-channel cumulative decay, a unit lower-triangular

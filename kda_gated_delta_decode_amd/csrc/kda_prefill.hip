@@ -22,26 +22,28 @@
 // contraction and runs on the matrix cores (v_mfma_f32_16x16x4_f32: fp32
 // operands, fp32 accumulation).
 //
-// Bounded exponentials.  A and P need e^(G_t - G_s) <= 1 as a product of a
-// t-factor and an s-factor.  Tokens are grouped in blocks of 16; for row
-// block bt the reference is the cumulative decay just before the block, so
-// the t-factor e^(G_t - G_ref) is <= 1 and, for s in an earlier block, the
-// s-factor e^(G_ref - G_s) is <= 1 too.  Inside the diagonal block the
-// s-factor exceeds 1 by at most the block's own decay; should that exceed
-// e^80 for some channel (a decay of more than 80 nats within 16 tokens) the
-// block is computed pair by pair instead.  All exponents are formed from
-// block-local sums, so the ones that matter (close tokens) are small and
-// accurate.
+// Bounded exponentials.  A and P need 2^(G_t - G_s) <= 1 (decays are kept
+// in log2 units, g log2 e, so each exponential is one v_exp_f32) as a
+// product of a t-factor and an s-factor.  Tokens are grouped in blocks of
+// 16; for row block bt the reference is the cumulative decay just before the
+// block, so the t-factor 2^(G_t - G_ref) is <= 1 and, for s in an earlier
+// block, the s-factor 2^(G_ref - G_s) is <= 1 too.  Inside the diagonal
+// block the s-factor exceeds 1 by at most the block's own decay; should that
+// exceed 2^115 (80 nats) for some channel, the block is computed pair by
+// pair instead.  All exponents are formed from block-local sums, so the ones
+// that matter (close tokens) are small and accurate.
 //
-// Work decomposition.  One workgroup = one (sequence, head); its 4
-// wavefronts split the 128 value columns (32 each) for everything that
-// touches the state, and split the chunk's token blocks for the per-chunk
-// quantities (norms, decays, A, P, the diagonal inverses), which they share
-// through LDS.  The state slice of a wave stays in registers, in the matrix
-// cores' accumulator layout, for the whole prompt; that layout is also a
-// valid B operand for the next contraction over the key channels (the
-// k-order of a 16x16x4 step is permuted to match, and the A operand is read
-// from LDS in the same order).
+// Work decomposition.  One workgroup = one (sequence, head) with 8
+// wavefronts.  For everything that touches the state they split the 128
+// value columns (16 each); for the per-chunk quantities (norms, decays,
+// the operands) they split token blocks and channel parts, and the products
+// A and P (one chain per block pair and matrix) go round-robin to them; all
+// of it is shared through LDS.  The state slice of a wave stays in
+// registers, in the matrix cores' accumulator layout, for the whole prompt;
+// that layout is also a valid B operand for the next contraction over the
+// key channels (the k-order of a 16x16x4 step is permuted to match, and the
+// A operand is read from LDS in the same order).  The next chunk's rows are
+// loaded while the current chunk is processed.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -55,11 +57,13 @@
 namespace kda {
 namespace {
 
-constexpr int kPWaves = 4;     // wavefronts per workgroup
-constexpr int kPCols = 32;     // value columns per wavefront
 constexpr int kLdK = 132;      // row stride (floats) of [C][128] LDS arrays
-constexpr float kDiagLimit = 80.0f;  // largest in-block decay (nats) of the factored path
-constexpr int32_t kDefaultChunk = 64;
+// Decays are carried in log2 units (g * log2 e) so every exponential is one
+// v_exp_f32 (2^x, about 1 ulp); the factored path admits an in-block decay
+// of up to 2^115 (80 nats).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kDiagLimit = 115.0f;
+constexpr int32_t kDefaultChunk = 32;
 
 struct PrefillArgs {
   void* pool;
@@ -78,6 +82,8 @@ struct PrefillArgs {
   int32_t n_seq;
   float scale;
 };
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ f4 mma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -112,29 +118,40 @@ __device__ __forceinline__ void narrow1(T* p, float x) {
   }
 }
 
-// Chunk of NB blocks of 16 tokens (C = 16 NB).  Waves w < NB own token block
-// w for the per-chunk quantities; every wave owns value columns
-// 32 w .. 32 w + 31 of the state.
-template <typename T, int NB>
-__global__ __launch_bounds__(64 * kPWaves) void kda_prefill_kernel(PrefillArgs a) {
+// Chunk of NB blocks of 16 tokens (C = 16 NB), NW wavefronts.
+//  - per-token rows (norms, decays, operands): wave w takes token block
+//    w % NB and channel part w / NB (NW / NB parts of 128 / (NW / NB)
+//    channels; a lane holds CPL of them);
+//  - A and P: the NB (NB + 1) / 2 block pairs (bt >= bs) go round-robin to
+//    the waves;
+//  - the state: wave w owns value columns CPW w .. CPW w + CPW - 1.
+template <typename T, int NB, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+void kda_prefill_kernel(PrefillArgs a) {
   constexpr int C = 16 * NB;
-  constexpr int LdC = C + 4;  // row stride of [C][C] and [128][C] arrays
-  // kn, then -Kb (A operand of R = beta V - Kb S)
+  constexpr int LdC = C + 4;       // row stride of [C][C] arrays
+  constexpr int PARTS = NW / NB;   // channel parts of the per-token phases
+  constexpr int CPL = 32 / PARTS;  // channels per lane in those phases
+  constexpr int CPW = 128 / NW;    // value columns per wave
+  constexpr int NCB = CPW / 16;    // 16-column blocks per wave
+  constexpr int NPAIR = NB * (NB + 1) / 2;
+  static_assert(NW % NB == 0 && CPL % 4 == 0 && CPW % 16 == 0, "launch shape");
+  // Per-token rows [C][128]: raw k, block-local cumulative log2-decay and
+  // raw q; then, in place, the operands -Kb, Qg and Kd.
   __shared__ __attribute__((aligned(16))) float sX[C * kLdK];
-  // block-local cumulative log-decay, then Qg
   __shared__ __attribute__((aligned(16))) float sY[C * kLdK];
-  __shared__ __attribute__((aligned(16))) float sKdT[128 * LdC];  // Kd^T
+  __shared__ __attribute__((aligned(16))) float sZ[C * kLdK];
   __shared__ __attribute__((aligned(16))) float sA[C * LdC];      // -A (strictly lower)
   __shared__ __attribute__((aligned(16))) float sP[C * LdC];      // P (lower)
   __shared__ __attribute__((aligned(16))) float sTd[NB][16 * 20]; // (I + A_bb)^-1
-  __shared__ float sBtot[NB][128];  // per block: sum of g over its tokens
-  __shared__ float sGC[128];        // e^(G_C)
+  __shared__ __attribute__((aligned(16))) float sBtot[NB][128];   // per block: sum of g log2 e
+  __shared__ __attribute__((aligned(16))) float sPre[NB + 1][128];  // sums of Btot over blocks < u
+  __shared__ float sGC[128];                                      // 2^(G_C)
   __shared__ float sBeta[C];
+  __shared__ float sSq[PARTS][C];  // partial sums of q^2, k^2 per channel part
+  __shared__ float sSk[PARTS][C];
 
-  const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
-  const int li = lane % 16;  // MFMA row / column index
-  const int gq = lane / 16;  // lane group
   const int seq = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
 
@@ -147,240 +164,294 @@ __global__ __launch_bounds__(64 * kPWaves) void kda_prefill_kernel(PrefillArgs a
     return;  // refused by the host checks; never touch memory outside the launch's bounds
 
   const int64_t hk = static_cast<int64_t>(a.H) * 128;  // floats per token of q, k, g, v, out
-  const int col_w = kPCols * wave;                       // this wave's first value column
+  const int col_w = CPW * wave;                          // this wave's first value column
+  const int64_t head_off = static_cast<int64_t>(h) * 128 * 128;
 
   // -- initial state slice: S[sb][cb] holds rows 16 sb + 4 gq + r, column
   //    col_w + 16 cb + li (the 16x16 accumulator layout)
-  const T* pool = static_cast<const T*>(a.pool);
-  const int64_t head_off = static_cast<int64_t>(h) * 128 * 128;
-  f4 S[8][2];
+  f4 S[8][NCB];
   {
-    const T* src = pool + static_cast<int64_t>(init) * a.H * 128 * 128 + head_off;
+    const int li = threadIdx.x % 16, gq = (threadIdx.x % 64) / 16;
+    const T* src = static_cast<const T*>(a.pool) + static_cast<int64_t>(init) * a.H * 128 * 128 +
+                   head_off;
 #pragma unroll
     for (int sb = 0; sb < 8; ++sb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           S[sb][cb][r] = widen1(src + (16 * sb + 4 * gq + r) * 128 + col_w + 16 * cb + li);
   }
 
+  // Rows of the next chunk are loaded one chunk ahead (q, k, g of this
+  // lane's token and channels, b, and v of the wave's columns), so the loads
+  // overlap the current chunk's work instead of opening each chunk.
+  f4 nq[CPL / 4], nk[CPL / 4], ng[CPL / 4], nv[NB][NCB];
+  float nb = 0.0f;
+  auto prefetch = [&](int64_t c, int li_, int gq_) {
+    const int m_ = static_cast<int>(t1 - c < C ? t1 - c : C);
+    const int tl_ = 16 * (wave % NB) + li_;
+    const int ch_ = (wave / NB) * (128 / PARTS) + gq_ * CPL;
+    const bool ok = tl_ < m_;
+    const int64_t off = (c + tl_) * hk + static_cast<int64_t>(h) * 128 + ch_;
+#pragma unroll
+    for (int m = 0; m < CPL / 4; ++m) {
+      nq[m] = ok ? *reinterpret_cast<const f4*>(a.q + off + 4 * m) : f4{0.f, 0.f, 0.f, 0.f};
+      nk[m] = ok ? *reinterpret_cast<const f4*>(a.k + off + 4 * m) : f4{0.f, 0.f, 0.f, 0.f};
+      ng[m] = ok ? *reinterpret_cast<const f4*>(a.g + off + 4 * m) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    nb = ok ? a.b[(c + tl_) * a.H + h] : 0.0f;
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = 16 * tb + 4 * gq_ + r;
+          nv[tb][cb][r] = tr < m_ ? a.v[(c + tr) * hk + static_cast<int64_t>(h) * 128 + col_w +
+                                        16 * cb + li_]
+                                  : 0.0f;
+        }
+  };
+  if (t0 < t1) prefetch(t0, threadIdx.x % 16, (threadIdx.x % 64) / 16);
+
   for (int64_t c0 = t0; c0 < t1; c0 += C) {
     const int n = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
+    // Lane indices re-derived from an opaque copy of the thread id in every
+    // chunk: the many lane-dependent LDS addresses and constants of the loop
+    // body are then recomputed per chunk (a few integer ops) instead of being
+    // hoisted out of the loop and held in registers, which would leave too
+    // few for the state and accumulators.
+    int tid_v = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid_v));
+    const int li = tid_v % 16;
+    const int gq = (tid_v % 64) / 16;
+    // the per-token phases: token block, channel part, this lane's row and channels
+    const int pb = wave % NB;
+    const int pp = wave / NB;
+    const int tl = 16 * pb + li;
+    const int ch0 = pp * (128 / PARTS) + gq * CPL;
+    const int row = tl * kLdK + ch0;
 
-    // ---- per-chunk quantities: wave w < NB, token 16 w + li, channels 32 gq .. 32 gq + 31
-    float qn[32], kn[32], gl[32];
-    float beta = 0.0f;
-    const bool tok_wave = wave < NB;
-    if (tok_wave) {
-      const int tl = 16 * wave + li;
+    // ---- per-token rows from the prefetched registers: raw q and k, partial
+    // sums of squares, block-local cumulative decays
+    f4 D[NB][NCB];
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) D[tb][cb] = nv[tb][cb];  // v; beta is applied later
+    {
       const bool valid = tl < n;
       float sq = 0.0f, sk = 0.0f;
-      if (valid) {
-        const int64_t off = (c0 + tl) * hk + static_cast<int64_t>(h) * 128 + 32 * gq;
 #pragma unroll
-        for (int m = 0; m < 32; m += 4) {
-          const f4 x = *reinterpret_cast<const f4*>(a.q + off + m);
-          const f4 y = *reinterpret_cast<const f4*>(a.k + off + m);
-          const f4 z = *reinterpret_cast<const f4*>(a.g + off + m);
+      for (int m = 0; m < CPL / 4; ++m) {
+        f4 gl4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qn[m + e] = x[e];
-            kn[m + e] = y[e];
-            gl[m + e] = z[e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          sq = fmaf(nq[m][e], nq[m][e], sq);
+          sk = fmaf(nk[m][e], nk[m][e], sk);
+          gl4[e] = row_scan(ng[m][e] * kLog2e);  // block-local inclusive cumulative sum
         }
-        beta = 1.0f / (1.0f + expf(-a.b[(c0 + tl) * a.H + h]));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) qn[i] = kn[i] = gl[i] = 0.0f;
+        *reinterpret_cast<f4*>(sZ + row + 4 * m) = nq[m];
+        *reinterpret_cast<f4*>(sX + row + 4 * m) = nk[m];
+        *reinterpret_cast<f4*>(sY + row + 4 * m) = gl4;
+        if (li == 15) *reinterpret_cast<f4*>(&sBtot[pb][ch0 + 4 * m]) = gl4;
       }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        sq = fmaf(qn[i], qn[i], sq);
-        sk = fmaf(kn[i], kn[i], sk);
+      sq = group_sum(sq);
+      sk = group_sum(sk);
+      if (gq == 0) {
+        sSq[pp][tl] = sq;
+        sSk[pp][tl] = sk;
+        if (pp == 0) sBeta[tl] = valid ? 1.0f / (1.0f + expf(-nb)) : 0.0f;
       }
-      const float rq = 1.0f / sqrtf(group_sum(sq) + 1e-6f);
-      const float rk = 1.0f / sqrtf(group_sum(sk) + 1e-6f);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        qn[i] *= rq;
-        kn[i] *= rk;
-        gl[i] = row_scan(gl[i]);  // block-local inclusive cumulative log-decay
-      }
-      float* xr = sX + tl * kLdK + 32 * gq;
-      float* yr = sY + tl * kLdK + 32 * gq;
-#pragma unroll
-      for (int m = 0; m < 32; m += 4) {
-        *reinterpret_cast<f4*>(xr + m) = f4{kn[m], kn[m + 1], kn[m + 2], kn[m + 3]};
-        *reinterpret_cast<f4*>(yr + m) = f4{gl[m], gl[m + 1], gl[m + 2], gl[m + 3]};
-      }
-      if (li == 15) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) sBtot[wave][32 * gq + i] = gl[i];
-      }
-      if (gq == 0) sBeta[tl] = beta;
     }
+    if (c0 + C < t1) prefetch(c0 + C, li, gq);
     __syncthreads();
 
-    // ---- A and P, row block w: t-factors e^(G_t - G_ref) = e^(gl_t)
-    if (tok_wave) {
-      const int w = wave;
-      float lq[32], lk[32];
+    // ---- block prefix sums of the decay and 2^(G_C) (wave 0), then A and P
+    if (wave == 0) {
+      const int lane = tid_v % 64;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float e = expf(gl[i]);
-        lq[i] = qn[i] * e;
-        lk[i] = (beta * kn[i]) * e;
-      }
-      // in-block decay beyond the factored range: this wave's block goes pair by pair
-      float span = 0.0f;
+      for (int e = 0; e < 2; ++e) {
+        const int ch = 2 * lane + e;
+        float acc = 0.0f;
+        sPre[0][ch] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) span = fmaxf(span, -gl[i]);
-      const bool exact_diag = __builtin_amdgcn_ballot_w64(span > kDiagLimit) != 0;
-
-      // column blocks bs = w, w - 1, .., 0; cum = sum of Btot_u over bs <= u < w
-      float cum[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) cum[i] = 0.0f;
-      for (int bs = w; bs >= 0; --bs) {
-        if (bs < w) {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) cum[i] += sBtot[bs][32 * gq + i];
+        for (int u = 0; u < NB; ++u) {
+          acc += sBtot[u][ch];
+          sPre[u + 1][ch] = acc;
         }
-        // s-factors for token s = 16 bs + li, channels 32 gq + i:
-        // e^(G_ref - G_s) = e^(cum - gl_s)
-        const float* kr = sX + (16 * bs + li) * kLdK + 32 * gq;
-        const float* gr = sY + (16 * bs + li) * kLdK + 32 * gq;
-        f4 accp = {0.f, 0.f, 0.f, 0.f}, acca = {0.f, 0.f, 0.f, 0.f};
-        if (bs < w || !exact_diag) {
+        sGC[ch] = exp2_fast(acc);
+      }
+    }
+    // Chains (block pair (bt, bs), P or A) go round-robin to the waves.  Step
+    // (m, e) of the contraction is channel 32 gq + m + e in both operands.
+    // t-factors 2^(G_t - G_ref) = 2^(gl_t); s-factors for token s = 16 bs + li:
+    // 2^(G_ref - G_s) = 2^(cum - gl_s), cum = sum of Btot over bs <= u < bt.
+    for (int ci = wave; ci < 2 * NPAIR; ci += NW) {
+      const int pi = ci / 2;
+      const bool is_a = (ci & 1) != 0;  // A (with beta kn) or P (with qn)
+      int bt = 0;
+      while ((bt + 1) * (bt + 2) / 2 <= pi) ++bt;
+      const int bs = pi - bt * (bt + 1) / 2;
+      const int trow = (16 * bt + li) * kLdK + 32 * gq;
+      const int srow = (16 * bs + li) * kLdK + 32 * gq;
+      float st = 0.0f, ss = 0.0f;
 #pragma unroll
-          for (int m = 0; m < 32; m += 4) {
-            const f4 kx = *reinterpret_cast<const f4*>(kr + m);
-            const f4 gx = *reinterpret_cast<const f4*>(gr + m);
+      for (int u = 0; u < PARTS; ++u) {
+        st += is_a ? sSk[u][16 * bt + li] : sSq[u][16 * bt + li];
+        ss += sSk[u][16 * bs + li];
+      }
+      const float beta = sBeta[16 * bt + li];
+      // t-side scale: beta / |k_t| for A, 1 / |q_t| for P
+      const float r_t = (is_a ? beta : 1.0f) / sqrtf(st + 1e-6f);
+      const float rk_s = 1.0f / sqrtf(ss + 1e-6f);
+      const float* tsrc = is_a ? sX : sZ;
+      // in-block decay beyond the factored range: the diagonal block goes pair by pair
+      bool exact = false;
+      if (bt == bs) {
+        float span = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float rf = kx[e] * expf(cum[m + e] - gx[e]);
-              accp = mma(lq[m + e], rf, accp);
-              acca = mma(lk[m + e], rf, acca);
-            }
+        for (int m = 0; m < 32; m += 4) {
+          const f4 gl4 = *reinterpret_cast<const f4*>(sY + trow + m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) span = fmaxf(span, -gl4[e]);
+        }
+        exact = __builtin_amdgcn_ballot_w64(span > kDiagLimit) != 0;
+      }
+      if (!exact) {
+        f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int m = 0; m < 32; m += 4) {
+          f4 cum = {0.f, 0.f, 0.f, 0.f};
+          for (int u = bs; u < bt; ++u) cum += *reinterpret_cast<const f4*>(&sBtot[u][32 * gq + m]);
+          const f4 xt = *reinterpret_cast<const f4*>(tsrc + trow + m);
+          const f4 gt = *reinterpret_cast<const f4*>(sY + trow + m);
+          const f4 ks = *reinterpret_cast<const f4*>(sX + srow + m);
+          const f4 gs = *reinterpret_cast<const f4*>(sY + srow + m);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lf = (xt[e] * r_t) * exp2_fast(gt[e]);
+            const float rf = (ks[e] * rk_s) * exp2_fast(cum[e] - gs[e]);
+            if (e % 2 == 0)
+              acc0 = mma(lf, rf, acc0);
+            else
+              acc1 = mma(lf, rf, acc1);
           }
         }
-        // accumulator layout: row 16 w + 4 gq + r, column 16 bs + li
+        // accumulator layout: row 16 bt + 4 gq + r, column 16 bs + li
+        float* dstm = is_a ? sA : sP;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tr = 4 * gq + r;
-          float p = accp[r], x = acca[r];
-          if (bs == w) {
-            if (li > tr) p = 0.0f;
-            if (li >= tr) x = 0.0f;
-          }
-          sP[(16 * w + tr) * LdC + 16 * bs + li] = p;
-          sA[(16 * w + tr) * LdC + 16 * bs + li] = -x;
+          float x = acc0[r] + acc1[r];
+          if (bs == bt && (is_a ? li >= tr : li > tr)) x = 0.0f;
+          dstm[(16 * bt + tr) * LdC + 16 * bs + li] = is_a ? -x : x;
         }
-      }
-      if (exact_diag) {
+      } else {
         // pair by pair: lane (li = t, gq) sums its 32 channels for every s <= t
-        const float* grow = sY + 16 * w * kLdK + 32 * gq;
-        const float* krow = sX + 16 * w * kLdK + 32 * gq;
-        for (int s = 0; s < 16; ++s) {
-          float pp = 0.0f, pa = 0.0f;
-          if (s <= li) {
-#pragma unroll 4
+        for (int s2 = 0; s2 < 16; ++s2) {
+          const int s2row = (16 * bt + s2) * kLdK + 32 * gq;
+          float sk2 = 0.0f;
+#pragma unroll
+          for (int u = 0; u < PARTS; ++u) sk2 += sSk[u][16 * bt + s2];
+          const float rk_s2 = 1.0f / sqrtf(sk2 + 1e-6f);
+          float acc = 0.0f;
+          if (s2 <= li) {
             for (int i = 0; i < 32; ++i) {
-              const float f = krow[s * kLdK + i] * expf(gl[i] - grow[s * kLdK + i]);
-              pp = fmaf(qn[i], f, pp);
-              pa = fmaf(kn[i], f, pa);
+              const float f = (sX[s2row + i] * rk_s2) * exp2_fast(sY[trow + i] - sY[s2row + i]);
+              acc = fmaf(tsrc[trow + i] * r_t, f, acc);
             }
           }
-          pp = group_sum(pp);
-          pa = group_sum(pa);
+          acc = group_sum(acc);
           if (gq == 0) {
-            sP[(16 * w + li) * LdC + 16 * w + s] = s <= li ? pp : 0.0f;
-            sA[(16 * w + li) * LdC + 16 * w + s] = s < li ? -(beta * pa) : 0.0f;
+            if (is_a)
+              sA[(16 * bt + li) * LdC + 16 * bt + s2] = s2 < li ? -acc : 0.0f;
+            else
+              sP[(16 * bt + li) * LdC + 16 * bt + s2] = s2 <= li ? acc : 0.0f;
           }
         }
       }
     }
     __syncthreads();
 
-    // ---- operands of the state contractions; diagonal inverses
-    if (tok_wave) {
-      const int w = wave;
-      const int tl = 16 * w + li;
-      float before[32], after[32];  // sums of Btot over blocks before / after w
+    // ---- operands of the state contractions (in place of the rows); diagonal inverses
+    {
+      float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        float sb = 0.0f, sa = 0.0f;
-        for (int u = 0; u < w; ++u) sb += sBtot[u][32 * gq + i];
-        for (int u = w + 1; u < NB; ++u) sa += sBtot[u][32 * gq + i];
-        before[i] = sb;
-        after[i] = sa + (sBtot[w][32 * gq + i] - gl[i]);  // G_C - G_t
+      for (int u = 0; u < PARTS; ++u) {
+        ssq += sSq[u][tl];
+        ssk += sSk[u][tl];
       }
-      float* xr = sX + tl * kLdK + 32 * gq;
-      float* yr = sY + tl * kLdK + 32 * gq;
+      const float rq = 1.0f / sqrtf(ssq + 1e-6f);
+      const float rk = 1.0f / sqrtf(ssk + 1e-6f);
+      const float beta = sBeta[tl];
+      // G_t = (sum of Btot before block pb) + gl_t;
+      // G_C - G_t = (sum of Btot after block pb) + (Btot_pb - gl_t), both parts <= 0
 #pragma unroll
-      for (int m = 0; m < 32; m += 4) {
-        f4 nkb, qg;
+      for (int m = 0; m < CPL; m += 4) {
+        const int ch = ch0 + m;
+        const f4 k4 = *reinterpret_cast<const f4*>(sX + row + m);
+        const f4 gl4 = *reinterpret_cast<const f4*>(sY + row + m);
+        const f4 q4 = *reinterpret_cast<const f4*>(sZ + row + m);
+        const f4 pre = *reinterpret_cast<const f4*>(&sPre[pb][ch]);
+        const f4 post = *reinterpret_cast<const f4*>(&sPre[NB][ch]) -
+                        *reinterpret_cast<const f4*>(&sPre[pb + 1][ch]);
+        const f4 bt = *reinterpret_cast<const f4*>(&sBtot[pb][ch]);
+        f4 nkb, qg, kd;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float eg = expf(before[m + e] + gl[m + e]);  // e^(G_t)
-          nkb[e] = -((beta * kn[m + e]) * eg);
-          qg[e] = qn[m + e] * eg;
+          const float kn = k4[e] * rk;
+          const float eg = exp2_fast(pre[e] + gl4[e]);
+          nkb[e] = -((beta * kn) * eg);
+          qg[e] = (q4[e] * rq) * eg;
+          kd[e] = kn * exp2_fast(post[e] + (bt[e] - gl4[e]));
         }
-        *reinterpret_cast<f4*>(xr + m) = nkb;
-        *reinterpret_cast<f4*>(yr + m) = qg;
+        *reinterpret_cast<f4*>(sX + row + m) = nkb;
+        *reinterpret_cast<f4*>(sY + row + m) = qg;
+        *reinterpret_cast<f4*>(sZ + row + m) = kd;
       }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) sKdT[(32 * gq + i) * LdC + tl] = kn[i] * expf(after[i]);
-      // (I + A_ww)^-1 by forward substitution, one column per lane of group 0
-      if (gq == 0) {
+      // (I + A_bb)^-1 by forward substitution, one column per lane of group 0
+      if (wave < NB && gq == 0) {
+        const int b = wave;
         float x[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           float acc = t == li ? 1.0f : 0.0f;
 #pragma unroll
-          for (int s = 0; s < t; ++s) acc = fmaf(sA[(16 * w + t) * LdC + 16 * w + s], x[s], acc);
+          for (int s2 = 0; s2 < t; ++s2)
+            acc = fmaf(sA[(16 * b + t) * LdC + 16 * b + s2], x[s2], acc);
           x[t] = acc;  // sA holds -A
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) sTd[w][t * 20 + li] = x[t];
-      }
-    }
-    if (wave == 0) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float gc = 0.0f;
-        for (int u = 0; u < NB; ++u) gc += sBtot[u][2 * lane + e];
-        sGC[2 * lane + e] = expf(gc);
+        for (int t = 0; t < 16; ++t) sTd[b][t * 20 + li] = x[t];
       }
     }
     __syncthreads();
 
-    // ---- the state contractions, this wave's 32 value columns
+    // ---- the state contractions, this wave's CPW value columns.  Loops keep
+    // several independent accumulators in flight per step.
     // R = beta V - Kb S  (token block tb: rows 16 tb + 4 gq + r)
-    f4 D[NB][2];
 #pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
+    for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int r = 0; r < 4; ++r) {
+        const float bt = sBeta[16 * tb + 4 * gq + r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tl = 16 * tb + 4 * gq + r;
-          D[tb][cb][r] = tl < n ? sBeta[tl] * a.v[(c0 + tl) * hk + static_cast<int64_t>(h) * 128 +
-                                                  col_w + 16 * cb + li]
-                               : 0.0f;
-        }
+        for (int cb = 0; cb < NCB; ++cb) D[tb][cb][r] *= bt;
       }
 #pragma unroll
-      for (int sb = 0; sb < 8; ++sb) {
-        const f4 x = *reinterpret_cast<const f4*>(sX + (16 * tb + li) * kLdK + 16 * sb + 4 * gq);
+    for (int sb = 0; sb < 8; ++sb) {
+      f4 x[NB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          D[tb][0] = mma(x[r], S[sb][0][r], D[tb][0]);
-          D[tb][1] = mma(x[r], S[sb][1][r], D[tb][1]);
-        }
-      }
+      for (int tb = 0; tb < NB; ++tb)
+        x[tb] = *reinterpret_cast<const f4*>(sX + (16 * tb + li) * kLdK + 16 * sb + 4 * gq);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) D[tb][cb] = mma(x[tb][r], S[sb][cb][r], D[tb][cb]);
     }
     // Delta = (I + A)^-1 R, block by block: Delta_b = T_bb (R_b - sum_{k<b} A_bk Delta_k)
 #pragma unroll
@@ -389,90 +460,113 @@ __global__ __launch_bounds__(64 * kPWaves) void kda_prefill_kernel(PrefillArgs a
       for (int k = 0; k < b; ++k) {
         const f4 x = *reinterpret_cast<const f4*>(sA + (16 * b + li) * LdC + 16 * k + 4 * gq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          D[b][0] = mma(x[r], D[k][0][r], D[b][0]);
-          D[b][1] = mma(x[r], D[k][1][r], D[b][1]);
-        }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) D[b][cb] = mma(x[r], D[k][cb][r], D[b][cb]);
       }
       const f4 x = *reinterpret_cast<const f4*>(&sTd[b][li * 20 + 4 * gq]);
-      f4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+      f4 y[NCB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        y0 = mma(x[r], D[b][0][r], y0);
-        y1 = mma(x[r], D[b][1][r], y1);
-      }
-      D[b][0] = y0;
-      D[b][1] = y1;
+      for (int cb = 0; cb < NCB; ++cb) y[cb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) y[cb] = mma(x[r], D[b][cb][r], y[cb]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) D[b][cb] = y[cb];
     }
     // o = scale (Qg S + P Delta)
+    {
+      f4 O[NB][NCB];
 #pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-      f4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) O[tb][cb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sb = 0; sb < 8; ++sb) {
-        const f4 x = *reinterpret_cast<const f4*>(sY + (16 * tb + li) * kLdK + 16 * sb + 4 * gq);
+        f4 x[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+          x[tb] = *reinterpret_cast<const f4*>(sY + (16 * tb + li) * kLdK + 16 * sb + 4 * gq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) O[tb][cb] = mma(x[tb][r], S[sb][cb][r], O[tb][cb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        f4 x[NB];
+#pragma unroll
+        for (int tb = kb; tb < NB; ++tb)
+          x[tb] = *reinterpret_cast<const f4*>(sP + (16 * tb + li) * LdC + 16 * kb + 4 * gq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int tb = kb; tb < NB; ++tb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) O[tb][cb] = mma(x[tb][r], D[kb][cb][r], O[tb][cb]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          o0 = mma(x[r], S[sb][0][r], o0);
-          o1 = mma(x[r], S[sb][1][r], o1);
-        }
-      }
+          const int tr = 16 * tb + 4 * gq + r;
+          if (tr < n) {
+            float* op = a.out + (c0 + tr) * hk + static_cast<int64_t>(h) * 128 + col_w + li;
 #pragma unroll
-      for (int kb = 0; kb <= tb; ++kb) {
-        const f4 x = *reinterpret_cast<const f4*>(sP + (16 * tb + li) * LdC + 16 * kb + 4 * gq);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          o0 = mma(x[r], D[kb][0][r], o0);
-          o1 = mma(x[r], D[kb][1][r], o1);
+            for (int cb = 0; cb < NCB; ++cb) op[16 * cb] = a.scale * O[tb][cb][r];
+          }
         }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tl = 16 * tb + 4 * gq + r;
-        if (tl < n) {
-          float* op = a.out + (c0 + tl) * hk + static_cast<int64_t>(h) * 128 + col_w + li;
-          op[0] = a.scale * o0[r];
-          op[16] = a.scale * o1[r];
-        }
-      }
     }
-    // S = e^(G_C) S + Kd^T Delta
+    // S = 2^(G_C) S + Kd^T Delta
 #pragma unroll
-    for (int sb = 0; sb < 8; ++sb) {
+    for (int sb = 0; sb < 8; ++sb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float d = sGC[16 * sb + 4 * gq + r];
-        S[sb][0][r] *= d;
-        S[sb][1][r] *= d;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) S[sb][cb][r] *= d;
       }
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb) {
-        const f4 x = *reinterpret_cast<const f4*>(sKdT + (16 * sb + li) * LdC + 16 * tb + 4 * gq);
+    for (int tb = 0; tb < NB; ++tb) {
+      // A operand Kd^T[channel 16 sb + li][token 16 tb + 4 gq + r], read from the Kd rows
+      f4 x[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          S[sb][0] = mma(x[r], D[tb][0][r], S[sb][0]);
-          S[sb][1] = mma(x[r], D[tb][1][r], S[sb][1]);
-        }
-      }
+      for (int sb = 0; sb < 8; ++sb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[sb][r] = sZ[(16 * tb + 4 * gq + r) * kLdK + 16 * sb + li];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int sb = 0; sb < 8; ++sb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) S[sb][cb] = mma(x[sb][r], D[tb][cb][r], S[sb][cb]);
     }
     __syncthreads();  // the next chunk overwrites the LDS operands
   }
 
-  // -- final state to the destination slot
-  T* dstp = static_cast<T*>(a.pool) + static_cast<int64_t>(dst) * a.H * 128 * 128 + head_off;
+  // -- final state to the destination slot.  The empty asm makes the slot
+  // offset opaque, so the compiler cannot compute these addresses before the
+  // chunk loop and hold them in registers through it.
+  int64_t dst_off = static_cast<int64_t>(dst) * a.H * 128 * 128 + head_off;
+  asm volatile("" : "+s"(dst_off));
+  T* dstp = static_cast<T*>(a.pool) + dst_off;
+  const int li = threadIdx.x % 16, gq = (threadIdx.x % 64) / 16;
 #pragma unroll
   for (int sb = 0; sb < 8; ++sb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         narrow1(dstp + (16 * sb + 4 * gq + r) * 128 + col_w + 16 * cb + li, S[sb][cb][r]);
 }
 
-template <typename T, int NB>
+template <typename T, int NB, int NW>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((kda_prefill_kernel<T, NB>), dim3(static_cast<uint32_t>(a.n_seq) * a.H),
-                     dim3(64 * kPWaves), 0, s, a);
+  hipLaunchKernelGGL((kda_prefill_kernel<T, NB, NW>), dim3(static_cast<uint32_t>(a.n_seq) * a.H),
+                     dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -524,8 +618,8 @@ extern "C" int kda_prefill(const kda_pool* pool, const int32_t* init_slot_ids,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (state_dtype == KDA_F32)
-    err = chunk == 64 ? launch_prefill<float, 4>(a, s) : launch_prefill<float, 2>(a, s);
+    err = chunk == 64 ? launch_prefill<float, 4, 8>(a, s) : launch_prefill<float, 2, 8>(a, s);
   else
-    err = chunk == 64 ? launch_prefill<_Float16, 4>(a, s) : launch_prefill<_Float16, 2>(a, s);
+    err = chunk == 64 ? launch_prefill<_Float16, 4, 8>(a, s) : launch_prefill<_Float16, 2, 8>(a, s);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
