@@ -328,6 +328,8 @@ def main():
             for name, (n_req, n_rows, dt) in (("batched_%s_fused_conv" % args.dtype, (64, 1, args.dtype)),
                                               ("spec_verify_f16_fused_conv", (8, 8, "f16"))):
                 extras[name] = fused_conv(n_req, n_rows, dt, B, torch, max(50, args.steps // 2))
+        if args.extras == "all":
+            extras["prefill_" + args.dtype] = prefill_extra(args.dtype, B, torch, 20)
         # a 69-layer decode step: 69 independent 64-slot pools, one launch each
         for dt in (("f32", "f16") if args.extras == "all" else ()):
             extras["layers69_" + dt] = layers69(dt, B, torch, steps=10, warmup=2)
@@ -378,6 +380,46 @@ def fused_conv(n_req, n_rows, dtype, B, torch, steps):
     return {"workload": inp.name, "us_per_step": round(us, 3),
             "algorithmic_GB/s": round(ab / us / 1e3, 1),
             "frac_of_peak": round(ab / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+MFMA_F32_PEAK_TFLOPS = 157.3  # AMD MI355X spec: dense fp32 matrix throughput
+# Algorithmic flops of the chunked prefill per (token, head) at 32-token
+# chunks: the three state contractions (Kb S, Qg S, Kd^T Delta: 3 x 2 x 128 x
+# 128 per token), A and P over the block pairs, the block solve and P Delta
+# (each 3 x 16 x 16 x 128 x 2 per 32 tokens).  Padding of ragged chunks is
+# not counted.
+PREFILL_FLOP_PER_TOKEN_HEAD = (3 * 2 * 32 * 128 * 128 + 2 * 3 * 2 * 16 * 16 * 128
+                               + 2 * 3 * 2 * 16 * 16 * 128) // 32
+
+
+def prefill_extra(dtype, B, torch, steps):
+    """Time kda_prefill on the prefill workload (32 ragged prompts, ~34K
+    tokens, H = 12): launches replayed from a HIP graph; the roofline is the
+    fp32 matrix-core peak (the contractions run as fp32 MFMA)."""
+    import numpy as np
+    import kda_inputs
+    inp = kda_inputs.prefill_batch(dtype)
+    dev = torch.device("cuda", 0)
+    pool = torch.from_numpy(inp.pool if dtype == "f32" else inp.pool.view(np.float16)).to(dev)
+    t = {n: torch.from_numpy(getattr(inp, n)).to(dev) for n in ("q", "k", "v", "g", "b")}
+    init = torch.from_numpy(inp.init_slot_ids).to(dev)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    out = torch.empty((inp.q.shape[0], 12, 128), device=dev)
+
+    def step(_i):
+        B.kda_prefill(pool, init, cu, t["q"], t["k"], t["v"], t["g"], t["b"], out, scale=inp.scale)
+    tt = time_launches(step, steps, 3, torch)
+    us = tt["ms_per_step"] * 1e3
+    flops = inp.n_tokens * 12 * PREFILL_FLOP_PER_TOKEN_HEAD
+    tfs = flops / (us * 1e-6) / 1e12
+    res = {"workload": inp.name, "tokens": inp.n_tokens, "us_per_launch": round(us, 1),
+           "tokens_per_s": round(inp.n_tokens / (us * 1e-6)),
+           "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tfs / MFMA_F32_PEAK_TFLOPS, 4),
+                        "traffic": None, "algorithmic_flops_per_launch": flops},
+           "hbm_GB/s": round(inp.io_bytes() / (us * 1e-6) / 1e9, 1)}
+    del pool, t, out
+    return res
 
 
 def layers69(dtype, B, torch, steps, warmup, n_layers=69):

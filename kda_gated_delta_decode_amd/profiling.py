@@ -30,8 +30,8 @@ COPY_KERNEL = "kda_copy_probe_kernel"
 DECODE_KERNEL = "kda_decode_tile"
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -119,7 +119,8 @@ def trace(args):
     lines = ["# %s" % args.title, "",
              "Command (from the repository root, `TMPDIR=/tmp`):", "", "```"]
     lines += args.command + ["```", "",
-                             "Kernel source sha256[:16] at the time: `%s`." % kernel_hash(), "",
+                             "Kernel source (%s) sha256[:16] at the time: `%s`." % (
+                                 args.source, kernel_hash(os.path.join(HERE, "csrc", args.source))), "",
                              "## rocprofv3 kernel stats (all dispatches of the run)", "",
                              "| Kernel | Calls | Average µs | Min µs | Max µs |", "|---|---|---|---|---|"]
     for r in stats:
@@ -147,6 +148,11 @@ def trace(args):
         lines.append("- %d algorithmic bytes / %.3f µs = %.0f GB/s = %.1f%% of 8 TB/s" % (
             args.algorithmic_bytes, m, args.algorithmic_bytes / m / 1e3,
             100 * args.algorithmic_bytes / m / 1e3 / 8000))
+    if args.algorithmic_flops:
+        m = statistics.mean(dur)
+        tf = args.algorithmic_flops / m / 1e6
+        lines.append("- %d algorithmic flops / %.3f µs = %.1f TFLOP/s = %.1f%% of %.1f TFLOP/s" % (
+            args.algorithmic_flops, m, tf, 100 * tf / args.peak_tflops, args.peak_tflops))
     for note in args.note or []:
         lines += ["", note]
     with open(args.out, "w") as f:
@@ -167,6 +173,9 @@ def main():
     t.add_argument("--kernel", required=True)
     t.add_argument("--timed", type=int, required=True)
     t.add_argument("--algorithmic-bytes", type=int, default=0)
+    t.add_argument("--algorithmic-flops", type=int, default=0)
+    t.add_argument("--source", default="kda_decode.hip", help="kernel source file under csrc/")
+    t.add_argument("--peak-tflops", type=float, default=157.3)
     t.add_argument("--command", action="append", required=True)
     t.add_argument("--title", required=True)
     t.add_argument("--note", action="append")
