@@ -197,7 +197,41 @@ def cpu_baseline(inp, seconds: float):
                   % (calls, n_req, inp.n_req, H, inp.dtype, inp.n_rows, el),
         "us_per_full_step": el / calls * (inp.n_req / n_req) * 1e6,
         "host_cpus_available": len(os.sched_getaffinity(0)),
+        "parallel": cpu_baseline_parallel(inp, min(seconds, 6.0)),
     }
+
+
+def cpu_baseline_parallel(inp, seconds: float, max_threads: int = 16):
+    """The same oracle, one thread per available core (at most 16): each
+    thread runs whole oracle launches over its own 2 requests on its own
+    copy of the pool (the C oracle releases the GIL while it runs), for
+    about `seconds`.  A reported baseline, not tuned."""
+    import threading
+    from oracle import kda_oracle
+    n_threads = max(1, min(max_threads, len(os.sched_getaffinity(0)), inp.n_req // 2))
+    done = [0] * n_threads
+    stop = time.perf_counter() + seconds
+
+    def work(i):
+        sel = slice(2 * i * inp.n_rows, 2 * (i + 1) * inp.n_rows)
+        pool = inp.pool.copy()
+        while time.perf_counter() < stop:
+            kda_oracle.step_f32(pool, inp.slot_ids[sel], inp.q[sel], inp.k[sel], inp.v[sel],
+                                inp.g[sel], inp.b[sel], n_rows=inp.n_rows, scale=inp.scale)
+            done[i] += 1
+    t0 = time.perf_counter()
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(n_threads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    el = time.perf_counter() - t0
+    H, K, V = inp.pool.shape[1:]
+    elem = 4 if inp.dtype == "f32" else 2
+    state_bytes = sum(done) * 2 * H * K * V * elem * (1 + inp.n_rows)
+    return {"value": state_bytes / el / 1e9, "unit": "GB/s", "cores": n_threads,
+            "sample": "%d threads x whole oracle launches of 2 requests x %d heads, %.1f s"
+                      % (n_threads, H, el)}
 
 
 def main():
