@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -133,6 +133,15 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
  *  waves_per_tile  wavefronts that split one tile's 128 key rows: 1, 2, 4, 8.
  *  bv              value columns per tile: 32, 64 or 128 for fp32 pools
  *                  (8, 16, 32 lanes per tile row), 64 or 128 for fp16.
+ *  block_rows      chained rows only: 0 (default) runs a request's rows
+ *                  one after the other (two column sums over K and a
+ *                  cross-lane reduction per row); non-zero takes them as one
+ *                  block (all 2 n column sums of the initial state in one
+ *                  pass, an n x n triangular solve, then element-wise
+ *                  snapshots).  Both compute the same chain and round
+ *                  differently; on MI355X the block form measured slower at
+ *                  8 rows (its n x n coupling sums cost more than the
+ *                  per-row reductions they replace).
  * Supported combinations keep 2..32 key rows per lane (rows per lane =
  * 2 * lanes per row / waves).  The shape changes the order of the fp32
  * column sums over K (so results may differ in the last bits), never the
@@ -141,6 +150,7 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
 typedef struct kda_launch_opts {
   int32_t waves_per_tile;
   int32_t bv;
+  int32_t block_rows;
 } kda_launch_opts;
 
 /*

@@ -51,7 +51,8 @@ class kda_conv_pool(ctypes.Structure):
 
 
 class kda_launch_opts(ctypes.Structure):
-    _fields_ = [("waves_per_tile", ctypes.c_int32), ("bv", ctypes.c_int32)]
+    _fields_ = [("waves_per_tile", ctypes.c_int32), ("bv", ctypes.c_int32),
+                ("block_rows", ctypes.c_int32)]
 
 
 class kda_prefill_opts(ctypes.Structure):
@@ -201,7 +202,7 @@ def _check(code: int, where: str) -> None:
 def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1,
                     state_dtype=None, scale: float | None = None, stream=None,
                     waves_per_tile: int = 0, bv: int = 0, pool_dtype=None,
-                    init_slot_ids=None) -> None:
+                    init_slot_ids=None, block_rows: bool = False) -> None:
     """One decode launch (see kda_decode_step in include/kda_decode.h).
 
     pool: device tensor [n_slots, H, 128, 128], float32 or float16, updated
@@ -209,8 +210,9 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
     v, out: [R, H, 128]; b: [R, H].  state_dtype defaults to the pool's
     dtype; pool_dtype overrides what the pool struct declares (tests of the
     refusals).  init_slot_ids (device int32 [n_req]) reads each request's
-    initial state from that slot; it, or a non-zero waves_per_tile or bv,
-    selects kda_decode_step_ex."""
+    initial state from that slot; block_rows takes chained rows as one block
+    instead of one after the other; any of these, or a non-zero
+    waves_per_tile or bv, selects kda_decode_step_ex."""
     import torch
     P = make_pool(pool, pool_dtype)
     sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
@@ -229,10 +231,10 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
             _dev(g, "g", torch.float32), _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
             n_req, n_rows_per_slot, sd, float(scale))
     ids = _dev(slot_ids, "slot_ids", torch.int32)
-    if waves_per_tile or bv or init_slot_ids is not None:
+    if waves_per_tile or bv or block_rows or init_slot_ids is not None:
         if init_slot_ids is not None and init_slot_ids.numel() != n_req:
             raise ValueError("init_slot_ids needs one entry per request")
-        opts = kda_launch_opts(int(waves_per_tile), int(bv))
+        opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)))
         rc = library().kda_decode_step_ex(ctypes.byref(P), ids,
                                           _dev(init_slot_ids, "init_slot_ids", torch.int32), *rows,
                                           ctypes.byref(opts), _stream_ptr(stream))
@@ -254,7 +256,8 @@ def make_conv_pool(conv) -> kda_conv_pool:
 
 def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot: int = 1,
                          state_dtype=None, scale: float | None = None, stream=None,
-                         init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0) -> None:
+                         init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0,
+                         block_rows: bool = False) -> None:
     """Decode step with the short causal convolution fused in front (see
     kda_decode_step_conv in include/kda_decode.h).  conv: bfloat16 history
     [n_slots, 3, 3, H, 128]; x: fp32 raw q|k|v [R, 3, H, 128]; conv_w: fp32
@@ -274,7 +277,7 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
                        (g, "g", R * H * KDA_HEAD_K), (out, "out", R * H * KDA_HEAD_K),
                        (b, "b", R * H), (init_slot_ids, "init_slot_ids", n_req)):
         _need_numel(t, name, n)
-    opts = kda_launch_opts(int(waves_per_tile), int(bv))
+    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)))
     rc = library().kda_decode_step_conv(
         ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32),
         _dev(init_slot_ids, "init_slot_ids", torch.int32), _dev(x, "x", torch.float32),
@@ -367,9 +370,9 @@ def kda_tile_bv(dtype) -> int:
 
 
 def kda_describe_launch(n_req: int, n_rows: int, H: int, dtype, waves_per_tile: int = 0,
-                        bv: int = 0) -> dict:
+                        bv: int = 0, block_rows: bool = False) -> dict:
     d = kda_launch_desc()
-    opts = kda_launch_opts(int(waves_per_tile), int(bv))
+    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)))
     _check(library().kda_describe_launch(n_req, n_rows, H, _dtype_arg(dtype), ctypes.byref(opts),
                                          ctypes.byref(d)), "kda_describe_launch")
     return {"bv": d.bv, "waves_per_tile": d.waves_per_tile, "threads": d.threads,

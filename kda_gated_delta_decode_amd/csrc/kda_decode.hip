@@ -61,6 +61,7 @@ struct Args {
   int32_t H;
   int32_t n_rows;
   int32_t n_vt;  // V-tiles per head
+  int32_t rows_block;  // chained rows: 1 = as one block, 0 = row after row (default)
   float scale;
 };
 
@@ -154,7 +155,7 @@ __device__ __forceinline__ void lds_rows(const float* src, float (&dst)[N]) {
 // in registers across the request's rows); otherwise the request has one row
 // and the tile stays packed in its storage type, widened where it is used.
 // ---------------------------------------------------------------------------
-template <typename T, int LPR, int NW, bool MULTI, bool CONV>
+template <typename T, int LPR, int NW, bool MULTI, bool CONV, bool BLOCK>
 __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   using L = Lane16<T>;
   using vec = typename L::vec;
@@ -180,7 +181,14 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   __shared__ __attribute__((aligned(16))) float s_v[TMAX][BV];
   __shared__ float s_beta[TMAX];
   __shared__ float s_qk[TMAX];
-  __shared__ __attribute__((aligned(16))) float s_red[NW > 1 ? 2 : 1][NW > 1 ? NW : 1][2][BV];
+  __shared__ __attribute__((aligned(16))) float s_red[NW > 1 && !BLOCK ? 2 : 1][NW > 1 && !BLOCK ? NW : 1][2][BV];
+  // rows as a block: each wave's partial column sums of the 2 x TMAX
+  // projections of the initial state, and the TMAX x TMAX coupling matrices
+  constexpr int BW = BLOCK && NW > 1 ? NW : 1;
+  constexpr int BR = BLOCK && NW > 1 ? 2 * TMAX : 1;
+  __shared__ __attribute__((aligned(16))) float s_wp[BW][BR][BLOCK && NW > 1 ? BV : 4];
+  __shared__ float s_cA[BLOCK ? TMAX : 1][BLOCK ? TMAX : 1];
+  __shared__ float s_cP[BLOCK ? TMAX : 1][BLOCK ? TMAX : 1];
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -381,6 +389,176 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
     for (int m = 0; m < RPL; ++m) L::widen(raw[m], S[m]);
   }
 
+  if constexpr (BLOCK) {
+    // ---- the request's rows as one block ------------------------------------
+    // With gamma_t = a_0 ... a_t (per key channel), Delta_t = beta_t u_t and
+    // E_ts = a_(s+1) ... a_t, the chain unrolls to
+    //   Delta_t = beta_t (v_t - w0_t - sum_{s<t} C_ts Delta_s),
+    //   w0_t = S0^T (gamma_t kn_t),     C_ts = sum_i kn_ti kn_si E_ts,i,
+    //   S_t  = diag(a_t) S_(t-1) + kn_t Delta_t^T,
+    //   o_t  = scale (p0_t + sum_{s<=t} P_ts Delta_s),
+    //   p0_t = S0^T (gamma_t qn_t),     P_ts = sum_i qn_ti kn_si E_ts,i.
+    // All 2 n column sums over K are taken in one pass over S0 and reduced
+    // together; the per-row work is then element-wise (no reduction, no
+    // barrier between rows).
+    // (1) C and P: wave w takes s = w, w + NW, ...; a lane two key channels
+    for (int s = wave; s < n_rows; s += NW) {
+      const int i0 = 2 * lane;
+      const f2 ks = *reinterpret_cast<const f2*>(&s_kn[s][i0]);
+      float e0 = 1.0f, e1 = 1.0f;
+      for (int t = s; t < n_rows; ++t) {
+        const f2 at = *reinterpret_cast<const f2*>(&s_a[t][i0]);
+        const f2 qt = *reinterpret_cast<const f2*>(&s_qn[t][i0]);
+        const f2 kt = *reinterpret_cast<const f2*>(&s_kn[t][i0]);
+        if (t > s) {
+          e0 *= at[0];
+          e1 *= at[1];
+        }
+        const float f0 = ks[0] * e0, f1 = ks[1] * e1;
+        const float pp = wave_sum(fmaf(qt[1], f1, qt[0] * f0));
+        const float pc = wave_sum(fmaf(kt[1], f1, kt[0] * f0));
+        if (lane == 0) {
+          s_cP[t][s] = pp;
+          s_cA[t][s] = pc;
+        }
+      }
+    }
+    // (2) per projection (w0: gamma kn, then p0: gamma qn): this lane's
+    // partial column sums over its rows, summed over the row groups (and,
+    // with NW > 1, left per wave in LDS for the sum over the waves)
+    constexpr int NP = TMAX * CPL;  // [t][column]
+    float w0[NP];                   // w0 totals (all lanes)
+    float p0[NW == 1 ? NP : 1];     // p0 totals (NW == 1 only; else read from LDS)
+#pragma unroll
+    for (int qty = 0; qty < 2; ++qty) {
+      float wp[NP];
+      float gam[RPL];
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) gam[m] = 1.0f;
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        float* w = &wp[t * CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) w[c] = 0.0f;
+        if (t < n_rows) {
+          float x[RPL], am[RPL];
+          lds_rows<RPL>(qty == 0 ? &s_kn[t][row0] : &s_qn[t][row0], x);
+          lds_rows<RPL>(&s_a[t][row0], am);
+#pragma unroll
+          for (int m = 0; m < RPL; ++m) {
+            gam[m] *= am[m];
+            const float gx = gam[m] * x[m];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) w[c] = fmaf(gx, S[m][c], w[c]);
+          }
+        }
+      }
+      if constexpr (NW == 1) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          if (qty == 0)
+            w0[i] = rowgroup_sum<LPR>(wp[i]);
+          else
+            p0[i] = rowgroup_sum<LPR>(wp[i]);
+        }
+      } else {
+        constexpr int Q = rs_quadrants<LPR>();
+        constexpr int M = NP / Q;
+        float part[M];
+        rowgroup_reduce_scatter<LPR>(wp, part);
+        const int quad = Q == 2 ? (lane >> 5) : ((lane >> 4) & 1) * 2 + (lane >> 5);
+        if (LPR != 8 || (lane & 8) == 0) {
+#pragma unroll
+          for (int j = 0; j < M; j += 4) {
+            const int f = quad * M + j;  // flat [t][column] index, 4 columns at a time
+            *reinterpret_cast<f4*>(&s_wp[wave][qty * TMAX + f / CPL][cg * CPL + f % CPL]) =
+                f4{part[j], part[j + 1], part[j + 2], part[j + 3]};
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // totals over the waves: w0 for every lane; p0 is read by the writers below
+    auto wave_total = [&](int row, float (&tot)[CPL]) {
+      lds_rows<CPL>(&s_wp[0][row][cg * CPL], tot);
+#pragma unroll
+      for (int x = 1; x < NW; ++x) {
+        float xs[CPL];
+        lds_rows<CPL>(&s_wp[x][row][cg * CPL], xs);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) tot[c] += xs[c];
+      }
+    };
+    if constexpr (NW > 1) {
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        if (t >= n_rows) break;
+        float tot[CPL];
+        wave_total(t, tot);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) w0[t * CPL + c] = tot[c];
+      }
+    }
+    // (4) Delta for this lane's columns, row after row
+    float dl[TMAX][CPL];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t >= n_rows) break;
+      const float beta = s_beta[t];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        float d = s_v[t][cg * CPL + c] - w0[t * CPL + c];
+#pragma unroll
+        for (int s2 = 0; s2 < t; ++s2) d = fmaf(-s_cA[t][s2], dl[s2][c], d);
+        dl[t][c] = beta * d;
+      }
+    }
+    // (5) each row's snapshot: S_t = diag(a_t) S_(t-1) + kn_t Delta_t^T
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      if (t >= n_rows) break;
+      float kn[RPL], am[RPL];
+      lds_rows<RPL>(&s_kn[t][row0], kn);
+      lds_rows<RPL>(&s_a[t][row0], am);
+      T* dst = pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off;
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) S[m][c] = fmaf(kn[m], dl[t][c], am[m] * S[m][c]);
+        __builtin_nontemporal_store(L::narrow(S[m]), reinterpret_cast<vec*>(dst + m * kHeadV));
+      }
+    }
+    // (6) outputs
+    if (writer) {
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        if (t >= n_rows) break;
+        const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+        float* op = a.out + (rho * a.H + h) * kHeadV + col0;
+        float pt[CPL];
+        if constexpr (NW == 1) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) pt[c] = p0[t * CPL + c];
+        } else {
+          wave_total(TMAX + t, pt);
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; c += 4) {
+          f4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = pt[c + e];
+#pragma unroll
+            for (int s2 = 0; s2 <= t; ++s2) x = fmaf(s_cP[t][s2], dl[s2][c + e], x);
+            o[e] = a.scale * x;
+          }
+          *reinterpret_cast<f4*>(op + c) = o;
+        }
+      }
+    }
+    return;
+  }
+
   // Rows unrolled: every LDS index and slot id below is static.
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
@@ -540,11 +718,14 @@ __global__ __launch_bounds__(256) void kda_state_copy_kernel(
 template <typename T, int LPR, int NW>
 static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream) {
   if (a.n_rows == 1)
-    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, false>), dim3(blocks), dim3(kWave * NW),
-                       0, stream, a);
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, false, false>), dim3(blocks),
+                       dim3(kWave * NW), 0, stream, a);
+  else if (a.rows_block)
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false, true>), dim3(blocks),
+                       dim3(kWave * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false>), dim3(blocks), dim3(kWave * NW),
-                       0, stream, a);
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false, false>), dim3(blocks),
+                       dim3(kWave * NW), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -553,11 +734,14 @@ static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream)
 template <typename T, int LPR, int NW>
 static hipError_t launch_conv(const Args& a, int32_t blocks, hipStream_t stream) {
   if (a.n_rows == 1)
-    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, true>), dim3(blocks), dim3(kWave * NW),
-                       0, stream, a);
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, true, false>), dim3(blocks),
+                       dim3(kWave * NW), 0, stream, a);
+  else if (a.rows_block)
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, true, true>), dim3(blocks),
+                       dim3(kWave * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, true>), dim3(blocks), dim3(kWave * NW),
-                       0, stream, a);
+    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, true, false>), dim3(blocks),
+                       dim3(kWave * NW), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -641,6 +825,7 @@ extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
   a.H = pool->H;
   a.n_rows = n_rows_per_slot;
   a.n_vt = kHeadV / shape.bv;
+  a.rows_block = opts != nullptr && opts->block_rows != 0 ? 1 : 0;
   a.scale = scale;
   const int32_t blocks = n_req * pool->H * a.n_vt;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -696,6 +881,7 @@ extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* c
   a.H = pool->H;
   a.n_rows = n_rows_per_slot;
   a.n_vt = 1;
+  a.rows_block = opts != nullptr && opts->block_rows != 0 ? 1 : 0;
   a.scale = scale;
   const int32_t blocks = n_req * pool->H;
   hipStream_t s = static_cast<hipStream_t>(stream);

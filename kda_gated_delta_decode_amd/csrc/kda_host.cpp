@@ -134,7 +134,7 @@ int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtyp
   desc->threads = nw * kWave;
   desc->tiles = static_cast<int32_t>(tiles);
   desc->blocks = static_cast<int32_t>(tiles);
-  desc->lds_bytes = lds_bytes(bv, nw, n_rows);
+  desc->lds_bytes = lds_bytes(bv, nw, n_rows, opts != nullptr && opts->block_rows != 0);
   desc->kernel = "kda_decode_tile";
   return KDA_OK;
 }

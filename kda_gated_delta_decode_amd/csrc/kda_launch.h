@@ -77,13 +77,18 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* o
 
 // Bytes of static LDS per workgroup: the staged per-row vectors (normalised
 // q and k and the decay, 128 each; the tile's bv columns of v; beta and
-// qn.kn) for up to KDA_MAX_ROWS rows (1 for single-row launches), plus, with
-// nw > 1, the double-buffered cross-wave sums [2][nw][2][bv].
-inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows) {
+// qn.kn) for up to KDA_MAX_ROWS rows (1 for single-row launches), plus the
+// cross-wave sums: row after row, double-buffered [2][nw][2][bv] (nw > 1);
+// as a block, [nw][2 KDA_MAX_ROWS][bv] (nw > 1) and the two coupling
+// matrices [KDA_MAX_ROWS][KDA_MAX_ROWS].
+inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block) {
   const int32_t tmax = n_rows == 1 ? 1 : KDA_MAX_ROWS;
   const int32_t staged = tmax * (3 * kHeadK + bv + 2);
-  const int32_t red = nw == 1 ? 0 : 2 * nw * 2 * bv;
-  return 4 * (staged + red);
+  const bool block = n_rows > 1 && rows_block;
+  const int32_t red = (nw > 1 && !block ? 2 * nw : 1) * 2 * bv;
+  const int32_t wp = block && nw > 1 ? nw * 2 * tmax * bv : 4;
+  const int32_t coupling = block ? 2 * tmax * tmax : 2;
+  return 4 * (staged + red + wp + coupling);
 }
 
 // Fused-convolution launches take whole heads (bv = 128) so that a head's

@@ -20,7 +20,7 @@ def _gpu():
     need_gpu()
 
 
-def gpu_conv(ci, init=None, waves=0):
+def gpu_conv(ci, init=None, waves=0, block_rows=False):
     d = ci.dec
     dev = torch.device("cuda", 0)
     pool = torch.from_numpy(d.pool if d.dtype == "f32" else d.pool.view(np.float16)).to(dev)
@@ -33,7 +33,8 @@ def gpu_conv(ci, init=None, waves=0):
     out = torch.full((d.slot_ids.size, d.pool.shape[1], 128), float("nan"), device=dev)
     init_d = None if init is None else torch.from_numpy(np.asarray(init, np.int32)).to(dev)
     B.kda_decode_step_conv(pool, conv, ids, x, w, g, b, out, n_rows_per_slot=d.n_rows,
-                           scale=d.scale, init_slot_ids=init_d, waves_per_tile=waves)
+                           scale=d.scale, init_slot_ids=init_d, waves_per_tile=waves,
+                           block_rows=block_rows)
     torch.cuda.synchronize()
     return pool_to_host(pool), conv.view(torch.int16).cpu().numpy().view(np.uint16), out.cpu().numpy()
 
@@ -53,8 +54,8 @@ def oracle_conv(oracle, ci, init=None):
     return pool, conv.reshape(ci.conv.shape), out
 
 
-def check(oracle, ci, init=None, waves=0):
-    gp, gc, go = gpu_conv(ci, init, waves)
+def check(oracle, ci, init=None, waves=0, block_rows=False):
+    gp, gc, go = gpu_conv(ci, init, waves, block_rows)
     op, oc, oo = oracle_conv(oracle, ci, init)
     d = ci.dec
     if d.dtype == "f32":
@@ -81,6 +82,12 @@ def test_fused_conv_parity(oracle, dtype, n_req, n_rows):
 def test_fused_conv_every_wave_count(oracle, waves, n_rows):
     ci = kda_inputs.make_conv_inputs("conv waves", 40, 4, n_rows, "f16", H=3, seed=131 + waves)
     check(oracle, ci, waves=waves)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_fused_conv_rows_as_block(oracle, dtype):
+    ci = kda_inputs.make_conv_inputs("conv block", 64, 6, 7, dtype, H=4, seed=161)
+    check(oracle, ci, block_rows=True)
 
 
 @pytest.mark.parametrize("n_rows", [1, 4])

@@ -206,12 +206,27 @@ def test_fp32_twin_of_fp16_launch(n_rows, lanes, waves):
     np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
 
 
+@pytest.mark.parametrize("lanes,waves", [(8, 1), (8, 4), (16, 8)])
+def test_fp32_twin_of_fp16_launch_rows_as_block(lanes, waves):
+    """The same twin property for the block form of chained rows."""
+    inp16 = kda_inputs.make_inputs("twin block", 96, 8, 8, "f16", seed=24)
+    inp32 = kda_inputs.DecodeInputs("twin32", "f32", inp16.pool.view(np.float16).astype(np.float32),
+                                    inp16.slot_ids, inp16.q, inp16.k, inp16.v, inp16.g, inp16.b,
+                                    8, inp16.scale)
+    p16, o16 = run_gpu(inp16, waves_per_tile=waves, bv=8 * lanes, block_rows=True)
+    p32, o32 = run_gpu(inp32, waves_per_tile=waves, bv=4 * lanes, block_rows=True)
+    np.testing.assert_array_equal(o16.view(np.uint32), o32.view(np.uint32))
+    np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
+
+
 F32_SHAPES = [(32, 1), (32, 2), (32, 4), (32, 8), (64, 1), (64, 2), (64, 4), (64, 8),
               (128, 2), (128, 4), (128, 8)]
 
 
 @pytest.mark.parametrize("bv,waves", F32_SHAPES)
 def test_chained_rows_equal_single_row_launches_fp32(bv, waves):
+    """Rows run one after the other do the single-row launch's arithmetic
+    per row, so n chained single-row launches reproduce them bit for bit."""
     n_req, n = 4, 6
     inp = kda_inputs.make_inputs("chain", 40, n_req, n, "f32", seed=29)
     pm, om = run_gpu(inp, waves_per_tile=waves, bv=bv)
@@ -230,6 +245,19 @@ def test_chained_rows_equal_single_row_launches_fp32(bv, waves):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(pool_to_host(pool).view(np.uint32), pm.view(np.uint32))
     np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), om.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("n_rows", [2, 5, 8])
+@pytest.mark.parametrize("bv,waves", [(64, 1), (64, 4), (64, 8), (128, 2), (128, 8)])
+def test_rows_as_block_and_row_after_row_both_match_the_oracle(oracle, dtype, n_rows, bv, waves):
+    """The block form of a request's rows (one pass of 2 n column sums, an
+    n x n triangular solve, element-wise snapshots) and the row-after-row
+    chain compute the same recurrence: both within the oracle tolerances."""
+    inp = kda_inputs.make_inputs("rows", 40, 40 // 8, n_rows, dtype, H=3, seed=41 + n_rows)
+    for blk in (False, True):
+        gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv, block_rows=blk)
+        check_parity(oracle, inp, gp, go, label="block" if blk else "sequential")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
