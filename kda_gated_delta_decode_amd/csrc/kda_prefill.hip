@@ -64,6 +64,9 @@ constexpr int kLdK = 132;      // row stride (floats) of [C][128] LDS arrays
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kDiagLimit = 115.0f;
 constexpr int32_t kDefaultChunk = 32;
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (gfx950 included):
+// 32-bit data format, no swizzle; out-of-range accesses are dropped.
+constexpr int kBufferWord3 = 0x00020000;
 
 struct PrefillArgs {
   void* pool;
@@ -84,6 +87,22 @@ struct PrefillArgs {
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer stores: a 128-bit descriptor {base, range in bytes, word 3} in
+// scalar registers and a per-lane byte offset; the hardware drops a store
+// whose offset is past the range.
+using i32x4 = int __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_store_f32(float v, i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.f32");
+__device__ __forceinline__ i32x4 buffer_descriptor(const void* base, uint32_t range_bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(p));
+  r[1] = static_cast<int>(static_cast<uint32_t>(p >> 32));  // stride 0: raw buffer
+  r[2] = static_cast<int>(range_bytes);
+  r[3] = kBufferWord3;
+  return r;
+}
 
 __device__ __forceinline__ f4 mma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -188,19 +207,29 @@ void kda_prefill_kernel(PrefillArgs a) {
   // overlap the current chunk's work instead of opening each chunk.
   f4 nq[CPL / 4], nk[CPL / 4], ng[CPL / 4], nv[NB][NCB];
   float nb = 0.0f;
+  // Addresses: a chunk-uniform 64-bit base plus a 32-bit per-lane offset.
+  // Rows past the end of the sequence read row 0 of the chunk instead, so no
+  // load sits behind a branch; they are zeroed where the data is used (a
+  // select right after the load would make the wave wait for it here).
+  const uint32_t hk32 = static_cast<uint32_t>(hk);
   auto prefetch = [&](int64_t c, int li_, int gq_) {
     const int m_ = static_cast<int>(t1 - c < C ? t1 - c : C);
     const int tl_ = 16 * (wave % NB) + li_;
     const int ch_ = (wave / NB) * (128 / PARTS) + gq_ * CPL;
-    const bool ok = tl_ < m_;
-    const int64_t off = (c + tl_) * hk + static_cast<int64_t>(h) * 128 + ch_;
+    const uint32_t row_ = static_cast<uint32_t>(tl_ < m_ ? tl_ : 0);
+    const int64_t base = c * hk + static_cast<int64_t>(h) * 128;
+    const float* qb = a.q + base;
+    const float* kb = a.k + base;
+    const float* gb = a.g + base;
+    const uint32_t off = row_ * hk32 + static_cast<uint32_t>(ch_);
 #pragma unroll
     for (int m = 0; m < CPL / 4; ++m) {
-      nq[m] = ok ? *reinterpret_cast<const f4*>(a.q + off + 4 * m) : f4{0.f, 0.f, 0.f, 0.f};
-      nk[m] = ok ? *reinterpret_cast<const f4*>(a.k + off + 4 * m) : f4{0.f, 0.f, 0.f, 0.f};
-      ng[m] = ok ? *reinterpret_cast<const f4*>(a.g + off + 4 * m) : f4{0.f, 0.f, 0.f, 0.f};
+      nq[m] = *reinterpret_cast<const f4*>(qb + (off + 4 * m));
+      nk[m] = *reinterpret_cast<const f4*>(kb + (off + 4 * m));
+      ng[m] = *reinterpret_cast<const f4*>(gb + (off + 4 * m));
     }
-    nb = ok ? a.b[(c + tl_) * a.H + h] : 0.0f;
+    nb = (a.b + c * a.H + h)[row_ * static_cast<uint32_t>(a.H)];
+    const float* vb = a.v + base + col_w;
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
@@ -208,9 +237,8 @@ void kda_prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tr = 16 * tb + 4 * gq_ + r;
-          nv[tb][cb][r] = tr < m_ ? a.v[(c + tr) * hk + static_cast<int64_t>(h) * 128 + col_w +
-                                        16 * cb + li_]
-                                  : 0.0f;
+          const uint32_t rr = static_cast<uint32_t>(tr < m_ ? tr : 0);
+          nv[tb][cb][r] = vb[rr * hk32 + static_cast<uint32_t>(16 * cb + li_)];
         }
   };
   if (t0 < t1) prefetch(t0, threadIdx.x % 16, (threadIdx.x % 64) / 16);
@@ -235,25 +263,31 @@ void kda_prefill_kernel(PrefillArgs a) {
 
     // ---- per-token rows from the prefetched registers: raw q and k, partial
     // sums of squares, block-local cumulative decays
-    f4 D[NB][NCB];
+    f4 D[NB][NCB];  // v (rows past the sequence zeroed); beta is applied later
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) D[tb][cb] = nv[tb][cb];  // v; beta is applied later
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) D[tb][cb][r] = 16 * tb + 4 * gq + r < n ? nv[tb][cb][r] : 0.0f;
     {
       const bool valid = tl < n;
+      const f4 zero = {0.f, 0.f, 0.f, 0.f};
       float sq = 0.0f, sk = 0.0f;
 #pragma unroll
       for (int m = 0; m < CPL / 4; ++m) {
+        const f4 q4 = valid ? nq[m] : zero;
+        const f4 k4 = valid ? nk[m] : zero;
+        const f4 g4 = valid ? ng[m] : zero;
         f4 gl4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sq = fmaf(nq[m][e], nq[m][e], sq);
-          sk = fmaf(nk[m][e], nk[m][e], sk);
-          gl4[e] = row_scan(ng[m][e] * kLog2e);  // block-local inclusive cumulative sum
+          sq = fmaf(q4[e], q4[e], sq);
+          sk = fmaf(k4[e], k4[e], sk);
+          gl4[e] = row_scan(g4[e] * kLog2e);  // block-local inclusive cumulative sum
         }
-        *reinterpret_cast<f4*>(sZ + row + 4 * m) = nq[m];
-        *reinterpret_cast<f4*>(sX + row + 4 * m) = nk[m];
+        *reinterpret_cast<f4*>(sZ + row + 4 * m) = q4;
+        *reinterpret_cast<f4*>(sX + row + 4 * m) = k4;
         *reinterpret_cast<f4*>(sY + row + 4 * m) = gl4;
         if (li == 15) *reinterpret_cast<f4*>(&sBtot[pb][ch0 + 4 * m]) = gl4;
       }
@@ -265,7 +299,10 @@ void kda_prefill_kernel(PrefillArgs a) {
         if (pp == 0) sBeta[tl] = valid ? 1.0f / (1.0f + expf(-nb)) : 0.0f;
       }
     }
-    if (c0 + C < t1) prefetch(c0 + C, li, gq);
+    // unconditional (the last chunk reloads its own rows): a conditional
+    // prefetch would merge old and new registers with copies that wait for
+    // the previous chunk's stores
+    prefetch(c0 + C < t1 ? c0 + C : c0, li, gq);
     __syncthreads();
 
     // ---- block prefix sums of the decay and 2^(G_C) (wave 0), then A and P
@@ -321,10 +358,12 @@ void kda_prefill_kernel(PrefillArgs a) {
       }
       if (!exact) {
         f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+#pragma unroll
         for (int m = 0; m < 32; m += 4) {
           f4 cum = {0.f, 0.f, 0.f, 0.f};
-          for (int u = bs; u < bt; ++u) cum += *reinterpret_cast<const f4*>(&sBtot[u][32 * gq + m]);
+#pragma unroll
+          for (int u = 0; u < NB - 1; ++u)
+            if (u >= bs && u < bt) cum += *reinterpret_cast<const f4*>(&sBtot[u][32 * gq + m]);
           const f4 xt = *reinterpret_cast<const f4*>(tsrc + trow + m);
           const f4 gt = *reinterpret_cast<const f4*>(sY + trow + m);
           const f4 ks = *reinterpret_cast<const f4*>(sX + srow + m);
@@ -508,16 +547,23 @@ void kda_prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) O[tb][cb] = mma(x[tb][r], D[kb][cb][r], O[tb][cb]);
       }
+      // Buffer stores: the descriptor's range ends after the chunk's last
+      // token, so the hardware drops the rows past the sequence without a
+      // branch (a branch around the stores would make the next chunk's first
+      // use of the prefetched rows wait for every store to be acknowledged).
+      const i32x4 orsrc =
+          buffer_descriptor(a.out + (c0 * hk + static_cast<int64_t>(h) * 128 + col_w),
+                            (static_cast<uint32_t>(n - 1) * hk32 + CPW) * 4);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int tr = 16 * tb + 4 * gq + r;
-          if (tr < n) {
-            float* op = a.out + (c0 + tr) * hk + static_cast<int64_t>(h) * 128 + col_w + li;
+          const uint32_t tr = static_cast<uint32_t>(16 * tb + 4 * gq + r);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) op[16 * cb] = a.scale * O[tb][cb][r];
-          }
+          for (int cb = 0; cb < NCB; ++cb)
+            raw_buffer_store_f32(
+                a.scale * O[tb][cb][r], orsrc,
+                static_cast<int>((tr * hk32 + static_cast<uint32_t>(16 * cb + li)) * 4), 0, 0);
         }
     }
     // S = 2^(G_C) S + Kd^T Delta
@@ -588,6 +634,7 @@ extern "C" int kda_prefill(const kda_pool* pool, const int32_t* init_slot_ids,
   if (rc != KDA_OK) return rc;
   if (n_tokens < 0) return KDA_ERR_ARG;
   if (static_cast<int64_t>(n_seq) * pool->H > INT32_MAX) return KDA_ERR_ARG;
+  if (pool->H > 16384) return KDA_ERR_SHAPE;  // byte offsets within a chunk stay below 2^31
   const int32_t chunk = opts != nullptr && opts->chunk != 0 ? opts->chunk : kDefaultChunk;
   if (chunk != 32 && chunk != 64) return KDA_ERR_ARG;
   if (n_seq == 0) return KDA_OK;
