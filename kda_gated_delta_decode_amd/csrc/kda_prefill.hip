@@ -33,17 +33,17 @@
 // pair instead.  All exponents are formed from block-local sums, so the ones
 // that matter (close tokens) are small and accurate.
 //
-// Work decomposition.  One workgroup = one (sequence, head) with 8
-// wavefronts.  For everything that touches the state they split the 128
-// value columns (16 each); for the per-chunk quantities (norms, decays,
-// the operands) they split token blocks and channel parts, and the products
-// A and P (one chain per block pair and matrix) go round-robin to them; all
-// of it is shared through LDS.  The state slice of a wave stays in
-// registers, in the matrix cores' accumulator layout, for the whole prompt;
-// that layout is also a valid B operand for the next contraction over the
-// key channels (the k-order of a 16x16x4 step is permuted to match, and the
-// A operand is read from LDS in the same order).  The next chunk's rows are
-// loaded while the current chunk is processed.
+// Work decomposition.  One workgroup = one (sequence, head).  The default
+// 32-token chunks use the warp-specialised kernel (kda_prefill_ws_kernel):
+// 8 state waves keep 16 value columns of the state each, in registers, in
+// the matrix cores' accumulator layout, for the whole prompt, and run the
+// contractions of one chunk while 8 preparation waves build the next chunk
+// (rows, decays, A, P, operands, diagonal inverses) in the other half of a
+// double-buffered LDS.  The accumulator layout is also a valid B operand for
+// the next contraction over the key channels (the k-order of a 16x16x4 step
+// is permuted to match, and the A operand is read from LDS in the same
+// order).  64-token chunks use kda_prefill_kernel, where the same 8 waves do
+// both in turn (two buffers of 64 tokens would not fit in LDS).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -609,6 +609,461 @@ void kda_prefill_kernel(PrefillArgs a) {
         narrow1(dstp + (16 * sb + 4 * gq + r) * 128 + col_w + 16 * cb + li, S[sb][cb][r]);
 }
 
+// ---------------------------------------------------------------------------
+// Warp-specialised form for 32-token chunks (the default).  Eight state
+// waves keep the state (16 value columns each) and run the contractions of
+// chunk i - 1 while four preparation waves build chunk i (rows, decays, A,
+// P, operands, diagonal inverses) in the other half of a double-buffered LDS.
+// The two groups meet at three barriers per chunk; between two barriers the
+// state waves issue matrix-core work while the preparation waves issue
+// vector, transcendental and LDS work, so the two overlap on every SIMD.
+// ---------------------------------------------------------------------------
+constexpr int kWsNB = 2;                // token blocks per chunk
+constexpr int kWsC = 16 * kWsNB;        // tokens per chunk
+constexpr int kWsState = 8;             // state waves (16 value columns each)
+constexpr int kWsPrep = 8;              // preparation waves
+constexpr int kWsParts = kWsPrep / kWsNB;  // channel parts of the per-token phases
+constexpr int kWsCpl = 32 / kWsParts;   // channels per lane in those phases
+constexpr int kWsLdC = kWsC + 4;
+
+struct __attribute__((aligned(16))) WsBuf {
+  float X[kWsC * kLdK];   // raw k, then -Kb
+  float Y[kWsC * kLdK];   // block-local cumulative log2 decay, then Qg
+  float Z[kWsC * kLdK];   // raw q, then Kd
+  float A[kWsC * kWsLdC];  // -A (strictly lower)
+  float P[kWsC * kWsLdC];  // P (lower)
+  float Td[kWsNB][16 * 20];  // (I + A_bb)^-1
+  float Btot[kWsNB][128];
+  float Pre[kWsNB + 1][128];
+  float GC[128];
+  float Beta[kWsC];
+  float Sq[kWsParts][kWsC];
+  float Sk[kWsParts][kWsC];
+};
+
+template <typename T>
+__global__ __launch_bounds__(64 * (kWsState + kWsPrep)) __attribute__((amdgpu_waves_per_eu((kWsState + kWsPrep) / 4)))
+void kda_prefill_ws_kernel(PrefillArgs a) {
+  constexpr int NB = kWsNB;
+  constexpr int C = kWsC;
+  constexpr int LdC = kWsLdC;
+  constexpr int PARTS = kWsParts;
+  constexpr int CPL = kWsCpl;
+  constexpr int NPAIR = NB * (NB + 1) / 2;
+  __shared__ WsBuf sb[2];
+
+  const int wave = threadIdx.x / 64;
+  const bool state_wave = wave < kWsState;
+  const int pw = wave - kWsState;  // preparation wave index (prep waves only)
+  const int seq = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+
+  const int64_t t0 = a.cu[seq];
+  const int64_t t1 = a.cu[seq + 1];
+  const int32_t init = a.init_ids[seq];
+  const int32_t dst = a.dst_ids != nullptr ? a.dst_ids[seq] : init;
+  if (!(t0 >= 0 && t0 <= t1 && t1 <= a.n_tokens && init >= 0 && init < a.n_slots && dst >= 0 &&
+        dst < a.n_slots))
+    return;  // refused by the host checks; never touch memory outside the launch's bounds
+
+  const int64_t hk = static_cast<int64_t>(a.H) * 128;
+  const uint32_t hk32 = static_cast<uint32_t>(hk);
+  const int64_t head_off = static_cast<int64_t>(h) * 128 * 128;
+  const int col_w = 16 * (state_wave ? wave : 0);  // a state wave's value columns
+  const int n_chunks = static_cast<int>((t1 - t0 + C - 1) / C);
+
+  // The registers carried from chunk to chunk, shared by the two roles (a
+  // wave only ever plays one): state waves keep the state slice (rows
+  // 16 sb + 4 gq + r of their 16 columns, accumulator layout) in reg[0..7],
+  // the next chunk's v in reg[8..9] and R / Delta in reg[10..11];
+  // preparation waves keep the next chunk's q, k, g in reg[0..3], reg[4..7],
+  // reg[8..11].
+  constexpr int kS = 0, kV = 8, kD = 10, kQ = 0, kK = CPL / 4, kG = 2 * (CPL / 4);
+  static_assert(3 * (CPL / 4) <= 12, "q, k, g of a preparation lane fit the shared registers");
+  f4 reg[12];
+  if (state_wave) {
+    const int li = threadIdx.x % 16, gq = (threadIdx.x % 64) / 16;
+    const T* src = static_cast<const T*>(a.pool) + static_cast<int64_t>(init) * a.H * 128 * 128 +
+                   head_off;
+#pragma unroll
+    for (int sb2 = 0; sb2 < 8; ++sb2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        reg[kS + sb2][r] = widen1(src + (16 * sb2 + 4 * gq + r) * 128 + col_w + li);
+  }
+
+  // prefetched rows: preparation waves hold q, k, g, b of their token and
+  // channels for the next chunk to prepare; state waves hold v of their
+  // columns for the next chunk to contract.  Rows past the sequence read
+  // row 0 of the chunk and are zeroed where used.
+  float nb = 0.0f;
+  auto prefetch_rows = [&](int64_t c, int li_, int gq_) {
+    const int m_ = static_cast<int>(t1 - c < C ? t1 - c : C);
+    const int tl_ = 16 * (pw % NB) + li_;
+    const int ch_ = (pw / NB) * (128 / PARTS) + gq_ * CPL;
+    const uint32_t row_ = static_cast<uint32_t>(tl_ < m_ ? tl_ : 0);
+    const int64_t base = c * hk + static_cast<int64_t>(h) * 128;
+    const uint32_t off = row_ * hk32 + static_cast<uint32_t>(ch_);
+#pragma unroll
+    for (int m = 0; m < CPL / 4; ++m) {
+      reg[kQ + m] = *reinterpret_cast<const f4*>(a.q + base + (off + 4 * m));
+      reg[kK + m] = *reinterpret_cast<const f4*>(a.k + base + (off + 4 * m));
+      reg[kG + m] = *reinterpret_cast<const f4*>(a.g + base + (off + 4 * m));
+    }
+    nb = (a.b + c * a.H + h)[row_ * static_cast<uint32_t>(a.H)];
+  };
+  auto prefetch_v = [&](int64_t c, int li_, int gq_) {
+    const int m_ = static_cast<int>(t1 - c < C ? t1 - c : C);
+    const float* vb = a.v + c * hk + static_cast<int64_t>(h) * 128 + col_w;
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 16 * tb + 4 * gq_ + r;
+        const uint32_t rr = static_cast<uint32_t>(tr < m_ ? tr : 0);
+        reg[kV + tb][r] = vb[rr * hk32 + static_cast<uint32_t>(li_)];
+      }
+  };
+  if (t0 < t1) {
+    if (state_wave)
+      prefetch_v(t0, threadIdx.x % 16, (threadIdx.x % 64) / 16);
+    else
+      prefetch_rows(t0, threadIdx.x % 16, (threadIdx.x % 64) / 16);
+  }
+
+  for (int it = 0; it <= n_chunks; ++it) {
+    int tid_v = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid_v));  // see the note in kda_prefill_kernel
+    const int li = tid_v % 16;
+    const int gq = (tid_v % 64) / 16;
+    const bool prep_now = !state_wave && it < n_chunks;   // prepares chunk it
+    const bool state_now = state_wave && it >= 1;          // contracts chunk it - 1
+    const int64_t cp = t0 + static_cast<int64_t>(it) * C;        // chunk being prepared
+    const int64_t cs = t0 + static_cast<int64_t>(it - 1) * C;    // chunk being contracted
+    const int np = prep_now ? static_cast<int>(t1 - cp < C ? t1 - cp : C) : 0;
+    const int ns = state_now ? static_cast<int>(t1 - cs < C ? t1 - cs : C) : 0;
+    WsBuf& bp = sb[it & 1];
+    WsBuf& bs = sb[(it + 1) & 1];
+
+    // ================= segment 1 =================
+    if (prep_now) {
+      // per-token rows of chunk it: raw q and k, partial sums of squares, decays
+      const int pb = pw % NB, pp = pw / NB;
+      const int tl = 16 * pb + li;
+      const int ch0 = pp * (128 / PARTS) + gq * CPL;
+      const int row = tl * kLdK + ch0;
+      const bool valid = tl < np;
+      const f4 zero = {0.f, 0.f, 0.f, 0.f};
+      float sq = 0.0f, sk = 0.0f;
+#pragma unroll
+      for (int m = 0; m < CPL / 4; ++m) {
+        const f4 q4 = valid ? reg[kQ + m] : zero;
+        const f4 k4 = valid ? reg[kK + m] : zero;
+        const f4 g4 = valid ? reg[kG + m] : zero;
+        f4 gl4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sq = fmaf(q4[e], q4[e], sq);
+          sk = fmaf(k4[e], k4[e], sk);
+          gl4[e] = row_scan(g4[e] * kLog2e);
+        }
+        *reinterpret_cast<f4*>(bp.Z + row + 4 * m) = q4;
+        *reinterpret_cast<f4*>(bp.X + row + 4 * m) = k4;
+        *reinterpret_cast<f4*>(bp.Y + row + 4 * m) = gl4;
+        if (li == 15) *reinterpret_cast<f4*>(&bp.Btot[pb][ch0 + 4 * m]) = gl4;
+      }
+      sq = group_sum(sq);
+      sk = group_sum(sk);
+      if (gq == 0) {
+        bp.Sq[pp][tl] = sq;
+        bp.Sk[pp][tl] = sk;
+        if (pp == 0) bp.Beta[tl] = valid ? 1.0f / (1.0f + expf(-nb)) : 0.0f;
+      }
+      prefetch_rows(cp + C < t1 ? cp + C : cp, li, gq);
+    }
+    if (state_now) {
+      // R = beta V - Kb S for chunk it - 1
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = 16 * tb + 4 * gq + r;
+          reg[kD + tb][r] = tr < ns ? bs.Beta[tr] * reg[kV + tb][r] : 0.0f;
+        }
+      prefetch_v(cs + C < t1 ? cs + C : cs, li, gq);
+#pragma unroll
+      for (int sb2 = 0; sb2 < 8; ++sb2) {
+        f4 x[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+          x[tb] = *reinterpret_cast<const f4*>(bs.X + (16 * tb + li) * kLdK + 16 * sb2 + 4 * gq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int tb = 0; tb < NB; ++tb) reg[kD + tb] = mma(x[tb][r], reg[kS + sb2][r], reg[kD + tb]);
+      }
+    }
+    __syncthreads();
+
+    // ================= segment 2 =================
+    if (prep_now) {
+      if (pw == 0) {
+        const int lane = tid_v % 64;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ch = 2 * lane + e;
+          float acc = 0.0f;
+          bp.Pre[0][ch] = 0.0f;
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            acc += bp.Btot[u][ch];
+            bp.Pre[u + 1][ch] = acc;
+          }
+          bp.GC[ch] = exp2_fast(acc);
+        }
+      }
+      // chains (block pair, P or A) round-robin over the preparation waves
+      for (int ci = pw; ci < 2 * NPAIR; ci += kWsPrep) {
+        const int pi = ci / 2;
+        const bool is_a = (ci & 1) != 0;
+        int bt = 0;
+        while ((bt + 1) * (bt + 2) / 2 <= pi) ++bt;
+        const int bsb = pi - bt * (bt + 1) / 2;
+        const int trow = (16 * bt + li) * kLdK + 32 * gq;
+        const int srow = (16 * bsb + li) * kLdK + 32 * gq;
+        float st = 0.0f, ss = 0.0f;
+#pragma unroll
+        for (int u = 0; u < PARTS; ++u) {
+          st += is_a ? bp.Sk[u][16 * bt + li] : bp.Sq[u][16 * bt + li];
+          ss += bp.Sk[u][16 * bsb + li];
+        }
+        const float beta = bp.Beta[16 * bt + li];
+        const float r_t = (is_a ? beta : 1.0f) / sqrtf(st + 1e-6f);
+        const float rk_s = 1.0f / sqrtf(ss + 1e-6f);
+        const float* tsrc = is_a ? bp.X : bp.Z;
+        bool exact = false;
+        if (bt == bsb) {
+          float span = 0.0f;
+#pragma unroll
+          for (int m = 0; m < 32; m += 4) {
+            const f4 gl4 = *reinterpret_cast<const f4*>(bp.Y + trow + m);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) span = fmaxf(span, -gl4[e]);
+          }
+          exact = __builtin_amdgcn_ballot_w64(span > kDiagLimit) != 0;
+        }
+        if (!exact) {
+          f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+          for (int m = 0; m < 32; m += 4) {
+            f4 cum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < NB - 1; ++u)
+              if (u >= bsb && u < bt) cum += *reinterpret_cast<const f4*>(&bp.Btot[u][32 * gq + m]);
+            const f4 xt = *reinterpret_cast<const f4*>(tsrc + trow + m);
+            const f4 gt = *reinterpret_cast<const f4*>(bp.Y + trow + m);
+            const f4 ks = *reinterpret_cast<const f4*>(bp.X + srow + m);
+            const f4 gs = *reinterpret_cast<const f4*>(bp.Y + srow + m);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float lf = (xt[e] * r_t) * exp2_fast(gt[e]);
+              const float rf = (ks[e] * rk_s) * exp2_fast(cum[e] - gs[e]);
+              if (e % 2 == 0)
+                acc0 = mma(lf, rf, acc0);
+              else
+                acc1 = mma(lf, rf, acc1);
+            }
+          }
+          float* dstm = is_a ? bp.A : bp.P;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tr = 4 * gq + r;
+            float x = acc0[r] + acc1[r];
+            if (bsb == bt && (is_a ? li >= tr : li > tr)) x = 0.0f;
+            dstm[(16 * bt + tr) * LdC + 16 * bsb + li] = is_a ? -x : x;
+          }
+        } else {
+          for (int s2 = 0; s2 < 16; ++s2) {
+            const int s2row = (16 * bt + s2) * kLdK + 32 * gq;
+            float sk2 = 0.0f;
+#pragma unroll
+            for (int u = 0; u < PARTS; ++u) sk2 += bp.Sk[u][16 * bt + s2];
+            const float rk_s2 = 1.0f / sqrtf(sk2 + 1e-6f);
+            float acc = 0.0f;
+            if (s2 <= li) {
+              for (int i = 0; i < 32; ++i) {
+                const float f =
+                    (bp.X[s2row + i] * rk_s2) * exp2_fast(bp.Y[trow + i] - bp.Y[s2row + i]);
+                acc = fmaf(tsrc[trow + i] * r_t, f, acc);
+              }
+            }
+            acc = group_sum(acc);
+            if (gq == 0) {
+              if (is_a)
+                bp.A[(16 * bt + li) * LdC + 16 * bt + s2] = s2 < li ? -acc : 0.0f;
+              else
+                bp.P[(16 * bt + li) * LdC + 16 * bt + s2] = s2 <= li ? acc : 0.0f;
+            }
+          }
+        }
+      }
+    }
+    if (state_now) {
+      // Delta = (I + A)^-1 R by blocks, then o = scale (Qg S + P Delta)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int k = 0; k < b; ++k) {
+          const f4 x = *reinterpret_cast<const f4*>(bs.A + (16 * b + li) * LdC + 16 * k + 4 * gq);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) reg[kD + b] = mma(x[r], reg[kD + k][r], reg[kD + b]);
+        }
+        const f4 x = *reinterpret_cast<const f4*>(&bs.Td[b][li * 20 + 4 * gq]);
+        f4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y = mma(x[r], reg[kD + b][r], y);
+        reg[kD + b] = y;
+      }
+      f4 O[NB];
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) O[tb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sb2 = 0; sb2 < 8; ++sb2) {
+        f4 x[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+          x[tb] = *reinterpret_cast<const f4*>(bs.Y + (16 * tb + li) * kLdK + 16 * sb2 + 4 * gq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int tb = 0; tb < NB; ++tb) O[tb] = mma(x[tb][r], reg[kS + sb2][r], O[tb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        f4 x[NB];
+#pragma unroll
+        for (int tb = kb; tb < NB; ++tb)
+          x[tb] = *reinterpret_cast<const f4*>(bs.P + (16 * tb + li) * LdC + 16 * kb + 4 * gq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int tb = kb; tb < NB; ++tb) O[tb] = mma(x[tb][r], reg[kD + kb][r], O[tb]);
+      }
+      const i32x4 orsrc =
+          buffer_descriptor(a.out + (cs * hk + static_cast<int64_t>(h) * 128 + col_w),
+                            (static_cast<uint32_t>(ns - 1) * hk32 + 16) * 4);
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t tr = static_cast<uint32_t>(16 * tb + 4 * gq + r);
+          raw_buffer_store_f32(a.scale * O[tb][r], orsrc,
+                               static_cast<int>((tr * hk32 + static_cast<uint32_t>(li)) * 4), 0, 0);
+        }
+    }
+    __syncthreads();
+
+    // ================= segment 3 =================
+    if (prep_now) {
+      // operands -Kb, Qg, Kd of chunk it in place of its rows; diagonal inverses
+      const int pb = pw % NB, pp = pw / NB;
+      const int tl = 16 * pb + li;
+      const int ch0 = pp * (128 / PARTS) + gq * CPL;
+      const int row = tl * kLdK + ch0;
+      float ssq = 0.0f, ssk = 0.0f;
+#pragma unroll
+      for (int u = 0; u < PARTS; ++u) {
+        ssq += bp.Sq[u][tl];
+        ssk += bp.Sk[u][tl];
+      }
+      const float rq = 1.0f / sqrtf(ssq + 1e-6f);
+      const float rk = 1.0f / sqrtf(ssk + 1e-6f);
+      const float beta = bp.Beta[tl];
+#pragma unroll
+      for (int m = 0; m < CPL; m += 4) {
+        const int ch = ch0 + m;
+        const f4 k4 = *reinterpret_cast<const f4*>(bp.X + row + m);
+        const f4 gl4 = *reinterpret_cast<const f4*>(bp.Y + row + m);
+        const f4 q4 = *reinterpret_cast<const f4*>(bp.Z + row + m);
+        const f4 pre = *reinterpret_cast<const f4*>(&bp.Pre[pb][ch]);
+        const f4 post = *reinterpret_cast<const f4*>(&bp.Pre[NB][ch]) -
+                        *reinterpret_cast<const f4*>(&bp.Pre[pb + 1][ch]);
+        const f4 btot = *reinterpret_cast<const f4*>(&bp.Btot[pb][ch]);
+        f4 nkb, qg, kd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float kn = k4[e] * rk;
+          const float eg = exp2_fast(pre[e] + gl4[e]);
+          nkb[e] = -((beta * kn) * eg);
+          qg[e] = (q4[e] * rq) * eg;
+          kd[e] = kn * exp2_fast(post[e] + (btot[e] - gl4[e]));
+        }
+        *reinterpret_cast<f4*>(bp.X + row + m) = nkb;
+        *reinterpret_cast<f4*>(bp.Y + row + m) = qg;
+        *reinterpret_cast<f4*>(bp.Z + row + m) = kd;
+      }
+      if (pw < NB && gq == 0) {
+        const int b = pw;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          float acc = t == li ? 1.0f : 0.0f;
+#pragma unroll
+          for (int s2 = 0; s2 < t; ++s2)
+            acc = fmaf(bp.A[(16 * b + t) * LdC + 16 * b + s2], x[s2], acc);
+          x[t] = acc;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) bp.Td[b][t * 20 + li] = x[t];
+      }
+    }
+    if (state_now) {
+      // S = 2^(G_C) S + Kd^T Delta
+#pragma unroll
+      for (int sb2 = 0; sb2 < 8; ++sb2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) reg[kS + sb2][r] *= bs.GC[16 * sb2 + 4 * gq + r];
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+        for (int hb = 0; hb < 8; hb += 4) {  // four state row blocks at a time
+          f4 x[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x[j][r] = bs.Z[(16 * tb + 4 * gq + r) * kLdK + 16 * (hb + j) + li];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              reg[kS + hb + j] = mma(x[j][r], reg[kD + tb][r], reg[kS + hb + j]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // -- final state (state waves) to the destination slot
+  if (state_wave) {
+    int64_t dst_off = static_cast<int64_t>(dst) * a.H * 128 * 128 + head_off;
+    asm volatile("" : "+s"(dst_off));
+    T* dstp = static_cast<T*>(a.pool) + dst_off;
+    const int li = threadIdx.x % 16, gq = (threadIdx.x % 64) / 16;
+#pragma unroll
+    for (int sb2 = 0; sb2 < 8; ++sb2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        narrow1(dstp + (16 * sb2 + 4 * gq + r) * 128 + col_w + li, reg[kS + sb2][r]);
+  }
+}
+
+template <typename T>
+hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((kda_prefill_ws_kernel<T>), dim3(static_cast<uint32_t>(a.n_seq) * a.H),
+                     dim3(64 * (kWsState + kWsPrep)), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int NB, int NW>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((kda_prefill_kernel<T, NB, NW>), dim3(static_cast<uint32_t>(a.n_seq) * a.H),
@@ -665,8 +1120,8 @@ extern "C" int kda_prefill(const kda_pool* pool, const int32_t* init_slot_ids,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (state_dtype == KDA_F32)
-    err = chunk == 64 ? launch_prefill<float, 4, 8>(a, s) : launch_prefill<float, 2, 8>(a, s);
+    err = chunk == 64 ? launch_prefill<float, 4, 8>(a, s) : launch_prefill_ws<float>(a, s);
   else
-    err = chunk == 64 ? launch_prefill<_Float16, 4, 8>(a, s) : launch_prefill<_Float16, 2, 8>(a, s);
+    err = chunk == 64 ? launch_prefill<_Float16, 4, 8>(a, s) : launch_prefill_ws<_Float16>(a, s);
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
