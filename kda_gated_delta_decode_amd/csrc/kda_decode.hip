@@ -401,27 +401,48 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
     // All 2 n column sums over K are taken in one pass over S0 and reduced
     // together; the per-row work is then element-wise (no reduction, no
     // barrier between rows).
-    // (1) C and P: wave w takes s = w, w + NW, ...; a lane two key channels
-    for (int s = wave; s < n_rows; s += NW) {
+    // (1) C and P (wave 0): each lane forms the 64 partial sums (36 P_ts,
+    // s <= t, then 28 C_ts, s < t) over its two key channels, and one
+    // reduce-scatter over the wave leaves each total in one lane
+    static_assert(TMAX == 8, "64 coupling values: 36 of P and 28 of C");
+    if (wave == 0) {
       const int i0 = 2 * lane;
-      const f2 ks = *reinterpret_cast<const f2*>(&s_kn[s][i0]);
-      float e0 = 1.0f, e1 = 1.0f;
-      for (int t = s; t < n_rows; ++t) {
-        const f2 at = *reinterpret_cast<const f2*>(&s_a[t][i0]);
-        const f2 qt = *reinterpret_cast<const f2*>(&s_qn[t][i0]);
-        const f2 kt = *reinterpret_cast<const f2*>(&s_kn[t][i0]);
-        if (t > s) {
-          e0 *= at[0];
-          e1 *= at[1];
-        }
-        const float f0 = ks[0] * e0, f1 = ks[1] * e1;
-        const float pp = wave_sum(fmaf(qt[1], f1, qt[0] * f0));
-        const float pc = wave_sum(fmaf(kt[1], f1, kt[0] * f0));
-        if (lane == 0) {
-          s_cP[t][s] = pp;
-          s_cA[t][s] = pc;
+      float cv[64];
+#pragma unroll
+      for (int f = 0; f < 64; ++f) cv[f] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < TMAX; ++s) {
+        if (s >= n_rows) break;
+        const f2 ks = *reinterpret_cast<const f2*>(&s_kn[s][i0]);
+        float e0 = 1.0f, e1 = 1.0f;
+#pragma unroll
+        for (int t = s; t < TMAX; ++t) {
+          if (t >= n_rows) break;
+          const f2 qt = *reinterpret_cast<const f2*>(&s_qn[t][i0]);
+          if (t > s) {
+            const f2 at = *reinterpret_cast<const f2*>(&s_a[t][i0]);
+            e0 *= at[0];
+            e1 *= at[1];
+          }
+          const float f0 = ks[0] * e0, f1 = ks[1] * e1;
+          cv[t * (t + 1) / 2 + s] = fmaf(qt[1], f1, qt[0] * f0);
+          if (t > s) {
+            const f2 kt = *reinterpret_cast<const f2*>(&s_kn[t][i0]);
+            cv[36 + t * (t - 1) / 2 + s] = fmaf(kt[1], f1, kt[0] * f0);
+          }
         }
       }
+      const float tot = wave_reduce_scatter64(cv, lane);
+      const int f = bitrev6(lane);
+      const bool is_p = f < 36;
+      const int c = is_p ? f : f - 36;
+      int t = is_p ? 0 : 1;
+      while ((is_p ? (t + 1) * (t + 2) / 2 : (t + 1) * t / 2) <= c) ++t;
+      const int s = c - (is_p ? t * (t + 1) / 2 : t * (t - 1) / 2);
+      if (is_p)
+        s_cP[t][s] = tot;
+      else
+        s_cA[t][s] = tot;
     }
     // (2) per projection (w0: gamma kn, then p0: gamma qn): this lane's
     // partial column sums over its rows, summed over the row groups (and,

@@ -111,4 +111,49 @@ __device__ __forceinline__ void rowgroup_reduce_scatter(const float (&orig)[N],
   }
 }
 
+// Reduce-scatter of 64 values over the 64 lanes of a wave: every lane
+// passes v[0..63]; lane l returns the sum over all lanes of v[bitrev6(l)]
+// (bitrev6 reverses the 6 lane-id bits).  Two permlane swaps of register
+// pairs halve the values per lane at lane bits 5 and 4; DPP exchanges with
+// a select do the same at bits 3..0.  63 exchange-adds in all, against 384
+// for 64 separate full-wave sums.
+__device__ __forceinline__ float wave_reduce_scatter64(const float (&v)[64], int lane) {
+  float y[32], z[16], w[8], u[4], p[2];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * i]),
+                                                    __float_as_uint(v[2 * i + 1]), false, false);
+    y[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[2 * i]),
+                                                    __float_as_uint(y[2 * i + 1]), false, false);
+    z[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0, b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float keep = b3 ? z[2 * i + 1] : z[2 * i], send = b3 ? z[2 * i] : z[2 * i + 1];
+    w[i] = keep + dpp<kDppRowRor8>(send);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = b2 ? w[2 * i + 1] : w[2 * i], send = b2 ? w[2 * i] : w[2 * i + 1];
+    u[i] = keep + dpp<kDppQuadXor3>(dpp<kDppRowHalfMirror>(send));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = b1 ? u[2 * i + 1] : u[2 * i], send = b1 ? u[2 * i] : u[2 * i + 1];
+    p[i] = keep + dpp<kDppQuadXor2>(send);
+  }
+  const float keep = b0 ? p[1] : p[0], send = b0 ? p[0] : p[1];
+  return keep + dpp<kDppQuadXor1>(send);
+}
+
+__device__ __forceinline__ int bitrev6(int l) {
+  return ((l & 1) << 5) | ((l & 2) << 3) | ((l & 4) << 1) | ((l & 8) >> 1) | ((l & 16) >> 3) |
+         ((l & 32) >> 5);
+}
+
 }  // namespace kda
