@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -128,11 +128,30 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
                     float scale, void* stream);
 
 /*
+ * Chained-row layouts (kda_launch_opts.rows_layout; chained rows only).
+ *  KDA_ROWS_K_SPLIT  each wave of a workgroup holds a slice of the 128 key
+ *                    rows for all of the tile's bv columns; every row's
+ *                    partial column sums over K meet in LDS behind a barrier.
+ *  KDA_ROWS_WAVE_K   each wave holds all 128 key rows of bv / waves_per_tile
+ *                    columns (2 or 4 lanes per 16-byte row piece): a
+ *                    row's column sums over K stay inside the wave (DPP and
+ *                    permlane exchanges), and the waves of a workgroup run
+ *                    their chains with no barrier between rows.
+ */
+#define KDA_ROWS_DEFAULT 0
+#define KDA_ROWS_K_SPLIT 1
+#define KDA_ROWS_WAVE_K 2
+
+/*
  * Launch options of kda_decode_step_ex.  Zero-initialise for the library's
  * defaults; each non-zero field overrides one choice.
- *  waves_per_tile  wavefronts that split one tile's 128 key rows: 1, 2, 4, 8.
- *  bv              value columns per tile: 32, 64 or 128 for fp32 pools
- *                  (8, 16, 32 lanes per tile row), 64 or 128 for fp16.
+ *  waves_per_tile  wavefronts per workgroup: 1, 2, 4, 8.  K-split layout and
+ *                  single rows: the waves split one tile's 128 key rows.
+ *  bv              value columns per workgroup.  K-split layout and single
+ *                  rows: 32, 64 or 128 for fp32 pools (8, 16, 32 lanes per
+ *                  tile row), 64 or 128 for fp16.  Whole-K layout: waves x
+ *                  lanes x columns per lane (4 fp32, 8 fp16) with 2 or 4
+ *                  lanes and 2, 4 or 8 waves, at most 128.
  *  block_rows      chained rows only: 0 (default) runs a request's rows
  *                  one after the other (two column sums over K and a
  *                  cross-lane reduction per row); non-zero takes them as one
@@ -141,16 +160,22 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
  *                  snapshots).  Both compute the same chain and round
  *                  differently; on MI355X the block form measured slower at
  *                  8 rows (its n x n coupling sums cost more than the
- *                  per-row reductions they replace).
- * Supported combinations keep 2..32 key rows per lane (rows per lane =
- * 2 * lanes per row / waves).  The shape changes the order of the fp32
- * column sums over K (so results may differ in the last bits), never the
- * operation; fixing it fixes every result bit for given inputs.
+ *                  per-row reductions they replace).  The block form uses
+ *                  the K-split layout (with KDA_ROWS_WAVE_K it is refused).
+ *  rows_layout     chained rows only: KDA_ROWS_DEFAULT (whole-K for fp16
+ *                  pools, bv 64 over 4 waves; K split for fp32, bv 64 over 8
+ *                  waves), KDA_ROWS_K_SPLIT or KDA_ROWS_WAVE_K; ignored for
+ *                  one row.
+ * Supported K-split combinations keep 2..32 key rows per lane (rows per
+ * lane = 2 * lanes per row / waves).  The shape changes the order of the
+ * fp32 column sums over K (so results may differ in the last bits), never
+ * the operation; fixing it fixes every result bit for given inputs.
  */
 typedef struct kda_launch_opts {
   int32_t waves_per_tile;
   int32_t bv;
   int32_t block_rows;
+  int32_t rows_layout;
 } kda_launch_opts;
 
 /*
@@ -346,13 +371,14 @@ int kda_prefill_validate(const kda_pool* pool, const int32_t* init_slot_ids_host
 
 /* Launch shape kda_decode_step uses for a given problem (host only). */
 typedef struct kda_launch_desc {
-  int32_t bv;              /* value columns per tile */
-  int32_t waves_per_tile;  /* wavefronts that split one tile's K rows */
+  int32_t bv;              /* value columns per workgroup */
+  int32_t waves_per_tile;  /* wavefronts per workgroup */
   int32_t threads;         /* threads per workgroup */
   int32_t tiles;           /* n_req * H * (V / bv) */
   int32_t blocks;          /* workgroups launched */
   int32_t lds_bytes;       /* static LDS per workgroup */
   const char* kernel;      /* kernel symbol family name */
+  int32_t rows_layout;     /* KDA_ROWS_K_SPLIT or KDA_ROWS_WAVE_K (one row: K_SPLIT) */
 } kda_launch_desc;
 
 /* Fills *desc for (n_req, n_rows, H, dtype) under opts (NULL = defaults).

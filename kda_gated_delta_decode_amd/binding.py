@@ -39,6 +39,9 @@ KDA_ERR_LAUNCH = 9
 KDA_HEAD_K = 128
 KDA_HEAD_V = 128
 KDA_MAX_ROWS = 8
+KDA_ROWS_DEFAULT = 0
+KDA_ROWS_K_SPLIT = 1
+KDA_ROWS_WAVE_K = 2
 
 
 class kda_pool(ctypes.Structure):
@@ -52,7 +55,7 @@ class kda_conv_pool(ctypes.Structure):
 
 class kda_launch_opts(ctypes.Structure):
     _fields_ = [("waves_per_tile", ctypes.c_int32), ("bv", ctypes.c_int32),
-                ("block_rows", ctypes.c_int32)]
+                ("block_rows", ctypes.c_int32), ("rows_layout", ctypes.c_int32)]
 
 
 class kda_prefill_opts(ctypes.Structure):
@@ -63,7 +66,7 @@ class kda_launch_desc(ctypes.Structure):
     _fields_ = [("bv", ctypes.c_int32), ("waves_per_tile", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("tiles", ctypes.c_int32),
                 ("blocks", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("kernel", ctypes.c_char_p)]
+                ("kernel", ctypes.c_char_p), ("rows_layout", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -202,7 +205,7 @@ def _check(code: int, where: str) -> None:
 def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1,
                     state_dtype=None, scale: float | None = None, stream=None,
                     waves_per_tile: int = 0, bv: int = 0, pool_dtype=None,
-                    init_slot_ids=None, block_rows: bool = False) -> None:
+                    init_slot_ids=None, block_rows: bool = False, rows_layout: int = 0) -> None:
     """One decode launch (see kda_decode_step in include/kda_decode.h).
 
     pool: device tensor [n_slots, H, 128, 128], float32 or float16, updated
@@ -211,7 +214,8 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
     dtype; pool_dtype overrides what the pool struct declares (tests of the
     refusals).  init_slot_ids (device int32 [n_req]) reads each request's
     initial state from that slot; block_rows takes chained rows as one block
-    instead of one after the other; any of these, or a non-zero
+    instead of one after the other; rows_layout picks the chained-row layout
+    (KDA_ROWS_K_SPLIT or KDA_ROWS_WAVE_K); any of these, or a non-zero
     waves_per_tile or bv, selects kda_decode_step_ex."""
     import torch
     P = make_pool(pool, pool_dtype)
@@ -231,10 +235,10 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
             _dev(g, "g", torch.float32), _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
             n_req, n_rows_per_slot, sd, float(scale))
     ids = _dev(slot_ids, "slot_ids", torch.int32)
-    if waves_per_tile or bv or block_rows or init_slot_ids is not None:
+    if waves_per_tile or bv or block_rows or rows_layout or init_slot_ids is not None:
         if init_slot_ids is not None and init_slot_ids.numel() != n_req:
             raise ValueError("init_slot_ids needs one entry per request")
-        opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)))
+        opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout))
         rc = library().kda_decode_step_ex(ctypes.byref(P), ids,
                                           _dev(init_slot_ids, "init_slot_ids", torch.int32), *rows,
                                           ctypes.byref(opts), _stream_ptr(stream))
@@ -370,14 +374,14 @@ def kda_tile_bv(dtype) -> int:
 
 
 def kda_describe_launch(n_req: int, n_rows: int, H: int, dtype, waves_per_tile: int = 0,
-                        bv: int = 0, block_rows: bool = False) -> dict:
+                        bv: int = 0, block_rows: bool = False, rows_layout: int = 0) -> dict:
     d = kda_launch_desc()
-    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)))
+    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout))
     _check(library().kda_describe_launch(n_req, n_rows, H, _dtype_arg(dtype), ctypes.byref(opts),
                                          ctypes.byref(d)), "kda_describe_launch")
     return {"bv": d.bv, "waves_per_tile": d.waves_per_tile, "threads": d.threads,
             "tiles": d.tiles, "blocks": d.blocks, "lds_bytes": d.lds_bytes,
-            "kernel": d.kernel.decode()}
+            "kernel": d.kernel.decode(), "rows_layout": d.rows_layout}
 
 
 def kda_tile_of_block(block: int, n_blocks: int) -> int:

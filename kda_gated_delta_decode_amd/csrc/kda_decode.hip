@@ -709,6 +709,316 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Chained rows with the whole of K inside each wavefront.  A workgroup takes
+// NWB x BVW value columns of one (request, head); each of its waves holds all
+// 128 key rows of BVW of them (LPR = 2 or 4 lanes per 16-byte piece of a
+// row, 64/LPR row groups, RPL rows per lane), so a row's two column sums over K never
+// leave the wave: no LDS round trip and no barrier between rows, and the
+// waves of a workgroup run their chains independently.  Per row:
+//  - in-lane partial sums w (over kn) and p (over qn) of the decayed state;
+//  - reduce-scatter over the top log2(CPL) lane bits (permlane32/16 swaps
+//    of register pairs, then DPP with a select) until each lane holds one w
+//    and one p, for the column c(lane) its top bits name;
+//  - all-reduce of those two over the remaining row-group bits (DPP);
+//  - all-gather of w back over the top bits, so every lane has the w of its
+//    CPL columns for the rank-1 update; the lanes whose all-reduced bits are
+//    zero write o for their column.
+// Rows t of the request run in order; row t's post-update state is stored
+// to its snapshot slot before row t + 1 starts (ROCm/ATOM PR #2945, Changes:
+// one snapshot per token, the state staying fp32 between tokens).
+// ---------------------------------------------------------------------------
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+// The value that lane (lane xor 2^B) holds, for B = 0 .. 3 (DPP).
+template <int B>
+__device__ __forceinline__ float partner(float x) {
+  static_assert(B >= 0 && B <= 3, "DPP partners only");
+  if constexpr (B == 0) return dpp<kDppQuadXor1>(x);
+  if constexpr (B == 1) return dpp<kDppQuadXor2>(x);
+  if constexpr (B == 2) return dpp<kDppQuadXor3>(dpp<kDppRowHalfMirror>(x));
+  return dpp<kDppRowRor8>(x);
+}
+
+// One reduce-scatter stage over lane bit B: pairs (x[2i], x[2i+1]) become
+// one value y[i], the sum over the lane pair of x[2i] where bit B is clear
+// and of x[2i+1] where it is set.
+template <int B, int N>
+__device__ __forceinline__ void rs_stage(const float (&x)[N], float (&y)[N / 2], int lane) {
+  if constexpr (B == 5 || B == 4) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const auto r = B == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[2 * i]),
+                                                               __float_as_uint(x[2 * i + 1]), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[2 * i]),
+                                                               __float_as_uint(x[2 * i + 1]), false, false);
+      y[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else {
+    const bool hi = (lane >> B) & 1;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = hi ? x[2 * i + 1] : x[2 * i];
+      const float send = hi ? x[2 * i] : x[2 * i + 1];
+      y[i] = keep + partner<B>(send);
+    }
+  }
+}
+
+// One all-gather stage over lane bit B: each lane's N values and its
+// partner's become 2N, ordered so that out[2j + b] comes from the lane whose
+// bit B is b.
+template <int B, int N>
+__device__ __forceinline__ void ag_stage(const float (&x)[N], float (&y)[2 * N], int lane) {
+  if constexpr (B == 5 || B == 4) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const auto r = B == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]),
+                                                               __float_as_uint(x[j]), false, false)
+                            : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[j]),
+                                                               __float_as_uint(x[j]), false, false);
+      y[2 * j] = __uint_as_float(r[0]);
+      y[2 * j + 1] = __uint_as_float(r[1]);
+    }
+  } else {
+    const bool hi = (lane >> B) & 1;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const float other = partner<B>(x[j]);
+      y[2 * j] = hi ? other : x[j];
+      y[2 * j + 1] = hi ? x[j] : other;
+    }
+  }
+}
+
+// Column sums over the 64/LPR row groups of a wave.  x = [w_0..w_{C-1},
+// p_0..p_{C-1}] per lane (C = CPL).  Returns the totals w_c, p_c of the
+// column c = sum_s bit(5 - s) << s that the lane's top log2(C) bits name,
+// and in wall[] the totals w_0 .. w_{C-1} of all C columns.
+template <int C, int LB>
+__device__ __forceinline__ void wave_column_sums(const float (&x)[2 * C], int lane, float& w_c,
+                                                 float& p_c, float (&wall)[C]) {
+  constexpr int TB = ilog2c(C);
+  static_assert(C == 4 || C == 8, "4 or 8 columns per lane");
+  static_assert(6 - TB >= LB, "the top bits must be row-group bits");
+  float y[C], z[C / 2];
+  rs_stage<5>(x, y, lane);
+  rs_stage<4>(y, z, lane);
+  float u[2];
+  if constexpr (C == 8) {
+    rs_stage<3>(z, u, lane);
+  } else {
+    u[0] = z[0];
+    u[1] = z[1];
+  }
+  // all-reduce over the row-group bits below the top ones
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    float v = u[e];
+    if constexpr (5 - TB >= 3 && LB <= 3) v += partner<3>(v);
+    if constexpr (5 - TB >= 2 && LB <= 2) v += partner<2>(v);
+    if constexpr (5 - TB >= 1 && LB <= 1) v += partner<1>(v);
+    if constexpr (LB <= 0) v += partner<0>(v);
+    u[e] = v;
+  }
+  w_c = u[0];
+  p_c = u[1];
+  // all-gather of w over the top bits, lowest of them first
+  float g1[1] = {w_c};
+  if constexpr (C == 8) {
+    float g2[2], g4[4];
+    ag_stage<3>(g1, g2, lane);
+    ag_stage<4>(g2, g4, lane);
+    ag_stage<5>(g4, wall, lane);
+  } else {
+    float g2[2];
+    ag_stage<4>(g1, g2, lane);
+    ag_stage<5>(g2, wall, lane);
+  }
+}
+
+template <typename T, int LPR, int NWB>
+__global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
+  using L = Lane16<T>;
+  using vec = typename L::vec;
+  constexpr int CPL = L::kCols;           // columns per lane
+  constexpr int BVW = LPR * CPL;          // columns per wave
+  constexpr int BVB = NWB * BVW;          // columns per workgroup
+  constexpr int GROUPS = kWave / LPR;     // row groups per wave
+  constexpr int RPL = kHeadK / GROUPS;    // rows per lane
+  constexpr int TMAX = KDA_MAX_ROWS;
+  constexpr int TPW = (TMAX + NWB - 1) / NWB;
+  constexpr int LB = ilog2c(LPR);         // lowest row-group lane bit
+  constexpr int TB = ilog2c(CPL);         // top lane bits that name a column
+  // lanes that write o: all-reduced bits (LB .. 5 - TB) clear
+  constexpr int kArMask = ((1 << (6 - TB)) - 1) & ~((1 << LB) - 1);
+  static_assert(RPL % 2 == 0 && RPL * CPL <= 64, "2+ rows and <= 64 state values per lane");
+  static_assert(BVB <= kHeadV && kHeadV % BVB == 0, "workgroups must divide V");
+
+  __shared__ __attribute__((aligned(16))) float s_qn[TMAX][kHeadK];
+  __shared__ __attribute__((aligned(16))) float s_kn[TMAX][kHeadK];
+  __shared__ __attribute__((aligned(16))) float s_a[TMAX][kHeadK];
+  __shared__ __attribute__((aligned(16))) float s_v[TMAX][BVB];
+  __shared__ float s_beta[TMAX];
+  __shared__ float s_qk[TMAX];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int cg = lane % LPR;
+  const int row0 = (lane / LPR) * RPL;
+
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int vt = tile % a.n_vt;
+  const int rh = tile / a.n_vt;
+  const int h = rh % a.H;
+  const int r = rh / a.H;
+  const int n_rows = a.n_rows;
+  const int wcol = wave * BVW + cg * CPL;  // the lane's first column inside the workgroup's
+  const int col0 = vt * BVB + wcol;
+
+  // Slot ids: wave-uniform scalar loads, issued first and read once (a
+  // re-read after the snapshot stores would be a vector load that waits for
+  // every earlier store).  The initial slot is one load from a selected
+  // address: a select between two loaded values would wait for the ids
+  // before the row loads below go out.
+  const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
+  int32_t sid[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
+  const int32_t init_slot = *(a.init_slot_ids != nullptr ? a.init_slot_ids + r : ids);
+
+  // Row inputs (wave w stages rows w, w + NWB, ...), issued before anything
+  // waits on the ids.  Every address is valid whatever n_rows is (a row past
+  // the last re-reads the last one; lanes past the workgroup's v columns
+  // re-read its first ones), so no branch join waits for their data.  b goes
+  // through a vector register (an opaque zero in its index): a scalar load
+  // would share the ids' counter and be waited for with them.
+  int zero_v;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
+  f2 q2[TPW], k2[TPW], g2[TPW];
+  f4 v4[TPW];
+  float braw[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = min(wave + j * NWB, n_rows - 1);
+    const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+    const int64_t off = (rho * a.H + h) * kHeadK;
+    q2[j] = reinterpret_cast<const f2*>(a.q + off)[lane];
+    k2[j] = reinterpret_cast<const f2*>(a.k + off)[lane];
+    g2[j] = reinterpret_cast<const f2*>(a.g + off)[lane];
+    v4[j] = *reinterpret_cast<const f4*>(a.v + off + vt * BVB + 4 * (lane % (BVB / 4)));
+    braw[j] = a.b[rho * a.H + h + zero_v];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // A request with an id out of range is skipped: out rows NaN, pool untouched.
+  bool ids_ok = init_slot >= 0 && init_slot < a.n_slots;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
+
+  // The state: RPL rows x 16 bytes per lane (slot 0 for a request that is
+  // skipped below, so every address stays valid).
+  const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
+  const int64_t slot_elems = static_cast<int64_t>(a.H) * head_elems;
+  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + col0;
+  T* const pool = static_cast<T*>(a.pool);
+  vec raw[RPL];
+  {
+    const T* src = pool + static_cast<int64_t>(ids_ok ? init_slot : 0) * slot_elems + lane_off;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m)
+      raw[m] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(src + m * kHeadV));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Per-row vectors: norms over all 128 entries (lane holds 2), staged.
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + j * NWB;
+    if (t < n_rows) {
+      const float sq = wave_sum(fmaf(q2[j][1], q2[j][1], q2[j][0] * q2[j][0]));
+      const float sk = wave_sum(fmaf(k2[j][1], k2[j][1], k2[j][0] * k2[j][0]));
+      const float sqk = wave_sum(fmaf(q2[j][1], k2[j][1], q2[j][0] * k2[j][0]));
+      const float rq = 1.0f / sqrtf(sq + 1e-6f);
+      const float rk = 1.0f / sqrtf(sk + 1e-6f);
+      *reinterpret_cast<f2*>(&s_qn[t][2 * lane]) = f2{q2[j][0] * rq, q2[j][1] * rq};
+      *reinterpret_cast<f2*>(&s_kn[t][2 * lane]) = f2{k2[j][0] * rk, k2[j][1] * rk};
+      *reinterpret_cast<f2*>(&s_a[t][2 * lane]) = f2{expf(g2[j][0]), expf(g2[j][1])};
+      if (lane < BVB / 4) *reinterpret_cast<f4*>(&s_v[t][4 * lane]) = v4[j];
+      if (lane == 0) {
+        s_beta[t] = 1.0f / (1.0f + expf(-braw[j]));
+        s_qk[t] = (sqk * rq) * rk;
+      }
+    }
+  }
+  if (!ids_ok) {  // uniform over the workgroup: no wave waits at the barrier
+    if (wave == 0 && lane < BVB / 4) {
+      for (int t = 0; t < n_rows; ++t) {
+        const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+        *reinterpret_cast<f4*>(a.out + (rho * a.H + h) * kHeadV + vt * BVB + 4 * lane) =
+            f4{NAN, NAN, NAN, NAN};
+      }
+    }
+    return;
+  }
+  __syncthreads();
+
+  float S[RPL][CPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) L::widen(raw[m], S[m]);
+
+  const int c_mine = ((lane >> 5) & 1) | (((lane >> 4) & 1) << 1) | (CPL == 8 ? ((lane >> 3) & 1) << 2 : 0);
+  const bool writer = (lane & kArMask) == 0;
+
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if (t >= n_rows) break;
+    float kn[RPL], qn[RPL], am[RPL], vv[CPL];
+    lds_rows<RPL>(&s_kn[t][row0], kn);
+    lds_rows<RPL>(&s_qn[t][row0], qn);
+    lds_rows<RPL>(&s_a[t][row0], am);
+    lds_rows<CPL>(&s_v[t][wcol], vv);
+
+    // decay, then this lane's partial sums over its rows
+    float x[2 * CPL];
+#pragma unroll
+    for (int c = 0; c < 2 * CPL; ++c) x[c] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float sp = am[m] * S[m][c];
+        S[m][c] = sp;
+        x[c] = fmaf(kn[m], sp, x[c]);
+        x[CPL + c] = fmaf(qn[m], sp, x[CPL + c]);
+      }
+    }
+    float w_c, p_c, w[CPL];
+    wave_column_sums<CPL, LB>(x, lane, w_c, p_c, w);
+
+    const float beta = s_beta[t];
+    float u[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) u[c] = vv[c] - w[c];
+
+    // rank-1 correction and this row's snapshot
+    T* dst = pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      const float bk = beta * kn[m];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) S[m][c] = fmaf(bk, u[c], S[m][c]);
+      __builtin_nontemporal_store(L::narrow(S[m]), reinterpret_cast<vec*>(dst + m * kHeadV));
+    }
+
+    if (writer) {
+      const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+      const float uc = s_v[t][wcol + c_mine] - w_c;
+      a.out[(rho * a.H + h) * kHeadV + col0 + c_mine] = a.scale * fmaf(beta * s_qk[t], uc, p_c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming copy used to calibrate bandwidth and byte counters: one 16-byte
 // vector per thread, consecutive threads on consecutive vectors (the copy
 // form that measured fastest on MI355X, ahead of grid-stride loops).
@@ -777,9 +1087,36 @@ static hipError_t dispatch_conv(const Args& a, int32_t nw, int32_t blocks, hipSt
   }
 }
 
+template <typename T, int LPR, int NWB>
+static hipError_t launch_rows(const Args& a, int32_t blocks, hipStream_t stream) {
+  if constexpr (NWB * LPR * Lane16<T>::kCols > kHeadV) {
+    return hipErrorInvalidValue;  // unreachable: wave_k_supported() refuses it
+  } else {
+    hipLaunchKernelGGL((kda_rows_kernel<T, LPR, NWB>), dim3(blocks), dim3(kWave * NWB), 0, stream,
+                       a);
+    return hipGetLastError();
+  }
+}
+
+// One instantiation per shape that wave_k_supported() admits.
+template <typename T>
+static hipError_t dispatch_rows(const Args& a, const Shape& sh, int32_t blocks, hipStream_t s) {
+  const int lpr = sh.bv / (sh.nw * Lane16<T>::kCols);
+  switch (lpr * 16 + sh.nw) {
+    case 2 * 16 + 2: return launch_rows<T, 2, 2>(a, blocks, s);
+    case 2 * 16 + 4: return launch_rows<T, 2, 4>(a, blocks, s);
+    case 2 * 16 + 8: return launch_rows<T, 2, 8>(a, blocks, s);
+    case 4 * 16 + 2: return launch_rows<T, 4, 2>(a, blocks, s);
+    case 4 * 16 + 4: return launch_rows<T, 4, 4>(a, blocks, s);
+    case 4 * 16 + 8: return launch_rows<T, 4, 8>(a, blocks, s);
+    default: return hipErrorInvalidValue;  // unreachable: shapes are checked first
+  }
+}
+
 // One instantiation per shape that shape_supported() admits.
 template <typename T>
 static hipError_t dispatch(const Args& a, const Shape& sh, int32_t blocks, hipStream_t s) {
+  if (sh.layout == KDA_ROWS_WAVE_K) return dispatch_rows<T>(a, sh, blocks, s);
   const int lpr = sh.bv / Lane16<T>::kCols;
   switch (lpr * 16 + sh.nw) {
     case 8 * 16 + 1: return launch_tile<T, 8, 1>(a, blocks, s);

@@ -58,32 +58,76 @@ inline bool shape_supported(kda_dtype dt, int32_t bv, int32_t nw) {
   return rpl >= 2 && rpl * cpl <= 128;
 }
 
+// Whole-K chained-row shapes: bv = waves x lanes x columns per lane, with 2
+// or 4 lanes per 16-byte row piece (32 or 16 row groups, 4 or 8 rows per
+// lane: 16 or 32 state values per lane for fp32, 32 or 64 for fp16) and 2, 4
+// or 8 waves; bv at most 128.  (One lane per piece, or one wave per
+// workgroup, measured far slower: 16-byte pieces of a row written by
+// different waves cost the stores most of their bandwidth.)
+inline bool wave_k_supported(kda_dtype dt, int32_t bv, int32_t nw) {
+  const int32_t cpl = cols_per_lane(dt);
+  if (nw != 2 && nw != 4 && nw != 8) return false;
+  if (bv <= 0 || bv % (nw * cpl) != 0 || kHeadV % bv != 0) return false;
+  const int32_t lpr = bv / (nw * cpl);
+  return lpr == 2 || lpr == 4;
+}
+
+// The chained-row default layout and shape, chosen by measurement on MI355X
+// (8 requests x 8 rows x 12 heads, graph-replayed launches, 1 GiB of
+// rotating pools): fp16 pools take the whole-K layout with 64-column
+// workgroups of 4 waves (11.0-11.6 us against 12.3 us for the K split);
+// fp32 pools keep the K split (11.5 us; the whole-K layout's best was 13.4
+// us: its 4 lanes per row piece write 64-byte pieces, the fp16 shape's 2
+// lanes 32-byte pieces of twice as many rows).
+inline int32_t default_rows_layout(kda_dtype dt) {
+  return dt == KDA_F16 ? KDA_ROWS_WAVE_K : KDA_ROWS_K_SPLIT;
+}
+inline int32_t default_wave_k_bv(kda_dtype /*dt*/) { return 64; }
+inline int32_t default_wave_k_waves(kda_dtype /*dt*/) { return 4; }
+
 struct Shape {
-  int32_t bv;  // value columns per tile
-  int32_t nw;  // waves per tile
+  int32_t bv;      // value columns per workgroup
+  int32_t nw;      // waves per workgroup
+  int32_t layout;  // KDA_ROWS_K_SPLIT (also every single-row launch) or KDA_ROWS_WAVE_K
 };
 
 // The shape a launch uses: each option field that is set overrides the
 // default.  Returns false if the result is not an instantiated shape.
 inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts, Shape* out) {
-  Shape s{default_bv(dt, n_rows), default_waves_per_tile(dt, n_rows)};
+  const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
+  if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_WAVE_K) return false;
+  int32_t layout = KDA_ROWS_K_SPLIT;
+  if (n_rows > 1) {
+    if (opts != nullptr && opts->block_rows != 0) {
+      if (asked == KDA_ROWS_WAVE_K) return false;  // the block form is a K-split kernel
+    } else {
+      layout = asked != KDA_ROWS_DEFAULT ? asked : default_rows_layout(dt);
+    }
+  }
+  Shape s{default_bv(dt, n_rows), default_waves_per_tile(dt, n_rows), layout};
+  if (layout == KDA_ROWS_WAVE_K) {
+    s.bv = default_wave_k_bv(dt);
+    s.nw = default_wave_k_waves(dt);
+  }
   if (opts != nullptr) {
     if (opts->bv != 0) s.bv = opts->bv;
     if (opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
   }
   *out = s;
-  return shape_supported(dt, s.bv, s.nw);
+  return layout == KDA_ROWS_WAVE_K ? wave_k_supported(dt, s.bv, s.nw)
+                                   : shape_supported(dt, s.bv, s.nw);
 }
 
 // Bytes of static LDS per workgroup: the staged per-row vectors (normalised
-// q and k and the decay, 128 each; the tile's bv columns of v; beta and
-// qn.kn) for up to KDA_MAX_ROWS rows (1 for single-row launches), plus the
-// cross-wave sums: row after row, double-buffered [2][nw][2][bv] (nw > 1);
-// as a block, [nw][2 KDA_MAX_ROWS][bv] (nw > 1) and the two coupling
-// matrices [KDA_MAX_ROWS][KDA_MAX_ROWS].
-inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block) {
+// q and k and the decay, 128 each; the workgroup's bv columns of v; beta and
+// qn.kn) for up to KDA_MAX_ROWS rows (1 for single-row launches), plus, in
+// the K-split layout, the cross-wave sums: row after row, double-buffered
+// [2][nw][2][bv] (nw > 1); as a block, [nw][2 KDA_MAX_ROWS][bv] (nw > 1)
+// and the two coupling matrices [KDA_MAX_ROWS][KDA_MAX_ROWS].
+inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block, int32_t layout) {
   const int32_t tmax = n_rows == 1 ? 1 : KDA_MAX_ROWS;
   const int32_t staged = tmax * (3 * kHeadK + bv + 2);
+  if (layout == KDA_ROWS_WAVE_K) return 4 * staged;
   const bool block = n_rows > 1 && rows_block;
   const int32_t red = (nw > 1 && !block ? 2 * nw : 1) * 2 * bv;
   const int32_t wp = block && nw > 1 ? nw * 2 * tmax * bv : 4;
@@ -94,11 +138,13 @@ inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block
 // Fused-convolution launches take whole heads (bv = 128) so that a head's
 // convolution history is read and rewritten inside one workgroup; waves per
 // tile 2, 4 or 8 (default: 2 fp32 / 4 fp16 for one row, 8 / 4 for chained
-// rows).  A bv option other than 0 or 128 is refused.
+// rows).  A bv option other than 0 or 128, or the whole-K row layout, is
+// refused.
 inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts,
                                Shape* out) {
-  Shape s{kHeadV, n_rows == 1 ? (dt == KDA_F32 ? 2 : 4) : (dt == KDA_F32 ? 8 : 4)};
+  Shape s{kHeadV, n_rows == 1 ? (dt == KDA_F32 ? 2 : 4) : (dt == KDA_F32 ? 8 : 4), KDA_ROWS_K_SPLIT};
   if (opts != nullptr) {
+    if (opts->rows_layout != KDA_ROWS_DEFAULT && opts->rows_layout != KDA_ROWS_K_SPLIT) return false;
     if (opts->bv != 0 && opts->bv != kHeadV) return false;
     if (opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
   }

@@ -47,12 +47,12 @@ def pool_to_host(pool) -> np.ndarray:
 
 
 def run_gpu(inp: kda_inputs.DecodeInputs, waves_per_tile: int = 0, bv: int = 0,
-            block_rows: bool = False):
+            block_rows: bool = False, rows_layout: int = 0):
     """One launch on the device; returns (pool after [host], out [host])."""
     pool, ids, t, out = device_inputs(inp)
     B.kda_decode_step(pool, ids, t["q"], t["k"], t["v"], t["g"], t["b"], out,
                       n_rows_per_slot=inp.n_rows, scale=inp.scale, waves_per_tile=waves_per_tile,
-                      bv=bv, block_rows=block_rows)
+                      bv=bv, block_rows=block_rows, rows_layout=rows_layout)
     torch.cuda.synchronize()
     return pool_to_host(pool), out.cpu().numpy()
 

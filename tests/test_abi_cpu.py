@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 3
+    assert B.kda_abi_version() == 4
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -79,6 +79,13 @@ def test_refusals_before_any_hip_call():
     assert step(pool(), opts=B.kda_launch_opts(0, 48)) == B.KDA_ERR_ARG
     assert step(pool(dtype=B.KDA_F16), opts=B.kda_launch_opts(0, 32)) == B.KDA_ERR_ARG
     assert step(pool(dtype=B.KDA_F16), opts=B.kda_launch_opts(1, 128)) == B.KDA_ERR_ARG  # spills
+    # chained-row layouts: an unknown layout, the block form in the whole-K
+    # layout, a whole-K shape with 1 lane per row piece or 1 wave
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, 3)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, -1)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 1, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(4, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(1, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
     assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE]) == B.KDA_ERR_ALIGN
@@ -225,15 +232,47 @@ def test_supported_launch_shapes(dtype, shapes):
     assert got == shapes
 
 
+WAVE_K_F32 = {(16, 2), (32, 2), (32, 4), (64, 4), (64, 8), (128, 8)}
+WAVE_K_F16 = {(32, 2), (64, 2), (64, 4), (128, 4), (128, 8)}
+
+
+@pytest.mark.parametrize("dtype,shapes", [("f32", WAVE_K_F32), ("f16", WAVE_K_F16)])
+def test_supported_whole_k_shapes(dtype, shapes):
+    got = set()
+    for bv in (8, 16, 32, 48, 64, 128, 256):
+        for w in (1, 2, 3, 4, 8, 16):
+            try:
+                d = B.kda_describe_launch(8, 8, 12, dtype, waves_per_tile=w, bv=bv,
+                                          rows_layout=B.KDA_ROWS_WAVE_K)
+            except B.KdaError as e:
+                assert e.code == B.KDA_ERR_ARG
+                continue
+            assert (d["bv"], d["waves_per_tile"], d["rows_layout"]) == (bv, w, B.KDA_ROWS_WAVE_K)
+            assert d["tiles"] == 8 * 12 * (128 // bv) and d["kernel"] == "kda_rows_kernel"
+            assert d["lds_bytes"] == 4 * 8 * (3 * 128 + bv + 2)
+            got.add((bv, w))
+    assert got == shapes
+
+
 def test_describe_launch():
     d = B.kda_describe_launch(64, 1, 12, "f32")
     assert (d["bv"], d["waves_per_tile"], d["tiles"], d["blocks"]) == (128, 2, 768, 768)
+    assert (d["kernel"], d["rows_layout"]) == ("kda_decode_tile", B.KDA_ROWS_K_SPLIT)
     d = B.kda_describe_launch(64, 1, 12, "f16")
     assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (128, 4, 768)
+    # one row: the layout option is ignored
+    d = B.kda_describe_launch(64, 1, 12, "f16", rows_layout=B.KDA_ROWS_WAVE_K)
+    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (128, 4, "kda_decode_tile")
+    # chained rows: whole K for fp16 pools, the K split for fp32
     d = B.kda_describe_launch(8, 8, 12, "f16")
     assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 4, 8 * 12 * 2)
-    d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8)
-    assert (d["waves_per_tile"], d["threads"]) == (8, 512)
+    assert (d["kernel"], d["rows_layout"]) == ("kda_rows_kernel", B.KDA_ROWS_WAVE_K)
+    d = B.kda_describe_launch(8, 8, 12, "f32")
+    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 8, "kda_decode_tile")
+    d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8, rows_layout=B.KDA_ROWS_K_SPLIT)
+    assert (d["waves_per_tile"], d["threads"], d["kernel"]) == (8, 512, "kda_decode_tile")
+    d = B.kda_describe_launch(8, 8, 12, "f16", block_rows=True)
+    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 4, "kda_decode_tile")
     with pytest.raises(B.KdaError):
         B.kda_describe_launch(8, 9, 12, "f16")
     with pytest.raises(B.KdaError):
@@ -272,6 +311,7 @@ def test_conv_step_refusals():
         assert conv_step(P, Cv, ptrs=ptrs) == B.KDA_ERR_NULL
     assert conv_step(P, Cv, opts=B.kda_launch_opts(0, 64)) == B.KDA_ERR_ARG   # whole heads only
     assert conv_step(P, Cv, opts=B.kda_launch_opts(1, 0)) == B.KDA_ERR_ARG
+    assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 0, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, scale=float("nan")) == B.KDA_ERR_ARG
     assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE + 8), 16, 12)) == B.KDA_ERR_ALIGN
 

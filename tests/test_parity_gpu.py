@@ -67,9 +67,26 @@ def test_small_shapes_every_launch_shape(oracle, dtype, bv, waves, n_req, H, n_r
     n_slots = n_req * n_rows + 3
     inp = kda_inputs.make_inputs("small", n_slots, n_req, n_rows, dtype, H=H,
                                  seed=1000 + 7 * n_req + 31 * H + n_rows)
-    gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv)
+    gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv, rows_layout=B.KDA_ROWS_K_SPLIT)
     check_parity(oracle, inp, gp, go,
                  label="small %s bv%d w%d %dx%dx%d" % (dtype, bv, waves, n_req, H, n_rows))
+
+
+# whole-K chained-row layout: (bv, waves) with 2 or 4 lanes per row piece
+WAVE_K_SHAPES = [("f32", bv, w) for bv, w in [(16, 2), (32, 2), (32, 4), (64, 4), (64, 8),
+                                              (128, 8)]] + \
+                [("f16", bv, w) for bv, w in [(32, 2), (64, 2), (64, 4), (128, 4), (128, 8)]]
+
+
+@pytest.mark.parametrize("dtype,bv,waves", WAVE_K_SHAPES)
+@pytest.mark.parametrize("n_req,H,n_rows", [s for s in SHAPES if s[2] > 1] + [(2, 3, 2)])
+def test_small_shapes_whole_k_layout(oracle, dtype, bv, waves, n_req, H, n_rows):
+    n_slots = n_req * n_rows + 3
+    inp = kda_inputs.make_inputs("small wk", n_slots, n_req, n_rows, dtype, H=H,
+                                 seed=2000 + 7 * n_req + 31 * H + n_rows)
+    gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv, rows_layout=B.KDA_ROWS_WAVE_K)
+    check_parity(oracle, inp, gp, go,
+                 label="small wk %s bv%d w%d %dx%dx%d" % (dtype, bv, waves, n_req, H, n_rows))
 
 
 # --- edge cases -----------------------------------------------------------
@@ -200,8 +217,26 @@ def test_fp32_twin_of_fp16_launch(n_rows, lanes, waves):
     inp32 = kda_inputs.DecodeInputs("twin32", "f32", inp16.pool.view(np.float16).astype(np.float32),
                                     inp16.slot_ids, inp16.q, inp16.k, inp16.v, inp16.g, inp16.b,
                                     n_rows, inp16.scale)
-    p16, o16 = run_gpu(inp16, waves_per_tile=waves, bv=8 * lanes)
-    p32, o32 = run_gpu(inp32, waves_per_tile=waves, bv=4 * lanes)
+    p16, o16 = run_gpu(inp16, waves_per_tile=waves, bv=8 * lanes, rows_layout=B.KDA_ROWS_K_SPLIT)
+    p32, o32 = run_gpu(inp32, waves_per_tile=waves, bv=4 * lanes, rows_layout=B.KDA_ROWS_K_SPLIT)
+    np.testing.assert_array_equal(o16.view(np.uint32), o32.view(np.uint32))
+    np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("lanes,waves", [(2, 2), (2, 4), (2, 8), (4, 2), (4, 4)])
+def test_fp32_twin_of_fp16_launch_whole_k(lanes, waves):
+    """The twin property in the whole-K layout: the same lanes per row piece
+    give the same rows per lane and the same exchange tree over the row
+    groups, so outputs are bit-equal and each fp16 snapshot is the RNE of
+    the fp32 one."""
+    inp16 = kda_inputs.make_inputs("twin wk", 96, 8, 8, "f16", seed=25)
+    inp32 = kda_inputs.DecodeInputs("twin32", "f32", inp16.pool.view(np.float16).astype(np.float32),
+                                    inp16.slot_ids, inp16.q, inp16.k, inp16.v, inp16.g, inp16.b,
+                                    8, inp16.scale)
+    p16, o16 = run_gpu(inp16, waves_per_tile=waves, bv=8 * lanes * waves,
+                       rows_layout=B.KDA_ROWS_WAVE_K)
+    p32, o32 = run_gpu(inp32, waves_per_tile=waves, bv=4 * lanes * waves,
+                       rows_layout=B.KDA_ROWS_WAVE_K)
     np.testing.assert_array_equal(o16.view(np.uint32), o32.view(np.uint32))
     np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
 
@@ -229,7 +264,7 @@ def test_chained_rows_equal_single_row_launches_fp32(bv, waves):
     per row, so n chained single-row launches reproduce them bit for bit."""
     n_req, n = 4, 6
     inp = kda_inputs.make_inputs("chain", 40, n_req, n, "f32", seed=29)
-    pm, om = run_gpu(inp, waves_per_tile=waves, bv=bv)
+    pm, om = run_gpu(inp, waves_per_tile=waves, bv=bv, rows_layout=B.KDA_ROWS_K_SPLIT)
     pool, ids, t, out = device_inputs(inp)
     for step in range(n):
         rows = torch.arange(n_req, device="cuda") * n + step
@@ -256,7 +291,8 @@ def test_rows_as_block_and_row_after_row_both_match_the_oracle(oracle, dtype, n_
     chain compute the same recurrence: both within the oracle tolerances."""
     inp = kda_inputs.make_inputs("rows", 40, 40 // 8, n_rows, dtype, H=3, seed=41 + n_rows)
     for blk in (False, True):
-        gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv, block_rows=blk)
+        gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv, block_rows=blk,
+                         rows_layout=B.KDA_ROWS_K_SPLIT)
         check_parity(oracle, inp, gp, go, label="block" if blk else "sequential")
 
 
