@@ -161,7 +161,10 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
  *                  differently; on MI355X the block form measured slower at
  *                  8 rows (its n x n coupling sums cost more than the
  *                  per-row reductions they replace).  The block form uses
- *                  the K-split layout (with KDA_ROWS_WAVE_K it is refused).
+ *                  the K-split layout (with KDA_ROWS_WAVE_K it is refused)
+ *                  and, for fp16 pools, at least 2 waves (one wave's 128
+ *                  state values and 8 x 8 x 3 column sums per lane do not
+ *                  fit in the register file: refused).
  *  rows_layout     chained rows only: KDA_ROWS_DEFAULT (whole-K for fp16
  *                  pools, bv 64 over 4 waves; K split for fp32, bv 64 over 8
  *                  waves), KDA_ROWS_K_SPLIT or KDA_ROWS_WAVE_K; ignored for

@@ -1051,10 +1051,14 @@ static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream)
   if (a.n_rows == 1)
     hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, false, false>), dim3(blocks),
                        dim3(kWave * NW), 0, stream, a);
-  else if (a.rows_block)
-    hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false, true>), dim3(blocks),
-                       dim3(kWave * NW), 0, stream, a);
-  else
+  else if (a.rows_block) {
+    // not instantiated for the shapes resolve_shape refuses (block_supported)
+    if constexpr (!std::is_same_v<T, _Float16> || NW > 1)
+      hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false, true>), dim3(blocks),
+                         dim3(kWave * NW), 0, stream, a);
+    else
+      return hipErrorInvalidValue;  // unreachable: shapes are checked first
+  } else
     hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false, false>), dim3(blocks),
                        dim3(kWave * NW), 0, stream, a);
   return hipGetLastError();

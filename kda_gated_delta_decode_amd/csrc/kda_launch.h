@@ -85,6 +85,9 @@ inline int32_t default_rows_layout(kda_dtype dt) {
 inline int32_t default_wave_k_bv(kda_dtype /*dt*/) { return 64; }
 inline int32_t default_wave_k_waves(kda_dtype /*dt*/) { return 4; }
 
+// The chained-rows block form: fp16 pools need at least 2 waves per tile.
+inline bool block_supported(kda_dtype dt, int32_t nw) { return dt != KDA_F16 || nw > 1; }
+
 struct Shape {
   int32_t bv;      // value columns per workgroup
   int32_t nw;      // waves per workgroup
@@ -114,8 +117,13 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* o
     if (opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
   }
   *out = s;
-  return layout == KDA_ROWS_WAVE_K ? wave_k_supported(dt, s.bv, s.nw)
-                                   : shape_supported(dt, s.bv, s.nw);
+  if (layout == KDA_ROWS_WAVE_K) return wave_k_supported(dt, s.bv, s.nw);
+  // The block form keeps, per lane, the fp32 state and 3 x 8 column sums per
+  // column; with one wave an fp16 tile (128 state values per lane) would
+  // spill registers.
+  if (n_rows > 1 && opts != nullptr && opts->block_rows != 0 && !block_supported(dt, s.nw))
+    return false;
+  return shape_supported(dt, s.bv, s.nw);
 }
 
 // Bytes of static LDS per workgroup: the staged per-row vectors (normalised

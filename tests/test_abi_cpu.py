@@ -84,6 +84,8 @@ def test_refusals_before_any_hip_call():
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, 3)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, -1)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 1, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
+    # the block form with one wave is refused for fp16 pools (it would spill)
+    assert step(pool(dtype=B.KDA_F16), n_rows=8, opts=B.kda_launch_opts(1, 64, 1)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(4, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(1, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
     assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
@@ -273,6 +275,13 @@ def test_describe_launch():
     assert (d["waves_per_tile"], d["threads"], d["kernel"]) == (8, 512, "kda_decode_tile")
     d = B.kda_describe_launch(8, 8, 12, "f16", block_rows=True)
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 4, "kda_decode_tile")
+    # the block form with one wave: fp32 admitted, fp16 refused (it would spill registers)
+    d = B.kda_describe_launch(8, 8, 12, "f32", block_rows=True, waves_per_tile=1, bv=32)
+    assert (d["bv"], d["waves_per_tile"]) == (32, 1)
+    with pytest.raises(B.KdaError):
+        B.kda_describe_launch(8, 8, 12, "f16", block_rows=True, waves_per_tile=1, bv=64)
+    d = B.kda_describe_launch(8, 8, 12, "f16", block_rows=True, waves_per_tile=2, bv=64)
+    assert (d["bv"], d["waves_per_tile"]) == (64, 2)
     with pytest.raises(B.KdaError):
         B.kda_describe_launch(8, 9, 12, "f16")
     with pytest.raises(B.KdaError):

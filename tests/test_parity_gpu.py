@@ -241,7 +241,7 @@ def test_fp32_twin_of_fp16_launch_whole_k(lanes, waves):
     np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
 
 
-@pytest.mark.parametrize("lanes,waves", [(8, 1), (8, 4), (16, 8)])
+@pytest.mark.parametrize("lanes,waves", [(8, 2), (8, 4), (16, 8)])
 def test_fp32_twin_of_fp16_launch_rows_as_block(lanes, waves):
     """The same twin property for the block form of chained rows."""
     inp16 = kda_inputs.make_inputs("twin block", 96, 8, 8, "f16", seed=24)
@@ -291,6 +291,8 @@ def test_rows_as_block_and_row_after_row_both_match_the_oracle(oracle, dtype, n_
     chain compute the same recurrence: both within the oracle tolerances."""
     inp = kda_inputs.make_inputs("rows", 40, 40 // 8, n_rows, dtype, H=3, seed=41 + n_rows)
     for blk in (False, True):
+        if blk and dtype == "f16" and waves == 1:
+            continue  # refused: the one-wave fp16 block form would spill (test_abi_cpu)
         gp, go = run_gpu(inp, waves_per_tile=waves, bv=bv, block_rows=blk,
                          rows_layout=B.KDA_ROWS_K_SPLIT)
         check_parity(oracle, inp, gp, go, label="block" if blk else "sequential")
