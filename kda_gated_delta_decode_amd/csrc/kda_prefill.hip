@@ -88,6 +88,46 @@ struct PrefillArgs {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Which sequence a workgroup takes.  A CU holds one prefill workgroup at a
+// time (its LDS), and workgroups are dispatched in block order (dealt over
+// the XCDs), so the launch is a list schedule over (sequence, head) pairs:
+// with the longest sequences first, the last workgroups to start are short
+// ones and the launch ends close to the longest sequence's own time, where
+// in index order a long sequence may start only as the others end.  Block b
+// takes head b mod H of the sequence of rank b / H, the rank of a sequence
+// being the number of sequences longer than it, or as long with a smaller
+// index (a permutation of 0 .. n_seq - 1).  Every wave ranks the lengths
+// itself: each lane counts, for its sequences, the longer ones, reading all
+// lengths through readlane.  Above kRankedSeqs sequences that costs more
+// than it saves, and blocks take the sequences in index order.
+constexpr int kRankedSeqs = 256;
+
+__device__ __forceinline__ int32_t seq_length(const int32_t* cu, int i) {
+  const int64_t d = static_cast<int64_t>(cu[i + 1]) - cu[i];
+  return d < 0 ? -1 : (d > INT32_MAX ? INT32_MAX : static_cast<int32_t>(d));
+}
+
+__device__ int seq_of_rank(const int32_t* cu, int n_seq, int rank) {
+  if (n_seq > kRankedSeqs) return rank;
+  const int lane = threadIdx.x % 64;
+  for (int ib = 0; ib < n_seq; ib += 64) {
+    const int i = ib + lane;
+    const int32_t li = i < n_seq ? seq_length(cu, i) : -1;
+    int r = 0;
+    for (int jb = 0; jb < n_seq; jb += 64) {
+      const int32_t lj = jb + lane < n_seq ? seq_length(cu, jb + lane) : -1;
+      const int cnt = min(64, n_seq - jb);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const int32_t l = __builtin_amdgcn_readlane(lj, jj);
+        r += (l > li || (l == li && jb + jj < i)) ? 1 : 0;
+      }
+    }
+    const unsigned long long hit = __ballot(i < n_seq && r == rank);
+    if (hit != 0) return ib + __ffsll(static_cast<long long>(hit)) - 1;
+  }
+  return rank;  // not reached: the ranks are a permutation of 0 .. n_seq - 1
+}
+
 // Raw buffer stores: a 128-bit descriptor {base, range in bytes, word 3} in
 // scalar registers and a per-lane byte offset; the hardware drops a store
 // whose offset is past the range.
@@ -171,7 +211,7 @@ void kda_prefill_kernel(PrefillArgs a) {
   __shared__ float sSk[PARTS][C];
 
   const int wave = threadIdx.x / 64;
-  const int seq = blockIdx.x / a.H;
+  const int seq = seq_of_rank(a.cu, a.n_seq, blockIdx.x / a.H);
   const int h = blockIdx.x % a.H;
 
   const int64_t t0 = a.cu[seq];
@@ -655,7 +695,7 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
   const int wave = threadIdx.x / 64;
   const bool state_wave = wave < kWsState;
   const int pw = wave - kWsState;  // preparation wave index (prep waves only)
-  const int seq = blockIdx.x / a.H;
+  const int seq = seq_of_rank(a.cu, a.n_seq, blockIdx.x / a.H);
   const int h = blockIdx.x % a.H;
 
   const int64_t t0 = a.cu[seq];

@@ -158,3 +158,25 @@ def test_prefill_full_batch_sampled(oracle, dtype):
     ref32, oo, idx = oracle_f32_states(oracle, inp, seqs)
     check_state(oracle, inp, gp, ref32, inp.dst_slot_ids[seqs])
     assert out_rel(go[idx], oo) <= OUT_REL
+
+
+@pytest.mark.parametrize("n_seq,in_place", [(100, False), (300, True)])
+def test_prefill_many_sequences_with_equal_lengths(oracle, n_seq, in_place):
+    """Workgroups take the sequences longest first (ties by index) when there
+    are at most 256 of them, and in index order beyond: 100 sequences span
+    two 64-lane ranking blocks, 300 take the index order; lengths repeat
+    (and include empty prompts), so every tie is broken.  Each sequence must
+    be computed exactly once: every state and output matches the oracle."""
+    rng = np.random.default_rng(n_seq)
+    lengths = [int(x) for x in rng.choice([0, 1, 3, 17, 33], size=n_seq)]
+    n_slots = n_seq * (1 if in_place else 2) + 4
+    inp = kda_inputs.make_prefill_inputs("prefill %d seqs" % n_seq, lengths, n_slots, "f32", H=1,
+                                         seed=15, in_place=in_place)
+    gp, go = run_gpu(inp)
+    ref32, oo, _ = oracle_f32_states(oracle, inp)
+    check_state(oracle, inp, gp, ref32, inp.dst_slot_ids)
+    assert out_rel(go[:inp.n_tokens], oo[:inp.n_tokens]) <= OUT_REL
+    named = set(inp.dst_slot_ids.tolist())
+    for s in range(n_slots):
+        if s not in named:
+            np.testing.assert_array_equal(gp[s], inp.pool[s])
