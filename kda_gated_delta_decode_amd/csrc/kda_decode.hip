@@ -85,6 +85,7 @@ struct Lane16<float> {
     for (int c = 0; c < kCols; ++c) r[c] = s[c];
     return r;
   }
+  __device__ __forceinline__ static void settle(float*) {}
 };
 
 template <>
@@ -97,19 +98,22 @@ struct Lane16<_Float16> {
     for (int c = 0; c < kCols; ++c) s[c] = static_cast<float>(r[c]);
   }
   // fp32 -> fp16 under the default round-to-nearest-even mode
-  // (v_cvt_pk_f16_f32).  The empty asm pins each value as a rounded fp32
-  // register first: otherwise the backend may fold the fp32 fma that made
-  // it and this narrowing into one mixed-precision fma, which rounds once,
-  // straight to fp16, instead of storing the rounded fp32 state's RNE.
+  // (v_cvt_pk_f16_f32).  Its operands must have been settled (below).
   __device__ __forceinline__ static vec narrow(const float* s) {
     vec r;
 #pragma unroll
-    for (int c = 0; c < kCols; ++c) {
-      float x = s[c];
-      asm("" : "+v"(x));
-      r[c] = static_cast<_Float16>(x);
-    }
+    for (int c = 0; c < kCols; ++c) r[c] = static_cast<_Float16>(s[c]);
     return r;
+  }
+  // Pins each fp32 value, where it is computed, as a rounded fp32 register:
+  // otherwise the backend may fold the fp32 fma that made it and a later
+  // narrowing into one mixed-precision fma, which rounds once, straight to
+  // fp16, instead of storing the rounded fp32 state's RNE (it does so even
+  // where the fp32 value stays live, by computing the fma twice).  Pinned
+  // at the definition, the value needs no copy when it stays live.
+  __device__ __forceinline__ static void settle(float* s) {
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) asm("" : "+v"(s[c]));
   }
 };
 
@@ -546,6 +550,7 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
       for (int m = 0; m < RPL; ++m) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) S[m][c] = fmaf(kn[m], dl[t][c], am[m] * S[m][c]);
+        L::settle(S[m]);
         __builtin_nontemporal_store(L::narrow(S[m]), reinterpret_cast<vec*>(dst + m * kHeadV));
       }
     }
@@ -683,13 +688,16 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
       if constexpr (MULTI) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) s1[c] = fmaf(bk, u[c], S[m][c]);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) S[m][c] = s1[c];
       } else {
         // S' recomputed from the packed tile: the same product as above
         L::widen(raw[m], s1);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) s1[c] = fmaf(bk, u[c], am[m] * s1[c]);
+      }
+      L::settle(s1);
+      if constexpr (MULTI) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) S[m][c] = s1[c];
       }
       __builtin_nontemporal_store(L::narrow(s1), reinterpret_cast<vec*>(dst + m * kHeadV));
     }
@@ -1000,14 +1008,23 @@ __global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) u[c] = vv[c] - w[c];
 
-    // rank-1 correction and this row's snapshot
+    // rank-1 correction and this row's snapshot.  A wave writes 32-byte
+    // (fp16) or 64-byte (fp32) pieces of each 128-byte line, the rest of the
+    // line coming from its sibling waves, so the stores are ordinary
+    // write-back stores: the L2 merges the pieces into whole lines.  With
+    // nontemporal stores the pieces reach memory as partial writes unless
+    // the waves' stores of a line happen to arrive together; measured on
+    // MI355X that made the launch 11.0 to 19.4 us depending on instruction
+    // timing alone (and 17 us at bv 128 over 8 waves), against a steady
+    // 11.9 (and 14.1) us with write-back stores.
     T* dst = pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off;
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
       const float bk = beta * kn[m];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) S[m][c] = fmaf(bk, u[c], S[m][c]);
-      __builtin_nontemporal_store(L::narrow(S[m]), reinterpret_cast<vec*>(dst + m * kHeadV));
+      L::settle(S[m]);
+      *reinterpret_cast<vec*>(dst + m * kHeadV) = L::narrow(S[m]);
     }
 
     if (writer) {
