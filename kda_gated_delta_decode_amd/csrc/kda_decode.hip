@@ -236,14 +236,37 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   }
 
   // -- prologue loads: each wave takes rows wave, wave + NW, ... ------------
+  // Every load a row's prologue needs is issued here, before the state
+  // tile's, and consumed after the tile's loads are issued: a wave that
+  // waited for its row inputs before issuing its tile would queue its tile
+  // behind every other wave's and finish last.
   f2 q2[TPW], k2[TPW], g2[TPW];
   f4 v4[TPW];
   float braw[TPW];
-  // fused convolution: the history each row's snapshot keeps (window
-  // entries t+1 .. t+3) for this lane's 2 q, 2 k and 4 v channels
+  // fused convolution: the window win[t + m], m = 0..3 (3-entry history,
+  // then this request's rows) of this lane's 2 q, 2 k and 4 v channels, and
+  // their taps
   constexpr int TC = CONV ? TPW : 1;
-  f2 hq[TC][3], hk[TC][3];
-  f4 hv[TC][3];
+  f2 eq[TC][4], ek[TC][4];
+  f4 ev[TC][4];
+  f4 wq0, wq1, wk0, wk1, wv[4];
+  const int64_t conv_c = static_cast<int64_t>(3) * a.H * kHeadK;  // channels per history entry
+  const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
+  const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
+  const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
+  const bool conv_vl = lane < BV / 4;
+  if constexpr (CONV) {
+    if (wave < n_rows) {
+      wq0 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4);
+      wq1 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4 + 4);
+      wk0 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4);
+      wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
+      if (conv_vl) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     const int t = wave + j * NW;
@@ -251,66 +274,26 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
       const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
       const int64_t voff = (rho * a.H + h) * kHeadK;
       if constexpr (CONV) {
-        // y_t = silu(sum_j w_j win[t + j]), win = (3-entry history, rows of
-        // this request); the history comes from the initial slot
-        const int64_t C = static_cast<int64_t>(3) * a.H * kHeadK;
-        const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
-        const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
-        const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
-        const bool vl = lane < BV / 4;
-        f2 eq[4], ek[4];
-        f4 ev[4];
+        // the history comes from the initial slot
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int pos = t + m;              // window index
           if (pos < 3) {
-            const uint16_t* hb = a.conv_pool + (static_cast<int64_t>(init_slot) * 3 + pos) * C;
+            const uint16_t* hb = a.conv_pool + (static_cast<int64_t>(init_slot) * 3 + pos) * conv_c;
             const uint32_t pq = *reinterpret_cast<const uint32_t*>(hb + chq);
             const uint32_t pk = *reinterpret_cast<const uint32_t*>(hb + chk);
-            eq[m] = f2{bf16_lo(pq), bf16_hi(pq)};
-            ek[m] = f2{bf16_lo(pk), bf16_hi(pk)};
-            if (vl) {
+            eq[j][m] = f2{bf16_lo(pq), bf16_hi(pq)};
+            ek[j][m] = f2{bf16_lo(pk), bf16_hi(pk)};
+            if (conv_vl) {
               const uint2 pv = *reinterpret_cast<const uint2*>(hb + chv);
-              ev[m] = f4{bf16_lo(pv.x), bf16_hi(pv.x), bf16_lo(pv.y), bf16_hi(pv.y)};
+              ev[j][m] = f4{bf16_lo(pv.x), bf16_hi(pv.x), bf16_lo(pv.y), bf16_hi(pv.y)};
             }
           } else {
-            const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * C;
-            eq[m] = *reinterpret_cast<const f2*>(xr + chq);
-            ek[m] = *reinterpret_cast<const f2*>(xr + chk);
-            if (vl) ev[m] = *reinterpret_cast<const f4*>(xr + chv);
+            const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * conv_c;
+            eq[j][m] = *reinterpret_cast<const f2*>(xr + chq);
+            ek[j][m] = *reinterpret_cast<const f2*>(xr + chk);
+            if (conv_vl) ev[j][m] = *reinterpret_cast<const f4*>(xr + chv);
           }
-        }
-        const f4 wq0 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4);
-        const f4 wq1 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4 + 4);
-        const f4 wk0 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4);
-        const f4 wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
-        float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          sq0 = fmaf(wq0[m], eq[m][0], sq0);
-          sq1 = fmaf(wq1[m], eq[m][1], sq1);
-          sk0 = fmaf(wk0[m], ek[m][0], sk0);
-          sk1 = fmaf(wk1[m], ek[m][1], sk1);
-        }
-        q2[j] = f2{silu(sq0), silu(sq1)};
-        k2[j] = f2{silu(sk0), silu(sk1)};
-        if (vl) {
-          f4 yv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f4 wv = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
-            float sv = 0.0f;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) sv = fmaf(wv[m], ev[m][e], sv);
-            yv[e] = silu(sv);
-          }
-          v4[j] = yv;
-        }
-#pragma unroll
-        for (int e = 0; e < 3; ++e) {
-          hq[j][e] = eq[e + 1];
-          hk[j][e] = ek[e + 1];
-          hv[j][e] = ev[e + 1];
         }
       } else {
         q2[j] = reinterpret_cast<const f2*>(a.q + voff)[lane];
@@ -334,6 +317,45 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
 #pragma unroll
     for (int m = 0; m < RPL; ++m)
       raw[m] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(src + m * kHeadV));
+  }
+
+  // -- fused convolution: y_t = silu(sum_m w_m win[t + m]) --------------------
+  f2 hq[TC][3], hk[TC][3];  // the history each row's snapshot keeps (entries t+1 .. t+3)
+  f4 hv[TC][3];
+  if constexpr (CONV) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + j * NW;
+      if (t < n_rows) {
+        float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          sq0 = fmaf(wq0[m], eq[j][m][0], sq0);
+          sq1 = fmaf(wq1[m], eq[j][m][1], sq1);
+          sk0 = fmaf(wk0[m], ek[j][m][0], sk0);
+          sk1 = fmaf(wk1[m], ek[j][m][1], sk1);
+        }
+        q2[j] = f2{silu(sq0), silu(sq1)};
+        k2[j] = f2{silu(sk0), silu(sk1)};
+        if (conv_vl) {
+          f4 yv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sv = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sv = fmaf(wv[e][m], ev[j][m][e], sv);
+            yv[e] = silu(sv);
+          }
+          v4[j] = yv;
+        }
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+          hq[j][e] = eq[j][e + 1];
+          hk[j][e] = ek[j][e + 1];
+          hv[j][e] = ev[j][e + 1];
+        }
+      }
+    }
   }
 
   // -- prologue compute: norms over all 128 entries (lane holds 2), stage ----
@@ -361,10 +383,6 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   if constexpr (CONV) {
     // every wave has read the history: the rows' snapshots may now overwrite
     // it (row 0's slot is the initial slot of an in-place launch)
-    const int64_t C = static_cast<int64_t>(3) * a.H * kHeadK;
-    const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
-    const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
-    const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
       const int t = wave + j * NW;
@@ -375,7 +393,7 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
           if (u == t) st = sid[u];
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
-          uint16_t* hb = a.conv_pool + (static_cast<int64_t>(st) * 3 + e) * C;
+          uint16_t* hb = a.conv_pool + (static_cast<int64_t>(st) * 3 + e) * conv_c;
           *reinterpret_cast<uint32_t*>(hb + chq) = bf16_pack(hq[j][e][0], hq[j][e][1]);
           *reinterpret_cast<uint32_t*>(hb + chk) = bf16_pack(hk[j][e][0], hk[j][e][1]);
           if (lane < BV / 4)
