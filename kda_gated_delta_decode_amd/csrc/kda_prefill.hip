@@ -1083,17 +1083,22 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // -- final state (state waves) to the destination slot
+  // -- final state (state waves) to the destination slot.  The lane indices
+  // and the wave's columns are re-derived from an opaque thread id, as in
+  // the chunk loop: kept live from the kernel's start, the column offset
+  // was spilled to scratch.
   if (state_wave) {
     int64_t dst_off = static_cast<int64_t>(dst) * a.H * 128 * 128 + head_off;
     asm volatile("" : "+s"(dst_off));
     T* dstp = static_cast<T*>(a.pool) + dst_off;
-    const int li = threadIdx.x % 16, gq = (threadIdx.x % 64) / 16;
+    int tid_f = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid_f));
+    const int li = tid_f % 16, gq = (tid_f % 64) / 16, cw = 16 * (tid_f / 64);
 #pragma unroll
     for (int sb2 = 0; sb2 < 8; ++sb2)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        narrow1(dstp + (16 * sb2 + 4 * gq + r) * 128 + col_w + li, reg[kS + sb2][r]);
+        narrow1(dstp + (16 * sb2 + 4 * gq + r) * 128 + cw + li, reg[kS + sb2][r]);
   }
 }
 

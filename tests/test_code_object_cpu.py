@@ -1,20 +1,21 @@
 """Checks on the gfx950 code object of the built library (no GPU needed).
 
 The kernels are read out of libkda_decode.so itself: its .hip_fatbin section
-is a clang offload bundle whose gfx950 entry is the device code object.  Its
+holds clang offload bundles whose gfx950 entries are the device code objects.  Its
 AMDGPU metadata gives each kernel's registers, scratch and spills; its
 disassembly shows the instructions the compiler chose.  Checked here:
 
 - every kernel runs without scratch memory and spills no register (the
   admitted launch shapes were chosen so that the state tile stays in VGPRs);
-- every kernel that stores an fp16 state narrows it with v_cvt_pk_f16_f32,
-  which rounds to nearest even under the default rounding mode, the store the
+- every kernel that stores an fp16 state narrows it with v_cvt_pk_f16_f32 or
+  v_cvt_f16_f32, which round to nearest even under the default mode, the store the
   fp16 pool is defined with (ROCm/ATOM PR #2945, Summary and Changes), and
   never with the round-toward-zero v_cvt_pkrtz_f16_f32 or a mixed-precision
   fma that rounds straight to fp16 (v_fma_mixlo/hi_f16);
 - no kernel contains a packed fp32 instruction (v_pk_fma_f32, v_pk_mul_f32,
   v_pk_add_f32): the build turns that feature off;
-- the bundle holds gfx950 device code only.
+- each bundle holds gfx950 device code only.  The section holds one bundle
+  per HIP source file (the decode kernels, the prefill kernels); all are read.
 
 Needs the built library and ROCm's LLVM tools (llvm-objcopy,
 clang-offload-bundler, llvm-readelf, llvm-objdump); skips if either is absent.
@@ -42,49 +43,79 @@ def tool(name):
     return path
 
 
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+# one bundle per compiled source file (decode kernels, prefill kernels)
+SOURCES_WITH_KERNELS = 2
+
+
 @pytest.fixture(scope="module")
 def code_object(tmp_path_factory):
+    """Every offload bundle of the library's .hip_fatbin section (one per
+    HIP source file, each aligned), unbundled to its gfx950 code object."""
     if not os.path.exists(LIB):
         pytest.skip("libkda_decode.so is not built")
     d = tmp_path_factory.mktemp("co")
-    fatbin, co = str(d / "fatbin.bin"), str(d / "gfx950.co")
+    fatbin = str(d / "fatbin.bin")
     subprocess.run([tool("llvm-objcopy"), "--dump-section=.hip_fatbin=" + fatbin, LIB,
                     str(d / "stripped.so")], check=True)
-    listed = subprocess.run([tool("clang-offload-bundler"), "--list", "--type=o", "--input=" + fatbin],
-                            check=True, capture_output=True, text=True).stdout.split()
-    subprocess.run([tool("clang-offload-bundler"), "--unbundle", "--type=o", "--input=" + fatbin,
-                    "--targets=" + TARGET, "--output=" + co], check=True)
-    return {"path": co, "bundle": listed}
+    data = open(fatbin, "rb").read()
+    starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
+    paths, bundles = [], []
+    for i, start in enumerate(starts):
+        end = starts[i + 1] if i + 1 < len(starts) else len(data)
+        part, co = str(d / ("bundle%d.bin" % i)), str(d / ("gfx950_%d.co" % i))
+        with open(part, "wb") as f:
+            f.write(data[start:end])
+        bundles.append(subprocess.run([tool("clang-offload-bundler"), "--list", "--type=o",
+                                       "--input=" + part], check=True, capture_output=True,
+                                      text=True).stdout.split())
+        subprocess.run([tool("clang-offload-bundler"), "--unbundle", "--type=o", "--input=" + part,
+                        "--targets=" + TARGET, "--output=" + co], check=True)
+        paths.append(co)
+    return {"paths": paths, "bundles": bundles}
 
 
 @pytest.fixture(scope="module")
 def kernels(code_object):
-    notes = subprocess.run([tool("llvm-readelf"), "--notes", code_object["path"]], check=True,
-                           capture_output=True, text=True).stdout
-    doc = notes[notes.index("---"):]
-    doc = doc[:doc.index("...") + 3] if "..." in doc else doc
-    meta = yaml.safe_load(doc)
-    return {k[".name"]: k for k in meta["amdhsa.kernels"]}
+    out = {}
+    for path in code_object["paths"]:
+        notes = subprocess.run([tool("llvm-readelf"), "--notes", path], check=True,
+                               capture_output=True, text=True).stdout
+        doc = notes[notes.index("---"):]
+        doc = doc[:doc.index("...") + 3] if "..." in doc else doc
+        out.update({k[".name"]: k for k in yaml.safe_load(doc)["amdhsa.kernels"]})
+    return out
 
 
 @pytest.fixture(scope="module")
 def disassembly(code_object):
-    text = subprocess.run([tool("llvm-objdump"), "-d", "--no-show-raw-insn", code_object["path"]],
-                          check=True, capture_output=True, text=True).stdout
-    body, name = {}, None
-    for line in text.splitlines():
-        m = re.match(r"^[0-9a-f]+ <(.+)>:$", line)
-        if m:
-            name = m.group(1)
-            body[name] = []
-        elif name is not None and line.strip():
-            body[name].append(line.split()[0])
+    body = {}
+    for path in code_object["paths"]:
+        text = subprocess.run([tool("llvm-objdump"), "-d", "--no-show-raw-insn", path],
+                              check=True, capture_output=True, text=True).stdout
+        name = None
+        for line in text.splitlines():
+            m = re.match(r"^[0-9a-f]+ <(.+)>:$", line)
+            if m:
+                name = m.group(1)
+                body[name] = []
+            elif name is not None and line.strip():
+                body[name].append(line.split()[0])
     return body
 
 
-def test_bundle_is_gfx950_device_code_only(code_object):
-    devices = [t for t in code_object["bundle"] if not t.startswith("host-")]
-    assert devices == [TARGET]
+def test_bundles_are_gfx950_device_code_only(code_object):
+    assert len(code_object["bundles"]) >= SOURCES_WITH_KERNELS
+    for listed in code_object["bundles"]:
+        devices = [t for t in listed if not t.startswith("host-")]
+        assert devices == [TARGET]
+
+
+def test_every_source_file_is_checked(kernels):
+    # the decode kernels and the prefill kernels come from different bundles
+    assert any("kda_decode_tile" in n for n in kernels)
+    assert any("kda_rows_kernel" in n for n in kernels)
+    assert sum("kda_prefill" in n for n in kernels) == 4
 
 
 def test_every_kernel_has_no_scratch_and_no_spills(kernels):
@@ -110,7 +141,8 @@ def test_fp16_state_is_narrowed_to_nearest_even(disassembly):
     f16 = {n: ops for n, ops in disassembly.items() if "kda" in n and "DF16_" in n}
     assert len(f16) >= 30
     for name, ops in f16.items():
-        assert "v_cvt_pk_f16_f32" in ops, name
+        # packed (decode) or one value at a time (the prefill's final state)
+        assert any(op.startswith(("v_cvt_pk_f16_f32", "v_cvt_f16_f32")) for op in ops), name
         for banned in ("v_cvt_pkrtz_f16_f32", "v_fma_mixlo_f16", "v_fma_mixhi_f16",
                        "v_mad_mixlo_f16", "v_mad_mixhi_f16"):
             assert banned not in ops, (name, banned)
