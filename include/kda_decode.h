@@ -310,11 +310,12 @@ size_t kda_pool_bytes(int32_t n_slots, int32_t H, int32_t K, int32_t V,
 
 /*
  * kda_tile_bv -- value columns per state tile that single-row launches use
- * by default (128 for both dtypes: whole state rows per wave instruction).
- * Narrower tiles (32 fp32 / 64 fp16 columns, the V-block cap of the pages'
- * portable kernel, ROCm/ATOM PR #2130, Copilot review) remain available
- * through kda_launch_opts.  Returns a negative kda_status for a refused
- * dtype.
+ * by default: 128 for fp32 pools (whole 512-byte state rows per wave
+ * instruction, K over 2 waves), 64 for fp16 (whole 128-byte lines, one wave
+ * per tile).  Other widths (32 fp32 / 64 fp16 columns is the V-block cap of
+ * the pages' portable kernel, ROCm/ATOM PR #2130, Copilot review) remain
+ * available through kda_launch_opts.  Returns a negative kda_status for a
+ * refused dtype.
  */
 int32_t kda_tile_bv(kda_dtype dtype);
 

@@ -26,17 +26,22 @@ inline int32_t cols_per_lane(kda_dtype dt) { return dt == KDA_F32 ? 4 : 8; }
 
 // Default launch shape, chosen by measurement on MI355X (graph-replayed
 // launches, 1 GiB of rotating pools, nontemporal state traffic):
-//  - one row per request: whole 128-column tile rows, so every wave
-//    instruction reads or writes whole 512-byte (fp32) / 256-byte (fp16)
-//    state rows; K split over 2 (fp32) or 4 (fp16) waves.  At 64 requests x
-//    12 heads: fp32 17.9 us, fp16 9.7 us, against 20-21 us and 10-14 us for
-//    the narrow 32/64-column tiles.
+//  - one row per request, fp32: whole 128-column tile rows, so every wave
+//    instruction reads or writes whole 512-byte state rows, K split over 2
+//    waves.  At 64 requests x 12 heads: 18.0 us, against 19.8 us over 4 or
+//    8 waves and 20.6-22.1 us for 32/64-column tiles.
+//  - one row per request, fp16: 64-column tiles (a whole 128-byte line per
+//    tile row) held by one wave, so a row's column sums never leave the
+//    wave: no LDS exchange and no barrier.  9.6-9.7 us, against 9.9 us for
+//    128 columns over 2 waves and 10.0-10.1 us over 4.
 //  - chained rows: 64-column tiles with K over 8 (fp32) or 4 (fp16) waves:
 //    few tiles exist, so K is spread over more waves and each row's partial
 //    column sums meet in LDS.
-inline int32_t default_bv(kda_dtype /*dt*/, int32_t n_rows) { return n_rows == 1 ? 128 : 64; }
+inline int32_t default_bv(kda_dtype dt, int32_t n_rows) {
+  return n_rows == 1 && dt == KDA_F32 ? 128 : 64;
+}
 inline int32_t default_waves_per_tile(kda_dtype dt, int32_t n_rows) {
-  if (n_rows == 1) return dt == KDA_F32 ? 2 : 4;
+  if (n_rows == 1) return dt == KDA_F32 ? 2 : 1;
   return dt == KDA_F32 ? 8 : 4;
 }
 

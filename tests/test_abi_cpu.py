@@ -198,7 +198,7 @@ def test_pages_tile_widths_are_supported_shapes():
         d = B.kda_describe_launch(64, 1, 12, dt, waves_per_tile=1, bv=bv)
         assert d["bv"] == bv and d["tiles"] == 64 * 12 * (128 // bv)
         assert bv * (4 if dt == "f32" else 2) == 128
-    assert B.kda_tile_bv("f32") == B.kda_tile_bv("f16") == 128
+    assert B.kda_tile_bv("f32") == 128 and B.kda_tile_bv("f16") == 64
     assert B.kda_tile_bv("bf16") == -B.KDA_ERR_DTYPE_REFUSED
 
 
@@ -261,10 +261,10 @@ def test_describe_launch():
     assert (d["bv"], d["waves_per_tile"], d["tiles"], d["blocks"]) == (128, 2, 768, 768)
     assert (d["kernel"], d["rows_layout"]) == ("kda_decode_tile", B.KDA_ROWS_K_SPLIT)
     d = B.kda_describe_launch(64, 1, 12, "f16")
-    assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (128, 4, 768)
+    assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 1, 1536)
     # one row: the layout option is ignored
     d = B.kda_describe_launch(64, 1, 12, "f16", rows_layout=B.KDA_ROWS_WAVE_K)
-    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (128, 4, "kda_decode_tile")
+    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 1, "kda_decode_tile")
     # chained rows: whole K for fp16 pools, the K split for fp32
     d = B.kda_describe_launch(8, 8, 12, "f16")
     assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 4, 8 * 12 * 2)
