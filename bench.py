@@ -26,7 +26,6 @@ bandwidth probe.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -52,8 +51,10 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """The hash the committed counter summary records (decode kernel source
+    and the csrc headers it is built with)."""
+    from kda_gated_delta_decode_amd.profiling import kernel_hash as kh
+    return kh(KERNEL_SRC)
 
 
 def parse():

@@ -30,9 +30,19 @@ COPY_KERNEL = "kda_copy_probe_kernel"
 DECODE_KERNEL = "kda_decode_tile"
 
 
+# headers a kernel's code and launch shapes also come from
+KERNEL_HEADERS = ("kda_launch.h", "kda_device.h", "kda_internal.h")
+
+
 def kernel_hash(src: str = KERNEL_SRC) -> str:
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of a kernel source file and the csrc headers it is built
+    with (device helpers, launch-shape defaults): a summary taken on other
+    sources no longer describes the kernel that runs."""
+    h = hashlib.sha256()
+    for path in [src] + [os.path.join(HERE, "csrc", n) for n in KERNEL_HEADERS]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _rows(path):
@@ -119,8 +129,9 @@ def trace(args):
     lines = ["# %s" % args.title, "",
              "Command (from the repository root, `TMPDIR=/tmp`):", "", "```"]
     lines += args.command + ["```", "",
-                             "Kernel source (%s) sha256[:16] at the time: `%s`." % (
-                                 args.source, kernel_hash(os.path.join(HERE, "csrc", args.source))), "",
+                             "Kernel sources (%s with %s) sha256[:16] at the time: `%s`." % (
+                                 args.source, ", ".join(KERNEL_HEADERS),
+                                 kernel_hash(os.path.join(HERE, "csrc", args.source))), "",
                              "## rocprofv3 kernel stats (all dispatches of the run)", "",
                              "| Kernel | Calls | Average µs | Min µs | Max µs |", "|---|---|---|---|---|"]
     for r in stats:
