@@ -137,10 +137,19 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
  *                    row's column sums over K stay inside the wave (DPP and
  *                    permlane exchanges), and the waves of a workgroup run
  *                    their chains with no barrier between rows.
+ *  KDA_ROWS_MATRIX   the request's rows as one block: all 2 n column sums
+ *                    of the initial state (w0_t = S0^T (gamma_t kn_t) and
+ *                    p0_t = S0^T (gamma_t qn_t), gamma_t the decays of rows
+ *                    0..t multiplied) in one fp32 matrix-core product per
+ *                    wave, the n x n couplings of the rows, a triangular
+ *                    solve per column, then element-wise snapshots streamed
+ *                    as whole rows.  Fixed shape: 64 columns over 4 waves
+ *                    (bv and waves_per_tile must be 0 or 64 and 4).
  */
 #define KDA_ROWS_DEFAULT 0
 #define KDA_ROWS_K_SPLIT 1
 #define KDA_ROWS_WAVE_K 2
+#define KDA_ROWS_MATRIX 3
 
 /*
  * Launch options of kda_decode_step_ex.  Zero-initialise for the library's
@@ -165,10 +174,14 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
  *                  and, for fp16 pools, at least 2 waves (one wave's 128
  *                  state values and 8 x 8 x 3 column sums per lane do not
  *                  fit in the register file: refused).
- *  rows_layout     chained rows only: KDA_ROWS_DEFAULT (whole-K for fp16
- *                  pools, bv 64 over 4 waves; K split for fp32, bv 64 over 8
- *                  waves), KDA_ROWS_K_SPLIT or KDA_ROWS_WAVE_K; ignored for
- *                  one row.
+ *  rows_layout     chained rows only: KDA_ROWS_DEFAULT, KDA_ROWS_K_SPLIT,
+ *                  KDA_ROWS_WAVE_K or KDA_ROWS_MATRIX (a block form
+ *                  whatever block_rows says); ignored for one row.  The
+ *                  default: for fp16 pools the matrix-core block form, or,
+ *                  when bv or waves_per_tile is set, the whole-K layout (bv
+ *                  64 over 4 waves unless set); for fp32 pools the K split
+ *                  (bv 64 over 8 waves); block_rows alone selects the
+ *                  K-split block form.
  * Supported K-split combinations keep 2..32 key rows per lane (rows per
  * lane = 2 * lanes per row / waves).  The shape changes the order of the
  * fp32 column sums over K (so results may differ in the last bits), never
@@ -382,7 +395,7 @@ typedef struct kda_launch_desc {
   int32_t blocks;          /* workgroups launched */
   int32_t lds_bytes;       /* static LDS per workgroup */
   const char* kernel;      /* kernel symbol family name */
-  int32_t rows_layout;     /* KDA_ROWS_K_SPLIT or KDA_ROWS_WAVE_K (one row: K_SPLIT) */
+  int32_t rows_layout;     /* KDA_ROWS_K_SPLIT, _WAVE_K or _MATRIX (one row: K_SPLIT) */
 } kda_launch_desc;
 
 /* Fills *desc for (n_req, n_rows, H, dtype) under opts (NULL = defaults).

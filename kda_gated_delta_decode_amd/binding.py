@@ -42,6 +42,7 @@ KDA_MAX_ROWS = 8
 KDA_ROWS_DEFAULT = 0
 KDA_ROWS_K_SPLIT = 1
 KDA_ROWS_WAVE_K = 2
+KDA_ROWS_MATRIX = 3
 
 
 class kda_pool(ctypes.Structure):
@@ -215,7 +216,7 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
     refusals).  init_slot_ids (device int32 [n_req]) reads each request's
     initial state from that slot; block_rows takes chained rows as one block
     instead of one after the other; rows_layout picks the chained-row layout
-    (KDA_ROWS_K_SPLIT or KDA_ROWS_WAVE_K); any of these, or a non-zero
+    (KDA_ROWS_K_SPLIT, KDA_ROWS_WAVE_K or KDA_ROWS_MATRIX); any of these, or a non-zero
     waves_per_tile or bv, selects kda_decode_step_ex."""
     import torch
     P = make_pool(pool, pool_dtype)

@@ -1054,6 +1054,347 @@ __global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Chained rows as one block on the matrix cores (kda_rows_mfma_kernel<T>).
+//
+// With gamma_t = a_0 ... a_t and E_ts = a_(s+1) ... a_t (per key channel)
+// and Delta_t = beta_t u_t, a request's n rows unroll to
+//   w_t  = w0_t + sum_{s<t} C_ts Delta_s,      w0_t = S0^T (gamma_t kn_t),
+//   C_ts = sum_i kn_ti kn_si E_ts,i,           Delta_t = beta_t (v_t - w_t),
+//   o_t  = scale (p0_t + sum_{s<=t} P_ts Delta_s),   p0_t = S0^T (gamma_t qn_t),
+//   P_ts = sum_i qn_ti kn_si E_ts,i,           S_t = diag(a_t) S_(t-1) + kn_t Delta_t^T.
+// The 2n column sums are one product of the stacked weights [16 x 128]
+// (gamma_t kn_t, then gamma_t qn_t) with the initial state, a dense
+// contraction over the key channels that runs on the matrix cores
+// (v_mfma_f32_16x16x4_f32, fp32 operands and accumulation) and needs no
+// exchange between the lanes of a wave.  The n x n couplings depend only on
+// the row vectors.  After a triangular solve per column, every snapshot is
+// element-wise: no reduction and no barrier between rows, so the snapshot
+// stores stream.
+//
+// Workgroup: (request, head, 64-column half), 4 waves.  Wave w holds key
+// rows 32 w .. 32 w + 31; lane (gq = lane / 16, li = lane % 16) holds rows
+// 32 w + 8 gq + j (j < 8) and columns 4 li .. 4 li + 3 of the half.  Each
+// state load or store instruction therefore covers whole rows of the half:
+// 4 rows of 128 bytes (fp16) or 256 bytes (fp32).  In matrix-core step j,
+// the B operand B[k][n] = S[32 w + 8 k + j][4 n + e] is exactly that
+// register of lane (k, n), for each of the 4 column offsets e (4
+// accumulators), and the A operand is W[m][32 w + 8 k + j] for row m = li
+// of the stacked weights; D[m][n] accumulates the wave's share of the sums
+// over K (lane (gq, li), register r: D[4 gq + r][li]).  The four waves'
+// shares meet in LDS.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Piece4;  // 4 consecutive columns of one state row
+template <>
+struct Piece4<float> {
+  using vec = f4;
+};
+template <>
+struct Piece4<_Float16> {
+  using vec = h4;
+};
+
+constexpr int kMfmaBV = kMatrixBV;  // columns per workgroup
+constexpr int kMfmaWaves = kMatrixWaves;
+constexpr int kLdRow = kHeadK + 4;  // padded row stride of the [t][channel] LDS arrays
+
+// The couplings P_ts (s <= t) and C_ts (s < t) for the two columns s = W and
+// s = 7 - W of the n x n matrices: 16 values in all, for every W.  Lane l
+// sums over its key channels 2 l and 2 l + 1; a reduce-scatter over the wave
+// leaves each total in 4 lanes, one of which stores it.
+template <int W>
+__device__ __forceinline__ void coupling_pair(const float (*kn)[kLdRow], const float (*qn)[kLdRow],
+                                              const float (*am)[kLdRow], int lane, float (*cP)[8],
+                                              float (*cA)[8]) {
+  constexpr int S0 = W, S1 = 7 - W;
+  constexpr int N0P = 8 - S0, N0C = 7 - S0, N1P = 8 - S1;
+  const int i0 = 2 * lane;
+  float cv[16];
+  int k = 0;
+#pragma unroll
+  for (int slot = 0; slot < 2; ++slot) {
+    const int s = slot == 0 ? S0 : S1;
+    const f2 ks = *reinterpret_cast<const f2*>(&kn[s][i0]);
+    float P[8], C[8];
+    float e0 = 1.0f, e1 = 1.0f;
+#pragma unroll
+    for (int t = s; t < 8; ++t) {
+      if (t > s) {
+        const f2 at = *reinterpret_cast<const f2*>(&am[t][i0]);
+        e0 *= at[0];
+        e1 *= at[1];
+      }
+      const float f0 = ks[0] * e0, f1 = ks[1] * e1;
+      const f2 qt = *reinterpret_cast<const f2*>(&qn[t][i0]);
+      P[t] = fmaf(qt[1], f1, qt[0] * f0);
+      if (t > s) {
+        const f2 kt = *reinterpret_cast<const f2*>(&kn[t][i0]);
+        C[t] = fmaf(kt[1], f1, kt[0] * f0);
+      }
+    }
+#pragma unroll
+    for (int t = s; t < 8; ++t) cv[k++] = P[t];
+#pragma unroll
+    for (int t = s + 1; t < 8; ++t) cv[k++] = C[t];
+  }
+  float y[8], z[4], u[2], p[1];
+  rs_stage<5>(cv, y, lane);
+  rs_stage<4>(y, z, lane);
+  rs_stage<3>(z, u, lane);
+  rs_stage<2>(u, p, lane);
+  float tot = p[0];
+  tot += partner<1>(tot);
+  tot += partner<0>(tot);
+  // the value this lane holds: index 8 b2 + 4 b3 + 2 b4 + b5 of cv
+  const int idx = ((lane >> 2) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 5) & 1);
+  if ((lane & 3) == 0) {
+    if (idx < N0P)
+      cP[S0 + idx][S0] = tot;
+    else if (idx < N0P + N0C)
+      cA[S0 + 1 + (idx - N0P)][S0] = tot;
+    else if (idx < N0P + N0C + N1P)
+      cP[S1 + (idx - N0P - N0C)][S1] = tot;
+    else
+      cA[S1 + 1 + (idx - N0P - N0C - N1P)][S1] = tot;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args a) {
+  using vec = typename Piece4<T>::vec;
+  constexpr int TMAX = KDA_MAX_ROWS;
+  constexpr int NW = kMfmaWaves;
+  constexpr int BV = kMfmaBV;
+  static_assert(TMAX == 8, "the stacked weights fill the 16 rows of the matrix-core operand");
+
+  __shared__ __attribute__((aligned(16))) float s_kn[TMAX][kLdRow];
+  __shared__ __attribute__((aligned(16))) float s_qn[TMAX][kLdRow];
+  __shared__ __attribute__((aligned(16))) float s_a[TMAX][kLdRow];
+  __shared__ __attribute__((aligned(16))) float s_gam[TMAX][kLdRow];
+  __shared__ __attribute__((aligned(16))) float s_v[TMAX][BV];
+  __shared__ __attribute__((aligned(16))) float s_dl[TMAX][BV];
+  __shared__ __attribute__((aligned(16))) f4 s_part[NW][4][BV];  // [wave][gq][column] = D[4 gq + r]
+  __shared__ __attribute__((aligned(16))) float s_cP[TMAX][TMAX];
+  __shared__ __attribute__((aligned(16))) float s_cA[TMAX][TMAX];
+  __shared__ __attribute__((aligned(16))) float s_beta[TMAX];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int gq = lane / 16, li = lane % 16;
+
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int vt = tile % a.n_vt;
+  const int rh = tile / a.n_vt;
+  const int h = rh % a.H;
+  const int r = rh / a.H;
+  const int n_rows = a.n_rows;
+
+  const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
+  int32_t sid[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
+  const int32_t init_slot = *(a.init_slot_ids != nullptr ? a.init_slot_ids + r : ids);
+
+  // Row inputs: wave w normalises rows w and w + 4 (a row past the last
+  // re-reads the last one and is staged as zeros).
+  int zero_v;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
+  constexpr int TPW = TMAX / NW;
+  f2 q2[TPW], k2[TPW];
+  f4 v4[TPW];
+  float braw[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = min(wave + j * NW, n_rows - 1);
+    const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+    const int64_t off = (rho * a.H + h) * kHeadK;
+    q2[j] = reinterpret_cast<const f2*>(a.q + off)[lane];
+    k2[j] = reinterpret_cast<const f2*>(a.k + off)[lane];
+    v4[j] = *reinterpret_cast<const f4*>(a.v + off + vt * BV + 4 * (lane % (BV / 4)));
+    braw[j] = a.b[rho * a.H + h + zero_v];
+  }
+  // Decays per key channel: threads 0..127 each take one channel through all
+  // rows (the cumulative products need every row).
+  float graw[TMAX];
+  const int chan = threadIdx.x % kHeadK;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    const int tt = min(t, n_rows - 1);
+    const int64_t rho = static_cast<int64_t>(r) * n_rows + tt;
+    graw[t] = a.g[(rho * a.H + h) * kHeadK + chan];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  bool ids_ok = init_slot >= 0 && init_slot < a.n_slots;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
+
+  // The initial state: rows 32 w + 8 gq + j, columns 4 li .. 4 li + 3.
+  const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
+  const int64_t slot_elems = static_cast<int64_t>(a.H) * head_elems;
+  const int row0 = 32 * wave + 8 * gq;
+  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + vt * BV + 4 * li;
+  T* const pool = static_cast<T*>(a.pool);
+  vec raw[8];
+  {
+    const T* src = pool + static_cast<int64_t>(ids_ok ? init_slot : 0) * slot_elems + lane_off;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(src + j * kHeadV));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + j * NW;
+    const bool live = t < n_rows;
+    const float sq = wave_sum(fmaf(q2[j][1], q2[j][1], q2[j][0] * q2[j][0]));
+    const float sk = wave_sum(fmaf(k2[j][1], k2[j][1], k2[j][0] * k2[j][0]));
+    const float rq = live ? 1.0f / sqrtf(sq + 1e-6f) : 0.0f;
+    const float rk = live ? 1.0f / sqrtf(sk + 1e-6f) : 0.0f;
+    *reinterpret_cast<f2*>(&s_qn[t][2 * lane]) = f2{q2[j][0] * rq, q2[j][1] * rq};
+    *reinterpret_cast<f2*>(&s_kn[t][2 * lane]) = f2{k2[j][0] * rk, k2[j][1] * rk};
+    if (lane < BV / 4) *reinterpret_cast<f4*>(&s_v[t][4 * lane]) = live ? v4[j] : f4{0, 0, 0, 0};
+    if (lane == 0) s_beta[t] = live ? 1.0f / (1.0f + expf(-braw[j])) : 0.0f;
+  }
+  if (threadIdx.x < kHeadK) {
+    float gam = 1.0f;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const float at = t < n_rows ? expf(graw[t]) : 0.0f;
+      gam *= at;
+      s_a[t][chan] = at;
+      s_gam[t][chan] = gam;
+    }
+  }
+  if (!ids_ok) {  // uniform over the workgroup: no wave waits at the barrier
+    if (wave == 0 && lane < BV / 4) {
+      for (int t = 0; t < n_rows; ++t) {
+        const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+        *reinterpret_cast<f4*>(a.out + (rho * a.H + h) * kHeadV + vt * BV + 4 * lane) =
+            f4{NAN, NAN, NAN, NAN};
+      }
+    }
+    return;
+  }
+  __syncthreads();
+
+  // fp32 state
+  float S[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[j][e] = static_cast<float>(raw[j][e]);
+
+  // (1) the wave's share of w0 and p0 on the matrix cores, then (2) the
+  // couplings on the vector units (on MI355X the fp32 products and the
+  // vector instructions of one wave did not overlap: interleaving them
+  // measured no faster)
+  {
+    const int tw = li & 7;
+    const float* wsrc = li < 8 ? &s_kn[tw][row0] : &s_qn[tw][row0];
+    float x[8], gm[8];
+    lds_rows<8>(wsrc, x);
+    lds_rows<8>(&s_gam[tw][row0], gm);
+    f4 acc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = gm[j] * x[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(wj, S[j][e], acc[e], 0, 0, 0);
+    }
+    switch (wave) {  // wave-uniform: each wave takes two columns of the couplings
+      case 0: coupling_pair<0>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+      case 1: coupling_pair<1>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+      case 2: coupling_pair<2>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+      default: coupling_pair<3>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_part[wave][gq][4 * li + e] = acc[e];
+  }
+  __syncthreads();
+
+  // (3) per column: the totals over the waves, Delta row after row, outputs.
+  // The couplings and beta are the same for every column: each lane reads
+  // one of them (a wave-wide read of a shared address costs the LDS as much
+  // as 64 different ones) and the solve takes them with readlane.
+  // (The empty volatile asm keeps the reads in every lane: otherwise the
+  // compiler sinks them into the branch below, whose inactive lanes then
+  // never load the values that readlane takes from them.)
+  float cA_l = s_cA[lane >> 3][lane & 7];
+  float cP_l = s_cP[lane >> 3][lane & 7];
+  float bt_l = s_beta[lane & 7];
+  asm volatile("" : "+v"(cA_l), "+v"(cP_l), "+v"(bt_l));
+  if (gq == 0) {
+    const int c = 16 * wave + li;
+    f4 part[NW][4];
+    float vv[TMAX];
+#pragma unroll
+    for (int x = 0; x < NW; ++x)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) part[x][g] = s_part[x][g][c];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][c];
+    auto cA = [&](int t, int s2) { return __builtin_amdgcn_readlane(__float_as_int(cA_l), 8 * t + s2); };
+    auto cP = [&](int t, int s2) { return __builtin_amdgcn_readlane(__float_as_int(cP_l), 8 * t + s2); };
+    float tot[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tot[4 * g + e] = (part[0][g][e] + part[1][g][e]) + (part[2][g][e] + part[3][g][e]);
+    float dl[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      float d = vv[t] - tot[t];
+#pragma unroll
+      for (int s2 = 0; s2 < t; ++s2) d = fmaf(-__int_as_float(cA(t, s2)), dl[s2], d);
+      dl[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt_l), t)) * d;
+    }
+    // rows past n are zero throughout (their weights, v and beta are
+    // staged as zeros); only the stores are predicated
+    float* op = a.out + (static_cast<int64_t>(r) * n_rows * a.H + h) * kHeadV + vt * BV + c;
+    const int64_t o_row = static_cast<int64_t>(a.H) * kHeadV;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      float o = tot[8 + t];
+#pragma unroll
+      for (int s2 = 0; s2 <= t; ++s2) o = fmaf(__int_as_float(cP(t, s2)), dl[s2], o);
+      if (t < n_rows) {
+        s_dl[t][c] = dl[t];
+        op[t * o_row] = a.scale * o;
+      }
+    }
+  }
+  __syncthreads();
+
+  // (4) the snapshots, element-wise
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if (t >= n_rows) break;
+    float kn[8], am[8], dl[4];
+    lds_rows<8>(&s_kn[t][row0], kn);
+    lds_rows<8>(&s_a[t][row0], am);
+    lds_rows<4>(&s_dl[t][4 * li], dl);
+    T* dst = pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      vec o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s1 = fmaf(kn[j], dl[e], am[j] * S[j][e]);
+        asm("" : "+v"(s1));  // a rounded fp32 value before any narrowing
+        S[j][e] = s1;
+        o[e] = static_cast<T>(s1);
+      }
+      __builtin_nontemporal_store(o, reinterpret_cast<vec*>(dst + j * kHeadV));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming copy used to calibrate bandwidth and byte counters: one 16-byte
 // vector per thread, consecutive threads on consecutive vectors (the copy
 // form that measured fastest on MI355X, ahead of grid-stride loops).
@@ -1156,6 +1497,10 @@ static hipError_t dispatch_rows(const Args& a, const Shape& sh, int32_t blocks, 
 template <typename T>
 static hipError_t dispatch(const Args& a, const Shape& sh, int32_t blocks, hipStream_t s) {
   if (sh.layout == KDA_ROWS_WAVE_K) return dispatch_rows<T>(a, sh, blocks, s);
+  if (sh.layout == KDA_ROWS_MATRIX) {
+    hipLaunchKernelGGL((kda_rows_mfma_kernel<T>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s, a);
+    return hipGetLastError();
+  }
   const int lpr = sh.bv / Lane16<T>::kCols;
   switch (lpr * 16 + sh.nw) {
     case 8 * 16 + 1: return launch_tile<T, 8, 1>(a, blocks, s);

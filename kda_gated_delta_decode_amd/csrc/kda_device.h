@@ -11,6 +11,7 @@ namespace kda {
 
 using f2 = float __attribute__((ext_vector_type(2)));
 using f4 = float __attribute__((ext_vector_type(4)));
+using h4 = _Float16 __attribute__((ext_vector_type(4)));
 using h8 = _Float16 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------

@@ -135,7 +135,9 @@ int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtyp
   desc->tiles = static_cast<int32_t>(tiles);
   desc->blocks = static_cast<int32_t>(tiles);
   desc->lds_bytes = lds_bytes(bv, nw, n_rows, opts != nullptr && opts->block_rows != 0, shape.layout);
-  desc->kernel = shape.layout == KDA_ROWS_WAVE_K ? "kda_rows_kernel" : "kda_decode_tile";
+  desc->kernel = shape.layout == KDA_ROWS_WAVE_K   ? "kda_rows_kernel"
+                 : shape.layout == KDA_ROWS_MATRIX ? "kda_rows_mfma_kernel"
+                                                   : "kda_decode_tile";
   desc->rows_layout = shape.layout;
   return KDA_OK;
 }

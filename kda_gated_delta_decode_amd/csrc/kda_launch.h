@@ -77,15 +77,24 @@ inline bool wave_k_supported(kda_dtype dt, int32_t bv, int32_t nw) {
   return lpr == 2 || lpr == 4;
 }
 
-// The chained-row default layout and shape, chosen by measurement on MI355X
-// (8 requests x 8 rows x 12 heads, graph-replayed launches, 1 GiB of
-// rotating pools): fp16 pools take the whole-K layout with 64-column
-// workgroups of 4 waves (11.0-11.6 us against 12.3 us for the K split);
-// fp32 pools keep the K split (11.5 us; the whole-K layout's best was 13.4
-// us: its 4 lanes per row piece write 64-byte pieces, the fp16 shape's 2
-// lanes 32-byte pieces of twice as many rows).
-inline int32_t default_rows_layout(kda_dtype dt) {
-  return dt == KDA_F16 ? KDA_ROWS_WAVE_K : KDA_ROWS_K_SPLIT;
+// The chained-row layout of a launch.  An explicit rows_layout wins; the
+// block_rows option alone means the K-split block form.  Otherwise, chosen by
+// measurement on MI355X (8 requests x 8 rows x 12 heads, graph-replayed
+// launches, 1 GiB of rotating pools): fp16 pools take the matrix-core block
+// form (9.9 us, against 11.8 us row after row with the whole of K in each
+// wave and 12.3 us with K split) unless a bv or waves option asks for a
+// row-after-row shape (then the whole-K layout, as before the block form
+// existed); fp32 pools keep the K split (11.5-11.6 us; the block form 14.1
+// us: its twice larger snapshot stores start only after the column sums,
+// the couplings and the solve, while the row-after-row chain stores from its
+// first row on).
+inline int32_t chained_rows_layout(kda_dtype dt, const kda_launch_opts* opts) {
+  const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
+  if (asked != KDA_ROWS_DEFAULT) return asked;
+  if (opts != nullptr && opts->block_rows != 0) return KDA_ROWS_K_SPLIT;
+  const bool shaped = opts != nullptr && (opts->bv != 0 || opts->waves_per_tile != 0);
+  if (dt == KDA_F16) return shaped ? KDA_ROWS_WAVE_K : KDA_ROWS_MATRIX;
+  return KDA_ROWS_K_SPLIT;
 }
 inline int32_t default_wave_k_bv(kda_dtype /*dt*/) { return 64; }
 inline int32_t default_wave_k_waves(kda_dtype /*dt*/) { return 4; }
@@ -93,25 +102,32 @@ inline int32_t default_wave_k_waves(kda_dtype /*dt*/) { return 4; }
 // The chained-rows block form: fp16 pools need at least 2 waves per tile.
 inline bool block_supported(kda_dtype dt, int32_t nw) { return dt != KDA_F16 || nw > 1; }
 
+// The matrix-core block form of chained rows: one shape.
+constexpr int32_t kMatrixBV = 64;
+constexpr int32_t kMatrixWaves = 4;
+
 struct Shape {
   int32_t bv;      // value columns per workgroup
   int32_t nw;      // waves per workgroup
-  int32_t layout;  // KDA_ROWS_K_SPLIT (also every single-row launch) or KDA_ROWS_WAVE_K
+  int32_t layout;  // KDA_ROWS_K_SPLIT (also every single-row launch), _WAVE_K or _MATRIX
 };
 
 // The shape a launch uses: each option field that is set overrides the
 // default.  Returns false if the result is not an instantiated shape.
 inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts, Shape* out) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
-  if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_WAVE_K) return false;
-  int32_t layout = KDA_ROWS_K_SPLIT;
-  if (n_rows > 1) {
-    if (opts != nullptr && opts->block_rows != 0) {
-      if (asked == KDA_ROWS_WAVE_K) return false;  // the block form is a K-split kernel
-    } else {
-      layout = asked != KDA_ROWS_DEFAULT ? asked : default_rows_layout(dt);
-    }
+  if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX) return false;
+  const int32_t layout = n_rows > 1 ? chained_rows_layout(dt, opts) : KDA_ROWS_K_SPLIT;
+  if (layout == KDA_ROWS_MATRIX) {
+    // one fixed shape: 64 columns over 4 waves; a block form whatever
+    // block_rows says
+    const bool bv_ok = opts == nullptr || opts->bv == 0 || opts->bv == kMatrixBV;
+    const bool nw_ok = opts == nullptr || opts->waves_per_tile == 0 || opts->waves_per_tile == kMatrixWaves;
+    *out = Shape{kMatrixBV, kMatrixWaves, KDA_ROWS_MATRIX};
+    return bv_ok && nw_ok;
   }
+  // the K-split block form
+  if (n_rows > 1 && opts != nullptr && opts->block_rows != 0 && layout == KDA_ROWS_WAVE_K) return false;
   Shape s{default_bv(dt, n_rows), default_waves_per_tile(dt, n_rows), layout};
   if (layout == KDA_ROWS_WAVE_K) {
     s.bv = default_wave_k_bv(dt);
@@ -138,6 +154,12 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* o
 // [2][nw][2][bv] (nw > 1); as a block, [nw][2 KDA_MAX_ROWS][bv] (nw > 1)
 // and the two coupling matrices [KDA_MAX_ROWS][KDA_MAX_ROWS].
 inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block, int32_t layout) {
+  if (layout == KDA_ROWS_MATRIX) {
+    // kn, qn, decays, cumulative decays [8][132]; v and Delta [8][bv]; the
+    // waves' partial sums [nw][16][bv]; two 8 x 8 couplings; beta
+    constexpr int32_t t = KDA_MAX_ROWS;
+    return 4 * (4 * t * (kHeadK + 4) + 2 * t * bv + nw * 16 * bv + 2 * t * t + t);
+  }
   const int32_t tmax = n_rows == 1 ? 1 : KDA_MAX_ROWS;
   const int32_t staged = tmax * (3 * kHeadK + bv + 2);
   if (layout == KDA_ROWS_WAVE_K) return 4 * staged;

@@ -81,13 +81,16 @@ def test_refusals_before_any_hip_call():
     assert step(pool(dtype=B.KDA_F16), opts=B.kda_launch_opts(1, 128)) == B.KDA_ERR_ARG  # spills
     # chained-row layouts: an unknown layout, the block form in the whole-K
     # layout, a whole-K shape with 1 lane per row piece or 1 wave
-    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, 3)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, 4)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, -1)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 1, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
     # the block form with one wave is refused for fp16 pools (it would spill)
     assert step(pool(dtype=B.KDA_F16), n_rows=8, opts=B.kda_launch_opts(1, 64, 1)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(4, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(1, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
+    # the matrix-core block form has one shape: 64 columns over 4 waves
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 32, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(8, 0, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
     assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE]) == B.KDA_ERR_ALIGN
@@ -265,10 +268,15 @@ def test_describe_launch():
     # one row: the layout option is ignored
     d = B.kda_describe_launch(64, 1, 12, "f16", rows_layout=B.KDA_ROWS_WAVE_K)
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 1, "kda_decode_tile")
-    # chained rows: whole K for fp16 pools, the K split for fp32
+    # chained rows: the matrix-core block form for fp16 pools (the whole-K
+    # layout when a shape option is set), the K split for fp32
     d = B.kda_describe_launch(8, 8, 12, "f16")
     assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 4, 8 * 12 * 2)
-    assert (d["kernel"], d["rows_layout"]) == ("kda_rows_kernel", B.KDA_ROWS_WAVE_K)
+    assert (d["kernel"], d["rows_layout"]) == ("kda_rows_mfma_kernel", B.KDA_ROWS_MATRIX)
+    d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=2)
+    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 2, "kda_rows_kernel")
+    d = B.kda_describe_launch(8, 8, 12, "f16", bv=128)
+    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (128, 4, "kda_rows_kernel")
     d = B.kda_describe_launch(8, 8, 12, "f32")
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 8, "kda_decode_tile")
     d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8, rows_layout=B.KDA_ROWS_K_SPLIT)
@@ -282,6 +290,20 @@ def test_describe_launch():
         B.kda_describe_launch(8, 8, 12, "f16", block_rows=True, waves_per_tile=1, bv=64)
     d = B.kda_describe_launch(8, 8, 12, "f16", block_rows=True, waves_per_tile=2, bv=64)
     assert (d["bv"], d["waves_per_tile"]) == (64, 2)
+    # the matrix-core block form: one shape, either dtype, block_rows implied
+    for dt in ("f32", "f16"):
+        for blk in (False, True):
+            d = B.kda_describe_launch(8, 8, 12, dt, rows_layout=B.KDA_ROWS_MATRIX, block_rows=blk)
+            assert (d["bv"], d["waves_per_tile"], d["threads"], d["tiles"]) == (64, 4, 256, 8 * 12 * 2)
+            assert (d["kernel"], d["rows_layout"]) == ("kda_rows_mfma_kernel", B.KDA_ROWS_MATRIX)
+    d = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX, waves_per_tile=4, bv=64)
+    assert (d["bv"], d["waves_per_tile"]) == (64, 4)
+    for w, bv in ((2, 0), (0, 128)):
+        with pytest.raises(B.KdaError):
+            B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX, waves_per_tile=w, bv=bv)
+    # one row: the layout option is ignored
+    d = B.kda_describe_launch(64, 1, 12, "f32", rows_layout=B.KDA_ROWS_MATRIX)
+    assert d["kernel"] == "kda_decode_tile"
     with pytest.raises(B.KdaError):
         B.kda_describe_launch(8, 9, 12, "f16")
     with pytest.raises(B.KdaError):

@@ -138,6 +138,23 @@ def test_default_single_row_tiles_keep_two_waves_per_simd(kernels):
         assert k[".vgpr_count"] + k.get(".agpr_count", 0) <= 256, (name, k[".vgpr_count"])
 
 
+def test_matrix_block_form_lds_matches_the_launch_description(kernels):
+    # the host's LDS figure for the matrix-core block form is the kernel's
+    # static LDS, for both pool dtypes
+    import kda_gated_delta_decode_amd.binding as B
+    want = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX)["lds_bytes"]
+    for name in ("_ZN3kda20kda_rows_mfma_kernelIfEEvNS_4ArgsE",
+                 "_ZN3kda20kda_rows_mfma_kernelIDF16_EEvNS_4ArgsE"):
+        assert kernels[name][".group_segment_fixed_size"] == want, name
+
+
+def test_matrix_block_form_runs_its_column_sums_on_the_matrix_cores(disassembly):
+    # 8 steps of 4 rows x 4 column offsets: 32 fp32 16x16x4 products per wave
+    for name in ("_ZN3kda20kda_rows_mfma_kernelIfEEvNS_4ArgsE",
+                 "_ZN3kda20kda_rows_mfma_kernelIDF16_EEvNS_4ArgsE"):
+        assert disassembly[name].count("v_mfma_f32_16x16x4_f32") == 32, name
+
+
 def test_fp16_state_is_narrowed_to_nearest_even(disassembly):
     f16 = {n: ops for n, ops in disassembly.items() if "kda" in n and "DF16_" in n}
     assert len(f16) >= 30

@@ -1,0 +1,183 @@
+"""GPU parity of the matrix-core block form of chained rows
+(KDA_ROWS_MATRIX, kda_rows_mfma_kernel) against the CPU oracle.
+
+The block form computes the same recurrence as the token-by-token oracle,
+reassociated: the column sums of every row come from one product of the
+initial state with the stacked weights gamma_t kn_t, gamma_t qn_t (fp32 on
+the matrix cores), the n x n couplings and a triangular solve per column.
+It is graded with the decode bounds (fp32: 1e-6 abs state against the fp32
+and fp64 oracles, 1e-5 relative output; fp16: 1 ulp of the oracle's RNE
+state).  Cases: the 8 x 8 fp16 workload and its fp32 pool at full size,
+every row count 2..8, ragged small shapes, the fp16/fp32 twin (same
+arithmetic on the exactly widened state: outputs bit-equal, fp16 snapshots
+the RNE of the fp32 ones), initial states from other slots, an out-of-range
+slot id, the identity gate, strong decays whose cumulative products
+underflow, zero q and k.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import kda_inputs
+from gpu_helpers import (B, F16_ULP, OUT_REL, STATE_ABS_F32, check_parity, device_inputs,
+                         f16_ulp_distance, need_gpu, out_rel_err, pool_to_host, run_gpu, torch)
+
+pytestmark = pytest.mark.gpu
+
+MATRIX = dict(rows_layout=B.KDA_ROWS_MATRIX)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_full_size_spec_verify(oracle, dtype):
+    inp = kda_inputs.make_inputs("matrix 8x8", 96, 8, 8, dtype, seed=0)
+    say("matrix block form, 8 req x 8 rows, H=12,", dtype)
+    gp, go = run_gpu(inp, **MATRIX)
+    say(check_parity(oracle, inp, gp, go, label="matrix 8x8 %s" % dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("n_rows", [2, 3, 4, 5, 6, 7, 8])
+def test_every_row_count(oracle, dtype, n_rows):
+    inp = kda_inputs.make_inputs("matrix rows", 40, 40 // n_rows, n_rows, dtype, H=3,
+                                 seed=300 + n_rows)
+    gp, go = run_gpu(inp, **MATRIX)
+    check_parity(oracle, inp, gp, go, label="matrix %s n=%d" % (dtype, n_rows))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("n_req,H,n_rows", [(1, 1, 8), (3, 2, 3), (2, 5, 8), (4, 3, 7), (2, 3, 2),
+                                            (5, 1, 4)])
+def test_small_shapes(oracle, dtype, n_req, H, n_rows):
+    n_slots = n_req * n_rows + 3
+    inp = kda_inputs.make_inputs("matrix small", n_slots, n_req, n_rows, dtype, H=H,
+                                 seed=3000 + 7 * n_req + 31 * H + n_rows)
+    gp, go = run_gpu(inp, **MATRIX)
+    check_parity(oracle, inp, gp, go, label="matrix small %s %dx%dx%d" % (dtype, n_req, H, n_rows))
+
+
+@pytest.mark.parametrize("n_rows", [2, 8])
+def test_fp32_twin_of_fp16_launch(n_rows):
+    """One kernel template for both pools: on the exactly widened state the
+    fp32 arithmetic is identical, so outputs are bit-equal and every fp16
+    snapshot is the RNE of the fp32 one."""
+    inp16 = kda_inputs.make_inputs("twin matrix", 96, 64 // n_rows, n_rows, "f16", seed=26 + n_rows)
+    inp32 = kda_inputs.DecodeInputs("twin32", "f32", inp16.pool.view(np.float16).astype(np.float32),
+                                    inp16.slot_ids, inp16.q, inp16.k, inp16.v, inp16.g, inp16.b,
+                                    n_rows, inp16.scale)
+    p16, o16 = run_gpu(inp16, **MATRIX)
+    p32, o32 = run_gpu(inp32, **MATRIX)
+    np.testing.assert_array_equal(o16.view(np.uint32), o32.view(np.uint32))
+    np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_agrees_with_the_other_layouts(dtype):
+    """The same launch in the row-after-row layouts: every result within
+    rounding (fp32 state 1e-6, fp16 1 ulp, outputs 1e-5)."""
+    inp = kda_inputs.make_inputs("layouts", 96, 8, 8, dtype, seed=44)
+    gm, om = run_gpu(inp, **MATRIX)
+    for layout in (B.KDA_ROWS_K_SPLIT, B.KDA_ROWS_WAVE_K):
+        gp, go = run_gpu(inp, rows_layout=layout)
+        if dtype == "f32":
+            assert np.max(np.abs(gp - gm)) <= STATE_ABS_F32
+        else:
+            assert f16_ulp_distance(gp, gm).max() <= F16_ULP
+        assert out_rel_err(go, om) <= OUT_REL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_initial_state_from_other_slots(oracle, dtype):
+    n_req, n_rows = 8, 8
+    inp = kda_inputs.make_inputs("matrix init", 128, n_req, n_rows, dtype, seed=62)
+    free = np.setdiff1d(np.arange(128), inp.slot_ids)
+    init = np.random.default_rng(3).permutation(free)[:n_req].astype(np.int32)
+    pool, ids, t, out = device_inputs(inp)
+    B.kda_decode_step(pool, ids, t["q"], t["k"], t["v"], t["g"], t["b"], out, n_rows_per_slot=n_rows,
+                      scale=inp.scale, init_slot_ids=torch.from_numpy(init).cuda(), **MATRIX)
+    torch.cuda.synchronize()
+    gp, go = pool_to_host(pool), out.cpu().numpy()
+    op = inp.pool.copy()
+    oo = oracle.step_f32(op, inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b, n_rows=n_rows,
+                         scale=inp.scale, init_slot_ids=init)
+    if dtype == "f32":
+        assert np.max(np.abs(gp - op)) <= STATE_ABS_F32
+    else:
+        assert f16_ulp_distance(gp, op).max() <= F16_ULP
+    assert out_rel_err(go, oo) <= OUT_REL
+    np.testing.assert_array_equal(gp[init], inp.pool[init])   # initial slots only read
+
+
+def test_out_of_range_slot_is_skipped(oracle):
+    n_req, n_rows = 3, 4
+    inp = kda_inputs.make_inputs("matrix bad id", 16, n_req, n_rows, "f16", H=2, seed=8)
+    ids = inp.slot_ids.copy()
+    ids[1 * n_rows + 2] = 16  # one past the end, request 1
+    pool, dids, t, out = device_inputs(inp)
+    dids.copy_(torch.from_numpy(ids))
+    before = pool_to_host(pool).copy()
+    B.kda_decode_step(pool, dids, t["q"], t["k"], t["v"], t["g"], t["b"], out,
+                      n_rows_per_slot=n_rows, **MATRIX)
+    torch.cuda.synchronize()
+    after, o = pool_to_host(pool), out.cpu().numpy()
+    bad = slice(n_rows, 2 * n_rows)
+    assert np.all(np.isnan(o[bad]))
+    np.testing.assert_array_equal(after[inp.slot_ids[bad]], before[inp.slot_ids[bad]])
+    good = np.r_[0:n_rows, 2 * n_rows:3 * n_rows]
+    sub = kda_inputs.DecodeInputs("good", "f16", inp.pool.copy(), inp.slot_ids[good], inp.q[good],
+                                  inp.k[good], inp.v[good], inp.g[good], inp.b[good], n_rows,
+                                  inp.scale)
+    op = sub.pool.copy()
+    oo = oracle.step_f32(op, sub.slot_ids, sub.q, sub.k, sub.v, sub.g, sub.b, n_rows=n_rows,
+                         scale=sub.scale)
+    assert out_rel_err(o[good], oo) <= OUT_REL
+    assert f16_ulp_distance(after[sub.slot_ids], op[sub.slot_ids]).max() <= F16_ULP
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_identity_gate_keeps_state_bits(oracle, dtype):
+    # a = 1 and beta = 0 exactly: Delta = 0, every snapshot equals S0
+    inp = kda_inputs.make_inputs("matrix identity", 24, 3, 8, dtype, seed=12)
+    inp.g[:] = 0.0
+    inp.b[:] = -1e4
+    gp, go = run_gpu(inp, **MATRIX)
+    as_float = (lambda x: x) if dtype == "f32" else (lambda x: x.view(np.float16))
+    for r in range(3):
+        s0 = inp.slot_ids[r * 8]
+        for t in range(8):
+            assert np.array_equal(as_float(gp[inp.slot_ids[r * 8 + t]]), as_float(inp.pool[s0]))
+    check_parity(oracle, inp, gp, go, label="matrix identity")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_strong_decays_underflow_cleanly(oracle, dtype):
+    """Log-decays down to -60 per row: the cumulative products gamma_t and
+    E_ts underflow to zero (no division, so no inf or NaN) and the results
+    stay within the bounds."""
+    inp = kda_inputs.make_inputs("matrix strong decay", 40, 5, 8, dtype, H=3, seed=71)
+    rng = np.random.default_rng(72)
+    strong = rng.random(inp.g.shape) < 0.3
+    inp.g[strong] = -rng.uniform(20.0, 60.0, size=int(strong.sum())).astype(np.float32)
+    gp, go = run_gpu(inp, **MATRIX)
+    assert np.all(np.isfinite(go))
+    check_parity(oracle, inp, gp, go, label="matrix strong decay %s" % dtype)
+
+
+def test_zero_q_and_k_stay_finite(oracle):
+    inp = kda_inputs.make_inputs("matrix zero qk", 40, 5, 8, "f32", H=2, seed=73)
+    inp.q[3] = 0.0
+    inp.k[3] = 0.0
+    inp.k[10, 1] = 0.0
+    gp, go = run_gpu(inp, **MATRIX)
+    assert np.all(np.isfinite(gp)) and np.all(np.isfinite(go))
+    check_parity(oracle, inp, gp, go, label="matrix zero qk")
