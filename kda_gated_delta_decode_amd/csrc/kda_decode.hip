@@ -1172,7 +1172,6 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   __shared__ __attribute__((aligned(16))) float s_a[TMAX][kLdRow];
   __shared__ __attribute__((aligned(16))) float s_gam[TMAX][kLdRow];
   __shared__ __attribute__((aligned(16))) float s_v[TMAX][BV];
-  __shared__ __attribute__((aligned(16))) float s_dl[TMAX][BV];
   __shared__ __attribute__((aligned(16))) f4 s_part[NW][4][BV];  // [wave][gq][column] = D[4 gq + r]
   __shared__ __attribute__((aligned(16))) float s_cP[TMAX][TMAX];
   __shared__ __attribute__((aligned(16))) float s_cA[TMAX][TMAX];
@@ -1316,75 +1315,65 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   }
   __syncthreads();
 
-  // (3) per column: the totals over the waves, Delta row after row, outputs.
-  // The couplings and beta are the same for every column: each lane reads
-  // one of them (a wave-wide read of a shared address costs the LDS as much
-  // as 64 different ones) and the solve takes them with readlane.
-  // (The empty volatile asm keeps the reads in every lane: otherwise the
-  // compiler sinks them into the branch below, whose inactive lanes then
-  // never load the values that readlane takes from them.)
+  // (3) and (4): every wave solves all 64 columns (lane l: column l) and
+  // writes row t's snapshot as soon as Delta_t is known, so the snapshot
+  // stores begin after the first step of the solve.  The couplings and beta
+  // are the same for every column: each lane reads one of them and the
+  // solve takes them with readlane.  (The empty volatile asm keeps those
+  // reads in every lane; a read sunk into a branch that only some lanes take
+  // would leave the others' registers unloaded.)
   float cA_l = s_cA[lane >> 3][lane & 7];
   float cP_l = s_cP[lane >> 3][lane & 7];
   float bt_l = s_beta[lane & 7];
   asm volatile("" : "+v"(cA_l), "+v"(cP_l), "+v"(bt_l));
-  if (gq == 0) {
-    const int c = 16 * wave + li;
+  auto cA = [&](int t, int s2) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cA_l), 8 * t + s2)); };
+  auto cP = [&](int t, int s2) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cP_l), 8 * t + s2)); };
+  float tot[16], vv[TMAX];
+  {
     f4 part[NW][4];
-    float vv[TMAX];
 #pragma unroll
     for (int x = 0; x < NW; ++x)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) part[x][g] = s_part[x][g][c];
+      for (int g = 0; g < 4; ++g) part[x][g] = s_part[x][g][lane];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][c];
-    auto cA = [&](int t, int s2) { return __builtin_amdgcn_readlane(__float_as_int(cA_l), 8 * t + s2); };
-    auto cP = [&](int t, int s2) { return __builtin_amdgcn_readlane(__float_as_int(cP_l), 8 * t + s2); };
-    float tot[16];
+    for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][lane];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         tot[4 * g + e] = (part[0][g][e] + part[1][g][e]) + (part[2][g][e] + part[3][g][e]);
-    float dl[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      float d = vv[t] - tot[t];
-#pragma unroll
-      for (int s2 = 0; s2 < t; ++s2) d = fmaf(-__int_as_float(cA(t, s2)), dl[s2], d);
-      dl[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt_l), t)) * d;
-    }
-    // rows past n are zero throughout (their weights, v and beta are
-    // staged as zeros); only the stores are predicated
-    float* op = a.out + (static_cast<int64_t>(r) * n_rows * a.H + h) * kHeadV + vt * BV + c;
-    const int64_t o_row = static_cast<int64_t>(a.H) * kHeadV;
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      float o = tot[8 + t];
-#pragma unroll
-      for (int s2 = 0; s2 <= t; ++s2) o = fmaf(__int_as_float(cP(t, s2)), dl[s2], o);
-      if (t < n_rows) {
-        s_dl[t][c] = dl[t];
-        op[t * o_row] = a.scale * o;
-      }
-    }
   }
-  __syncthreads();
-
-  // (4) the snapshots, element-wise
+  float* op = a.out + (static_cast<int64_t>(r) * n_rows * a.H + h) * kHeadV + vt * BV + lane;
+  const int64_t o_row = static_cast<int64_t>(a.H) * kHeadV;
+  float dl[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
     if (t >= n_rows) break;
-    float kn[8], am[8], dl[4];
+    float d = vv[t] - tot[t];
+#pragma unroll
+    for (int s2 = 0; s2 < t; ++s2) d = fmaf(-cA(t, s2), dl[s2], d);
+    dl[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt_l), t)) * d;
+    if ((t & 3) == wave) {  // this wave writes row t's outputs
+      float o = tot[8 + t];
+#pragma unroll
+      for (int s2 = 0; s2 <= t; ++s2) o = fmaf(cP(t, s2), dl[s2], o);
+      op[t * o_row] = a.scale * o;
+    }
+    // Delta_t of the lane's snapshot columns 4 li .. 4 li + 3
+    float dc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dc[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * li + e), __float_as_int(dl[t])));
+    float kn[8], am[8];
     lds_rows<8>(&s_kn[t][row0], kn);
     lds_rows<8>(&s_a[t][row0], am);
-    lds_rows<4>(&s_dl[t][4 * li], dl);
     T* dst = pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       vec o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float s1 = fmaf(kn[j], dl[e], am[j] * S[j][e]);
+        float s1 = fmaf(kn[j], dc[e], am[j] * S[j][e]);
         asm("" : "+v"(s1));  // a rounded fp32 value before any narrowing
         S[j][e] = s1;
         o[e] = static_cast<T>(s1);

@@ -81,13 +81,13 @@ inline bool wave_k_supported(kda_dtype dt, int32_t bv, int32_t nw) {
 // block_rows option alone means the K-split block form.  Otherwise, chosen by
 // measurement on MI355X (8 requests x 8 rows x 12 heads, graph-replayed
 // launches, 1 GiB of rotating pools): fp16 pools take the matrix-core block
-// form (9.9 us, against 11.8 us row after row with the whole of K in each
+// form (8.95 us, against 11.8 us row after row with the whole of K in each
 // wave and 12.3 us with K split) unless a bv or waves option asks for a
 // row-after-row shape (then the whole-K layout, as before the block form
-// existed); fp32 pools keep the K split (11.5-11.6 us; the block form 14.1
-// us: its twice larger snapshot stores start only after the column sums,
-// the couplings and the solve, while the row-after-row chain stores from its
-// first row on).
+// existed); fp32 pools keep the K split (11.5-11.6 us; the block form 13.3
+// us: its twice larger snapshot stores start only after the column sums
+// and the couplings, while the row-after-row chain stores from its first row
+// on).
 inline int32_t chained_rows_layout(kda_dtype dt, const kda_launch_opts* opts) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked != KDA_ROWS_DEFAULT) return asked;
@@ -155,10 +155,10 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* o
 // and the two coupling matrices [KDA_MAX_ROWS][KDA_MAX_ROWS].
 inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block, int32_t layout) {
   if (layout == KDA_ROWS_MATRIX) {
-    // kn, qn, decays, cumulative decays [8][132]; v and Delta [8][bv]; the
-    // waves' partial sums [nw][16][bv]; two 8 x 8 couplings; beta
+    // kn, qn, decays, cumulative decays [8][132]; v [8][bv]; the waves'
+    // partial sums [nw][16][bv]; two 8 x 8 couplings; beta
     constexpr int32_t t = KDA_MAX_ROWS;
-    return 4 * (4 * t * (kHeadK + 4) + 2 * t * bv + nw * 16 * bv + 2 * t * t + t);
+    return 4 * (4 * t * (kHeadK + 4) + t * bv + nw * 16 * bv + 2 * t * t + t);
   }
   const int32_t tmax = n_rows == 1 ? 1 : KDA_MAX_ROWS;
   const int32_t staged = tmax * (3 * kHeadK + bv + 2);
