@@ -385,7 +385,7 @@ def summarize(inp, tt):
             "frac_of_peak": round(ab / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
-def fused_conv(n_req, n_rows, dtype, B, torch, steps):
+def fused_conv(n_req, n_rows, dtype, B, torch, steps, **launch):
     """Time the decode step with the short convolution fused in front
     (kda_decode_step_conv) on a 96-slot pool; state pools and conv pools both
     rotate over >= 1 GiB.  Algorithmic bytes add to the plain step's the raw
@@ -403,7 +403,7 @@ def fused_conv(n_req, n_rows, dtype, B, torch, steps):
 
     def step(i):
         B.kda_decode_step_conv(w.pools[i % len(w.pools)], convs[i % len(convs)], w.ids, x, cw,
-                               w.g, w.b, w.out, n_rows_per_slot=n_rows, scale=inp.scale)
+                               w.g, w.b, w.out, n_rows_per_slot=n_rows, scale=inp.scale, **launch)
     tt = time_launches(step, steps, 10, torch)
     R, H = inp.slot_ids.size, inp.pool.shape[1]
     hist = 3 * 3 * H * 128 * 2

@@ -259,7 +259,12 @@ typedef struct kda_conv_pool {
  * then the decode update.  Row t's snapshot slot receives both the state and
  * the history after row t (its last 3 raw inputs, rounded to bfloat16 to
  * nearest even); rows of one launch use their fp32 inputs directly.
- * Launch shapes: whole heads only (opts->bv 0 or 128; waves 2, 4 or 8).
+ * Launch shapes: whole heads only (opts->bv 0 or 128).  Chained rows take
+ * the matrix-core block form (KDA_ROWS_MATRIX: 8 waves, two 64-column
+ * halves) when rows_layout asks for it, or by default for fp16 pools unless
+ * waves_per_tile or block_rows is set; otherwise the K-split kernel with 2,
+ * 4 or 8 waves.  KDA_ROWS_WAVE_K is refused; rows_layout is ignored for one
+ * row.
  * Errors: as kda_decode_step_ex, plus KDA_ERR_NULL for a missing conv pool,
  * x or conv_w, KDA_ERR_SHAPE if the pools' n_slots or H differ.
  */

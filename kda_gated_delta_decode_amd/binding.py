@@ -262,7 +262,7 @@ def make_conv_pool(conv) -> kda_conv_pool:
 def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot: int = 1,
                          state_dtype=None, scale: float | None = None, stream=None,
                          init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0,
-                         block_rows: bool = False) -> None:
+                         block_rows: bool = False, rows_layout: int = 0) -> None:
     """Decode step with the short causal convolution fused in front (see
     kda_decode_step_conv in include/kda_decode.h).  conv: bfloat16 history
     [n_slots, 3, 3, H, 128]; x: fp32 raw q|k|v [R, 3, H, 128]; conv_w: fp32
@@ -282,7 +282,7 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
                        (g, "g", R * H * KDA_HEAD_K), (out, "out", R * H * KDA_HEAD_K),
                        (b, "b", R * H), (init_slot_ids, "init_slot_ids", n_req)):
         _need_numel(t, name, n)
-    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)))
+    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout))
     rc = library().kda_decode_step_conv(
         ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32),
         _dev(init_slot_ids, "init_slot_ids", torch.int32), _dev(x, "x", torch.float32),

@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Chained rows as one block on the matrix cores (kda_rows_mfma_kernel<T>).
+// Chained rows as one block on the matrix cores (kda_rows_mfma_kernel<T, CONV>).
 //
 // With gamma_t = a_0 ... a_t and E_ts = a_(s+1) ... a_t (per key channel)
 // and Delta_t = beta_t u_t, a request's n rows unroll to
@@ -1159,12 +1159,18 @@ __device__ __forceinline__ void coupling_pair(const float (*kn)[kLdRow], const f
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args a) {
+// CONV fuses the short convolution in front (as kda_decode_tile's CONV
+// variant does): a workgroup then takes a whole head, two 64-column halves of
+// 4 waves each, so that the convolution history it reads at the initial slot
+// and rewrites at the rows' slots belongs to no other workgroup.
+template <typename T, bool CONV>
+__global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_mfma_kernel(Args a) {
   using vec = typename Piece4<T>::vec;
   constexpr int TMAX = KDA_MAX_ROWS;
-  constexpr int NW = kMfmaWaves;
-  constexpr int BV = kMfmaBV;
+  constexpr int HALVES = CONV ? 2 : 1;        // 64-column halves per workgroup
+  constexpr int NW = kMfmaWaves * HALVES;
+  constexpr int BH = kMfmaBV;                 // columns per half
+  constexpr int BV = BH * HALVES;             // columns per workgroup
   static_assert(TMAX == 8, "the stacked weights fill the 16 rows of the matrix-core operand");
 
   __shared__ __attribute__((aligned(16))) float s_kn[TMAX][kLdRow];
@@ -1172,13 +1178,15 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   __shared__ __attribute__((aligned(16))) float s_a[TMAX][kLdRow];
   __shared__ __attribute__((aligned(16))) float s_gam[TMAX][kLdRow];
   __shared__ __attribute__((aligned(16))) float s_v[TMAX][BV];
-  __shared__ __attribute__((aligned(16))) f4 s_part[NW][4][BV];  // [wave][gq][column] = D[4 gq + r]
+  // [half][wave of the half][gq][column of the half] = D[4 gq + r]
+  __shared__ __attribute__((aligned(16))) f4 s_part[HALVES][kMfmaWaves][4][BH];
   __shared__ __attribute__((aligned(16))) float s_cP[TMAX][TMAX];
   __shared__ __attribute__((aligned(16))) float s_cA[TMAX][TMAX];
   __shared__ __attribute__((aligned(16))) float s_beta[TMAX];
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
+  const int half = wave / kMfmaWaves, rw = wave % kMfmaWaves;
   const int gq = lane / 16, li = lane % 16;
 
   const int tile = tile_of_block(blockIdx.x, gridDim.x);
@@ -1187,6 +1195,7 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   const int h = rh % a.H;
   const int r = rh / a.H;
   const int n_rows = a.n_rows;
+  const int hcol = vt * BV + half * BH;  // the first column of this wave's half
 
   const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
   int32_t sid[TMAX];
@@ -1194,7 +1203,7 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
   const int32_t init_slot = *(a.init_slot_ids != nullptr ? a.init_slot_ids + r : ids);
 
-  // Row inputs: wave w normalises rows w and w + 4 (a row past the last
+  // Row inputs: wave w normalises rows w, w + NW, ... (a row past the last
   // re-reads the last one and is staged as zeros).
   int zero_v;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
@@ -1202,15 +1211,76 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   f2 q2[TPW], k2[TPW];
   f4 v4[TPW];
   float braw[TPW];
+  // fused convolution: the window win[t + m], m = 0..3 (3-entry history,
+  // then this request's rows) of this lane's 2 q, 2 k and 4 v channels
+  // (lanes < 32 hold the 128 v channels), and their taps
+  constexpr int TC = CONV ? TPW : 1;
+  f2 eq[TC][4], ek[TC][4];
+  f4 ev[TC][4];
+  f4 wq0, wq1, wk0, wk1, wv[4];
+  const int64_t conv_c = static_cast<int64_t>(3) * a.H * kHeadK;  // channels per history entry
+  const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
+  const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
+  const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
+  const bool conv_vl = lane < BV / 4;
+  if constexpr (!CONV) {
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int t = min(wave + j * NW, n_rows - 1);
-    const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
-    const int64_t off = (rho * a.H + h) * kHeadK;
-    q2[j] = reinterpret_cast<const f2*>(a.q + off)[lane];
-    k2[j] = reinterpret_cast<const f2*>(a.k + off)[lane];
-    v4[j] = *reinterpret_cast<const f4*>(a.v + off + vt * BV + 4 * (lane % (BV / 4)));
-    braw[j] = a.b[rho * a.H + h + zero_v];
+    for (int j = 0; j < TPW; ++j) {
+      const int t = min(wave + j * NW, n_rows - 1);
+      const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+      const int64_t off = (rho * a.H + h) * kHeadK;
+      q2[j] = reinterpret_cast<const f2*>(a.q + off)[lane];
+      k2[j] = reinterpret_cast<const f2*>(a.k + off)[lane];
+      v4[j] = *reinterpret_cast<const f4*>(a.v + off + vt * BV + 4 * (lane % (BV / 4)));
+      braw[j] = a.b[rho * a.H + h + zero_v];
+    }
+  } else {
+    // the history is read at the initial slot (slot 0 for a request with a
+    // bad id, which is skipped below, so every address stays valid)
+    bool ok0 = init_slot >= 0 && init_slot < a.n_slots;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) ok0 = ok0 && sid[t] >= 0 && sid[t] < a.n_slots;
+    const int64_t hslot = ok0 ? init_slot : 0;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) braw[j] = 0.0f;
+    if (wave < n_rows) {
+      wq0 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4);
+      wq1 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4 + 4);
+      wk0 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4);
+      wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
+      if (conv_vl) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + j * NW;
+      if (t < n_rows) {
+        const int64_t rho = static_cast<int64_t>(r) * n_rows + t;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int pos = t + m;  // window index
+          if (pos < 3) {
+            const uint16_t* hb = a.conv_pool + (hslot * 3 + pos) * conv_c;
+            const uint32_t pq = *reinterpret_cast<const uint32_t*>(hb + chq);
+            const uint32_t pk = *reinterpret_cast<const uint32_t*>(hb + chk);
+            eq[j][m] = f2{bf16_lo(pq), bf16_hi(pq)};
+            ek[j][m] = f2{bf16_lo(pk), bf16_hi(pk)};
+            if (conv_vl) {
+              const uint2 pv = *reinterpret_cast<const uint2*>(hb + chv);
+              ev[j][m] = f4{bf16_lo(pv.x), bf16_hi(pv.x), bf16_lo(pv.y), bf16_hi(pv.y)};
+            }
+          } else {
+            const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * conv_c;
+            eq[j][m] = *reinterpret_cast<const f2*>(xr + chq);
+            ek[j][m] = *reinterpret_cast<const f2*>(xr + chk);
+            if (conv_vl) ev[j][m] = *reinterpret_cast<const f4*>(xr + chv);
+          }
+        }
+        braw[j] = a.b[rho * a.H + h];
+      }
+    }
   }
   // Decays per key channel: threads 0..127 each take one channel through all
   // rows (the cumulative products need every row).
@@ -1228,11 +1298,12 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
 
-  // The initial state: rows 32 w + 8 gq + j, columns 4 li .. 4 li + 3.
+  // The initial state: rows 32 rw + 8 gq + j, columns 4 li .. 4 li + 3 of
+  // the wave's half.
   const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
   const int64_t slot_elems = static_cast<int64_t>(a.H) * head_elems;
-  const int row0 = 32 * wave + 8 * gq;
-  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + vt * BV + 4 * li;
+  const int row0 = 32 * rw + 8 * gq;
+  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + hcol + 4 * li;
   T* const pool = static_cast<T*>(a.pool);
   vec raw[8];
   {
@@ -1242,6 +1313,48 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
       raw[j] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(src + j * kHeadV));
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  // -- fused convolution: y_t = silu(sum_m w_m win[t + m]) --------------------
+  f2 hq[TC][3], hk[TC][3];  // the history each row's snapshot keeps (entries t+1 .. t+3)
+  f4 hv[TC][3];
+  if constexpr (CONV) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + j * NW;
+      q2[j] = f2{0.0f, 0.0f};
+      k2[j] = f2{0.0f, 0.0f};
+      v4[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (t < n_rows) {
+        float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          sq0 = fmaf(wq0[m], eq[j][m][0], sq0);
+          sq1 = fmaf(wq1[m], eq[j][m][1], sq1);
+          sk0 = fmaf(wk0[m], ek[j][m][0], sk0);
+          sk1 = fmaf(wk1[m], ek[j][m][1], sk1);
+        }
+        q2[j] = f2{silu(sq0), silu(sq1)};
+        k2[j] = f2{silu(sk0), silu(sk1)};
+        if (conv_vl) {
+          f4 yv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sv = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sv = fmaf(wv[e][m], ev[j][m][e], sv);
+            yv[e] = silu(sv);
+          }
+          v4[j] = yv;
+        }
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+          hq[j][e] = eq[j][e + 1];
+          hk[j][e] = ek[j][e + 1];
+          hv[j][e] = ev[j][e + 1];
+        }
+      }
+    }
+  }
 
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
@@ -1278,6 +1391,30 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   }
   __syncthreads();
 
+  if constexpr (CONV) {
+    // every wave has read the history: the rows' snapshots may now overwrite
+    // it (row 0's slot is the initial slot of an in-place launch)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + j * NW;
+      if (t < n_rows) {
+        int32_t st = sid[0];
+#pragma unroll
+        for (int u = 1; u < TMAX; ++u)
+          if (u == t) st = sid[u];
+#pragma unroll
+        for (int e = 0; e < 3; ++e) {
+          uint16_t* hb = a.conv_pool + (static_cast<int64_t>(st) * 3 + e) * conv_c;
+          *reinterpret_cast<uint32_t*>(hb + chq) = bf16_pack(hq[j][e][0], hq[j][e][1]);
+          *reinterpret_cast<uint32_t*>(hb + chk) = bf16_pack(hk[j][e][0], hk[j][e][1]);
+          if (conv_vl)
+            *reinterpret_cast<uint2*>(hb + chv) = uint2{bf16_pack(hv[j][e][0], hv[j][e][1]),
+                                                         bf16_pack(hv[j][e][2], hv[j][e][3])};
+        }
+      }
+    }
+  }
+
   // fp32 state
   float S[8][4];
 #pragma unroll
@@ -1304,18 +1441,21 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(wj, S[j][e], acc[e], 0, 0, 0);
     }
-    switch (wave) {  // wave-uniform: each wave takes two columns of the couplings
-      case 0: coupling_pair<0>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
-      case 1: coupling_pair<1>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
-      case 2: coupling_pair<2>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
-      default: coupling_pair<3>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+    if (half == 0) {
+      switch (rw) {  // wave-uniform: each wave of the first half takes two columns of the couplings
+        case 0: coupling_pair<0>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+        case 1: coupling_pair<1>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+        case 2: coupling_pair<2>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+        default: coupling_pair<3>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_part[wave][gq][4 * li + e] = acc[e];
+    for (int e = 0; e < 4; ++e) s_part[half][rw][gq][4 * li + e] = acc[e];
   }
   __syncthreads();
 
-  // (3) and (4): every wave solves all 64 columns (lane l: column l) and
+  // (3) and (4): every wave solves the 64 columns of its half (lane l:
+  // column l of the half) and
   // writes row t's snapshot as soon as Delta_t is known, so the snapshot
   // stores begin after the first step of the solve.  The couplings and beta
   // are the same for every column: each lane reads one of them and the
@@ -1330,20 +1470,20 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
   auto cP = [&](int t, int s2) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cP_l), 8 * t + s2)); };
   float tot[16], vv[TMAX];
   {
-    f4 part[NW][4];
+    f4 part[kMfmaWaves][4];
 #pragma unroll
-    for (int x = 0; x < NW; ++x)
+    for (int x = 0; x < kMfmaWaves; ++x)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) part[x][g] = s_part[x][g][lane];
+      for (int g = 0; g < 4; ++g) part[x][g] = s_part[half][x][g][lane];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][lane];
+    for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][half * BH + lane];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         tot[4 * g + e] = (part[0][g][e] + part[1][g][e]) + (part[2][g][e] + part[3][g][e]);
   }
-  float* op = a.out + (static_cast<int64_t>(r) * n_rows * a.H + h) * kHeadV + vt * BV + lane;
+  float* op = a.out + (static_cast<int64_t>(r) * n_rows * a.H + h) * kHeadV + hcol + lane;
   const int64_t o_row = static_cast<int64_t>(a.H) * kHeadV;
   float dl[TMAX];
 #pragma unroll
@@ -1353,7 +1493,7 @@ __global__ __launch_bounds__(kWave * kMfmaWaves) void kda_rows_mfma_kernel(Args 
 #pragma unroll
     for (int s2 = 0; s2 < t; ++s2) d = fmaf(-cA(t, s2), dl[s2], d);
     dl[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt_l), t)) * d;
-    if ((t & 3) == wave) {  // this wave writes row t's outputs
+    if ((t & 3) == rw) {  // this wave writes row t's outputs of its half
       float o = tot[8 + t];
 #pragma unroll
       for (int s2 = 0; s2 <= t; ++s2) o = fmaf(cP(t, s2), dl[s2], o);
@@ -1487,7 +1627,7 @@ template <typename T>
 static hipError_t dispatch(const Args& a, const Shape& sh, int32_t blocks, hipStream_t s) {
   if (sh.layout == KDA_ROWS_WAVE_K) return dispatch_rows<T>(a, sh, blocks, s);
   if (sh.layout == KDA_ROWS_MATRIX) {
-    hipLaunchKernelGGL((kda_rows_mfma_kernel<T>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s, a);
+    hipLaunchKernelGGL((kda_rows_mfma_kernel<T, false>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s, a);
     return hipGetLastError();
   }
   const int lpr = sh.bv / Lane16<T>::kCols;
@@ -1616,8 +1756,19 @@ extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* c
   a.scale = scale;
   const int32_t blocks = n_req * pool->H;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = state_dtype == KDA_F32 ? dispatch_conv<float>(a, shape.nw, blocks, s)
-                                                : dispatch_conv<_Float16>(a, shape.nw, blocks, s);
+  hipError_t err;
+  if (shape.layout == KDA_ROWS_MATRIX) {
+    if (state_dtype == KDA_F32)
+      hipLaunchKernelGGL((kda_rows_mfma_kernel<float, true>), dim3(blocks), dim3(kWave * kMatrixConvWaves),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((kda_rows_mfma_kernel<_Float16, true>), dim3(blocks),
+                         dim3(kWave * kMatrixConvWaves), 0, s, a);
+    err = hipGetLastError();
+  } else {
+    err = state_dtype == KDA_F32 ? dispatch_conv<float>(a, shape.nw, blocks, s)
+                                 : dispatch_conv<_Float16>(a, shape.nw, blocks, s);
+  }
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -102,9 +102,11 @@ inline int32_t default_wave_k_waves(kda_dtype /*dt*/) { return 4; }
 // The chained-rows block form: fp16 pools need at least 2 waves per tile.
 inline bool block_supported(kda_dtype dt, int32_t nw) { return dt != KDA_F16 || nw > 1; }
 
-// The matrix-core block form of chained rows: one shape.
+// The matrix-core block form of chained rows: one shape (with the fused
+// convolution, whole heads: two 64-column halves of 4 waves).
 constexpr int32_t kMatrixBV = 64;
 constexpr int32_t kMatrixWaves = 4;
+constexpr int32_t kMatrixConvWaves = 2 * kMatrixWaves;
 
 struct Shape {
   int32_t bv;      // value columns per workgroup
@@ -158,7 +160,7 @@ inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block
     // kn, qn, decays, cumulative decays [8][132]; v [8][bv]; the waves'
     // partial sums [nw][16][bv]; two 8 x 8 couplings; beta
     constexpr int32_t t = KDA_MAX_ROWS;
-    return 4 * (4 * t * (kHeadK + 4) + t * bv + nw * 16 * bv + 2 * t * t + t);
+    return 4 * (4 * t * (kHeadK + 4) + t * bv + nw * 16 * kMatrixBV + 2 * t * t + t);
   }
   const int32_t tmax = n_rows == 1 ? 1 : KDA_MAX_ROWS;
   const int32_t staged = tmax * (3 * kHeadK + bv + 2);
@@ -171,18 +173,30 @@ inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block
 }
 
 // Fused-convolution launches take whole heads (bv = 128) so that a head's
-// convolution history is read and rewritten inside one workgroup; waves per
-// tile 2, 4 or 8 (default: 2 fp32 / 4 fp16 for one row, 8 / 4 for chained
-// rows).  A bv option other than 0 or 128, or the whole-K row layout, is
-// refused.
+// convolution history is read and rewritten inside one workgroup.  Chained
+// rows take the matrix-core block form (8 waves: two 64-column halves) when
+// rows_layout asks for it or, by default for fp16 pools, when no waves or
+// block_rows option asks for a K-split shape (measured on MI355X, 8 x 8 rows:
+// fp16 13.4 us against 17.6 us K-split; fp32 16.5 against 16.4 us, so fp32
+// keeps the K split); otherwise the K-split
+// kernel with 2, 4 or 8 waves per tile (default: 2 fp32 / 4 fp16 for one
+// row, 8 / 4 for chained rows).  A bv option other than 0 or 128, or the
+// whole-K row layout, is refused; rows_layout is ignored for one row.
 inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts,
                                Shape* out) {
-  Shape s{kHeadV, n_rows == 1 ? (dt == KDA_F32 ? 2 : 4) : (dt == KDA_F32 ? 8 : 4), KDA_ROWS_K_SPLIT};
-  if (opts != nullptr) {
-    if (opts->rows_layout != KDA_ROWS_DEFAULT && opts->rows_layout != KDA_ROWS_K_SPLIT) return false;
-    if (opts->bv != 0 && opts->bv != kHeadV) return false;
-    if (opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
+  const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
+  if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX || asked == KDA_ROWS_WAVE_K) return false;
+  if (opts != nullptr && opts->bv != 0 && opts->bv != kHeadV) return false;
+  if (n_rows > 1) {
+    const bool shaped = opts != nullptr && (opts->waves_per_tile != 0 || opts->block_rows != 0);
+    const bool matrix = asked == KDA_ROWS_MATRIX || (asked == KDA_ROWS_DEFAULT && !shaped && dt == KDA_F16);
+    if (matrix) {
+      *out = Shape{kHeadV, kMatrixConvWaves, KDA_ROWS_MATRIX};
+      return opts == nullptr || opts->waves_per_tile == 0 || opts->waves_per_tile == kMatrixConvWaves;
+    }
   }
+  Shape s{kHeadV, n_rows == 1 ? (dt == KDA_F32 ? 2 : 4) : (dt == KDA_F32 ? 8 : 4), KDA_ROWS_K_SPLIT};
+  if (opts != nullptr && opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
   *out = s;
   return s.nw == 2 || s.nw == 4 || s.nw == 8;
 }

@@ -343,6 +343,10 @@ def test_conv_step_refusals():
     assert conv_step(P, Cv, opts=B.kda_launch_opts(0, 64)) == B.KDA_ERR_ARG   # whole heads only
     assert conv_step(P, Cv, opts=B.kda_launch_opts(1, 0)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 0, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
+    # the matrix-core block form with the convolution: whole heads over 8 waves only
+    assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(4, 0, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 64, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 0, 0, 4)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, scale=float("nan")) == B.KDA_ERR_ARG
     assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE + 8), 16, 12)) == B.KDA_ERR_ALIGN
 

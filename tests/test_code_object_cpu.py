@@ -143,15 +143,18 @@ def test_matrix_block_form_lds_matches_the_launch_description(kernels):
     # static LDS, for both pool dtypes
     import kda_gated_delta_decode_amd.binding as B
     want = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX)["lds_bytes"]
-    for name in ("_ZN3kda20kda_rows_mfma_kernelIfEEvNS_4ArgsE",
-                 "_ZN3kda20kda_rows_mfma_kernelIDF16_EEvNS_4ArgsE"):
+    for name in ("_ZN3kda20kda_rows_mfma_kernelIfLb0EEEvNS_4ArgsE",
+                 "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb0EEEvNS_4ArgsE"):
         assert kernels[name][".group_segment_fixed_size"] == want, name
 
 
 def test_matrix_block_form_runs_its_column_sums_on_the_matrix_cores(disassembly):
     # 8 steps of 4 rows x 4 column offsets: 32 fp32 16x16x4 products per wave
-    for name in ("_ZN3kda20kda_rows_mfma_kernelIfEEvNS_4ArgsE",
-                 "_ZN3kda20kda_rows_mfma_kernelIDF16_EEvNS_4ArgsE"):
+    # (with and without the fused convolution)
+    for name in ("_ZN3kda20kda_rows_mfma_kernelIfLb0EEEvNS_4ArgsE",
+                 "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb0EEEvNS_4ArgsE",
+                 "_ZN3kda20kda_rows_mfma_kernelIfLb1EEEvNS_4ArgsE",
+                 "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb1EEEvNS_4ArgsE"):
         assert disassembly[name].count("v_mfma_f32_16x16x4_f32") == 32, name
 
 

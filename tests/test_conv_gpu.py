@@ -20,7 +20,7 @@ def _gpu():
     need_gpu()
 
 
-def gpu_conv(ci, init=None, waves=0, block_rows=False):
+def gpu_conv(ci, init=None, waves=0, block_rows=False, rows_layout=0):
     d = ci.dec
     dev = torch.device("cuda", 0)
     pool = torch.from_numpy(d.pool if d.dtype == "f32" else d.pool.view(np.float16)).to(dev)
@@ -34,7 +34,7 @@ def gpu_conv(ci, init=None, waves=0, block_rows=False):
     init_d = None if init is None else torch.from_numpy(np.asarray(init, np.int32)).to(dev)
     B.kda_decode_step_conv(pool, conv, ids, x, w, g, b, out, n_rows_per_slot=d.n_rows,
                            scale=d.scale, init_slot_ids=init_d, waves_per_tile=waves,
-                           block_rows=block_rows)
+                           block_rows=block_rows, rows_layout=rows_layout)
     torch.cuda.synchronize()
     return pool_to_host(pool), conv.view(torch.int16).cpu().numpy().view(np.uint16), out.cpu().numpy()
 
@@ -54,8 +54,8 @@ def oracle_conv(oracle, ci, init=None):
     return pool, conv.reshape(ci.conv.shape), out
 
 
-def check(oracle, ci, init=None, waves=0, block_rows=False):
-    gp, gc, go = gpu_conv(ci, init, waves, block_rows)
+def check(oracle, ci, init=None, waves=0, block_rows=False, rows_layout=0):
+    gp, gc, go = gpu_conv(ci, init, waves, block_rows, rows_layout)
     op, oc, oo = oracle_conv(oracle, ci, init)
     d = ci.dec
     if d.dtype == "f32":
@@ -113,3 +113,25 @@ def test_fused_conv_identity_taps_equal_plain_decode_of_silu(oracle):
                          np.ascontiguousarray(y[:, 2]), d.g, d.b, n_rows=1, scale=d.scale)
     assert np.max(np.abs(gp - op)) <= STATE_ABS_F32
     assert out_rel_err(go, oo) <= OUT_REL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("n_req,n_rows", [(8, 8), (3, 5), (5, 2)])
+@pytest.mark.parametrize("layout", ["matrix", "k_split"])
+def test_fused_conv_chained_rows_in_both_layouts(oracle, dtype, n_req, n_rows, layout):
+    """Chained rows with the convolution fused in front, in the matrix-core
+    block form (whole heads over 8 waves) and in the K-split layout."""
+    ci = kda_inputs.make_conv_inputs("conv layouts", 72, n_req, n_rows, dtype, H=12 if n_req == 8 else 3,
+                                     seed=150 + 7 * n_req + n_rows)
+    check(oracle, ci, rows_layout=B.KDA_ROWS_MATRIX if layout == "matrix" else B.KDA_ROWS_K_SPLIT)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_fused_conv_matrix_initial_slots_and_in_place_history(oracle, dtype):
+    """The matrix-core form reads the history at the initial slot and writes
+    row 0's history at the same slot (in place) or at another one."""
+    ci = kda_inputs.make_conv_inputs("conv matrix init", 64, 4, 6, dtype, H=3, seed=171)
+    free = np.setdiff1d(np.arange(64), ci.dec.slot_ids)
+    init = np.random.default_rng(5).permutation(free)[:4].astype(np.int32)
+    check(oracle, ci, init=init, rows_layout=B.KDA_ROWS_MATRIX)
+    check(oracle, ci, rows_layout=B.KDA_ROWS_MATRIX)
