@@ -1067,11 +1067,13 @@ __global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
 // contraction over the key channels that runs on the matrix cores
 // (v_mfma_f32_16x16x4_f32, fp32 operands and accumulation) and needs no
 // exchange between the lanes of a wave.  The n x n couplings depend only on
-// the row vectors.  After a triangular solve per column, every snapshot is
-// element-wise: no reduction and no barrier between rows, so the snapshot
-// stores stream.
+// the row vectors.  Each column then needs a triangular solve, Delta_t row
+// after row, and each row's snapshot is element-wise, so a wave writes row
+// t's snapshot as soon as its Delta_t is known: no reduction and no barrier
+// between rows, and the snapshot stores stream.
 //
-// Workgroup: (request, head, 64-column half), 4 waves.  Wave w holds key
+// Workgroup: (request, head, 64-column half), 4 waves (with the fused
+// convolution a whole head: two halves of 4 waves).  Wave w of a half holds key
 // rows 32 w .. 32 w + 31; lane (gq = lane / 16, li = lane % 16) holds rows
 // 32 w + 8 gq + j (j < 8) and columns 4 li .. 4 li + 3 of the half.  Each
 // state load or store instruction therefore covers whole rows of the half:
@@ -1094,7 +1096,7 @@ struct Piece4<_Float16> {
   using vec = h4;
 };
 
-constexpr int kMfmaBV = kMatrixBV;  // columns per workgroup
+constexpr int kMfmaBV = kMatrixBV;  // columns per half (per workgroup without the convolution)
 constexpr int kMfmaWaves = kMatrixWaves;
 constexpr int kLdRow = kHeadK + 4;  // padded row stride of the [t][channel] LDS arrays
 
