@@ -13,7 +13,7 @@ arithmetic on the exactly widened state: outputs bit-equal, fp16 snapshots
 the RNE of the fp32 ones), initial states from other slots, an out-of-range
 slot id, the identity gate, strong decays whose cumulative products
 underflow, decays of about -5 per row on every channel, heads in different
-decay regimes in one launch, zero q and k.
+decay regimes in one launch, zero q and k, slots beyond 2^31 pool elements.
 """
 import sys
 
@@ -233,3 +233,28 @@ def test_heads_in_different_decay_regimes(oracle, dtype):
     assert out_rel_err(go[:, both], o_out32[:, both]) <= OUT_REL
     assert out_rel_err(go[:, both], o_out64[:, both]) <= OUT_REL
     assert out_rel_err(go[:, 1:2], o_out64[:, 1:2]) <= STRONG_DECAY_OUT_REL
+
+
+def test_64bit_pool_offsets(oracle):
+    """Snapshot and initial slots beyond 2^31 pool elements: an fp16 pool of
+    11,000 slots (4.3 GB), 2 requests x 4 rows near its top."""
+    n_slots, H, n_req, n_rows = 11000, 12, 2, 4
+    inp = kda_inputs.make_inputs("matrix high slots", 8, n_req, n_rows, "f16", seed=77)
+    high = np.array([10999, 10990, 10950, 10925, 10930, 10998, 10960, 10940], dtype=np.int32)
+    remap = dict(zip(inp.slot_ids.tolist(), high.tolist()))   # compact slot -> high slot
+    pool = torch.zeros((n_slots, H, 128, 128), dtype=torch.float16, device="cuda")
+    for s_small, s_big in remap.items():
+        pool[s_big] = torch.from_numpy(inp.pool[s_small].view(np.float16)).cuda()
+    ids = torch.from_numpy(np.array([remap[s] for s in inp.slot_ids.tolist()], dtype=np.int32)).cuda()
+    dev = {n: torch.from_numpy(getattr(inp, n)).cuda() for n in ("q", "k", "v", "g", "b")}
+    out = torch.empty((n_req * n_rows, H, 128), dtype=torch.float32, device="cuda")
+    B.kda_decode_step(pool, ids, dev["q"], dev["k"], dev["v"], dev["g"], dev["b"], out,
+                      n_rows_per_slot=n_rows, **MATRIX)
+    torch.cuda.synchronize()
+    got = pool[ids.long()].cpu().numpy().view(np.uint16)
+    o_pool, o_out = run_oracle_f32(oracle, inp)
+    assert f16_ulp_distance(got, o_pool[inp.slot_ids]).max() <= F16_ULP
+    assert out_rel_err(out.cpu().numpy(), o_out) <= OUT_REL
+    assert int(high.min()) * H * 128 * 128 > 2 ** 31
+    del pool
+    torch.cuda.empty_cache()
