@@ -199,7 +199,40 @@ def cpu_baseline(inp, seconds: float):
         "us_per_full_step": el / calls * (inp.n_req / n_req) * 1e6,
         "host_cpus_available": len(os.sched_getaffinity(0)),
         "parallel": cpu_baseline_parallel(inp, min(seconds, 6.0)),
+        "other_configs": cpu_other_configs(min(seconds / 6.0, 2.0)),
     }
+
+
+def cpu_other_configs(seconds: float):
+    """The same oracle (one thread) on the other workloads: the batched step
+    on both pool dtypes, the 8 x 8 chained rows on an fp16 pool (whole oracle
+    launches, repeated for about `seconds` each), and one pass of the 69-layer
+    fp32 step (69 oracle launches of 64 requests; one pool serves every layer,
+    since the oracle's time does not depend on the values)."""
+    from oracle import kda_oracle
+    import kda_inputs
+    res = {}
+
+    def timed(inp, secs):
+        pool = inp.pool.copy()
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            kda_oracle.step_f32(pool, inp.slot_ids, inp.q, inp.k, inp.v, inp.g, inp.b,
+                                n_rows=inp.n_rows, scale=inp.scale)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= secs:
+                return el / calls
+    for name, inp in (("batched_f32", kda_inputs.batched_f32(0)), ("batched_f16", kda_inputs.batched_f16(0)),
+                      ("spec_verify_f16", kda_inputs.spec_verify_f16(0))):
+        per = timed(inp, seconds)
+        res[name] = {"us_per_step": round(per * 1e6, 1),
+                     "state_GB/s": round(inp.state_bytes() / per / 1e9, 2)}
+    inp = kda_inputs.layer_step(0, "f32")
+    per = timed(inp, 0.0) * 69
+    res["layers69_f32_one_pass"] = {"us_per_step": round(per * 1e6, 1),
+                                    "state_GB/s": round(69 * inp.state_bytes() / per / 1e9, 2)}
+    return res
 
 
 def cpu_baseline_parallel(inp, seconds: float, max_threads: int = 16):

@@ -55,3 +55,6 @@ def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
     assert "of the 4 requests" in res["sample"]
     par = res["parallel"]
     assert par["cores"] >= 1 and par["value"] > 0
+    other = res["other_configs"]
+    assert set(other) == {"batched_f32", "batched_f16", "spec_verify_f16", "layers69_f32_one_pass"}
+    assert all(v["us_per_step"] > 0 and v["state_GB/s"] > 0 for v in other.values())
