@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5  /* 5: KDA_ROWS_MATRIX, and rows_layout for kda_decode_step_conv */
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
