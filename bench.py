@@ -198,9 +198,23 @@ def cpu_baseline(inp, seconds: float):
                   % (calls, n_req, inp.n_req, H, inp.dtype, inp.n_rows, el),
         "us_per_full_step": el / calls * (inp.n_req / n_req) * 1e6,
         "host_cpus_available": len(os.sched_getaffinity(0)),
+        "host_cpus_online": os.cpu_count(),
+        "cpu_model": cpu_model(),
         "parallel": cpu_baseline_parallel(inp, min(seconds, 6.0)),
         "other_configs": cpu_other_configs(min(seconds / 6.0, 2.0)),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_other_configs(seconds: float):

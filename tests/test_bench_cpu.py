@@ -53,6 +53,7 @@ def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
     assert res["kind"] == "oracle" and res["unit"] == "GB/s" and res["cores"] == 1
     assert res["value"] > 0 and res["us_per_full_step"] > 0
     assert "of the 4 requests" in res["sample"]
+    assert res["host_cpus_available"] >= 1 and isinstance(res["cpu_model"], str) and res["cpu_model"]
     par = res["parallel"]
     assert par["cores"] >= 1 and par["value"] > 0
     other = res["other_configs"]
