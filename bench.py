@@ -383,7 +383,8 @@ def main():
         other = () if args.extras == "copy" else (
                         ("batched_f16" if args.dtype == "f32" else "batched_f32",
                           kda_inputs.batched_f16 if args.dtype == "f32" else kda_inputs.batched_f32),
-                         ("spec_verify_f16", kda_inputs.spec_verify_f16))
+                         ("spec_verify_f16", kda_inputs.spec_verify_f16),
+                         ("single_slot_f32", kda_inputs.single_slot_f32))
         for name, fn in other:
             inp = fn(0)
             w = Workload(inp, ROT, torch)

@@ -328,9 +328,12 @@ size_t kda_pool_bytes(int32_t n_slots, int32_t H, int32_t K, int32_t V,
 
 /*
  * kda_tile_bv -- value columns per state tile that single-row launches use
- * by default: 128 for fp32 pools (whole 512-byte state rows per wave
- * instruction, K over 2 waves), 64 for fp16 (whole 128-byte lines, one wave
- * per tile).  Other widths (32 fp32 / 64 fp16 columns is the V-block cap of
+ * by default once they are large enough to be bound by bandwidth (more than
+ * 128 requests x heads for fp32, 96 for fp16): 128 for fp32 pools (whole
+ * 512-byte state rows per wave instruction, K over 2 waves), 64 for fp16
+ * (whole 128-byte lines, one wave per tile).  Smaller single-row launches
+ * take narrower tiles or more waves by default (kda_describe_launch reports
+ * the shape of any launch).  Other widths (32 fp32 / 64 fp16 columns is the V-block cap of
  * the pages' portable kernel, ROCm/ATOM PR #2130, Copilot review) remain
  * available through kda_launch_opts.  Returns a negative kda_status for a
  * refused dtype.

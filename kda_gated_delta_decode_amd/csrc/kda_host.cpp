@@ -124,7 +124,7 @@ int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtyp
   if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
   if (n_req < 0) return KDA_ERR_ARG;
   Shape shape;
-  if (!resolve_shape(dtype, n_rows, opts, &shape)) return KDA_ERR_ARG;
+  if (!resolve_shape(dtype, n_rows, static_cast<int64_t>(n_req) * H, opts, &shape)) return KDA_ERR_ARG;
   const int32_t bv = shape.bv;
   const int32_t nw = shape.nw;
   const int64_t tiles = static_cast<int64_t>(n_req) * H * (kHeadV / bv);

@@ -34,18 +34,31 @@ inline int32_t cols_per_lane(kda_dtype dt) { return dt == KDA_F32 ? 4 : 8; }
 //    tile row) held by one wave, so a row's column sums never leave the
 //    wave: no LDS exchange and no barrier.  9.6-9.7 us, against 9.9 us for
 //    128 columns over 2 waves and 10.0-10.1 us over 4.
+//  - one row per request, small launches (units = requests x heads), where
+//    latency rather than bandwidth decides: narrower tiles or more waves
+//    put more workgroups and waves in flight.  fp32: up to 48 units 32
+//    columns over 1 wave (1 request: 3.7 us against 5.3 us; 4 requests: 4.0
+//    against 5.4), up to 128 units 64 columns over 8 waves (8 requests: 4.6
+//    against 5.8; 16 requests measured even, 32 best at the wide default).
+//    fp16: up to 96 units 64 columns over 4 waves (1 request: 4.1 against
+//    4.6 us; 8 requests: 4.5 against 4.9; 32 best at one wave).
 //  - chained rows: 64-column tiles with K over 8 (fp32) or 4 (fp16) waves:
 //    few tiles exist, so K is spread over more waves and each row's partial
 //    column sums meet in LDS.
-inline int32_t default_bv(kda_dtype dt, int32_t n_rows) {
-  return n_rows == 1 && dt == KDA_F32 ? 128 : 64;
+inline int32_t default_bv(kda_dtype dt, int32_t n_rows, int64_t units = 1 << 30) {
+  if (n_rows == 1 && dt == KDA_F32) return units <= 48 ? 32 : units <= 128 ? 64 : 128;
+  return 64;
 }
-inline int32_t default_waves_per_tile(kda_dtype dt, int32_t n_rows) {
-  if (n_rows == 1) return dt == KDA_F32 ? 2 : 1;
+inline int32_t default_waves_per_tile(kda_dtype dt, int32_t n_rows, int64_t units = 1 << 30) {
+  if (n_rows == 1) {
+    if (dt == KDA_F32) return units <= 48 ? 1 : units <= 128 ? 8 : 2;
+    return units <= 96 ? 4 : 1;
+  }
   return dt == KDA_F32 ? 8 : 4;
 }
 
-// The single-row default tile width (what kda_tile_bv reports).
+// The single-row default tile width of launches large enough to be bound by
+// bandwidth (what kda_tile_bv reports).
 inline int32_t tile_bv(kda_dtype dt) { return default_bv(dt, 1); }
 
 // The (bv, waves) shapes the kernels are instantiated for: 8, 16 or 32
@@ -114,9 +127,11 @@ struct Shape {
   int32_t layout;  // KDA_ROWS_K_SPLIT (also every single-row launch), _WAVE_K or _MATRIX
 };
 
-// The shape a launch uses: each option field that is set overrides the
-// default.  Returns false if the result is not an instantiated shape.
-inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts, Shape* out) {
+// The shape a launch of `units` = requests x heads uses: each option field
+// that is set overrides the default.  Returns false if the result is not an
+// instantiated shape.
+inline bool resolve_shape(kda_dtype dt, int32_t n_rows, int64_t units, const kda_launch_opts* opts,
+                          Shape* out) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX) return false;
   const int32_t layout = n_rows > 1 ? chained_rows_layout(dt, opts) : KDA_ROWS_K_SPLIT;
@@ -130,7 +145,7 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* o
   }
   // the K-split block form
   if (n_rows > 1 && opts != nullptr && opts->block_rows != 0 && layout == KDA_ROWS_WAVE_K) return false;
-  Shape s{default_bv(dt, n_rows), default_waves_per_tile(dt, n_rows), layout};
+  Shape s{default_bv(dt, n_rows, units), default_waves_per_tile(dt, n_rows, units), layout};
   if (layout == KDA_ROWS_WAVE_K) {
     s.bv = default_wave_k_bv(dt);
     s.nw = default_wave_k_waves(dt);

@@ -265,6 +265,13 @@ def test_describe_launch():
     assert (d["kernel"], d["rows_layout"]) == ("kda_decode_tile", B.KDA_ROWS_K_SPLIT)
     d = B.kda_describe_launch(64, 1, 12, "f16")
     assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 1, 1536)
+    # small single-row launches (requests x heads): narrower tiles or more waves
+    for n_req, dt, want in ((1, "f32", (32, 1)), (4, "f32", (32, 1)), (5, "f32", (64, 8)), (10, "f32", (64, 8)),
+                            (11, "f32", (128, 2)), (1, "f16", (64, 4)), (8, "f16", (64, 4)),
+                            (9, "f16", (64, 1))):
+        d = B.kda_describe_launch(n_req, 1, 12, dt)
+        assert (d["bv"], d["waves_per_tile"]) == want, (n_req, dt)
+    assert (B.kda_describe_launch(1, 1, 12, "f32", waves_per_tile=2)["bv"]) == 32   # bv stays the small default
     # one row: the layout option is ignored
     d = B.kda_describe_launch(64, 1, 12, "f16", rows_layout=B.KDA_ROWS_WAVE_K)
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 1, "kda_decode_tile")
