@@ -180,8 +180,10 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
  *                  default: for fp16 pools the matrix-core block form, or,
  *                  when bv or waves_per_tile is set, the whole-K layout (bv
  *                  64 over 4 waves unless set); for fp32 pools the K split
- *                  (bv 64 over 8 waves); block_rows alone selects the
- *                  K-split block form.
+ *                  (bv 64 over 8 waves), or the matrix-core block form for
+ *                  launches of at most 48 requests x heads with no bv or
+ *                  waves option; block_rows alone selects the K-split block
+ *                  form.
  * Supported K-split combinations keep 2..32 key rows per lane (rows per
  * lane = 2 * lanes per row / waves).  The shape changes the order of the
  * fp32 column sums over K (so results may differ in the last bits), never

@@ -286,6 +286,10 @@ def test_describe_launch():
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (128, 4, "kda_rows_kernel")
     d = B.kda_describe_launch(8, 8, 12, "f32")
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 8, "kda_decode_tile")
+    # small fp32 chained-row launches take the matrix-core block form
+    assert B.kda_describe_launch(4, 8, 12, "f32")["kernel"] == "kda_rows_mfma_kernel"
+    assert B.kda_describe_launch(5, 8, 12, "f32")["kernel"] == "kda_decode_tile"
+    assert B.kda_describe_launch(4, 8, 12, "f32", waves_per_tile=8)["kernel"] == "kda_decode_tile"
     d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8, rows_layout=B.KDA_ROWS_K_SPLIT)
     assert (d["waves_per_tile"], d["threads"], d["kernel"]) == (8, 512, "kda_decode_tile")
     d = B.kda_describe_launch(8, 8, 12, "f16", block_rows=True)
