@@ -263,8 +263,9 @@ typedef struct kda_conv_pool {
  * nearest even); rows of one launch use their fp32 inputs directly.
  * Launch shapes: whole heads only (opts->bv 0 or 128).  Chained rows take
  * the matrix-core block form (KDA_ROWS_MATRIX: 8 waves, two 64-column
- * halves) when rows_layout asks for it, or by default for fp16 pools unless
- * waves_per_tile or block_rows is set; otherwise the K-split kernel with 2,
+ * halves) when rows_layout asks for it, or by default for fp16 pools and
+ * for fp32 launches of at most 48 requests x heads, unless waves_per_tile or
+ * block_rows is set; otherwise the K-split kernel with 2,
  * 4 or 8 waves.  KDA_ROWS_WAVE_K is refused; rows_layout is ignored for one
  * row.
  * Errors: as kda_decode_step_ex, plus KDA_ERR_NULL for a missing conv pool,

@@ -1733,7 +1733,8 @@ extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* c
     return KDA_ERR_NULL;
   if (!std::isfinite(scale)) return KDA_ERR_ARG;
   Shape shape;
-  if (!resolve_conv_shape(state_dtype, n_rows_per_slot, opts, &shape)) return KDA_ERR_ARG;
+  if (!resolve_conv_shape(state_dtype, n_rows_per_slot, static_cast<int64_t>(n_req) * pool->H, opts, &shape))
+    return KDA_ERR_ARG;
   if (!aligned16(pool->base) || !aligned16(conv->base) || !aligned16(x) || !aligned16(conv_w) ||
       !aligned16(g) || !aligned16(out) || !aligned4(b) || !aligned4(slot_ids) ||
       !aligned4(init_slot_ids))

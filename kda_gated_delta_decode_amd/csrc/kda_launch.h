@@ -192,21 +192,23 @@ inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block
 // Fused-convolution launches take whole heads (bv = 128) so that a head's
 // convolution history is read and rewritten inside one workgroup.  Chained
 // rows take the matrix-core block form (8 waves: two 64-column halves) when
-// rows_layout asks for it or, by default for fp16 pools, when no waves or
-// block_rows option asks for a K-split shape (measured on MI355X, 8 x 8 rows:
-// fp16 13.4 us against 17.6 us K-split; fp32 16.5 against 16.4 us, so fp32
-// keeps the K split); otherwise the K-split
+// rows_layout asks for it or, by default for fp16 pools and for fp32 launches
+// of at most 48 requests x heads, when no waves or block_rows option asks
+// for a K-split shape (measured on MI355X: 8 x 8 rows, fp16 13.4 us against
+// 17.6 us K-split, fp32 16.5 against 16.4 us; 1 and 4 requests x 8 rows,
+// fp32 13.0 and 14.0 us against 14.9 and 15.7 us); otherwise the K-split
 // kernel with 2, 4 or 8 waves per tile (default: 2 fp32 / 4 fp16 for one
 // row, 8 / 4 for chained rows).  A bv option other than 0 or 128, or the
 // whole-K row layout, is refused; rows_layout is ignored for one row.
-inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts,
+inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, int64_t units, const kda_launch_opts* opts,
                                Shape* out) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX || asked == KDA_ROWS_WAVE_K) return false;
   if (opts != nullptr && opts->bv != 0 && opts->bv != kHeadV) return false;
   if (n_rows > 1) {
     const bool shaped = opts != nullptr && (opts->waves_per_tile != 0 || opts->block_rows != 0);
-    const bool matrix = asked == KDA_ROWS_MATRIX || (asked == KDA_ROWS_DEFAULT && !shaped && dt == KDA_F16);
+    const bool matrix = asked == KDA_ROWS_MATRIX ||
+                        (asked == KDA_ROWS_DEFAULT && !shaped && (dt == KDA_F16 || units <= 48));
     if (matrix) {
       *out = Shape{kHeadV, kMatrixConvWaves, KDA_ROWS_MATRIX};
       return opts == nullptr || opts->waves_per_tile == 0 || opts->waves_per_tile == kMatrixConvWaves;
