@@ -152,10 +152,21 @@ def _dtype_arg(d) -> int:
     return dtype_code(d)
 
 
+def _on_gpu(t, name):
+    """The library takes device addresses only: a host tensor's pointer
+    would reach a kernel as a wild address, so it is refused here."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor, got one on %s" % (name, t.device))
+
+
 def make_pool(pool, dtype=None) -> kda_pool:
     """kda_pool describing a device tensor [n_slots, H, K, V] (contiguous).
     `dtype` overrides the element type the struct declares (default: the
     tensor's own)."""
+    _on_gpu(pool, "pool")
     if not pool.is_contiguous():
         raise ValueError("pool must be contiguous [n_slots, H, K, V]")
     if pool.dim() != 4:
@@ -165,12 +176,15 @@ def make_pool(pool, dtype=None) -> kda_pool:
     return kda_pool(ctypes.c_void_p(pool.data_ptr()), n_slots, H, K, V, code)
 
 
-def _dev(t, name, dtype=None):
-    import torch
+def _dev(t, name, dtype=None, device=None):
+    """The device address of tensor t (None passes through as NULL).  t must
+    be a contiguous GPU tensor, of `dtype` if given and on the same device
+    as `device` (the pool) if given."""
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor):
-        raise TypeError("%s must be a torch tensor" % name)
+    _on_gpu(t, name)
+    if device is not None and t.device != device:
+        raise TypeError("%s is on %s, the pool on %s" % (name, t.device, device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
@@ -220,6 +234,7 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
     waves_per_tile or bv, selects kda_decode_step_ex."""
     import torch
     P = make_pool(pool, pool_dtype)
+    dv = pool.device
     sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
     R = slot_ids.numel()
     if R % n_rows_per_slot != 0:
@@ -232,16 +247,17 @@ def kda_decode_step(pool, slot_ids, q, k, v, g, b, out, n_rows_per_slot: int = 1
                        (g, "g", R * H * pool.shape[2]), (v, "v", R * H * pool.shape[3]),
                        (out, "out", R * H * pool.shape[3]), (b, "b", R * H)):
         _need_numel(t, name, n)
-    rows = (_dev(q, "q", torch.float32), _dev(k, "k", torch.float32), _dev(v, "v", torch.float32),
-            _dev(g, "g", torch.float32), _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
+    f32 = torch.float32
+    rows = (_dev(q, "q", f32, dv), _dev(k, "k", f32, dv), _dev(v, "v", f32, dv),
+            _dev(g, "g", f32, dv), _dev(b, "b", f32, dv), _dev(out, "out", f32, dv),
             n_req, n_rows_per_slot, sd, float(scale))
-    ids = _dev(slot_ids, "slot_ids", torch.int32)
+    ids = _dev(slot_ids, "slot_ids", torch.int32, dv)
     if waves_per_tile or bv or block_rows or rows_layout or init_slot_ids is not None:
         if init_slot_ids is not None and init_slot_ids.numel() != n_req:
             raise ValueError("init_slot_ids needs one entry per request")
         opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout))
         rc = library().kda_decode_step_ex(ctypes.byref(P), ids,
-                                          _dev(init_slot_ids, "init_slot_ids", torch.int32), *rows,
+                                          _dev(init_slot_ids, "init_slot_ids", torch.int32, dv), *rows,
                                           ctypes.byref(opts), _stream_ptr(stream))
         _check(rc, "kda_decode_step_ex")
     else:
@@ -270,6 +286,7 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
     import torch
     P = make_pool(pool)
     Cv = make_conv_pool(conv)
+    dv = pool.device
     sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
     R = slot_ids.numel()
     if R % n_rows_per_slot != 0:
@@ -284,11 +301,11 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
         _need_numel(t, name, n)
     opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout))
     rc = library().kda_decode_step_conv(
-        ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32),
-        _dev(init_slot_ids, "init_slot_ids", torch.int32), _dev(x, "x", torch.float32),
-        _dev(conv_w, "conv_w", torch.float32), _dev(g, "g", torch.float32),
-        _dev(b, "b", torch.float32), _dev(out, "out", torch.float32), n_req, n_rows_per_slot, sd,
-        float(scale), ctypes.byref(opts), _stream_ptr(stream))
+        ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32, dv),
+        _dev(init_slot_ids, "init_slot_ids", torch.int32, dv), _dev(x, "x", torch.float32, dv),
+        _dev(conv_w, "conv_w", torch.float32, dv), _dev(g, "g", torch.float32, dv),
+        _dev(b, "b", torch.float32, dv), _dev(out, "out", torch.float32, dv), n_req,
+        n_rows_per_slot, sd, float(scale), ctypes.byref(opts), _stream_ptr(stream))
     _check(rc, "kda_decode_step_conv")
 
 
@@ -300,6 +317,7 @@ def kda_prefill(pool, init_slot_ids, cu_seqlens, q, k, v, g, b, out, dst_slot_id
     out: device float32 [T, H, 128]; b: [T, H]."""
     import torch
     P = make_pool(pool)
+    dv = pool.device
     sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
     n_seq = init_slot_ids.numel()
     H = pool.shape[1]
@@ -312,12 +330,12 @@ def kda_prefill(pool, init_slot_ids, cu_seqlens, q, k, v, g, b, out, dst_slot_id
     if scale is None:
         scale = 1.0 / math.sqrt(pool.shape[2])
     opts = kda_prefill_opts(int(chunk))
-    rc = library().kda_prefill(ctypes.byref(P), _dev(init_slot_ids, "init_slot_ids", torch.int32),
-                               _dev(dst_slot_ids, "dst_slot_ids", torch.int32),
-                               _dev(cu_seqlens, "cu_seqlens", torch.int32),
-                               _dev(q, "q", torch.float32), _dev(k, "k", torch.float32),
-                               _dev(v, "v", torch.float32), _dev(g, "g", torch.float32),
-                               _dev(b, "b", torch.float32), _dev(out, "out", torch.float32),
+    rc = library().kda_prefill(ctypes.byref(P), _dev(init_slot_ids, "init_slot_ids", torch.int32, dv),
+                               _dev(dst_slot_ids, "dst_slot_ids", torch.int32, dv),
+                               _dev(cu_seqlens, "cu_seqlens", torch.int32, dv),
+                               _dev(q, "q", torch.float32, dv), _dev(k, "k", torch.float32, dv),
+                               _dev(v, "v", torch.float32, dv), _dev(g, "g", torch.float32, dv),
+                               _dev(b, "b", torch.float32, dv), _dev(out, "out", torch.float32, dv),
                                n_seq, T, sd, float(scale), ctypes.byref(opts), _stream_ptr(stream))
     _check(rc, "kda_prefill")
 
@@ -350,12 +368,13 @@ def kda_state_copy(pool, src_slot_ids, dst_slot_ids, state_dtype=None, stream=No
     """Copy whole slots: pool[dst[i]] = pool[src[i]] (device int32 id tensors)."""
     import torch
     P = make_pool(pool)
+    dv = pool.device
     sd = P.dtype if state_dtype is None else _dtype_arg(state_dtype)
     n = src_slot_ids.numel()
     if dst_slot_ids.numel() != n:
         raise ValueError("src and dst slot tables differ in length")
-    _check(library().kda_state_copy(ctypes.byref(P), _dev(src_slot_ids, "src_slot_ids", torch.int32),
-                                    _dev(dst_slot_ids, "dst_slot_ids", torch.int32), n, sd,
+    _check(library().kda_state_copy(ctypes.byref(P), _dev(src_slot_ids, "src_slot_ids", torch.int32, dv),
+                                    _dev(dst_slot_ids, "dst_slot_ids", torch.int32, dv), n, sd,
                                     _stream_ptr(stream)), "kda_state_copy")
 
 
@@ -390,8 +409,16 @@ def kda_tile_of_block(block: int, n_blocks: int) -> int:
 
 
 def kda_copy_probe(dst, src, nbytes: int | None = None, stream=None) -> None:
-    """Device-to-device streaming copy of nbytes (default: all of src)."""
+    """Device-to-device streaming copy of nbytes (default: all of src); nbytes
+    may not exceed either tensor's size."""
+    _on_gpu(dst, "dst")
+    _on_gpu(src, "src")
+    if dst.device != src.device:
+        raise TypeError("dst is on %s, src on %s" % (dst.device, src.device))
     nb = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    cap = min(src.numel() * src.element_size(), dst.numel() * dst.element_size())
+    if nb < 0 or nb > cap:
+        raise ValueError("nbytes %d outside [0, %d], the smaller buffer's size" % (nb, cap))
     _check(library().kda_copy_probe(_dev(dst, "dst"), _dev(src, "src"), nb, _stream_ptr(stream)),
            "kda_copy_probe")
 

@@ -52,20 +52,46 @@ def flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always; a build check must compile).  Returns the
-    path of the .so.  The output is written atomically."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(), *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so;
     # that notice is expected and is filtered out of the log.
     noise = ("packed-fp32-ops' is not a recognized feature", "argument unused during compilation")
     log = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if not any(n in l for n in noise))
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, log))
+    return r.returncode, log
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always; a build check must compile).  Returns the
+    path of the .so.  Each source compiles to its own object, in parallel
+    (no device code crosses files), then one link; the output is written
+    atomically."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    tmp = LIB + ".tmp%d" % os.getpid()
+    compile_flags = [f for f in flags() if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="kda_build_") as work:
+        objs = [os.path.join(work, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *compile_flags, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with ThreadPoolExecutor(len(cmds)) as ex:
+            results = list(ex.map(_run, cmds))
+        logs = []
+        for (rc, log), src in zip(results, SOURCES):
+            if rc != 0:
+                raise RuntimeError("hipcc failed on %s (%d):\n%s" % (src, rc, log))
+            logs.append(log)
+        link = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, log = _run(link)
+        if rc != 0:
+            raise RuntimeError("hipcc link failed (%d):\n%s" % (rc, log))
+        logs.append(log)
+    log = "\n".join(l for l in logs if l.strip())
     if verbose and log.strip():
         print(log)
     os.replace(tmp, LIB)

@@ -128,20 +128,15 @@ __device__ int seq_of_rank(const int32_t* cu, int n_seq, int rank) {
   return rank;  // not reached: the ranks are a permutation of 0 .. n_seq - 1
 }
 
-// Raw buffer stores: a 128-bit descriptor {base, range in bytes, word 3} in
-// scalar registers and a per-lane byte offset; the hardware drops a store
-// whose offset is past the range.
-using i32x4 = int __attribute__((ext_vector_type(4)));
-__device__ void raw_buffer_store_f32(float v, i32x4 rsrc, int voffset, int soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.store.f32");
-__device__ __forceinline__ i32x4 buffer_descriptor(const void* base, uint32_t range_bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = static_cast<int>(static_cast<uint32_t>(p));
-  r[1] = static_cast<int>(static_cast<uint32_t>(p >> 32));  // stride 0: raw buffer
-  r[2] = static_cast<int>(range_bytes);
-  r[3] = kBufferWord3;
-  return r;
+// Raw buffer stores: a 128-bit descriptor {base, stride 0, range in bytes,
+// word 3} in scalar registers and a per-lane byte offset; the hardware drops
+// a store whose offset is past the range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_descriptor(const void* base, uint32_t range_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(range_bytes), kBufferWord3);
+}
+__device__ __forceinline__ void raw_buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, voffset, 0, 0);
 }
 
 __device__ __forceinline__ f4 mma(float a, float b, f4 c) {
@@ -591,7 +586,7 @@ void kda_prefill_kernel(PrefillArgs a) {
       // token, so the hardware drops the rows past the sequence without a
       // branch (a branch around the stores would make the next chunk's first
       // use of the prefetched rows wait for every store to be acknowledged).
-      const i32x4 orsrc =
+      const __amdgpu_buffer_rsrc_t orsrc =
           buffer_descriptor(a.out + (c0 * hk + static_cast<int64_t>(h) * 128 + col_w),
                             (static_cast<uint32_t>(n - 1) * hk32 + CPW) * 4);
 #pragma unroll
@@ -603,7 +598,7 @@ void kda_prefill_kernel(PrefillArgs a) {
           for (int cb = 0; cb < NCB; ++cb)
             raw_buffer_store_f32(
                 a.scale * O[tb][cb][r], orsrc,
-                static_cast<int>((tr * hk32 + static_cast<uint32_t>(16 * cb + li)) * 4), 0, 0);
+                static_cast<int>((tr * hk32 + static_cast<uint32_t>(16 * cb + li)) * 4));
         }
     }
     // S = 2^(G_C) S + Kd^T Delta
@@ -989,7 +984,7 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
 #pragma unroll
           for (int tb = kb; tb < NB; ++tb) O[tb] = mma(x[tb][r], reg[kD + kb][r], O[tb]);
       }
-      const i32x4 orsrc =
+      const __amdgpu_buffer_rsrc_t orsrc =
           buffer_descriptor(a.out + (cs * hk + static_cast<int64_t>(h) * 128 + col_w),
                             (static_cast<uint32_t>(ns - 1) * hk32 + 16) * 4);
 #pragma unroll
@@ -998,7 +993,7 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
         for (int r = 0; r < 4; ++r) {
           const uint32_t tr = static_cast<uint32_t>(16 * tb + 4 * gq + r);
           raw_buffer_store_f32(a.scale * O[tb][r], orsrc,
-                               static_cast<int>((tr * hk32 + static_cast<uint32_t>(li)) * 4), 0, 0);
+                               static_cast<int>((tr * hk32 + static_cast<uint32_t>(li)) * 4));
         }
     }
     __syncthreads();

@@ -22,13 +22,16 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load oracle/libkda_oracle.so, compiling it first if it is missing."""
+    """Load oracle/libkda_oracle.so, compiling it first if it is missing.
+    KDA_ORACLE_LIB names another build of the same source to load instead
+    (the tests' sanitizer run)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
+    path = os.environ.get("KDA_ORACLE_LIB") or _build.LIB
+    if path == _build.LIB and not os.path.exists(path):
         _build.build()
-    L = ctypes.CDLL(_build.LIB)
+    L = ctypes.CDLL(path)
     c_f = ctypes.POINTER(ctypes.c_float)
     c_d = ctypes.POINTER(ctypes.c_double)
     c_i = ctypes.POINTER(ctypes.c_int32)

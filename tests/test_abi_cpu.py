@@ -404,3 +404,28 @@ def test_prefill_refusals():
 def test_prefill_validate(init, dst, cu, n_tokens, code):
     assert B.kda_prefill_validate(pool(n_slots=16), init, cu, n_tokens, B.KDA_F32,
                                   dst_slot_ids_host=dst) == code
+
+
+def test_binding_refuses_host_tensors():
+    """The library dereferences device addresses only: the binding refuses a
+    CPU tensor for any buffer with a TypeError before the library is
+    called, and a copy length past either buffer with a ValueError."""
+    torch = pytest.importorskip("torch")
+    f = lambda *s: torch.zeros(*s, dtype=torch.float32)  # noqa: E731
+    ids = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.kda_decode_step(f(8, 2, 128, 128), ids, f(4, 2, 128), f(4, 2, 128), f(4, 2, 128),
+                          f(4, 2, 128), f(4, 2), f(4, 2, 128))
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.make_pool(f(8, 2, 128, 128))
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B._dev(f(4), "q")
+    with pytest.raises(TypeError, match="torch tensor"):
+        B._dev(np.zeros(4, np.float32), "q")
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.kda_prefill(f(8, 2, 128, 128), ids, torch.zeros(5, dtype=torch.int32), f(4, 2, 128),
+                      f(4, 2, 128), f(4, 2, 128), f(4, 2, 128), f(4, 2), f(4, 2, 128))
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.kda_state_copy(f(8, 2, 128, 128), ids, ids)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.kda_copy_probe(f(16), f(16))

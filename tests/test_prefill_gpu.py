@@ -145,19 +145,30 @@ def test_prefill_strong_decay_takes_the_exact_path(oracle):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
-def test_prefill_full_batch_sampled(oracle, dtype):
-    """The bench's workload (32 ragged prompts, ~34K tokens, H = 12) in the
-    launch configuration the bench times; the oracle recomputes the three
-    shortest prompts (all heads) and every output must be finite."""
+def test_prefill_full_batch(oracle, dtype):
+    """The bench's workload (32 ragged prompts of 264 to 1778 tokens, 34,463
+    in all, H = 12) in the launch configuration the bench times.  The oracle
+    recomputes every prompt (about 5 s of CPU): every final state and every
+    output row is graded, the longest prompts (about 56 chunks, where the
+    chunked form's reassociation has the most steps to accumulate) included.
+    The worst prompts are printed."""
     inp = kda_inputs.prefill_batch(dtype)
     gp, go = run_gpu(inp)
     T = inp.n_tokens
     assert np.all(np.isfinite(go[:T]))
+    ref32, oo, _ = oracle_f32_states(oracle, inp)
+    check_state(oracle, inp, gp, ref32, inp.dst_slot_ids)
     lens = np.diff(inp.cu_seqlens)
-    seqs = [int(s) for s in np.argsort(lens, kind="stable")[:3]]
-    ref32, oo, idx = oracle_f32_states(oracle, inp, seqs)
-    check_state(oracle, inp, gp, ref32, inp.dst_slot_ids[seqs])
-    assert out_rel(go[idx], oo) <= OUT_REL
+    per_seq = [out_rel(go[inp.cu_seqlens[s]:inp.cu_seqlens[s + 1]],
+                       oo[inp.cu_seqlens[s]:inp.cu_seqlens[s + 1]]) for s in range(lens.size)]
+    worst = np.argsort(per_seq)[::-1][:3]
+    print("prefill full batch %s: worst out rel %s at lengths %s" % (
+        dtype, ["%.3g" % per_seq[s] for s in worst], [int(lens[s]) for s in worst]), flush=True)
+    if inp.dtype == "f32":
+        errs = [float(np.max(np.abs(gp[d] - ref32[d]))) for d in inp.dst_slot_ids]
+        print("  state abs max %.3g (longest prompt %.3g)" % (max(errs), errs[int(np.argmax(lens))]),
+              flush=True)
+    assert out_rel(go[:T], oo[:T]) <= OUT_REL
 
 
 @pytest.mark.parametrize("n_seq,in_place", [(100, False), (300, True)])

@@ -28,7 +28,13 @@ from gpu_helpers import (B, F16_ULP, OUT_REL, STATE_ABS_F32, check_parity, devic
 pytestmark = pytest.mark.gpu
 
 MATRIX = dict(rows_layout=B.KDA_ROWS_MATRIX)
-STRONG_DECAY_OUT_REL = 1e-4  # outputs against fp64 where the fp32 oracle itself exceeds 1e-5
+
+
+def strong_decay_bound(oracle_err64: float) -> float:
+    """Output bound against fp64 where decays are strong enough that the
+    fp32 oracle's own outputs leave 1e-5: the kernel may be at most half as
+    far again from fp64 as the oracle's own rounding (and always 1e-5)."""
+    return max(OUT_REL, 1.5 * oracle_err64)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -202,14 +208,18 @@ def test_decays_of_minus_5_per_row(oracle, dtype):
         assert np.max(np.abs(gp[written] - o_pool32[written])) <= STATE_ABS_F32
     else:
         assert f16_ulp_distance(gp[written], o_pool32[written]).max() <= F16_ULP
-    # Under decays this strong the fp32 oracle's own outputs are 1.5e-5 from
-    # fp64 here, so outputs are graded against fp64 at 1e-4, as the prefill's
-    # strong-decay case is; the row-after-row kernel is reported beside it.
+    # Under decays this strong the fp32 oracle's own outputs are about 1.5e-5
+    # from fp64 here, so outputs are graded against fp64 relative to the
+    # oracle's own error; the row-after-row layout is held to the same bound.
+    o_err = out_rel_err(o_out32, o_out64)
+    bound = strong_decay_bound(o_err)
     err = out_rel_err(go, o_out64)
     _, go_seq = run_gpu(inp, rows_layout=B.KDA_ROWS_K_SPLIT)
-    say("edge decay %s: out rel vs fp64 %.3g (row after row %.3g, fp32 oracle %.3g)" % (
-        dtype, err, out_rel_err(go_seq, o_out64), out_rel_err(o_out32, o_out64)))
-    assert err <= STRONG_DECAY_OUT_REL
+    err_seq = out_rel_err(go_seq, o_out64)
+    say("edge decay %s: out rel vs fp64 %.3g (row after row %.3g, fp32 oracle %.3g, bound %.3g)" % (
+        dtype, err, err_seq, o_err, bound))
+    assert err <= bound
+    assert err_seq <= bound
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
@@ -228,11 +238,18 @@ def test_heads_in_different_decay_regimes(oracle, dtype):
         assert f16_ulp_distance(gp[written], o_pool32[written]).max() <= F16_ULP
     # heads 0 and 2: the decode bound; head 1 (decays of -12 per row: the
     # fp32 oracle's outputs are 2e-5 from fp64) the strong-decay bound
-    # against fp64
+    # against fp64, relative to the oracle's own error; the row-after-row
+    # layout is held to the same bounds
     both = [0, 2]
-    assert out_rel_err(go[:, both], o_out32[:, both]) <= OUT_REL
-    assert out_rel_err(go[:, both], o_out64[:, both]) <= OUT_REL
-    assert out_rel_err(go[:, 1:2], o_out64[:, 1:2]) <= STRONG_DECAY_OUT_REL
+    _, go_seq = run_gpu(inp, rows_layout=B.KDA_ROWS_K_SPLIT)
+    bound = strong_decay_bound(out_rel_err(o_out32[:, 1:2], o_out64[:, 1:2]))
+    say("mixed decay %s: head 1 out rel vs fp64 %.3g (row after row %.3g, bound %.3g)" % (
+        dtype, out_rel_err(go[:, 1:2], o_out64[:, 1:2]), out_rel_err(go_seq[:, 1:2], o_out64[:, 1:2]),
+        bound))
+    for o in (go, go_seq):
+        assert out_rel_err(o[:, both], o_out32[:, both]) <= OUT_REL
+        assert out_rel_err(o[:, both], o_out64[:, both]) <= OUT_REL
+        assert out_rel_err(o[:, 1:2], o_out64[:, 1:2]) <= bound
 
 
 def test_64bit_pool_offsets(oracle):
