@@ -64,8 +64,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--dtype", choices=["f32", "f16"], default="f32")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
-    ap.add_argument("--extras", choices=["all", "copy"], default="all",
-                    help="'copy' runs only the plain-copy probe after the main workload")
+    ap.add_argument("--extras", choices=["all", "copy", "probes"], default="all",
+                    help="'copy' runs only the plain-copy probe after the main workload, "
+                         "'probes' only the bandwidth probes")
     ap.add_argument("--eager", action="store_true",
                     help="launch eagerly instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -368,6 +369,8 @@ def main():
         # latter rotates over >= 1 GiB of buffer pairs like the decode pools
         for label, nbytes in (("copy_probe_1GiB", 1 << 30),
                               ("copy_probe_same_bytes", (state_bytes // 2) // 16 * 16)):
+            if args.extras == "probes":
+                break
             pairs = max(1, math.ceil((1 << 30) / (2 * nbytes)))
             bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
                      torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(pairs)]
@@ -379,8 +382,19 @@ def main():
                              "GB/s_read_plus_write": round(2 * nbytes / (tc["launch_ms_mean"] * 1e-3) / 1e9, 1),
                              "us": round(tc["launch_ms_mean"] * 1e3, 2)}
             del bufs
-        rec["pct_of_copy_bandwidth"] = round(100.0 * achieved / extras["copy_probe_1GiB"]["GB/s_read_plus_write"], 2)
-        other = () if args.extras == "copy" else (
+        if args.extras in ("all", "probes"):
+            probes = bandwidth_probes(B, torch, state_bytes)
+            extras["bandwidth_probes"] = probes
+            best = max(v["GB/s"] for k, v in probes.items() if k.startswith("copy_") and "1GiB" in k)
+            rec["achievable_copy_GB/s"] = best
+            rec["pct_of_copy_bandwidth"] = round(100.0 * achieved / best, 2)
+            tp = probes.get("tile_pattern_" + args.dtype)
+            if tp is not None:
+                rec["pct_of_tile_pattern"] = round(100.0 * tp["us"] / (t["launch_ms_mean"] * 1e3), 2)
+        else:
+            rec["pct_of_copy_bandwidth"] = round(
+                100.0 * achieved / extras["copy_probe_1GiB"]["GB/s_read_plus_write"], 2)
+        other = () if args.extras in ("copy", "probes") else (
                         ("batched_f16" if args.dtype == "f32" else "batched_f32",
                           kda_inputs.batched_f16 if args.dtype == "f32" else kda_inputs.batched_f32),
                          ("spec_verify_f16", kda_inputs.spec_verify_f16),
@@ -432,6 +446,65 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(main_inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def bandwidth_probes(B, torch, step_state_bytes):
+    """What this GPU reaches on plain traffic, measured like the decode
+    (graph replay, buffers rotated over >= 1 GiB where one is smaller):
+    streaming copies (plain or nontemporal, 1, 2 or 4 16-byte vectors per
+    thread) at 1 GiB, the best of them at 100 MB and 4 GiB, read-only and
+    write-only streams at 1 GiB and at one decode step's bytes, and the decode
+    launch's own tile traffic (kda_tile_probe: same grid, layout and
+    nontemporal loads and stores, no arithmetic) on the batched workloads'
+    rotated pools.  GB/s counts every byte read plus every byte written."""
+    import kda_inputs
+    GiB = 1 << 30
+    res = {}
+
+    def run(label, mode, v, nt, nbytes):
+        nbytes = nbytes // 16 * 16
+        moved = nbytes * (2 if mode == B.KDA_PROBE_COPY else 1)
+        sets = max(1, math.ceil(GiB / moved))
+        bufs = []
+        for _ in range(sets):
+            src = None
+            if mode != B.KDA_PROBE_WRITE:
+                src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+                src.fill_(1)
+            dst = torch.empty(nbytes if mode != B.KDA_PROBE_READ else 16, dtype=torch.uint8, device="cuda")
+            bufs.append((src, dst))
+        tc = time_launches(lambda i: B.kda_bw_probe(bufs[i % sets][1], bufs[i % sets][0], nbytes, mode, v, nt),
+                           max(20, 2 * sets), 3, torch)
+        us = tc["launch_ms_mean"] * 1e3
+        res[label] = {"bytes_moved": moved, "buffer_sets_rotated": sets, "us": round(us, 2),
+                      "GB/s": round(moved / us / 1e3, 1)}
+        del bufs
+        torch.cuda.empty_cache()
+
+    C, R, W = B.KDA_PROBE_COPY, B.KDA_PROBE_READ, B.KDA_PROBE_WRITE
+    for v in (1, 2, 4):
+        run("copy_nt_v%d_1GiB" % v, C, v, True, GiB // 2)
+        run("copy_plain_v%d_1GiB" % v, C, v, False, GiB // 2)
+    best_v = max((1, 2, 4), key=lambda v: res["copy_nt_v%d_1GiB" % v]["GB/s"])
+    run("copy_nt_v%d_100MB" % best_v, C, best_v, True, 50 * 10 ** 6)
+    run("copy_nt_v%d_4GiB" % best_v, C, best_v, True, 2 * GiB)
+    for nt, tag in ((True, "nt"), (False, "plain")):
+        run("read_%s_v4_1GiB" % tag, R, 4, nt, GiB)
+        run("write_%s_v4_1GiB" % tag, W, 4, nt, GiB)
+    half = step_state_bytes // 2
+    run("read_nt_v4_step_bytes", R, 4, True, half)
+    run("write_nt_v4_step_bytes", W, 4, True, half)
+    run("copy_nt_v%d_step_bytes" % best_v, C, best_v, True, half)
+    for dtype, fn in (("f32", kda_inputs.batched_f32), ("f16", kda_inputs.batched_f16)):
+        inp = fn(0)
+        w = Workload(inp, ROT, torch)
+        tc = time_launches(lambda i: B.kda_tile_probe(w.pools[i % len(w.pools)], w.ids), 100, 10, torch)
+        us = tc["launch_ms_mean"] * 1e3
+        res["tile_pattern_" + dtype] = {"bytes_moved": inp.state_bytes(), "pools_rotated": len(w.pools),
+                                        "us": round(us, 2), "GB/s": round(inp.state_bytes() / us / 1e3, 1)}
+        del w
+        torch.cuda.empty_cache()
+    return res
 
 
 def summarize(inp, tt):

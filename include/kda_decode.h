@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5  /* 5: KDA_ROWS_MATRIX, and rows_layout for kda_decode_step_conv */
+#define KDA_ABI_VERSION 6  /* 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -432,6 +432,44 @@ int32_t kda_tile_of_block(int32_t block, int32_t n_blocks);
  * bandwidth and hardware byte counters.  Both pointers 16-byte aligned.
  */
 int kda_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
+
+/*
+ * kda_bw_probe -- measurement helper: a streaming kernel over `bytes` (a
+ * multiple of 16) on `stream`, to set the decode's bandwidth against what the
+ * GPU reaches on plain traffic (ROCm/ATOM PR #2130, What: the production
+ * kernel is quoted at 71-90% of "achievable" bandwidth, which the pages leave
+ * undefined).
+ *  mode                KDA_PROBE_COPY: read src, write dst; KDA_PROBE_READ:
+ *                      read src only (dst must be a 16-byte device buffer it
+ *                      never writes in practice); KDA_PROBE_WRITE: write dst
+ *                      only (src may be NULL).
+ *  vectors_per_thread  1, 2 or 4 16-byte vectors per thread, all loads
+ *                      issued before the first store; consecutive threads
+ *                      on consecutive vectors.
+ *  nontemporal         non-zero: loads and stores carry the nontemporal
+ *                      hint, as the decode's state traffic does.
+ * Both pointers 16-byte aligned; src and dst hold at least `bytes` (dst 16
+ * bytes for KDA_PROBE_READ).  Errors: KDA_ERR_NULL, KDA_ERR_ALIGN,
+ * KDA_ERR_ARG (mode, vectors_per_thread, bytes), KDA_ERR_LAUNCH.
+ */
+#define KDA_PROBE_COPY 0
+#define KDA_PROBE_READ 1
+#define KDA_PROBE_WRITE 2
+int kda_bw_probe(void* dst, const void* src, size_t bytes, int32_t mode,
+                 int32_t vectors_per_thread, int32_t nontemporal, void* stream);
+
+/*
+ * kda_tile_probe -- measurement helper: the memory traffic of a single-row
+ * decode launch over n_req requests with the arithmetic taken out.  Same grid
+ * and block-to-tile map as kda_decode_step at its default shape for launches
+ * bound by bandwidth (kda_tile_bv columns; fp32 2 waves, fp16 1 wave), same
+ * slot id load, lane layout and 16-byte nontemporal loads; each tile is
+ * written back unchanged, in place, to slot_ids[r].  slot_ids: device int32
+ * [n_req]; an id out of range skips its request.  Errors: as kda_state_copy
+ * for the pool; KDA_ERR_ARG (n_req outside [0, n_slots]).
+ */
+int kda_tile_probe(const kda_pool* pool, const int32_t* slot_ids, int32_t n_req,
+                   kda_dtype state_dtype, void* stream);
 
 /* Message for a kda_status code (static string, never NULL). */
 const char* kda_strerror(int code);

@@ -43,6 +43,9 @@ KDA_ROWS_DEFAULT = 0
 KDA_ROWS_K_SPLIT = 1
 KDA_ROWS_WAVE_K = 2
 KDA_ROWS_MATRIX = 3
+KDA_PROBE_COPY = 0
+KDA_PROBE_READ = 1
+KDA_PROBE_WRITE = 2
 
 
 class kda_pool(ctypes.Structure):
@@ -103,6 +106,8 @@ SIGNATURES = {
                                            ctypes.POINTER(kda_launch_desc)]),
     "kda_tile_of_block": (_I32, [_I32, _I32]),
     "kda_copy_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "kda_bw_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _I32, _I32, _I32, _P]),
+    "kda_tile_probe": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _I32, ctypes.c_int, _P]),
     "kda_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_abi_version": (ctypes.c_int, []),
 }
@@ -421,6 +426,39 @@ def kda_copy_probe(dst, src, nbytes: int | None = None, stream=None) -> None:
         raise ValueError("nbytes %d outside [0, %d], the smaller buffer's size" % (nb, cap))
     _check(library().kda_copy_probe(_dev(dst, "dst"), _dev(src, "src"), nb, _stream_ptr(stream)),
            "kda_copy_probe")
+
+
+def kda_bw_probe(dst, src, nbytes: int, mode: int = KDA_PROBE_COPY, vectors_per_thread: int = 1,
+                 nontemporal: bool = True, stream=None) -> None:
+    """Streaming bandwidth probe over nbytes (see kda_bw_probe in
+    include/kda_decode.h): copy src -> dst, read src only, or write dst
+    only.  nbytes may not exceed the buffers it reads or writes (dst: 16
+    bytes for a read-only probe)."""
+    _on_gpu(dst, "dst")
+    nb = int(nbytes)
+    dst_need = 16 if mode == KDA_PROBE_READ else nb
+    if nb < 0 or dst.numel() * dst.element_size() < dst_need:
+        raise ValueError("dst holds fewer than the %d bytes the probe writes" % dst_need)
+    if mode != KDA_PROBE_WRITE:
+        _on_gpu(src, "src")
+        if src.device != dst.device:
+            raise TypeError("dst is on %s, src on %s" % (dst.device, src.device))
+        if src.numel() * src.element_size() < nb:
+            raise ValueError("src holds fewer than the %d bytes the probe reads" % nb)
+    _check(library().kda_bw_probe(_dev(dst, "dst"), None if mode == KDA_PROBE_WRITE else _dev(src, "src"),
+                                  nb, int(mode), int(vectors_per_thread), int(bool(nontemporal)),
+                                  _stream_ptr(stream)), "kda_bw_probe")
+
+
+def kda_tile_probe(pool, slot_ids, stream=None) -> None:
+    """The single-row decode launch's state traffic without its arithmetic
+    (see kda_tile_probe in include/kda_decode.h): each request's tiles of
+    slot slot_ids[r] are read and written back unchanged."""
+    import torch
+    P = make_pool(pool)
+    n_req = slot_ids.numel()
+    _check(library().kda_tile_probe(ctypes.byref(P), _dev(slot_ids, "slot_ids", torch.int32, pool.device),
+                                    n_req, P.dtype, _stream_ptr(stream)), "kda_tile_probe")
 
 
 def kda_strerror(code: int) -> str:

@@ -3,7 +3,8 @@
     python -m kda_gated_delta_decode_amd.build [-v]
 
 Compiles csrc/kda_decode.hip (decode kernels and launch entry points),
-csrc/kda_prefill.hip (the chunked prefill) and csrc/kda_host.cpp (validation, addressing, sizing) with hipcc into
+csrc/kda_prefill.hip (the chunked prefill), csrc/kda_probe.hip (bandwidth
+probes) and csrc/kda_host.cpp (validation, addressing, sizing) with hipcc into
 kda_gated_delta_decode_amd/libkda_decode.so.  Flags:
   --offload-arch=gfx950          MI355X only
   -ffp-contract=off              no implicit multiply-add fusion: every fused
@@ -26,7 +27,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda_decode.so")
 SOURCES = [os.path.join(CSRC, "kda_decode.hip"), os.path.join(CSRC, "kda_prefill.hip"),
-           os.path.join(CSRC, "kda_host.cpp")]
+           os.path.join(CSRC, "kda_probe.hip"), os.path.join(CSRC, "kda_host.cpp")]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,188 @@
+// kda_probe.hip -- measurement helpers of the KDA decode library: streaming
+// bandwidth probes and the decode tile's own access pattern without its
+// arithmetic.  None of them is on the decode path; they exist so that the
+// bandwidth a decode launch reaches can be set against what this GPU reaches
+// on the same traffic (ROCm/ATOM PR #2130, What: the production kernel is
+// quoted as a fraction of achievable bandwidth, a figure the pages do not
+// define; these probes define it here).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda_decode.h"
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int kProbeThreads = 256;
+
+// One workgroup covers kProbeThreads * V consecutive 16-byte vectors; thread
+// x takes vectors x, x + 256, ..., so every wave instruction touches 1 KiB of
+// consecutive bytes.  All loads of a thread are issued before its first
+// store.  MODE: KDA_PROBE_COPY (src -> dst), KDA_PROBE_READ (src only; the
+// loaded bits are folded and written to dst[0] only if they equal `tag`,
+// which the caller makes impossible, so no byte is written in practice but
+// the loads cannot be dropped), KDA_PROBE_WRITE (dst only: the vector index).
+template <int MODE, int V, bool NT>
+__global__ __launch_bounds__(kProbeThreads) void kda_bw_probe_kernel(const f4* __restrict__ src,
+                                                                     f4* __restrict__ dst, int64_t n,
+                                                                     uint32_t tag) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kProbeThreads * V + threadIdx.x;
+  if constexpr (MODE == KDA_PROBE_WRITE) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = base + static_cast<int64_t>(j) * kProbeThreads;
+      if (i < n) {
+        const float x = static_cast<float>(i);
+        const f4 w = f4{x, x, x, x};
+        if constexpr (NT)
+          __builtin_nontemporal_store(w, dst + i);
+        else
+          dst[i] = w;
+      }
+    }
+  } else {
+    f4 r[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t i = base + static_cast<int64_t>(j) * kProbeThreads;
+      if (i < n) r[j] = NT ? __builtin_nontemporal_load(src + i) : src[i];
+    }
+    if constexpr (MODE == KDA_PROBE_COPY) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int64_t i = base + static_cast<int64_t>(j) * kProbeThreads;
+        if (i < n) {
+          if constexpr (NT)
+            __builtin_nontemporal_store(r[j], dst + i);
+          else
+            dst[i] = r[j];
+        }
+      }
+    } else {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int64_t i = base + static_cast<int64_t>(j) * kProbeThreads;
+        if (i < n)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc ^= __float_as_uint(r[j][e]);
+      }
+      if (acc == tag) dst[0] = f4{0.0f, 0.0f, 0.0f, 1.0f};
+    }
+  }
+}
+
+template <int MODE, bool NT>
+hipError_t launch_bw(int v, const f4* src, f4* dst, int64_t n, hipStream_t s) {
+  const int64_t per = static_cast<int64_t>(kProbeThreads) * v;
+  const int64_t blocks = (n + per - 1) / per;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(blocks));
+  const uint32_t tag = 0x5a5a5a5au;
+  switch (v) {
+    case 1: hipLaunchKernelGGL((kda_bw_probe_kernel<MODE, 1, NT>), grid, dim3(kProbeThreads), 0, s, src, dst, n, tag); break;
+    case 2: hipLaunchKernelGGL((kda_bw_probe_kernel<MODE, 2, NT>), grid, dim3(kProbeThreads), 0, s, src, dst, n, tag); break;
+    case 4: hipLaunchKernelGGL((kda_bw_probe_kernel<MODE, 4, NT>), grid, dim3(kProbeThreads), 0, s, src, dst, n, tag); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The single-row decode launch's memory traffic with the arithmetic taken
+// out: the same grid, the same XCD-aware block-to-tile map, the same slot id
+// load and the same lane-to-row layout and 16-byte nontemporal loads and
+// stores of the state tile; each tile is read and written back in place
+// (xor with a zero the compiler cannot see, so the store is not elided).
+template <typename T, int LPR, int NW>
+__global__ __launch_bounds__(kWave * NW) void kda_tile_probe_kernel(T* pool, const int32_t* slot_ids,
+                                                                    int32_t n_slots, int32_t H,
+                                                                    int32_t n_vt, uint32_t zero) {
+  constexpr int CPL = 16 / static_cast<int>(sizeof(T));
+  constexpr int BV = LPR * CPL;
+  constexpr int GROUPS = kWave / LPR;
+  constexpr int RPW = kHeadK / NW;
+  constexpr int RPL = RPW / GROUPS;
+  using u4 = uint32_t __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int row0 = wave * RPW + (lane / LPR) * RPL;
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int vt = tile % n_vt;
+  const int rh = tile / n_vt;
+  const int h = rh % H;
+  const int r = rh / H;
+  const int32_t sid = slot_ids[r];
+  if (sid < 0 || sid >= n_slots) return;  // as the decode: a bad id is skipped
+  const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
+  const int64_t off = static_cast<int64_t>(sid) * H * head_elems + h * head_elems +
+                      static_cast<int64_t>(row0) * kHeadV + vt * BV + (lane % LPR) * CPL;
+  u4* p = reinterpret_cast<u4*>(pool + off);
+  u4 raw[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) raw[m] = __builtin_nontemporal_load(p + m * (kHeadV / CPL));
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) __builtin_nontemporal_store(raw[m] ^ zero, p + m * (kHeadV / CPL));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" int kda_bw_probe(void* dst, const void* src, size_t bytes, int32_t mode,
+                            int32_t vectors_per_thread, int32_t nontemporal, void* stream) {
+  if (mode != KDA_PROBE_COPY && mode != KDA_PROBE_READ && mode != KDA_PROBE_WRITE) return KDA_ERR_ARG;
+  if (vectors_per_thread != 1 && vectors_per_thread != 2 && vectors_per_thread != 4) return KDA_ERR_ARG;
+  if (dst == nullptr || (mode != KDA_PROBE_WRITE && src == nullptr)) return KDA_ERR_NULL;
+  if (!aligned16(dst) || !aligned16(src)) return KDA_ERR_ALIGN;
+  if (bytes % 16 != 0) return KDA_ERR_ARG;
+  if (bytes == 0) return KDA_OK;
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  const f4* s = static_cast<const f4*>(src);
+  f4* d = static_cast<f4*>(dst);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const int v = vectors_per_thread;
+  if (mode == KDA_PROBE_COPY)
+    e = nontemporal ? launch_bw<KDA_PROBE_COPY, true>(v, s, d, n, st) : launch_bw<KDA_PROBE_COPY, false>(v, s, d, n, st);
+  else if (mode == KDA_PROBE_READ)
+    e = nontemporal ? launch_bw<KDA_PROBE_READ, true>(v, s, d, n, st) : launch_bw<KDA_PROBE_READ, false>(v, s, d, n, st);
+  else
+    e = nontemporal ? launch_bw<KDA_PROBE_WRITE, true>(v, s, d, n, st) : launch_bw<KDA_PROBE_WRITE, false>(v, s, d, n, st);
+  if (e == hipErrorInvalidValue) return KDA_ERR_ARG;
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+extern "C" int kda_tile_probe(const kda_pool* pool, const int32_t* slot_ids, int32_t n_req,
+                              kda_dtype state_dtype, void* stream) {
+  if (pool == nullptr || pool->base == nullptr) return KDA_ERR_NULL;
+  if (state_dtype != KDA_F32 && state_dtype != KDA_F16) return KDA_ERR_DTYPE_REFUSED;
+  if (pool->dtype != state_dtype) return KDA_ERR_DTYPE_MISMATCH;
+  if (pool->K != kHeadK || pool->V != kHeadV || pool->H < 1 || pool->n_slots < 1) return KDA_ERR_SHAPE;
+  if (n_req < 0 || n_req > pool->n_slots) return KDA_ERR_ARG;
+  if (n_req == 0) return KDA_OK;
+  if (slot_ids == nullptr) return KDA_ERR_NULL;
+  if (!aligned16(pool->base) || (reinterpret_cast<uintptr_t>(slot_ids) & 3u) != 0) return KDA_ERR_ALIGN;
+  const int32_t bv = tile_bv(state_dtype);
+  const int32_t nw = default_waves_per_tile(state_dtype, 1);
+  const int64_t blocks = static_cast<int64_t>(n_req) * pool->H * (kHeadV / bv);
+  if (blocks > INT32_MAX) return KDA_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the single-row default shapes of launches bound by bandwidth
+  if (state_dtype == KDA_F32 && bv == 128 && nw == 2)
+    hipLaunchKernelGGL((kda_tile_probe_kernel<float, 32, 2>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kWave * 2), 0, s, static_cast<float*>(pool->base), slot_ids, pool->n_slots, pool->H,
+                       kHeadV / bv, 0u);
+  else if (state_dtype == KDA_F16 && bv == 64 && nw == 1)
+    hipLaunchKernelGGL((kda_tile_probe_kernel<_Float16, 8, 1>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kWave), 0, s, static_cast<_Float16*>(pool->base), slot_ids, pool->n_slots, pool->H,
+                       kHeadV / bv, 0u);
+  else
+    return KDA_ERR_ARG;  // the default shapes changed: this probe follows them
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}

@@ -34,7 +34,8 @@ def test_header_declares_the_abi():
                      "kda_state_copy", "kda_decode_step_conv", "kda_prefill",
                      "kda_prefill_validate",
                      "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
-                     "kda_copy_probe", "kda_strerror", "kda_abi_version"]:
+                     "kda_copy_probe", "kda_bw_probe", "kda_tile_probe", "kda_strerror",
+                     "kda_abi_version"]:
         assert expected in names
 
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 5
+    assert B.kda_abi_version() == 6
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -429,3 +430,24 @@ def test_binding_refuses_host_tensors():
         B.kda_state_copy(f(8, 2, 128, 128), ids, ids)
     with pytest.raises(TypeError, match="GPU tensor"):
         B.kda_copy_probe(f(16), f(16))
+
+
+def test_probe_refusals_before_any_hip_call():
+    lib = B.library()
+    f = ctypes.c_void_p(FAKE)
+    assert lib.kda_bw_probe(f, f, 64, 3, 1, 1, None) == B.KDA_ERR_ARG        # mode
+    assert lib.kda_bw_probe(f, f, 64, 0, 3, 1, None) == B.KDA_ERR_ARG        # vectors per thread
+    assert lib.kda_bw_probe(f, f, 60, 0, 1, 1, None) == B.KDA_ERR_ARG        # not whole vectors
+    assert lib.kda_bw_probe(None, f, 64, 0, 1, 1, None) == B.KDA_ERR_NULL
+    assert lib.kda_bw_probe(f, None, 64, 1, 1, 1, None) == B.KDA_ERR_NULL    # a read needs src
+    assert lib.kda_bw_probe(ctypes.c_void_p(FAKE + 4), f, 64, 0, 1, 1, None) == B.KDA_ERR_ALIGN
+    assert lib.kda_bw_probe(f, f, 0, 0, 4, 0, None) == B.KDA_OK             # empty: no launch
+    ids = ctypes.c_void_p(FAKE)
+    assert lib.kda_tile_probe(None, ids, 4, B.KDA_F32, None) == B.KDA_ERR_NULL
+    assert lib.kda_tile_probe(ctypes.byref(pool(dtype=B.KDA_BF16)), ids, 4, B.KDA_BF16, None) == \
+        B.KDA_ERR_DTYPE_REFUSED
+    assert lib.kda_tile_probe(ctypes.byref(pool()), ids, 4, B.KDA_F16, None) == B.KDA_ERR_DTYPE_MISMATCH
+    assert lib.kda_tile_probe(ctypes.byref(pool(Kd=64)), ids, 4, B.KDA_F32, None) == B.KDA_ERR_SHAPE
+    assert lib.kda_tile_probe(ctypes.byref(pool(n_slots=3)), ids, 4, B.KDA_F32, None) == B.KDA_ERR_ARG
+    assert lib.kda_tile_probe(ctypes.byref(pool()), None, 4, B.KDA_F32, None) == B.KDA_ERR_NULL
+    assert lib.kda_tile_probe(ctypes.byref(pool()), ids, 0, B.KDA_F32, None) == B.KDA_OK

@@ -159,7 +159,9 @@ def test_matrix_block_form_runs_its_column_sums_on_the_matrix_cores(disassembly)
 
 
 def test_fp16_state_is_narrowed_to_nearest_even(disassembly):
-    f16 = {n: ops for n, ops in disassembly.items() if "kda" in n and "DF16_" in n}
+    # every kernel that stores an fp16 state it computed in fp32 (the probes
+    # only move bits)
+    f16 = {n: ops for n, ops in disassembly.items() if "kda" in n and "DF16_" in n and "probe" not in n}
     assert len(f16) >= 30
     for name, ops in f16.items():
         # packed (decode) or one value at a time (the prefill's final state)
