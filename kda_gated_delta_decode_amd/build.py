@@ -13,6 +13,7 @@ kda_gated_delta_decode_amd/libkda_decode.so.  Flags:
                                  arithmetic
   -target-feature -packed-fp32-ops   keep the compiler from forming packed
                                  fp32 instructions
+  -amdgpu-kernarg-preload-count=14   preload the leading kernel arguments
 """
 from __future__ import annotations
 
@@ -47,6 +48,9 @@ def flags() -> list[str]:
         "-shared",
         "-ffp-contract=off",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # kernels whose leading arguments are plain pointers and integers get
+        # the first 14 argument dwords preloaded into scalar registers
+        "-mllvm", "-amdgpu-kernarg-preload-count=14",
         "-Wall",
         "-I", INCLUDE,
         "-I", CSRC,

@@ -1097,7 +1097,7 @@ struct Piece4<_Float16> {
 };
 
 constexpr int kMfmaBV = kMatrixBV;  // columns per half (per workgroup without the convolution)
-constexpr int kMfmaWaves = kMatrixWaves;
+constexpr int kMfmaWaves = kMatrixWaves4;  // waves per half of the 4-wave form
 constexpr int kLdRow = kHeadK + 4;  // padded row stride of the [t][channel] LDS arrays
 
 // The couplings P_ts (s <= t) and C_ts (s < t) for the two columns s = W and
@@ -1526,6 +1526,249 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
 }
 
 // ---------------------------------------------------------------------------
+// The same block form with K split over 8 waves (kda_rows_mfma8_kernel<T>,
+// the default layout of chained rows on the matrix cores, without the
+// convolution).  Workgroup = (request, head, 64-column half), 8 waves: wave w
+// holds key rows 16 w .. 16 w + 15, lane (gq, li) rows 16 w + 4 gq + j (j <
+// 4) and columns 4 li .. 4 li + 3 of the half, so each state load or store
+// instruction still covers whole 128-byte (fp16) or 256-byte (fp32) rows of
+// the half.  Against the 4-wave form, each wave runs half the matrix-core
+// steps (16 instead of 32 of v_mfma_f32_16x16x4_f32) and half the snapshot
+// work per row, and two waves share each SIMD, so one wave's vector work
+// runs while the other's products or stores are in flight.  Each wave loads
+// and normalises one row of the request (one 8-byte q, k and g vector per
+// lane): the prologue issues 4 row loads per wave instead of 22.  The eight
+// waves' partial column sums meet in LDS in two steps (each thread sums one
+// 8-byte piece over the waves, then every lane reads the 16 totals of its
+// column), which keeps the LDS traffic of the 4-wave form.
+//
+// The leading kernel arguments are plain pointers and integers (14 dwords),
+// which the dispatcher preloads into scalar registers, so the slot ids and
+// the row inputs are requested without first fetching the arguments from
+// memory; the block count is one of them (the block-to-tile map needs it
+// before anything else, and the grid size would be another fetch).  `dims`
+// packs H (bits 0..15), the rows per request (16..19) and the stride of the
+// initial-slot table (20..23: 1 for init_slot_ids, n_rows when the row-0 ids
+// serve as the initial slots).
+// ---------------------------------------------------------------------------
+constexpr int kMfma8Waves = 8;
+
+template <typename T>
+__global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(
+    const int32_t* __restrict__ slot_ids, const int32_t* __restrict__ init_ids, void* pool_v,
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
+    int32_t n_blocks, int32_t dims, Args a) {
+  using vec = typename Piece4<T>::vec;
+  constexpr int TMAX = KDA_MAX_ROWS;
+  constexpr int NW = kMfma8Waves;
+  constexpr int BH = kMfmaBV;          // columns per workgroup (one half of a head)
+  constexpr int RPW = kHeadK / NW;     // key rows per wave
+  constexpr int J = RPW / 4;           // key rows per lane (= matrix-core steps)
+  static_assert(TMAX == NW, "one row of the request per wave");
+
+  __shared__ __attribute__((aligned(16))) float s_kn[TMAX][kLdRow];
+  __shared__ __attribute__((aligned(16))) float s_qn[TMAX][kLdRow];
+  __shared__ __attribute__((aligned(16))) float s_a[TMAX][kLdRow];
+  __shared__ __attribute__((aligned(16))) float s_v[TMAX][BH];
+  // [wave][gq][column] = the wave's D[4 gq + r][column], r = 0..3
+  __shared__ __attribute__((aligned(16))) f4 s_part[NW][4][BH];
+  // [gq][column] = the totals over the waves
+  __shared__ __attribute__((aligned(16))) f4 s_tot[4][BH];
+  __shared__ __attribute__((aligned(16))) float s_cP[TMAX][TMAX];
+  __shared__ __attribute__((aligned(16))) float s_cA[TMAX][TMAX];
+  __shared__ __attribute__((aligned(16))) float s_beta[TMAX];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int gq = lane / 16, li = lane % 16;
+  const int H = dims & 0xFFFF;
+  const int n_rows = (dims >> 16) & 0xF;
+  const int init_stride = (dims >> 20) & 0xF;
+
+  const int tile = tile_of_block(blockIdx.x, n_blocks);
+  const int vt = tile % (kHeadV / BH);
+  const int rh = tile / (kHeadV / BH);
+  const int h = rh % H;
+  const int r = rh / H;
+  const int hcol = vt * BH;
+
+  const int32_t* ids = slot_ids + static_cast<int64_t>(r) * n_rows;
+  int32_t sid[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
+  const int32_t init_slot = init_ids[static_cast<int64_t>(r) * init_stride];
+
+  // This wave's row of the request (a wave past the last row re-reads the
+  // last one and stages zeros).
+  int zero_v;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
+  const int trow = min(wave, n_rows - 1);
+  const int64_t rho = static_cast<int64_t>(r) * n_rows + trow;
+  const int64_t roff = (rho * H + h) * kHeadK;
+  const f2 q2 = reinterpret_cast<const f2*>(q + roff)[lane];
+  const f2 k2 = reinterpret_cast<const f2*>(k + roff)[lane];
+  const f2 g2 = reinterpret_cast<const f2*>(g + roff)[lane];
+  const float v1 = a.v[roff + hcol + lane];
+  const float braw = a.b[rho * H + h + zero_v];
+  __builtin_amdgcn_sched_barrier(0);
+
+  bool ids_ok = init_slot >= 0 && init_slot < a.n_slots;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
+
+  // The initial state: rows 16 wave + 4 gq + j, columns 4 li .. 4 li + 3 of the half.
+  const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
+  const int64_t slot_elems = static_cast<int64_t>(H) * head_elems;
+  const int row0 = RPW * wave + J * gq;
+  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + hcol + 4 * li;
+  T* const pool = static_cast<T*>(pool_v);
+  vec raw[J];
+  {
+    const T* src = pool + static_cast<int64_t>(ids_ok ? init_slot : 0) * slot_elems + lane_off;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(src + j * kHeadV));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  {
+    const bool live = wave < n_rows;
+    const float sq = wave_sum(fmaf(q2[1], q2[1], q2[0] * q2[0]));
+    const float sk = wave_sum(fmaf(k2[1], k2[1], k2[0] * k2[0]));
+    const float rq = live ? 1.0f / sqrtf(sq + 1e-6f) : 0.0f;
+    const float rk = live ? 1.0f / sqrtf(sk + 1e-6f) : 0.0f;
+    *reinterpret_cast<f2*>(&s_qn[wave][2 * lane]) = f2{q2[0] * rq, q2[1] * rq};
+    *reinterpret_cast<f2*>(&s_kn[wave][2 * lane]) = f2{k2[0] * rk, k2[1] * rk};
+    *reinterpret_cast<f2*>(&s_a[wave][2 * lane]) =
+        live ? f2{expf(g2[0]), expf(g2[1])} : f2{0.0f, 0.0f};
+    s_v[wave][lane] = live ? v1 : 0.0f;
+    if (lane == 0) s_beta[wave] = live ? 1.0f / (1.0f + expf(-braw)) : 0.0f;
+  }
+  if (!ids_ok) {  // uniform over the workgroup: no wave waits at the barrier
+    if (wave < n_rows) {
+      const int64_t orow = static_cast<int64_t>(r) * n_rows + wave;
+      a.out[(orow * H + h) * kHeadV + hcol + lane] = NAN;
+    }
+    return;
+  }
+  __syncthreads();
+
+  // couplings (waves 0..3: two columns of the n x n matrices each), then
+  // this wave's share of w0 and p0 on the matrix cores
+  switch (wave) {  // wave-uniform
+    case 0: coupling_pair<0>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+    case 1: coupling_pair<1>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+    case 2: coupling_pair<2>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+    case 3: coupling_pair<3>(s_kn, s_qn, s_a, lane, s_cP, s_cA); break;
+    default: break;
+  }
+  float S[J][4];
+  {
+    // weight row li: gamma_t kn_t (li < 8) or gamma_t qn_t, t = li mod 8,
+    // with gamma_t = a_0 ... a_t multiplied in row order
+    const int tw = li & 7;
+    float x[J], gm[J];
+    lds_rows<J>(li < 8 ? &s_kn[tw][row0] : &s_qn[tw][row0], x);
+#pragma unroll
+    for (int j = 0; j < J; ++j) gm[j] = 1.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < TMAX; ++s2) {
+      float as[J];
+      lds_rows<J>(&s_a[s2][row0], as);
+#pragma unroll
+      for (int j = 0; j < J; ++j) gm[j] = s2 <= tw ? gm[j] * as[j] : gm[j];
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[j][e] = static_cast<float>(raw[j][e]);
+    f4 acc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float wj = gm[j] * x[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(wj, S[j][e], acc[e], 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_part[wave][gq][4 * li + e] = acc[e];
+  }
+  __syncthreads();
+  // totals over the waves: thread i sums the 8-byte piece (i mod 2) of entry
+  // i / 2 of the [4][64] f4 array, in a fixed tree order
+  {
+    const int ent = threadIdx.x >> 1, pc = threadIdx.x & 1;
+    const int eg = ent / BH, ec = ent % BH;
+    f2 x[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x[w] = reinterpret_cast<const f2*>(&s_part[w][eg][ec])[pc];
+    const f2 t01 = x[0] + x[1], t23 = x[2] + x[3], t45 = x[4] + x[5], t67 = x[6] + x[7];
+    reinterpret_cast<f2*>(&s_tot[eg][ec])[pc] = (t01 + t23) + (t45 + t67);
+  }
+  __syncthreads();
+
+  // Every wave solves the 64 columns of the half (lane l: column l) and
+  // writes row t's snapshot as soon as Delta_t is known; wave t writes row
+  // t's outputs.  The couplings and beta are the same for every column: each
+  // lane reads one and the solve takes them with readlane (the empty
+  // volatile asm keeps those reads in every lane).
+  float cA_l = s_cA[lane >> 3][lane & 7];
+  float cP_l = s_cP[lane >> 3][lane & 7];
+  float bt_l = s_beta[lane & 7];
+  asm volatile("" : "+v"(cA_l), "+v"(cP_l), "+v"(bt_l));
+  auto cA = [&](int t, int s2) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cA_l), 8 * t + s2)); };
+  auto cP = [&](int t, int s2) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cP_l), 8 * t + s2)); };
+  float tot[16], vv[TMAX];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const f4 x = s_tot[gi][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tot[4 * gi + e] = x[e];
+  }
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][lane];
+  float* op = a.out + (static_cast<int64_t>(r) * n_rows * H + h) * kHeadV + hcol + lane;
+  const int64_t o_row = static_cast<int64_t>(H) * kHeadV;
+  float dl[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if (t >= n_rows) break;
+    float d = vv[t] - tot[t];
+#pragma unroll
+    for (int s2 = 0; s2 < t; ++s2) d = fmaf(-cA(t, s2), dl[s2], d);
+    dl[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt_l), t)) * d;
+    if (t == wave) {  // this wave writes row t's outputs of the half
+      float o = tot[8 + t];
+#pragma unroll
+      for (int s2 = 0; s2 <= t; ++s2) o = fmaf(cP(t, s2), dl[s2], o);
+      op[t * o_row] = a.scale * o;
+    }
+    // Delta_t of the lane's snapshot columns 4 li .. 4 li + 3
+    float dc[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dc[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * li + e), __float_as_int(dl[t])));
+    float kn[J], am[J];
+    lds_rows<J>(&s_kn[t][row0], kn);
+    lds_rows<J>(&s_a[t][row0], am);
+    T* dst = pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      vec o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float s1 = fmaf(kn[j], dc[e], am[j] * S[j][e]);
+        asm("" : "+v"(s1));  // a rounded fp32 value before any narrowing
+        S[j][e] = s1;
+        o[e] = static_cast<T>(s1);
+      }
+      __builtin_nontemporal_store(o, reinterpret_cast<vec*>(dst + j * kHeadV));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming copy used to calibrate bandwidth and byte counters: one 16-byte
 // vector per thread, consecutive threads on consecutive vectors (the copy
 // form that measured fastest on MI355X, ahead of grid-stride loops).
@@ -1629,7 +1872,16 @@ template <typename T>
 static hipError_t dispatch(const Args& a, const Shape& sh, int32_t blocks, hipStream_t s) {
   if (sh.layout == KDA_ROWS_WAVE_K) return dispatch_rows<T>(a, sh, blocks, s);
   if (sh.layout == KDA_ROWS_MATRIX) {
-    hipLaunchKernelGGL((kda_rows_mfma_kernel<T, false>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s, a);
+    if (matrix_waves(sh.nw, a.H) == kMatrixWaves) {
+      // the row-0 ids serve as initial slots unless a table is given
+      const int32_t* init = a.init_slot_ids != nullptr ? a.init_slot_ids : a.slot_ids;
+      const int32_t stride = a.init_slot_ids != nullptr ? 1 : a.n_rows;
+      const int32_t dims = a.H | (a.n_rows << 16) | (stride << 20);
+      hipLaunchKernelGGL((kda_rows_mfma8_kernel<T>), dim3(blocks), dim3(kWave * kMatrixWaves), 0, s,
+                         a.slot_ids, init, a.pool, a.q, a.k, a.g, blocks, dims, a);
+    } else {
+      hipLaunchKernelGGL((kda_rows_mfma_kernel<T, false>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s, a);
+    }
     return hipGetLastError();
   }
   const int lpr = sh.bv / Lane16<T>::kCols;

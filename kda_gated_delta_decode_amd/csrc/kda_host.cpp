@@ -126,7 +126,7 @@ int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtyp
   Shape shape;
   if (!resolve_shape(dtype, n_rows, static_cast<int64_t>(n_req) * H, opts, &shape)) return KDA_ERR_ARG;
   const int32_t bv = shape.bv;
-  const int32_t nw = shape.nw;
+  const int32_t nw = shape.layout == KDA_ROWS_MATRIX ? matrix_waves(shape.nw, H) : shape.nw;
   const int64_t tiles = static_cast<int64_t>(n_req) * H * (kHeadV / bv);
   if (tiles > INT32_MAX) return KDA_ERR_ARG;
   desc->bv = bv;
@@ -136,7 +136,8 @@ int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtyp
   desc->blocks = static_cast<int32_t>(tiles);
   desc->lds_bytes = lds_bytes(bv, nw, n_rows, opts != nullptr && opts->block_rows != 0, shape.layout);
   desc->kernel = shape.layout == KDA_ROWS_WAVE_K   ? "kda_rows_kernel"
-                 : shape.layout == KDA_ROWS_MATRIX ? "kda_rows_mfma_kernel"
+                 : shape.layout == KDA_ROWS_MATRIX ? (nw == kMatrixWaves ? "kda_rows_mfma8_kernel"
+                                                                         : "kda_rows_mfma_kernel")
                                                    : "kda_decode_tile";
   desc->rows_layout = shape.layout;
   return KDA_OK;

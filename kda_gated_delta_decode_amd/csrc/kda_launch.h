@@ -117,11 +117,21 @@ inline int32_t default_wave_k_waves(kda_dtype /*dt*/) { return 4; }
 // The chained-rows block form: fp16 pools need at least 2 waves per tile.
 inline bool block_supported(kda_dtype dt, int32_t nw) { return dt != KDA_F16 || nw > 1; }
 
-// The matrix-core block form of chained rows: one shape (with the fused
-// convolution, whole heads: two 64-column halves of 4 waves).
+// The matrix-core block form of chained rows: 64 columns per workgroup, K
+// over 8 waves by default or over 4 (the first form, kept selectable); with
+// the fused convolution, whole heads: two 64-column halves of 4 waves.
+// Measured on MI355X (8 requests x 8 rows x 12 heads, fp16, graph replay,
+// rotated pools): see the kernel's header for the figures.
 constexpr int32_t kMatrixBV = 64;
-constexpr int32_t kMatrixWaves = 4;
-constexpr int32_t kMatrixConvWaves = 2 * kMatrixWaves;
+constexpr int32_t kMatrixWaves = 8;
+constexpr int32_t kMatrixWaves4 = 4;
+constexpr int32_t kMatrixConvWaves = 2 * kMatrixWaves4;
+// the 8-wave form packs H into 16 bits of a kernel argument; above that the
+// 4-wave form runs
+constexpr int32_t kMatrixMaxHeads8 = 0xFFFF;
+inline int32_t matrix_waves(int32_t nw, int32_t H) {
+  return nw == kMatrixWaves && H > kMatrixMaxHeads8 ? kMatrixWaves4 : nw;
+}
 
 struct Shape {
   int32_t bv;      // value columns per workgroup
@@ -138,12 +148,12 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, int64_t units, const kda
   if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX) return false;
   const int32_t layout = n_rows > 1 ? chained_rows_layout(dt, opts, units) : KDA_ROWS_K_SPLIT;
   if (layout == KDA_ROWS_MATRIX) {
-    // one fixed shape: 64 columns over 4 waves; a block form whatever
+    // 64 columns over 8 waves (default) or 4; a block form whatever
     // block_rows says
     const bool bv_ok = opts == nullptr || opts->bv == 0 || opts->bv == kMatrixBV;
-    const bool nw_ok = opts == nullptr || opts->waves_per_tile == 0 || opts->waves_per_tile == kMatrixWaves;
-    *out = Shape{kMatrixBV, kMatrixWaves, KDA_ROWS_MATRIX};
-    return bv_ok && nw_ok;
+    const int32_t nw = opts == nullptr || opts->waves_per_tile == 0 ? kMatrixWaves : opts->waves_per_tile;
+    *out = Shape{kMatrixBV, nw, KDA_ROWS_MATRIX};
+    return bv_ok && (nw == kMatrixWaves || nw == kMatrixWaves4);
   }
   // the K-split block form
   if (n_rows > 1 && opts != nullptr && opts->block_rows != 0 && layout == KDA_ROWS_WAVE_K) return false;
@@ -174,9 +184,12 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, int64_t units, const kda
 // and the two coupling matrices [KDA_MAX_ROWS][KDA_MAX_ROWS].
 inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block, int32_t layout) {
   if (layout == KDA_ROWS_MATRIX) {
-    // kn, qn, decays, cumulative decays [8][132]; v [8][bv]; the waves'
-    // partial sums [nw][16][bv]; two 8 x 8 couplings; beta
     constexpr int32_t t = KDA_MAX_ROWS;
+    // 8 waves: kn, qn, decays [8][132]; v [8][bv]; the waves' partial sums
+    // [8][16][bv] and their totals [16][bv]; two 8 x 8 couplings; beta
+    if (nw == kMatrixWaves) return 4 * (3 * t * (kHeadK + 4) + t * bv + (nw + 1) * 16 * bv + 2 * t * t + t);
+    // 4 waves (and the convolution's two halves of 4): kn, qn, decays,
+    // cumulative decays [8][132]; v [8][bv]; partial sums [nw][16][64]
     return 4 * (4 * t * (kHeadK + 4) + t * bv + nw * 16 * kMatrixBV + 2 * t * t + t);
   }
   const int32_t tmax = n_rows == 1 ? 1 : KDA_MAX_ROWS;

@@ -89,9 +89,9 @@ def test_refusals_before_any_hip_call():
     assert step(pool(dtype=B.KDA_F16), n_rows=8, opts=B.kda_launch_opts(1, 64, 1)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(4, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(1, 16, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
-    # the matrix-core block form has one shape: 64 columns over 4 waves
+    # the matrix-core block form: 64 columns over 8 (default) or 4 waves
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 32, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
-    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(8, 0, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(2, 0, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
     assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE]) == B.KDA_ERR_ALIGN
@@ -279,8 +279,8 @@ def test_describe_launch():
     # chained rows: the matrix-core block form for fp16 pools (the whole-K
     # layout when a shape option is set), the K split for fp32
     d = B.kda_describe_launch(8, 8, 12, "f16")
-    assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 4, 8 * 12 * 2)
-    assert (d["kernel"], d["rows_layout"]) == ("kda_rows_mfma_kernel", B.KDA_ROWS_MATRIX)
+    assert (d["bv"], d["waves_per_tile"], d["tiles"]) == (64, 8, 8 * 12 * 2)
+    assert (d["kernel"], d["rows_layout"]) == ("kda_rows_mfma8_kernel", B.KDA_ROWS_MATRIX)
     d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=2)
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 2, "kda_rows_kernel")
     d = B.kda_describe_launch(8, 8, 12, "f16", bv=128)
@@ -288,7 +288,7 @@ def test_describe_launch():
     d = B.kda_describe_launch(8, 8, 12, "f32")
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 8, "kda_decode_tile")
     # small fp32 chained-row launches take the matrix-core block form
-    assert B.kda_describe_launch(4, 8, 12, "f32")["kernel"] == "kda_rows_mfma_kernel"
+    assert B.kda_describe_launch(4, 8, 12, "f32")["kernel"] == "kda_rows_mfma8_kernel"
     assert B.kda_describe_launch(5, 8, 12, "f32")["kernel"] == "kda_decode_tile"
     assert B.kda_describe_launch(4, 8, 12, "f32", waves_per_tile=8)["kernel"] == "kda_decode_tile"
     d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8, rows_layout=B.KDA_ROWS_K_SPLIT)
@@ -302,14 +302,19 @@ def test_describe_launch():
         B.kda_describe_launch(8, 8, 12, "f16", block_rows=True, waves_per_tile=1, bv=64)
     d = B.kda_describe_launch(8, 8, 12, "f16", block_rows=True, waves_per_tile=2, bv=64)
     assert (d["bv"], d["waves_per_tile"]) == (64, 2)
-    # the matrix-core block form: one shape, either dtype, block_rows implied
+    # the matrix-core block form: 64 columns over 8 waves (or 4 on request),
+    # either dtype, block_rows implied
     for dt in ("f32", "f16"):
         for blk in (False, True):
             d = B.kda_describe_launch(8, 8, 12, dt, rows_layout=B.KDA_ROWS_MATRIX, block_rows=blk)
-            assert (d["bv"], d["waves_per_tile"], d["threads"], d["tiles"]) == (64, 4, 256, 8 * 12 * 2)
-            assert (d["kernel"], d["rows_layout"]) == ("kda_rows_mfma_kernel", B.KDA_ROWS_MATRIX)
+            assert (d["bv"], d["waves_per_tile"], d["threads"], d["tiles"]) == (64, 8, 512, 8 * 12 * 2)
+            assert (d["kernel"], d["rows_layout"]) == ("kda_rows_mfma8_kernel", B.KDA_ROWS_MATRIX)
+            assert d["lds_bytes"] == 52128
     d = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX, waves_per_tile=4, bv=64)
-    assert (d["bv"], d["waves_per_tile"]) == (64, 4)
+    assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 4, "kda_rows_mfma_kernel")
+    # H beyond 16 bits: the 8-wave form cannot take it and the 4-wave form runs
+    d = B.kda_describe_launch(1, 8, 70000, "f16", rows_layout=B.KDA_ROWS_MATRIX)
+    assert (d["waves_per_tile"], d["kernel"]) == (4, "kda_rows_mfma_kernel")
     for w, bv in ((2, 0), (0, 128)):
         with pytest.raises(B.KdaError):
             B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX, waves_per_tile=w, bv=bv)

@@ -138,24 +138,64 @@ def test_default_single_row_tiles_keep_two_waves_per_simd(kernels):
         assert k[".vgpr_count"] + k.get(".agpr_count", 0) <= 256, (name, k[".vgpr_count"])
 
 
+MFMA8 = ("_ZN3kda21kda_rows_mfma8_kernelIfEEvPKiS2_PvPKfS5_S5_iiNS_4ArgsE",
+         "_ZN3kda21kda_rows_mfma8_kernelIDF16_EEvPKiS2_PvPKfS5_S5_iiNS_4ArgsE")
+MFMA4 = ("_ZN3kda20kda_rows_mfma_kernelIfLb0EEEvNS_4ArgsE",
+         "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb0EEEvNS_4ArgsE")
+
+
 def test_matrix_block_form_lds_matches_the_launch_description(kernels):
     # the host's LDS figure for the matrix-core block form is the kernel's
-    # static LDS, for both pool dtypes
+    # static LDS, for both pool dtypes and both wave counts
     import kda_gated_delta_decode_amd.binding as B
-    want = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX)["lds_bytes"]
-    for name in ("_ZN3kda20kda_rows_mfma_kernelIfLb0EEEvNS_4ArgsE",
-                 "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb0EEEvNS_4ArgsE"):
-        assert kernels[name][".group_segment_fixed_size"] == want, name
+    for names, nw in ((MFMA8, 8), (MFMA4, 4)):
+        want = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX,
+                                     waves_per_tile=nw)["lds_bytes"]
+        for name in names:
+            assert kernels[name][".group_segment_fixed_size"] == want, name
 
 
 def test_matrix_block_form_runs_its_column_sums_on_the_matrix_cores(disassembly):
-    # 8 steps of 4 rows x 4 column offsets: 32 fp32 16x16x4 products per wave
-    # (with and without the fused convolution)
-    for name in ("_ZN3kda20kda_rows_mfma_kernelIfLb0EEEvNS_4ArgsE",
-                 "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb0EEEvNS_4ArgsE",
-                 "_ZN3kda20kda_rows_mfma_kernelIfLb1EEEvNS_4ArgsE",
-                 "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb1EEEvNS_4ArgsE"):
+    # 4 waves: 8 steps of 4 rows x 4 column offsets, 32 fp32 16x16x4 products
+    # per wave (with and without the fused convolution); 8 waves: 4 steps, 16
+    for name in MFMA4 + ("_ZN3kda20kda_rows_mfma_kernelIfLb1EEEvNS_4ArgsE",
+                         "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb1EEEvNS_4ArgsE"):
         assert disassembly[name].count("v_mfma_f32_16x16x4_f32") == 32, name
+    for name in MFMA8:
+        assert disassembly[name].count("v_mfma_f32_16x16x4_f32") == 16, name
+
+
+def kernel_descriptor(code_object, name):
+    """The 64-byte kernel descriptor (symbol NAME.kd) from whichever code
+    object holds it."""
+    for path in code_object["paths"]:
+        syms = subprocess.run([tool("llvm-readelf"), "-s", "-W", path], check=True,
+                              capture_output=True, text=True).stdout
+        hit = [l.split() for l in syms.splitlines() if l.split() and l.split()[-1] == name + ".kd"]
+        if not hit:
+            continue
+        value = int(hit[0][1], 16)
+        secs = subprocess.run([tool("llvm-readelf"), "-S", "-W", path], check=True,
+                              capture_output=True, text=True).stdout
+        for line in secs.splitlines():
+            f = line.replace("[", " ").replace("]", " ").split()
+            if ".rodata" in f:
+                i = f.index(".rodata")
+                addr, off = int(f[i + 2], 16), int(f[i + 3], 16)
+                with open(path, "rb") as fh:
+                    fh.seek(off + value - addr)
+                    return fh.read(64)
+    raise KeyError(name)
+
+
+def test_leading_arguments_are_preloaded(code_object):
+    # the 8-wave chained-rows kernel has its first 14 argument dwords (slot
+    # tables, pool, q, k, g, block count, packed sizes) preloaded into scalar
+    # registers: the descriptor's kernarg_preload field (bytes 58..59, length
+    # in bits 0..6)
+    for name in MFMA8:
+        kd = kernel_descriptor(code_object, name)
+        assert int.from_bytes(kd[58:60], "little") & 0x7F == 14, name
 
 
 def test_fp16_state_is_narrowed_to_nearest_even(disassembly):
