@@ -68,7 +68,7 @@ typedef enum kda_status {
   KDA_ERR_NULL = 1,           /* a required pointer is NULL */
   KDA_ERR_DTYPE_REFUSED = 2,  /* bf16 or an unknown dtype */
   KDA_ERR_DTYPE_MISMATCH = 3, /* state_dtype differs from the pool's dtype */
-  KDA_ERR_SHAPE = 4,          /* K or V != 128, H < 1, n_slots < 1 */
+  KDA_ERR_SHAPE = 4,          /* K or V != 128, H outside [1, 65535], n_slots < 1 */
   KDA_ERR_ROWS = 5,           /* rows per request outside [1, KDA_MAX_ROWS] */
   KDA_ERR_SLOT = 6,           /* slot id out of range or repeated, or more
                                  rows than slots */

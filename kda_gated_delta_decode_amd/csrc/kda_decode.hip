@@ -65,6 +65,48 @@ struct Args {
   float scale;
 };
 
+// Every decode kernel takes the values its first memory requests depend on
+// as leading plain arguments, 13 dwords in all, which the dispatcher
+// preloads into scalar registers (the build asks for 14): the slot tables,
+// the pool, q and k, the block count (the block-to-tile map needs it before
+// anything else; the grid size would be one more fetch), the slot count (the
+// range check of the ids gates the state loads) and the packed sizes
+//   dims = H | n_vt << 16 | n_rows << 20 | init_stride << 24
+// (H < 2^16, n_vt <= 4, n_rows <= 8; init_stride is 1 when an initial-slot
+// table is given and n_rows when the row-0 ids are the initial slots, so the
+// initial slot of request r is init_ids[r * init_stride] either way).  The
+// rest of Args is fetched from memory as usual.
+#define KDA_HOT_PARAMS                                                                         \
+  const int32_t *__restrict__ hot_ids, const int32_t *__restrict__ hot_init, void *hot_pool,     \
+      const float *__restrict__ hot_q, const float *__restrict__ hot_k, int32_t hot_blocks,    \
+      int32_t hot_slots, int32_t hot_dims
+struct Hot {
+  const int32_t* ids;
+  const int32_t* init;
+  void* pool;
+  const float* q;
+  const float* k;
+  int32_t blocks;
+  int32_t slots;
+  int32_t dims;
+};
+#define KDA_HOT_ARGS(h) (h).ids, (h).init, (h).pool, (h).q, (h).k, (h).blocks, (h).slots, (h).dims
+
+// The preloaded values back into Args (the kernels read them from there);
+// returns the initial-slot stride.
+__device__ __forceinline__ int unpack_hot(Args& a, const int32_t* ids, void* pool, const float* q,
+                                          const float* k, int32_t slots, int32_t dims) {
+  a.slot_ids = ids;
+  a.pool = pool;
+  a.q = q;
+  a.k = k;
+  a.n_slots = slots;
+  a.H = dims & 0xFFFF;
+  a.n_vt = (dims >> 16) & 0xF;
+  a.n_rows = (dims >> 20) & 0xF;
+  return (dims >> 24) & 0xF;
+}
+
 // ---------------------------------------------------------------------------
 // 16-byte state vectors: 4 fp32 or 8 fp16 columns of one tile row.
 // ---------------------------------------------------------------------------
@@ -160,7 +202,8 @@ __device__ __forceinline__ void lds_rows(const float* src, float (&dst)[N]) {
 // and the tile stays packed in its storage type, widened where it is used.
 // ---------------------------------------------------------------------------
 template <typename T, int LPR, int NW, bool MULTI, bool CONV, bool BLOCK>
-__global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
+__global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Args a) {
+  const int init_stride = unpack_hot(a, hot_ids, hot_pool, hot_q, hot_k, hot_slots, hot_dims);
   using L = Lane16<T>;
   using vec = typename L::vec;
   constexpr int CPL = L::kCols;         // columns per lane
@@ -200,7 +243,7 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
   const int rg = lane / LPR;
   const int row0 = wave * RPW + rg * RPL;
 
-  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int tile = tile_of_block(blockIdx.x, hot_blocks);
   const int vt = tile % a.n_vt;
   const int rh = tile / a.n_vt;
   const int h = rh % a.H;
@@ -221,7 +264,7 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(Args a) {
     sid[t] = t < n_rows ? ids[t] : 0;
     ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
   }
-  const int32_t init_slot = a.init_slot_ids != nullptr ? a.init_slot_ids[r] : sid[0];
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
   ids_ok = ids_ok && init_slot >= 0 && init_slot < a.n_slots;
   if (!ids_ok) {
     if (writer) {
@@ -863,7 +906,8 @@ __device__ __forceinline__ void wave_column_sums(const float (&x)[2 * C], int la
 }
 
 template <typename T, int LPR, int NWB>
-__global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
+__global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(KDA_HOT_PARAMS, Args a) {
+  const int init_stride = unpack_hot(a, hot_ids, hot_pool, hot_q, hot_k, hot_slots, hot_dims);
   using L = Lane16<T>;
   using vec = typename L::vec;
   constexpr int CPL = L::kCols;           // columns per lane
@@ -892,7 +936,7 @@ __global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
   const int cg = lane % LPR;
   const int row0 = (lane / LPR) * RPL;
 
-  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int tile = tile_of_block(blockIdx.x, hot_blocks);
   const int vt = tile % a.n_vt;
   const int rh = tile / a.n_vt;
   const int h = rh % a.H;
@@ -910,7 +954,7 @@ __global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(Args a) {
   int32_t sid[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
-  const int32_t init_slot = *(a.init_slot_ids != nullptr ? a.init_slot_ids + r : ids);
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
 
   // Row inputs (wave w stages rows w, w + NWB, ...), issued before anything
   // waits on the ids.  Every address is valid whatever n_rows is (a row past
@@ -1166,7 +1210,8 @@ __device__ __forceinline__ void coupling_pair(const float (*kn)[kLdRow], const f
 // 4 waves each, so that the convolution history it reads at the initial slot
 // and rewrites at the rows' slots belongs to no other workgroup.
 template <typename T, bool CONV>
-__global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_mfma_kernel(Args a) {
+__global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_mfma_kernel(KDA_HOT_PARAMS, Args a) {
+  const int init_stride = unpack_hot(a, hot_ids, hot_pool, hot_q, hot_k, hot_slots, hot_dims);
   using vec = typename Piece4<T>::vec;
   constexpr int TMAX = KDA_MAX_ROWS;
   constexpr int HALVES = CONV ? 2 : 1;        // 64-column halves per workgroup
@@ -1191,7 +1236,7 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
   const int half = wave / kMfmaWaves, rw = wave % kMfmaWaves;
   const int gq = lane / 16, li = lane % 16;
 
-  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int tile = tile_of_block(blockIdx.x, hot_blocks);
   const int vt = tile % a.n_vt;
   const int rh = tile / a.n_vt;
   const int h = rh % a.H;
@@ -1203,7 +1248,7 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
   int32_t sid[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
-  const int32_t init_slot = *(a.init_slot_ids != nullptr ? a.init_slot_ids + r : ids);
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
 
   // Row inputs: wave w normalises rows w, w + NW, ... (a row past the last
   // re-reads the last one and is staged as zeros).
@@ -1542,22 +1587,12 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
 // 8-byte piece over the waves, then every lane reads the 16 totals of its
 // column), which keeps the LDS traffic of the 4-wave form.
 //
-// The leading kernel arguments are plain pointers and integers (14 dwords),
-// which the dispatcher preloads into scalar registers, so the slot ids and
-// the row inputs are requested without first fetching the arguments from
-// memory; the block count is one of them (the block-to-tile map needs it
-// before anything else, and the grid size would be another fetch).  `dims`
-// packs H (bits 0..15), the rows per request (16..19) and the stride of the
-// initial-slot table (20..23: 1 for init_slot_ids, n_rows when the row-0 ids
-// serve as the initial slots).
 // ---------------------------------------------------------------------------
 constexpr int kMfma8Waves = 8;
 
 template <typename T>
-__global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(
-    const int32_t* __restrict__ slot_ids, const int32_t* __restrict__ init_ids, void* pool_v,
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ g,
-    int32_t n_blocks, int32_t dims, Args a) {
+__global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA_HOT_PARAMS, Args a) {
+  const int init_stride = unpack_hot(a, hot_ids, hot_pool, hot_q, hot_k, hot_slots, hot_dims);
   using vec = typename Piece4<T>::vec;
   constexpr int TMAX = KDA_MAX_ROWS;
   constexpr int NW = kMfma8Waves;
@@ -1581,22 +1616,21 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int gq = lane / 16, li = lane % 16;
-  const int H = dims & 0xFFFF;
-  const int n_rows = (dims >> 16) & 0xF;
-  const int init_stride = (dims >> 20) & 0xF;
+  const int H = a.H;
+  const int n_rows = a.n_rows;
 
-  const int tile = tile_of_block(blockIdx.x, n_blocks);
+  const int tile = tile_of_block(blockIdx.x, hot_blocks);
   const int vt = tile % (kHeadV / BH);
   const int rh = tile / (kHeadV / BH);
   const int h = rh % H;
   const int r = rh / H;
   const int hcol = vt * BH;
 
-  const int32_t* ids = slot_ids + static_cast<int64_t>(r) * n_rows;
+  const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
   int32_t sid[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
-  const int32_t init_slot = init_ids[static_cast<int64_t>(r) * init_stride];
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
 
   // This wave's row of the request (a wave past the last row re-reads the
   // last one and stages zeros).
@@ -1605,9 +1639,9 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(
   const int trow = min(wave, n_rows - 1);
   const int64_t rho = static_cast<int64_t>(r) * n_rows + trow;
   const int64_t roff = (rho * H + h) * kHeadK;
-  const f2 q2 = reinterpret_cast<const f2*>(q + roff)[lane];
-  const f2 k2 = reinterpret_cast<const f2*>(k + roff)[lane];
-  const f2 g2 = reinterpret_cast<const f2*>(g + roff)[lane];
+  const f2 q2 = reinterpret_cast<const f2*>(a.q + roff)[lane];
+  const f2 k2 = reinterpret_cast<const f2*>(a.k + roff)[lane];
+  const f2 g2 = reinterpret_cast<const f2*>(a.g + roff)[lane];
   const float v1 = a.v[roff + hcol + lane];
   const float braw = a.b[rho * H + h + zero_v];
   __builtin_amdgcn_sched_barrier(0);
@@ -1621,7 +1655,7 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(
   const int64_t slot_elems = static_cast<int64_t>(H) * head_elems;
   const int row0 = RPW * wave + J * gq;
   const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + hcol + 4 * li;
-  T* const pool = static_cast<T*>(pool_v);
+  T* const pool = static_cast<T*>(a.pool);
   vec raw[J];
   {
     const T* src = pool + static_cast<int64_t>(ids_ok ? init_slot : 0) * slot_elems + lane_off;
@@ -1796,21 +1830,37 @@ __global__ __launch_bounds__(256) void kda_state_copy_kernel(
   __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// The preloaded leading arguments of a launch (see KDA_HOT_PARAMS).
+static Hot hot_of(const Args& a, int32_t blocks) {
+  Hot h;
+  h.ids = a.slot_ids;
+  h.init = a.init_slot_ids != nullptr ? a.init_slot_ids : a.slot_ids;
+  h.pool = a.pool;
+  h.q = a.q;
+  h.k = a.k;
+  h.blocks = blocks;
+  h.slots = a.n_slots;
+  const int32_t stride = a.init_slot_ids != nullptr ? 1 : a.n_rows;
+  h.dims = a.H | (a.n_vt << 16) | (a.n_rows << 20) | (stride << 24);
+  return h;
+}
+
 template <typename T, int LPR, int NW>
 static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream) {
+  const Hot h = hot_of(a, blocks);
   if (a.n_rows == 1)
     hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, false, false>), dim3(blocks),
-                       dim3(kWave * NW), 0, stream, a);
+                       dim3(kWave * NW), 0, stream, KDA_HOT_ARGS(h), a);
   else if (a.rows_block) {
     // not instantiated for the shapes resolve_shape refuses (block_supported)
     if constexpr (!std::is_same_v<T, _Float16> || NW > 1)
       hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false, true>), dim3(blocks),
-                         dim3(kWave * NW), 0, stream, a);
+                         dim3(kWave * NW), 0, stream, KDA_HOT_ARGS(h), a);
     else
       return hipErrorInvalidValue;  // unreachable: shapes are checked first
   } else
     hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, false, false>), dim3(blocks),
-                       dim3(kWave * NW), 0, stream, a);
+                       dim3(kWave * NW), 0, stream, KDA_HOT_ARGS(h), a);
   return hipGetLastError();
 }
 
@@ -1818,15 +1868,16 @@ static hipError_t launch_tile(const Args& a, int32_t blocks, hipStream_t stream)
 // row), 2, 4 or 8 waves.
 template <typename T, int LPR, int NW>
 static hipError_t launch_conv(const Args& a, int32_t blocks, hipStream_t stream) {
+  const Hot h = hot_of(a, blocks);
   if (a.n_rows == 1)
     hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, false, true, false>), dim3(blocks),
-                       dim3(kWave * NW), 0, stream, a);
+                       dim3(kWave * NW), 0, stream, KDA_HOT_ARGS(h), a);
   else if (a.rows_block)
     hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, true, true>), dim3(blocks),
-                       dim3(kWave * NW), 0, stream, a);
+                       dim3(kWave * NW), 0, stream, KDA_HOT_ARGS(h), a);
   else
     hipLaunchKernelGGL((kda_decode_tile<T, LPR, NW, true, true, false>), dim3(blocks),
-                       dim3(kWave * NW), 0, stream, a);
+                       dim3(kWave * NW), 0, stream, KDA_HOT_ARGS(h), a);
   return hipGetLastError();
 }
 
@@ -1846,8 +1897,9 @@ static hipError_t launch_rows(const Args& a, int32_t blocks, hipStream_t stream)
   if constexpr (NWB * LPR * Lane16<T>::kCols > kHeadV) {
     return hipErrorInvalidValue;  // unreachable: wave_k_supported() refuses it
   } else {
+    const Hot h = hot_of(a, blocks);
     hipLaunchKernelGGL((kda_rows_kernel<T, LPR, NWB>), dim3(blocks), dim3(kWave * NWB), 0, stream,
-                       a);
+                       KDA_HOT_ARGS(h), a);
     return hipGetLastError();
   }
 }
@@ -1872,16 +1924,13 @@ template <typename T>
 static hipError_t dispatch(const Args& a, const Shape& sh, int32_t blocks, hipStream_t s) {
   if (sh.layout == KDA_ROWS_WAVE_K) return dispatch_rows<T>(a, sh, blocks, s);
   if (sh.layout == KDA_ROWS_MATRIX) {
-    if (matrix_waves(sh.nw, a.H) == kMatrixWaves) {
-      // the row-0 ids serve as initial slots unless a table is given
-      const int32_t* init = a.init_slot_ids != nullptr ? a.init_slot_ids : a.slot_ids;
-      const int32_t stride = a.init_slot_ids != nullptr ? 1 : a.n_rows;
-      const int32_t dims = a.H | (a.n_rows << 16) | (stride << 20);
+    const Hot h = hot_of(a, blocks);
+    if (sh.nw == kMatrixWaves)
       hipLaunchKernelGGL((kda_rows_mfma8_kernel<T>), dim3(blocks), dim3(kWave * kMatrixWaves), 0, s,
-                         a.slot_ids, init, a.pool, a.q, a.k, a.g, blocks, dims, a);
-    } else {
-      hipLaunchKernelGGL((kda_rows_mfma_kernel<T, false>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s, a);
-    }
+                         KDA_HOT_ARGS(h), a);
+    else
+      hipLaunchKernelGGL((kda_rows_mfma_kernel<T, false>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s,
+                         KDA_HOT_ARGS(h), a);
     return hipGetLastError();
   }
   const int lpr = sh.bv / Lane16<T>::kCols;
@@ -2014,12 +2063,13 @@ extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* c
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (shape.layout == KDA_ROWS_MATRIX) {
+    const Hot h = hot_of(a, blocks);
     if (state_dtype == KDA_F32)
       hipLaunchKernelGGL((kda_rows_mfma_kernel<float, true>), dim3(blocks), dim3(kWave * kMatrixConvWaves),
-                         0, s, a);
+                         0, s, KDA_HOT_ARGS(h), a);
     else
       hipLaunchKernelGGL((kda_rows_mfma_kernel<_Float16, true>), dim3(blocks),
-                         dim3(kWave * kMatrixConvWaves), 0, s, a);
+                         dim3(kWave * kMatrixConvWaves), 0, s, KDA_HOT_ARGS(h), a);
     err = hipGetLastError();
   } else {
     err = state_dtype == KDA_F32 ? dispatch_conv<float>(a, shape.nw, blocks, s)

@@ -23,7 +23,7 @@ int check_common(const kda_pool* pool, int32_t n_req, int32_t n_rows,
   if (pool == nullptr || pool->base == nullptr) return KDA_ERR_NULL;
   if (!dtype_known(state_dtype) || !dtype_known(pool->dtype)) return KDA_ERR_DTYPE_REFUSED;
   if (state_dtype != pool->dtype) return KDA_ERR_DTYPE_MISMATCH;
-  if (pool->K != kHeadK || pool->V != kHeadV || pool->H < 1 || pool->n_slots < 1)
+  if (pool->K != kHeadK || pool->V != kHeadV || pool->H < 1 || pool->H > kMaxHeads || pool->n_slots < 1)
     return KDA_ERR_SHAPE;
   if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
   if (n_req < 0) return KDA_ERR_ARG;
@@ -120,13 +120,13 @@ int kda_describe_launch(int32_t n_req, int32_t n_rows, int32_t H, kda_dtype dtyp
                         const kda_launch_opts* opts, kda_launch_desc* desc) {
   if (desc == nullptr) return KDA_ERR_NULL;
   if (!dtype_known(dtype)) return KDA_ERR_DTYPE_REFUSED;
-  if (H < 1) return KDA_ERR_SHAPE;
+  if (H < 1 || H > kMaxHeads) return KDA_ERR_SHAPE;
   if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
   if (n_req < 0) return KDA_ERR_ARG;
   Shape shape;
   if (!resolve_shape(dtype, n_rows, static_cast<int64_t>(n_req) * H, opts, &shape)) return KDA_ERR_ARG;
   const int32_t bv = shape.bv;
-  const int32_t nw = shape.layout == KDA_ROWS_MATRIX ? matrix_waves(shape.nw, H) : shape.nw;
+  const int32_t nw = shape.nw;
   const int64_t tiles = static_cast<int64_t>(n_req) * H * (kHeadV / bv);
   if (tiles > INT32_MAX) return KDA_ERR_ARG;
   desc->bv = bv;
@@ -154,7 +154,7 @@ const char* kda_strerror(int code) {
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_DTYPE_REFUSED: return "state dtype refused: only fp32 and fp16 pools are supported (bf16 is refused, not reinterpreted)";
     case KDA_ERR_DTYPE_MISMATCH: return "state dtype does not match the pool's dtype (it would be read at the wrong element size)";
-    case KDA_ERR_SHAPE: return "unsupported shape: K and V must be 128, H and n_slots at least 1";
+    case KDA_ERR_SHAPE: return "unsupported shape: K and V must be 128, H in [1, 65535], n_slots at least 1";
     case KDA_ERR_ROWS: return "rows per request must be in [1, 8]";
     case KDA_ERR_SLOT: return "slot id out of range or repeated, or more rows than slots";
     case KDA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";

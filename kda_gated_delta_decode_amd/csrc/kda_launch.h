@@ -126,12 +126,8 @@ constexpr int32_t kMatrixBV = 64;
 constexpr int32_t kMatrixWaves = 8;
 constexpr int32_t kMatrixWaves4 = 4;
 constexpr int32_t kMatrixConvWaves = 2 * kMatrixWaves4;
-// the 8-wave form packs H into 16 bits of a kernel argument; above that the
-// 4-wave form runs
-constexpr int32_t kMatrixMaxHeads8 = 0xFFFF;
-inline int32_t matrix_waves(int32_t nw, int32_t H) {
-  return nw == kMatrixWaves && H > kMatrixMaxHeads8 ? kMatrixWaves4 : nw;
-}
+// The kernels take H packed into 16 bits of a kernel argument.
+constexpr int32_t kMaxHeads = 0xFFFF;
 
 struct Shape {
   int32_t bv;      // value columns per workgroup

@@ -81,8 +81,11 @@ static void validate_refusals() {
   CHECK(kda_validate(&p, ids, nullptr, -1, 1, KDA_F32) == KDA_ERR_ARG);
   CHECK(kda_validate(&p, ids, nullptr, 3, 3, KDA_F32) == KDA_ERR_SLOT);  // 9 rows > 8 slots
   // the workgroup count must fit in int32 at the narrowest tile
-  kda_pool huge = make_pool(INT32_MAX, 1 << 20);
-  CHECK(kda_validate(&huge, ids, nullptr, 1 << 20, 1, KDA_F32) == KDA_ERR_ARG);
+  kda_pool huge = make_pool(INT32_MAX, 65535);
+  CHECK(kda_validate(&huge, ids, nullptr, 10000, 1, KDA_F32) == KDA_ERR_ARG);
+  // H is packed into 16 bits of the kernels' arguments
+  kda_pool wide = make_pool(8, 65536);
+  CHECK(kda_validate(&wide, ids, nullptr, 4, 1, KDA_F32) == KDA_ERR_SHAPE);
   CHECK(kda_validate(&p, ids, nullptr, 4, 1, KDA_F32) == KDA_OK);
   CHECK(kda_validate(&p, ids, nullptr, 0, 1, KDA_F32) == KDA_OK);
   const int32_t dup[4] = {0, 1, 1, 3};
@@ -218,6 +221,7 @@ static void describe_launch() {
   CHECK(kda_describe_launch(1, 1, 12, KDA_F32, nullptr, nullptr) == KDA_ERR_NULL);
   CHECK(kda_describe_launch(1, 1, 12, KDA_BF16, nullptr, &d) == KDA_ERR_DTYPE_REFUSED);
   CHECK(kda_describe_launch(1, 1, 0, KDA_F32, nullptr, &d) == KDA_ERR_SHAPE);
+  CHECK(kda_describe_launch(1, 1, 65536, KDA_F32, nullptr, &d) == KDA_ERR_SHAPE);
   CHECK(kda_describe_launch(1, 0, 12, KDA_F32, nullptr, &d) == KDA_ERR_ROWS);
   CHECK(kda_describe_launch(-1, 1, 12, KDA_F32, nullptr, &d) == KDA_ERR_ARG);
   // every default shape, and every option combination: a described launch

@@ -70,6 +70,7 @@ def test_refusals_before_any_hip_call():
     assert step(pool(Kd=64)) == B.KDA_ERR_SHAPE
     assert step(pool(V=256)) == B.KDA_ERR_SHAPE
     assert step(pool(H=0)) == B.KDA_ERR_SHAPE
+    assert step(pool(H=65536)) == B.KDA_ERR_SHAPE
     assert step(pool(), n_rows=0) == B.KDA_ERR_ROWS
     assert step(pool(), n_rows=9) == B.KDA_ERR_ROWS
     assert step(pool(), n_req=-1) == B.KDA_ERR_ARG
@@ -312,9 +313,9 @@ def test_describe_launch():
             assert d["lds_bytes"] == 52128
     d = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX, waves_per_tile=4, bv=64)
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 4, "kda_rows_mfma_kernel")
-    # H beyond 16 bits: the 8-wave form cannot take it and the 4-wave form runs
-    d = B.kda_describe_launch(1, 8, 70000, "f16", rows_layout=B.KDA_ROWS_MATRIX)
-    assert (d["waves_per_tile"], d["kernel"]) == (4, "kda_rows_mfma_kernel")
+    # H is packed into 16 bits of a kernel argument: more heads are refused
+    with pytest.raises(B.KdaError):
+        B.kda_describe_launch(1, 8, 70000, "f16")
     for w, bv in ((2, 0), (0, 128)):
         with pytest.raises(B.KdaError):
             B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX, waves_per_tile=w, bv=bv)
