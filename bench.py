@@ -437,6 +437,8 @@ def main():
                 extras[name] = fused_conv(n_req, n_rows, dt, B, torch, max(50, args.steps // 2))
         if args.extras == "all":
             extras["prefill_" + args.dtype] = prefill_extra(args.dtype, B, torch, 20)
+        if args.extras == "all":
+            extras["long_run_8192"] = long_run_extra(B, torch)
         # a 69-layer decode step: 69 independent 64-slot pools, one launch each
         for dt in (("f32", "f16") if args.extras == "all" else ()):
             extras["layers69_" + dt] = layers69(dt, B, torch, steps=10, warmup=2)
@@ -588,9 +590,74 @@ def prefill_extra(dtype, B, torch, steps):
     return res
 
 
+def long_run_extra(B, torch, n_tokens=8192, chunk=1024):
+    """The long single-slot run (H = 12, fresh seeded inputs per token, one
+    launch per token), fp32 and fp16 pools.  Timing: the n_tokens launches
+    replayed from one HIP graph, us per token.  Drift: the same run launched
+    token by token, each token's stored state kept, against the fp64 oracle
+    run from the same initial state (ROCm/ATOM PR #2130, Note on the default:
+    long-context error is offline numerics), reported per chunk of 1024
+    tokens as max abs and RMS state error; the comparison runs on the GPU
+    in fp64 on the oracle's trajectory."""
+    import numpy as np
+    import kda_inputs
+    from oracle import kda_oracle
+    H = 12
+    s0, q, k, v, g, b = kda_inputs.drift_tokens(n_tokens, seed=0, H=H)
+    dev = torch.device("cuda", 0)
+    d = {n: torch.from_numpy(a).to(dev) for n, a in zip("qkvgb", (q, k, v, g, b))}
+    ids = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((n_tokens, H, 128), device=dev)
+    pools = {"f32": torch.from_numpy(s0.copy()).to(dev),
+             "f16": torch.from_numpy(s0.astype(np.float16)).to(dev)}
+
+    def step(pool, t):
+        sl = slice(t, t + 1)
+        B.kda_decode_step(pool, ids, d["q"][sl], d["k"][sl], d["v"][sl], d["g"][sl], d["b"][sl],
+                          out[sl])
+
+    res = {"tokens": n_tokens, "heads": H, "chunk": chunk}
+    for dt, pool in pools.items():
+        tt = time_launches(lambda i, pool=pool: step(pool, i % n_tokens), n_tokens, 64, torch)
+        res["us_per_token_" + dt] = round(tt["launch_ms_mean"] * 1e3, 3)
+    # drift: fresh pools, token by token, each token's state kept per chunk
+    pools = {"f32": torch.from_numpy(s0.copy()).to(dev),
+             "f16": torch.from_numpy(s0.astype(np.float16)).to(dev)}
+    ref_state = s0[0].astype(np.float64)
+    chain = np.arange(1, chunk + 1, dtype=np.int32)
+    curves = {dt: [] for dt in pools}
+    for c0 in range(0, n_tokens, chunk):
+        sl = slice(c0, c0 + chunk)
+        traj = {dt: torch.empty((chunk, H, 128, 128), dtype=p.dtype, device=dev) for dt, p in pools.items()}
+        for t in range(c0, c0 + chunk):
+            for dt, p in pools.items():
+                step(p, t)
+                traj[dt][t - c0].copy_(p[0])
+        p64 = np.empty((chunk + 1, H, 128, 128), dtype=np.float64)
+        p64[1] = ref_state
+        kda_oracle.step_f64(p64, chain, q[sl], k[sl], v[sl], g[sl], b[sl], n_rows=chunk)
+        ref_state = p64[-1].copy()
+        ref = torch.from_numpy(p64[1:]).to(dev)
+        del p64
+        for dt in pools:
+            diff = traj[dt].double() - ref
+            curves[dt].append({"tokens": [c0, c0 + chunk],
+                               "max_abs": float(diff.abs().max()),
+                               "rms": float(diff.square().mean().sqrt())})
+            del diff
+        del ref, traj
+        torch.cuda.empty_cache()
+    for dt in pools:
+        res["drift_vs_fp64_" + dt] = curves[dt]
+        res["max_abs_" + dt] = max(c["max_abs"] for c in curves[dt])
+    del pools, d, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def layers69(dtype, B, torch, steps, warmup, n_layers=69):
-    """Time 69 back-to-back launches (one per layer pool of 64 slots, one
-    token each) as one decode step."""
+    """Time 69 back-to-back launches (one per layer: its own pool of 64
+    slots and its own row inputs, one token each) as one decode step."""
     import kda_inputs
     H, n = 12, 64
     tdt = torch.float32 if dtype == "f32" else torch.float16
@@ -603,15 +670,19 @@ def layers69(dtype, B, torch, steps, warmup, n_layers=69):
         del p
     inp = kda_inputs.make_inputs("row inputs", n, n, 1, "f32", H=1, seed=0)  # only for ids
     ids = torch.from_numpy(inp.slot_ids).cuda()
-    q = torch.randn((n, H, 128), generator=gen, device="cuda")
-    k = torch.randn((n, H, 128), generator=gen, device="cuda")
-    v = torch.randn((n, H, 128), generator=gen, device="cuda")
-    g = -torch.nn.functional.softplus(torch.randn((n, H, 128), generator=gen, device="cuda"))
-    b = torch.randn((n, H), generator=gen, device="cuda")
-    out = torch.empty((n, H, 128), device="cuda")
+    # every layer its own row inputs and outputs, as in a model (no layer
+    # reads another's q, k, v, g, b from cache)
+    rows = []
+    for _ in range(n_layers):
+        rows.append((torch.randn((n, H, 128), generator=gen, device="cuda"),
+                     torch.randn((n, H, 128), generator=gen, device="cuda"),
+                     torch.randn((n, H, 128), generator=gen, device="cuda"),
+                     -torch.nn.functional.softplus(torch.randn((n, H, 128), generator=gen, device="cuda")),
+                     torch.randn((n, H), generator=gen, device="cuda"),
+                     torch.empty((n, H, 128), device="cuda")))
 
     def one_step(_i):
-        for p in pools:
+        for p, (q, k, v, g, b, out) in zip(pools, rows):
             B.kda_decode_step(p, ids, q, k, v, g, b, out)
     tt = time_launches(one_step, steps, warmup, torch)
     elem = 4 if dtype == "f32" else 2
@@ -621,7 +692,7 @@ def layers69(dtype, B, torch, steps, warmup, n_layers=69):
            "state_GB/s": round(state / (tt["ms_per_step"] * 1e-3) / 1e9, 1),
            "algorithmic_bytes": state + io,
            "frac_of_peak": round((state + io) / (tt["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del pools
+    del pools, rows
     torch.cuda.empty_cache()
     return res
 
