@@ -64,9 +64,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--dtype", choices=["f32", "f16"], default="f32")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
-    ap.add_argument("--extras", choices=["all", "copy", "probes"], default="all",
+    ap.add_argument("--extras", choices=["all", "copy", "probes", "pmc"], default="all",
                     help="'copy' runs only the plain-copy probe after the main workload, "
-                         "'probes' only the bandwidth probes")
+                         "'probes' only the bandwidth probes, 'pmc' the copies that calibrate "
+                         "the byte counters (plain and nontemporal) and the 8 x 8 chained rows")
     ap.add_argument("--eager", action="store_true",
                     help="launch eagerly instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -382,6 +383,20 @@ def main():
                              "GB/s_read_plus_write": round(2 * nbytes / (tc["launch_ms_mean"] * 1e-3) / 1e9, 1),
                              "us": round(tc["launch_ms_mean"] * 1e3, 2)}
             del bufs
+        if args.extras == "pmc":
+            # the nontemporal copy (the decode's state traffic carries the
+            # hint) at the step's bytes and at 1 GiB, then the chained rows
+            for label, nbytes in (("copy_nt_v1_1GiB", 1 << 29), ("copy_nt_v1_step_bytes", state_bytes // 2)):
+                nbytes = nbytes // 16 * 16
+                src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+                dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+                tc = time_launches(lambda i: B.kda_bw_probe(dst, src, nbytes, B.KDA_PROBE_COPY, 1, True), 5, 1, torch)
+                extras[label] = {"bytes_copied": nbytes, "us": round(tc["launch_ms_mean"] * 1e3, 2)}
+                del src, dst
+            inp = kda_inputs.spec_verify_f16(0)
+            w = Workload(inp, ROT, torch)
+            extras["spec_verify_f16"] = summarize(inp, time_launches(lambda i: w.launch(i, B), 20, 2, torch))
+            del w
         if args.extras in ("all", "probes"):
             probes = bandwidth_probes(B, torch, state_bytes)
             extras["bandwidth_probes"] = probes
@@ -391,10 +406,10 @@ def main():
             tp = probes.get("tile_pattern_" + args.dtype)
             if tp is not None:
                 rec["pct_of_tile_pattern"] = round(100.0 * tp["us"] / (t["launch_ms_mean"] * 1e3), 2)
-        else:
+        elif "copy_probe_1GiB" in extras:
             rec["pct_of_copy_bandwidth"] = round(
                 100.0 * achieved / extras["copy_probe_1GiB"]["GB/s_read_plus_write"], 2)
-        other = () if args.extras in ("copy", "probes") else (
+        other = () if args.extras in ("copy", "probes", "pmc") else (
                         ("batched_f16" if args.dtype == "f32" else "batched_f32",
                           kda_inputs.batched_f16 if args.dtype == "f32" else kda_inputs.batched_f32),
                          ("spec_verify_f16", kda_inputs.spec_verify_f16),
@@ -404,6 +419,10 @@ def main():
             w = Workload(inp, ROT, torch)
             tt = time_launches(lambda i: w.launch(i, B), max(50, args.steps // 2), 10, torch)
             extras[name] = summarize(inp, tt)
+            if name == "spec_verify_f16":
+                # counter-derived HBM bytes of the chained-rows kernel (null
+                # unless the committed summary matches the kernel source)
+                extras[name]["traffic"] = pmc_traffic("%s_n64_rows1_spec_verify_8x8" % args.dtype)
             del w
         if args.extras == "all":
             # the same batched step out of place: each request reads slot A
@@ -551,13 +570,14 @@ def fused_conv(n_req, n_rows, dtype, B, torch, steps, **launch):
 
 
 MFMA_F32_PEAK_TFLOPS = 157.3  # AMD MI355X spec: dense fp32 matrix throughput
-# Algorithmic flops of the chunked prefill per (token, head) at 32-token
-# chunks: the three state contractions (Kb S, Qg S, Kd^T Delta: 3 x 2 x 128 x
-# 128 per token), A and P over the block pairs, the block solve and P Delta
-# (each 3 x 16 x 16 x 128 x 2 per 32 tokens).  Padding of ragged chunks is
-# not counted.
-PREFILL_FLOP_PER_TOKEN_HEAD = (3 * 2 * 32 * 128 * 128 + 2 * 3 * 2 * 16 * 16 * 128
-                               + 2 * 3 * 2 * 16 * 16 * 128) // 32
+# Algorithmic flops of the prefill per (token, head): the recurrence's own
+# work, 7 K V (decay, the two column sums over K, the rank-1 update, the
+# read-out).  The chunked form the kernel runs does more, 122,880 per (token,
+# head) at 32-token chunks (the three state contractions plus the block
+# couplings, solve and P Delta); the roofline credits only the method's.
+PREFILL_FLOP_PER_TOKEN_HEAD = 7 * 128 * 128
+PREFILL_CHUNKED_FLOP_PER_TOKEN_HEAD = (3 * 2 * 32 * 128 * 128 + 2 * 3 * 2 * 16 * 16 * 128
+                                       + 2 * 3 * 2 * 16 * 16 * 128) // 32
 
 
 def prefill_extra(dtype, B, torch, steps):
@@ -580,7 +600,9 @@ def prefill_extra(dtype, B, torch, steps):
     us = tt["ms_per_step"] * 1e3
     flops = inp.n_tokens * 12 * PREFILL_FLOP_PER_TOKEN_HEAD
     tfs = flops / (us * 1e-6) / 1e12
+    chunked = inp.n_tokens * 12 * PREFILL_CHUNKED_FLOP_PER_TOKEN_HEAD
     res = {"workload": inp.name, "tokens": inp.n_tokens, "us_per_launch": round(us, 1),
+           "chunked_form_TFLOP/s": round(chunked / (us * 1e-6) / 1e12, 2),
            "tokens_per_s": round(inp.n_tokens / (us * 1e-6)),
            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_F32_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_F32_PEAK_TFLOPS, 4),

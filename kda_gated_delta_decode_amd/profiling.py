@@ -6,11 +6,13 @@ benchmark (kernel durations, HBM traffic per launch).
     python -m kda_gated_delta_decode_amd.profiling pmc --run LABEL FETCH.csv WRITE.csv \
         [--run ...] --command "..." --out FILE.json
 
-`pmc` calibrates the counters on the plain copy kernel of the same runs:
-kda_copy_probe_kernel copies one 16-byte vector per thread, so a dispatch of
-grid G work-items reads and writes 16 G bytes.  FETCH_SIZE and WRITE_SIZE
-(KiB per dispatch) are scaled by (16 G) / (1024 * counter) averaged over the
-copy dispatches, then applied to the decode kernel's mean per dispatch.
+`pmc` calibrates the counters on the copy kernels of the same runs: the
+nontemporal copy (kda_bw_probe_kernel, the hint the decode's state traffic
+carries) and the plain one (kda_copy_probe_kernel) each copy one 16-byte
+vector per work-item, so a dispatch of grid G work-items reads and writes
+16 G bytes.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by
+(16 G) / (1024 * counter), averaged over the nontemporal copy's dispatches,
+then applied to each decode kernel's mean per dispatch.
 
 Reads only the CSV files it is given; runs nothing on the GPU.
 """
@@ -68,57 +70,94 @@ def _counter_by_dispatch(path, counter):
     return out
 
 
+# Calibration kernels: each dispatch of grid G work-items copies 16 G bytes
+# (one 16-byte vector per work-item), plain or with the nontemporal hint.
+CALIBRATION = {
+    "plain": ("kda_copy_probe_kernel",),
+    "nontemporal": ("kda_bw_probe_kernel<0, 1, true>", "kda_bw_probe_kernelILi0ELi1ELb1E"),
+}
+# Kernels whose traffic is summarised: (label suffix, name substrings, workload)
+SUMMARISED = (
+    ("", ("kda_decode_tile",), None),
+    ("_spec_verify_8x8", ("kda_rows_mfma8_kernel",), "spec_verify_f16"),
+)
+
+
+def _calibrate(fe, wr, label, calib):
+    """Counter-to-bytes factors of each calibration kernel found in one run."""
+    out = {}
+    for kind, subs in CALIBRATION.items():
+        for name in fe:
+            if not any(sub in name for sub in subs):
+                continue
+            by_f, by_w = defaultdict(list), defaultdict(list)
+            for grid, v in fe[name]:
+                by_f[16 * grid].append(v)
+            for grid, v in wr.get(name, []):
+                by_w[16 * grid].append(v)
+            for nbytes in sorted(by_f):
+                ff = nbytes / (statistics.mean(by_f[nbytes]) * 1024)
+                wf = nbytes / (statistics.mean(by_w[nbytes]) * 1024)
+                out.setdefault(kind, []).append((ff, wf))
+                calib["%s/%s/%d" % (label, kind, nbytes)] = {
+                    "kernel": name, "bytes_copied": nbytes,
+                    "FETCH_SIZE_KiB": round(statistics.mean(by_f[nbytes]), 1),
+                    "WRITE_SIZE_KiB": round(statistics.mean(by_w[nbytes]), 1),
+                    "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}
+    return out
+
+
 def pmc(args):
     import kda_inputs
-    runs = {}
-    fetch_factors, write_factors, calib = [], [], {}
+    factors = defaultdict(list)
+    calib, runs = {}, {}
     for label, fpath, wpath in args.run:
         fe = _counter_by_dispatch(fpath, "FETCH_SIZE")
         wr = _counter_by_dispatch(wpath, "WRITE_SIZE")
-        for name in fe:
-            if COPY_KERNEL not in name:
+        for kind, fw in _calibrate(fe, wr, label, calib).items():
+            factors[kind].extend(fw)
+        for suffix, subs, workload in SUMMARISED:
+            names = [n for n in fe if any(sub in n for sub in subs)]
+            if not names:
                 continue
-            by_bytes_f, by_bytes_w = defaultdict(list), defaultdict(list)
-            for grid, v in fe[name]:
-                by_bytes_f[16 * grid].append(v)
-            for grid, v in wr.get(name, []):
-                by_bytes_w[16 * grid].append(v)
-            for nbytes in sorted(by_bytes_f):
-                ff = nbytes / (statistics.mean(by_bytes_f[nbytes]) * 1024)
-                wf = nbytes / (statistics.mean(by_bytes_w[nbytes]) * 1024)
-                fetch_factors.append(ff)
-                write_factors.append(wf)
-                calib["%s/%d" % (label, nbytes)] = {
-                    "bytes_copied": nbytes,
-                    "FETCH_SIZE_KiB": round(statistics.mean(by_bytes_f[nbytes]), 1),
-                    "WRITE_SIZE_KiB": round(statistics.mean(by_bytes_w[nbytes]), 1),
-                    "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}
-        dec = [n for n in fe if DECODE_KERNEL in n]
-        if len(dec) != 1:
-            raise SystemExit("run %s: expected one decode kernel, found %r" % (label, dec))
-        runs[label] = (dec[0], fe[dec[0]], wr[dec[0]])
-    ff = statistics.mean(fetch_factors)
-    wf = statistics.mean(write_factors)
+            if len(names) != 1:
+                raise SystemExit("run %s: expected one %s kernel, found %r" % (label, subs, names))
+            runs[label + suffix] = (names[0], fe[names[0]], wr[names[0]], label.split("_")[0], workload)
+    if "nontemporal" not in factors:
+        raise SystemExit("no nontemporal copy dispatch to calibrate on")
+    fac = {kind: (statistics.mean(f for f, _ in v), statistics.mean(w for _, w in v))
+           for kind, v in factors.items()}
+    ff, wf = fac["nontemporal"]
     launches = {}
-    for label, (name, fe, wr) in runs.items():
-        dtype = label.split("_")[0]
-        inp = kda_inputs.batched_f32(0) if dtype == "f32" else kda_inputs.batched_f16(0)
+    for key, (name, fe, wr, dtype, workload) in runs.items():
+        if workload is not None:
+            inp = getattr(kda_inputs, workload)(0)
+        else:
+            inp = kda_inputs.batched_f32(0) if dtype == "f32" else kda_inputs.batched_f16(0)
         fk = statistics.mean(v for _, v in fe)
         wk = statistics.mean(v for _, v in wr)
         rd, wt = fk * 1024 * ff, wk * 1024 * wf
         alg = inp.state_bytes() + inp.io_bytes()
-        launches[label] = {"kernel": name, "dispatches": len(fe),
-                           "FETCH_SIZE_KiB": round(fk, 1), "WRITE_SIZE_KiB": round(wk, 1),
-                           "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wt),
-                           "hbm_bytes_per_launch": int(rd + wt),
-                           "algorithmic_bytes_per_launch": alg,
-                           "hbm_over_algorithmic": round((rd + wt) / alg, 4)}
-    doc = {"what": "HBM traffic of the decode kernel from rocprofv3 --pmc FETCH_SIZE and "
+        launches[key] = {"kernel": name, "dispatches": len(fe),
+                         "FETCH_SIZE_KiB": round(fk, 1), "WRITE_SIZE_KiB": round(wk, 1),
+                         "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wt),
+                         "hbm_bytes_per_launch": int(rd + wt),
+                         "algorithmic_bytes_per_launch": alg,
+                         "hbm_over_algorithmic": round((rd + wt) / alg, 4),
+                         "hbm_bytes_with_plain_copy_factors": int(fk * 1024 * fac["plain"][0] +
+                                                                  wk * 1024 * fac["plain"][1])
+                         if "plain" in fac else None}
+    doc = {"what": "HBM traffic of the decode kernels from rocprofv3 --pmc FETCH_SIZE and "
                    "WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps the same "
-                   "counter to the known bytes of the plain copy kernel in the same runs",
+                   "counter to the known bytes of the nontemporal copy kernel (kda_bw_probe_kernel, "
+                   "one 16-byte vector per work-item) in the same runs: the decode's state loads "
+                   "and stores carry the nontemporal hint.  The plain copy's factors are listed "
+                   "beside them",
            "commands": args.command, "kernel_source_sha256_16": kernel_hash(),
-           "calibration_copy_probe": calib, "fetch_factor": round(ff, 4),
-           "write_factor": round(wf, 4), "launches": launches}
+           "calibration_copies": calib,
+           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+           "plain_copy_factors": [round(x, 4) for x in fac["plain"]] if "plain" in fac else None,
+           "launches": launches}
     with open(args.out, "w") as f:
         json.dump(doc, f, indent=1)
         f.write("\n")
