@@ -516,6 +516,9 @@ def bandwidth_probes(B, torch, step_state_bytes):
     run("read_nt_v4_step_bytes", R, 4, True, half)
     run("write_nt_v4_step_bytes", W, 4, True, half)
     run("copy_nt_v%d_step_bytes" % best_v, C, best_v, True, half)
+    # the 8 x 8 chained rows' snapshot stores alone: 8 snapshots of 96 fp16
+    # (request, head) states, 25.2 MB
+    run("write_nt_v1_spec_verify_snapshot_bytes", W, 1, True, 8 * 96 * 128 * 128 * 2)
     for dtype, fn in (("f32", kda_inputs.batched_f32), ("f16", kda_inputs.batched_f16)):
         inp = fn(0)
         w = Workload(inp, ROT, torch)

@@ -47,21 +47,27 @@ def say(*a):
     sys.stdout.flush()
 
 
+# the default form (K over 8 waves) and the 4-wave form (waves_per_tile = 4)
+FORMS = [0, 4]
+
+
+@pytest.mark.parametrize("waves", FORMS)
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
-def test_full_size_spec_verify(oracle, dtype):
+def test_full_size_spec_verify(oracle, dtype, waves):
     inp = kda_inputs.make_inputs("matrix 8x8", 96, 8, 8, dtype, seed=0)
-    say("matrix block form, 8 req x 8 rows, H=12,", dtype)
-    gp, go = run_gpu(inp, **MATRIX)
+    say("matrix block form, 8 req x 8 rows, H=12,", dtype, "waves", waves or 8)
+    gp, go = run_gpu(inp, waves_per_tile=waves, **MATRIX)
     say(check_parity(oracle, inp, gp, go, label="matrix 8x8 %s" % dtype))
 
 
+@pytest.mark.parametrize("waves", FORMS)
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("n_rows", [2, 3, 4, 5, 6, 7, 8])
-def test_every_row_count(oracle, dtype, n_rows):
+def test_every_row_count(oracle, dtype, n_rows, waves):
     inp = kda_inputs.make_inputs("matrix rows", 40, 40 // n_rows, n_rows, dtype, H=3,
                                  seed=300 + n_rows)
-    gp, go = run_gpu(inp, **MATRIX)
-    check_parity(oracle, inp, gp, go, label="matrix %s n=%d" % (dtype, n_rows))
+    gp, go = run_gpu(inp, waves_per_tile=waves, **MATRIX)
+    check_parity(oracle, inp, gp, go, label="matrix %s n=%d waves %d" % (dtype, n_rows, waves or 8))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
@@ -75,17 +81,19 @@ def test_small_shapes(oracle, dtype, n_req, H, n_rows):
     check_parity(oracle, inp, gp, go, label="matrix small %s %dx%dx%d" % (dtype, n_req, H, n_rows))
 
 
+@pytest.mark.parametrize("waves", FORMS)
 @pytest.mark.parametrize("n_rows", [2, 8])
-def test_fp32_twin_of_fp16_launch(n_rows):
-    """One kernel template for both pools: on the exactly widened state the
-    fp32 arithmetic is identical, so outputs are bit-equal and every fp16
-    snapshot is the RNE of the fp32 one."""
+def test_fp32_twin_of_fp16_launch(n_rows, waves):
+    """One kernel template for both pools, in either form: on the exactly
+    widened state the fp32 arithmetic is identical, so outputs are
+    bit-equal and every fp16 snapshot is the RNE of the fp32 one (ROCm/ATOM
+    PR #2945, Testing: the fp32 twin of spec-verify launches)."""
     inp16 = kda_inputs.make_inputs("twin matrix", 96, 64 // n_rows, n_rows, "f16", seed=26 + n_rows)
     inp32 = kda_inputs.DecodeInputs("twin32", "f32", inp16.pool.view(np.float16).astype(np.float32),
                                     inp16.slot_ids, inp16.q, inp16.k, inp16.v, inp16.g, inp16.b,
                                     n_rows, inp16.scale)
-    p16, o16 = run_gpu(inp16, **MATRIX)
-    p32, o32 = run_gpu(inp32, **MATRIX)
+    p16, o16 = run_gpu(inp16, waves_per_tile=waves, **MATRIX)
+    p32, o32 = run_gpu(inp32, waves_per_tile=waves, **MATRIX)
     np.testing.assert_array_equal(o16.view(np.uint32), o32.view(np.uint32))
     np.testing.assert_array_equal(p16, p32.astype(np.float16).view(np.uint16))
 
