@@ -31,7 +31,23 @@
 // block the s-factor exceeds 1 by at most the block's own decay; should that
 // exceed 2^115 (80 nats) for some channel, the block is computed pair by
 // pair instead.  All exponents are formed from block-local sums, so the ones
-// that matter (close tokens) are small and accurate.
+// that matter (close tokens) are small and accurate.  Kd's exponent G_C - G_s
+// is summed from the decays after token s (in its block, then the totals of
+// the later blocks), never taken as a difference of cumulative sums: for the
+// last tokens of a chunk, whose Kd rows are the largest, it is then exactly 0
+// or small, where a difference would leave about one ulp of the chunk's total
+// decay (a relative error of 1e-6 in Kd at a total of 25 in log2 units).
+// In the 32-token kernel the block-local cumulative decays are compensated
+// sums (fp32 high and low parts, see row_scan2), and A and P take both parts:
+// their in-block factors 2^(G_t - G_s) are products of 2^(+-G) factors whose
+// exponents are large where the decay between t and s is small, so one ulp of
+// G would be a relative error of 1e-6 in an O(1) factor.  (The 64-token
+// kernel keeps plain sums: its LDS has no room for the low parts.)
+// P's diagonal, qn_t . kn_t with no decay, is summed without the two
+// exponentials: their per-channel rounding (about an ulp each, from
+// v_exp_f32) does not cancel in the product, and qn_t . kn_t is often a
+// small difference of terms (0.002 from terms summing to 0.6 in magnitude)
+// that multiplies the token's own, large, Delta_t in its output.
 //
 // Work decomposition.  One workgroup = one (sequence, head).  The default
 // 32-token chunks use the warp-specialised kernel (kda_prefill_ws_kernel):
@@ -158,6 +174,55 @@ __device__ __forceinline__ float row_scan(float x) {
   x += row_shr<8>(x);
   return x;
 }
+// exclusive suffix sum over the 16 lanes of a DPP row (row_shl with zero
+// fill): lane i gets the sum of lanes i + 1 .. 15, and lane 15 exactly 0.
+// The decays from a token to the end of its block are summed this way, not
+// taken as the block total minus the token's prefix sum: two lanes of the
+// prefix scan associate their sums differently, so that difference carries an
+// absolute error of about one ulp of the block total (2^-19 at a total of
+// 25 in log2 units) even where the true value is 0.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x100 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_suffix(float x) {
+  x = row_shl<1>(x);
+  x += row_shl<1>(x);
+  x += row_shl<2>(x);
+  x += row_shl<4>(x);
+  x += row_shl<8>(x);
+  return x;
+}
+// Inclusive prefix sum over a DPP row carried in fp64 (two 32-bit row_shr
+// moves and one fp64 add per step): the sums of at most 16 fp32 terms are
+// then exact but for a relative 2^-53, the same value whatever the lane's
+// association, and come back as an fp32 high part and the fp32 remainder
+// lo = sum - hi.  The in-block decays 2^(G_t - G_s) are formed as products of
+// 2^(hi + lo) factors whose only errors are the exponentials' and the
+// products' roundings, not an ulp of the (large) cumulative sums.
+template <int N>
+__device__ __forceinline__ double row_shr_f64(double x) {
+  const int2 v = __builtin_bit_cast(int2, x);
+  int2 r;
+  r.x = __builtin_amdgcn_mov_dpp(v.x, 0x110 + N, 0xF, 0xF, true);
+  r.y = __builtin_amdgcn_mov_dpp(v.y, 0x110 + N, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ void row_scan2(float& hi, float& lo) {
+  double d = static_cast<double>(hi);
+  d += row_shr_f64<1>(d);
+  d += row_shr_f64<2>(d);
+  d += row_shr_f64<4>(d);
+  d += row_shr_f64<8>(d);
+  hi = static_cast<float>(d);
+  lo = static_cast<float>(d - static_cast<double>(hi));
+}
+constexpr float kLn2 = 0.6931471805599453f;
+// 2^(hi + lo) for |lo| <= an ulp of hi: 2^hi (1 + lo ln 2), rounded once
+__device__ __forceinline__ float exp2_hilo(float hi, float lo) {
+  const float e = exp2_fast(hi);
+  return fmaf(e, lo * kLn2, e);
+}
 
 template <typename T>
 __device__ __forceinline__ float widen1(const T* p) { return static_cast<float>(*p); }
@@ -200,10 +265,12 @@ void kda_prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) float sTd[NB][16 * 20]; // (I + A_bb)^-1
   __shared__ __attribute__((aligned(16))) float sBtot[NB][128];   // per block: sum of g log2 e
   __shared__ __attribute__((aligned(16))) float sPre[NB + 1][128];  // sums of Btot over blocks < u
+  __shared__ __attribute__((aligned(16))) float sSuf[NB][128];      // sums of Btot over blocks > u
   __shared__ float sGC[128];                                      // 2^(G_C)
   __shared__ float sBeta[C];
   __shared__ float sSq[PARTS][C];  // partial sums of q^2, k^2 per channel part
   __shared__ float sSk[PARTS][C];
+  __shared__ float sSqk[PARTS][C];  // partial sums of q k
 
   const int wave = threadIdx.x / 64;
   const int seq = seq_of_rank(a.cu, a.n_seq, blockIdx.x / a.H);
@@ -308,7 +375,7 @@ void kda_prefill_kernel(PrefillArgs a) {
     {
       const bool valid = tl < n;
       const f4 zero = {0.f, 0.f, 0.f, 0.f};
-      float sq = 0.0f, sk = 0.0f;
+      float sq = 0.0f, sk = 0.0f, sqk = 0.0f;
 #pragma unroll
       for (int m = 0; m < CPL / 4; ++m) {
         const f4 q4 = valid ? nq[m] : zero;
@@ -319,6 +386,7 @@ void kda_prefill_kernel(PrefillArgs a) {
         for (int e = 0; e < 4; ++e) {
           sq = fmaf(q4[e], q4[e], sq);
           sk = fmaf(k4[e], k4[e], sk);
+          sqk = fmaf(q4[e], k4[e], sqk);
           gl4[e] = row_scan(g4[e] * kLog2e);  // block-local inclusive cumulative sum
         }
         *reinterpret_cast<f4*>(sZ + row + 4 * m) = q4;
@@ -328,16 +396,14 @@ void kda_prefill_kernel(PrefillArgs a) {
       }
       sq = group_sum(sq);
       sk = group_sum(sk);
+      sqk = group_sum(sqk);
       if (gq == 0) {
         sSq[pp][tl] = sq;
         sSk[pp][tl] = sk;
+        sSqk[pp][tl] = sqk;
         if (pp == 0) sBeta[tl] = valid ? 1.0f / (1.0f + expf(-nb)) : 0.0f;
       }
     }
-    // unconditional (the last chunk reloads its own rows): a conditional
-    // prefetch would merge old and new registers with copies that wait for
-    // the previous chunk's stores
-    prefetch(c0 + C < t1 ? c0 + C : c0, li, gq);
     __syncthreads();
 
     // ---- block prefix sums of the decay and 2^(G_C) (wave 0), then A and P
@@ -354,6 +420,12 @@ void kda_prefill_kernel(PrefillArgs a) {
           sPre[u + 1][ch] = acc;
         }
         sGC[ch] = exp2_fast(acc);
+        float later = 0.0f;
+#pragma unroll
+        for (int u = NB - 1; u >= 0; --u) {
+          sSuf[u][ch] = later;
+          later += sBtot[u][ch];
+        }
       }
     }
     // Chains (block pair (bt, bs), P or A) go round-robin to the waves.  Step
@@ -460,8 +532,11 @@ void kda_prefill_kernel(PrefillArgs a) {
       const float rq = 1.0f / sqrtf(ssq + 1e-6f);
       const float rk = 1.0f / sqrtf(ssk + 1e-6f);
       const float beta = sBeta[tl];
+      const bool valid = tl < n;
+      const f4 zero = {0.f, 0.f, 0.f, 0.f};
       // G_t = (sum of Btot before block pb) + gl_t;
-      // G_C - G_t = (sum of Btot after block pb) + (Btot_pb - gl_t), both parts <= 0
+      // G_C - G_t = (sum of Btot after block pb) + (decay from t to the end of
+      // block pb), both parts <= 0 and each summed directly
 #pragma unroll
       for (int m = 0; m < CPL; m += 4) {
         const int ch = ch0 + m;
@@ -469,9 +544,8 @@ void kda_prefill_kernel(PrefillArgs a) {
         const f4 gl4 = *reinterpret_cast<const f4*>(sY + row + m);
         const f4 q4 = *reinterpret_cast<const f4*>(sZ + row + m);
         const f4 pre = *reinterpret_cast<const f4*>(&sPre[pb][ch]);
-        const f4 post = *reinterpret_cast<const f4*>(&sPre[NB][ch]) -
-                        *reinterpret_cast<const f4*>(&sPre[pb + 1][ch]);
-        const f4 bt = *reinterpret_cast<const f4*>(&sBtot[pb][ch]);
+        const f4 post = *reinterpret_cast<const f4*>(&sSuf[pb][ch]);
+        const f4 g4 = valid ? ng[m / 4] : zero;
         f4 nkb, qg, kd;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -479,12 +553,26 @@ void kda_prefill_kernel(PrefillArgs a) {
           const float eg = exp2_fast(pre[e] + gl4[e]);
           nkb[e] = -((beta * kn) * eg);
           qg[e] = (q4[e] * rq) * eg;
-          kd[e] = kn * exp2_fast(post[e] + (bt[e] - gl4[e]));
+          kd[e] = kn * exp2_fast(post[e] + row_suffix(g4[e] * kLog2e));
         }
         *reinterpret_cast<f4*>(sX + row + m) = nkb;
         *reinterpret_cast<f4*>(sY + row + m) = qg;
         *reinterpret_cast<f4*>(sZ + row + m) = kd;
       }
+      // The next chunk's rows, once this chunk's g has been used for Kd (issued
+      // earlier, the prefetched rows would stay live through the chains and
+      // this phase, beyond the register budget).  Unconditional (the last
+      // chunk reloads its own rows): a conditional prefetch would merge old and
+      // new registers with copies that wait for the previous chunk's stores.
+      // P_tt = qn_t . kn_t (no decay) in place of the chain's value: summed
+      // from the partial sums of q k, without the chain's two exponentials
+      if (pp == 0 && gq == 0) {
+        float qk = 0.0f;
+#pragma unroll
+        for (int u = 0; u < PARTS; ++u) qk += sSqk[u][tl];
+        sP[tl * LdC + tl] = (qk * rq) * rk;
+      }
+      prefetch(c0 + C < t1 ? c0 + C : c0, li, gq);
       // (I + A_bb)^-1 by forward substitution, one column per lane of group 0
       if (wave < NB && gq == 0) {
         const int b = wave;
@@ -670,10 +758,12 @@ struct __attribute__((aligned(16))) WsBuf {
   float Td[kWsNB][16 * 20];  // (I + A_bb)^-1
   float Btot[kWsNB][128];
   float Pre[kWsNB + 1][128];
+  float Suf[kWsNB][128];   // sums of Btot over later blocks
   float GC[128];
   float Beta[kWsC];
   float Sq[kWsParts][kWsC];
   float Sk[kWsParts][kWsC];
+  float Sqk[kWsParts][kWsC];  // partial sums of q k
 };
 
 template <typename T>
@@ -686,8 +776,14 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
   constexpr int CPL = kWsCpl;
   constexpr int NPAIR = NB * (NB + 1) / 2;
   __shared__ WsBuf sb[2];
+  // low parts of the compensated block-local cumulative decays (the high
+  // parts are the rows of Y) and of the block totals: read only by the
+  // preparation waves within the chunk that wrote them, so single-buffered
+  __shared__ __attribute__((aligned(16))) float sYlo[kWsC * kLdK];
+  __shared__ __attribute__((aligned(16))) float sBlo[kWsNB][128];
 
-  const int wave = threadIdx.x / 64;
+  // wave-uniform: in scalar registers, and so everything derived from it
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
   const bool state_wave = wave < kWsState;
   const int pw = wave - kWsState;  // preparation wave index (prep waves only)
   const int seq = seq_of_rank(a.cu, a.n_seq, blockIdx.x / a.H);
@@ -711,10 +807,12 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
   // wave only ever plays one): state waves keep the state slice (rows
   // 16 sb + 4 gq + r of their 16 columns, accumulator layout) in reg[0..7],
   // the next chunk's v in reg[8..9] and R / Delta in reg[10..11];
-  // preparation waves keep the next chunk's q, k, g in reg[0..3], reg[4..7],
-  // reg[8..11].
-  constexpr int kS = 0, kV = 8, kD = 10, kQ = 0, kK = CPL / 4, kG = 2 * (CPL / 4);
-  static_assert(3 * (CPL / 4) <= 12, "q, k, g of a preparation lane fit the shared registers");
+  // preparation waves keep the next chunk's q, k, g in reg[0..1], reg[2..3],
+  // reg[4..5] and, from the per-token rows to the operands, the decay from
+  // each of their tokens to the end of its block in reg[6..7].
+  constexpr int kS = 0, kV = 8, kD = 10, kQ = 0, kK = CPL / 4, kG = 2 * (CPL / 4),
+                kF = 3 * (CPL / 4);
+  static_assert(4 * (CPL / 4) <= 12, "q, k, g, suffix of a preparation lane fit the shared registers");
   f4 reg[12];
   if (state_wave) {
     const int li = threadIdx.x % 16, gq = (threadIdx.x % 64) / 16;
@@ -789,32 +887,42 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
       const int row = tl * kLdK + ch0;
       const bool valid = tl < np;
       const f4 zero = {0.f, 0.f, 0.f, 0.f};
-      float sq = 0.0f, sk = 0.0f;
+      float sq = 0.0f, sk = 0.0f, sqk = 0.0f;
 #pragma unroll
       for (int m = 0; m < CPL / 4; ++m) {
         const f4 q4 = valid ? reg[kQ + m] : zero;
         const f4 k4 = valid ? reg[kK + m] : zero;
         const f4 g4 = valid ? reg[kG + m] : zero;
-        f4 gl4;
+        f4 gl4, lo4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sq = fmaf(q4[e], q4[e], sq);
           sk = fmaf(k4[e], k4[e], sk);
-          gl4[e] = row_scan(g4[e] * kLog2e);
+          sqk = fmaf(q4[e], k4[e], sqk);
+          float hi = g4[e] * kLog2e, lo = 0.0f;
+          row_scan2(hi, lo);
+          gl4[e] = hi;
+          lo4[e] = lo;
+          reg[kF + m][e] = row_suffix(g4[e] * kLog2e);
         }
         *reinterpret_cast<f4*>(bp.Z + row + 4 * m) = q4;
         *reinterpret_cast<f4*>(bp.X + row + 4 * m) = k4;
         *reinterpret_cast<f4*>(bp.Y + row + 4 * m) = gl4;
-        if (li == 15) *reinterpret_cast<f4*>(&bp.Btot[pb][ch0 + 4 * m]) = gl4;
+        *reinterpret_cast<f4*>(sYlo + row + 4 * m) = lo4;
+        if (li == 15) {
+          *reinterpret_cast<f4*>(&bp.Btot[pb][ch0 + 4 * m]) = gl4;
+          *reinterpret_cast<f4*>(&sBlo[pb][ch0 + 4 * m]) = lo4;
+        }
       }
       sq = group_sum(sq);
       sk = group_sum(sk);
+      sqk = group_sum(sqk);
       if (gq == 0) {
         bp.Sq[pp][tl] = sq;
         bp.Sk[pp][tl] = sk;
+        bp.Sqk[pp][tl] = sqk;
         if (pp == 0) bp.Beta[tl] = valid ? 1.0f / (1.0f + expf(-nb)) : 0.0f;
       }
-      prefetch_rows(cp + C < t1 ? cp + C : cp, li, gq);
     }
     if (state_now) {
       // R = beta V - Kb S for chunk it - 1
@@ -855,27 +963,33 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
             bp.Pre[u + 1][ch] = acc;
           }
           bp.GC[ch] = exp2_fast(acc);
+          float later = 0.0f;
+#pragma unroll
+          for (int u = NB - 1; u >= 0; --u) {
+            bp.Suf[u][ch] = later;
+            later += bp.Btot[u][ch];
+          }
         }
       }
-      // chains (block pair, P or A) round-robin over the preparation waves
-      for (int ci = pw; ci < 2 * NPAIR; ci += kWsPrep) {
-        const int pi = ci / 2;
-        const bool is_a = (ci & 1) != 0;
+      // chains: one block pair per preparation wave, P and A together (they
+      // share the decay factors of both operands)
+      for (int pi = pw; pi < NPAIR; pi += kWsPrep) {
         int bt = 0;
         while ((bt + 1) * (bt + 2) / 2 <= pi) ++bt;
         const int bsb = pi - bt * (bt + 1) / 2;
         const int trow = (16 * bt + li) * kLdK + 32 * gq;
         const int srow = (16 * bsb + li) * kLdK + 32 * gq;
-        float st = 0.0f, ss = 0.0f;
+        float sq_t = 0.0f, sk_t = 0.0f, ss = 0.0f;
 #pragma unroll
         for (int u = 0; u < PARTS; ++u) {
-          st += is_a ? bp.Sk[u][16 * bt + li] : bp.Sq[u][16 * bt + li];
+          sq_t += bp.Sq[u][16 * bt + li];
+          sk_t += bp.Sk[u][16 * bt + li];
           ss += bp.Sk[u][16 * bsb + li];
         }
         const float beta = bp.Beta[16 * bt + li];
-        const float r_t = (is_a ? beta : 1.0f) / sqrtf(st + 1e-6f);
+        const float rq_t = 1.0f / sqrtf(sq_t + 1e-6f);
+        const float rk_t = beta / sqrtf(sk_t + 1e-6f);
         const float rk_s = 1.0f / sqrtf(ss + 1e-6f);
-        const float* tsrc = is_a ? bp.X : bp.Z;
         bool exact = false;
         if (bt == bsb) {
           float span = 0.0f;
@@ -888,34 +1002,60 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
           exact = __builtin_amdgcn_ballot_w64(span > kDiagLimit) != 0;
         }
         if (!exact) {
-          f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+          // Step (m, e): channel 32 gq + m + e of both operands.  Diagonal
+          // block: t-factor 2^(gl_t), s-factor 2^(-gl_s), each from the
+          // compensated sums (their exponents cancel to the small in-block
+          // decay).  Block bt > bsb: t-factor 2^(gl_t), whose exponent is the
+          // product's own order (no low part needed), s-factor
+          // 2^(Btot_bsb - gl_s), the difference taken in high and low parts.
+          static_assert(NB == 2, "no blocks between bsb and bt");
+          f4 accp = {0.f, 0.f, 0.f, 0.f}, acca = {0.f, 0.f, 0.f, 0.f};
+          if (bsb == bt) {
 #pragma unroll 2
-          for (int m = 0; m < 32; m += 4) {
-            f4 cum = {0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < 32; m += 2) {
+              const f2 xq = *reinterpret_cast<const f2*>(bp.Z + trow + m);
+              const f2 xk = *reinterpret_cast<const f2*>(bp.X + trow + m);
+              const f2 gt = *reinterpret_cast<const f2*>(bp.Y + trow + m);
+              const f2 gtl = *reinterpret_cast<const f2*>(sYlo + trow + m);
+              const f2 ks = *reinterpret_cast<const f2*>(bp.X + srow + m);
+              const f2 gs = *reinterpret_cast<const f2*>(bp.Y + srow + m);
+              const f2 gsl = *reinterpret_cast<const f2*>(sYlo + srow + m);
 #pragma unroll
-            for (int u = 0; u < NB - 1; ++u)
-              if (u >= bsb && u < bt) cum += *reinterpret_cast<const f4*>(&bp.Btot[u][32 * gq + m]);
-            const f4 xt = *reinterpret_cast<const f4*>(tsrc + trow + m);
-            const f4 gt = *reinterpret_cast<const f4*>(bp.Y + trow + m);
-            const f4 ks = *reinterpret_cast<const f4*>(bp.X + srow + m);
-            const f4 gs = *reinterpret_cast<const f4*>(bp.Y + srow + m);
+              for (int e = 0; e < 2; ++e) {
+                const float et = exp2_hilo(gt[e], gtl[e]);
+                const float rf = (ks[e] * rk_s) * exp2_hilo(-gs[e], -gsl[e]);
+                accp = mma((xq[e] * rq_t) * et, rf, accp);
+                acca = mma((xk[e] * rk_t) * et, rf, acca);
+              }
+            }
+          } else {
+#pragma unroll 2
+            for (int m = 0; m < 32; m += 2) {
+              const f2 bh = *reinterpret_cast<const f2*>(&bp.Btot[bsb][32 * gq + m]);
+              const f2 bl = *reinterpret_cast<const f2*>(&sBlo[bsb][32 * gq + m]);
+              const f2 xq = *reinterpret_cast<const f2*>(bp.Z + trow + m);
+              const f2 xk = *reinterpret_cast<const f2*>(bp.X + trow + m);
+              const f2 gt = *reinterpret_cast<const f2*>(bp.Y + trow + m);
+              const f2 ks = *reinterpret_cast<const f2*>(bp.X + srow + m);
+              const f2 gs = *reinterpret_cast<const f2*>(bp.Y + srow + m);
+              const f2 gsl = *reinterpret_cast<const f2*>(sYlo + srow + m);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float lf = (xt[e] * r_t) * exp2_fast(gt[e]);
-              const float rf = (ks[e] * rk_s) * exp2_fast(cum[e] - gs[e]);
-              if (e % 2 == 0)
-                acc0 = mma(lf, rf, acc0);
-              else
-                acc1 = mma(lf, rf, acc1);
+              for (int e = 0; e < 2; ++e) {
+                const float et = exp2_fast(gt[e]);
+                const float rf = (ks[e] * rk_s) * exp2_hilo(bh[e] - gs[e], bl[e] - gsl[e]);
+                accp = mma((xq[e] * rq_t) * et, rf, accp);
+                acca = mma((xk[e] * rk_t) * et, rf, acca);
+              }
             }
           }
-          float* dstm = is_a ? bp.A : bp.P;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int tr = 4 * gq + r;
-            float x = acc0[r] + acc1[r];
-            if (bsb == bt && (is_a ? li >= tr : li > tr)) x = 0.0f;
-            dstm[(16 * bt + tr) * LdC + 16 * bsb + li] = is_a ? -x : x;
+            float xp = accp[r], xa = acca[r];
+            if (bsb == bt && li > tr) xp = 0.0f;
+            if (bsb == bt && li >= tr) xa = 0.0f;
+            bp.P[(16 * bt + tr) * LdC + 16 * bsb + li] = xp;
+            bp.A[(16 * bt + tr) * LdC + 16 * bsb + li] = -xa;
           }
         } else {
           for (int s2 = 0; s2 < 16; ++s2) {
@@ -924,20 +1064,21 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < PARTS; ++u) sk2 += bp.Sk[u][16 * bt + s2];
             const float rk_s2 = 1.0f / sqrtf(sk2 + 1e-6f);
-            float acc = 0.0f;
+            float ap = 0.0f, aa = 0.0f;
             if (s2 <= li) {
               for (int i = 0; i < 32; ++i) {
                 const float f =
-                    (bp.X[s2row + i] * rk_s2) * exp2_fast(bp.Y[trow + i] - bp.Y[s2row + i]);
-                acc = fmaf(tsrc[trow + i] * r_t, f, acc);
+                    (bp.X[s2row + i] * rk_s2) *
+                    exp2_fast((bp.Y[trow + i] - bp.Y[s2row + i]) + (sYlo[trow + i] - sYlo[s2row + i]));
+                ap = fmaf(bp.Z[trow + i] * rq_t, f, ap);
+                aa = fmaf(bp.X[trow + i] * rk_t, f, aa);
               }
             }
-            acc = group_sum(acc);
+            ap = group_sum(ap);
+            aa = group_sum(aa);
             if (gq == 0) {
-              if (is_a)
-                bp.A[(16 * bt + li) * LdC + 16 * bt + s2] = s2 < li ? -acc : 0.0f;
-              else
-                bp.P[(16 * bt + li) * LdC + 16 * bt + s2] = s2 <= li ? acc : 0.0f;
+              bp.A[(16 * bt + li) * LdC + 16 * bt + s2] = s2 < li ? -aa : 0.0f;
+              bp.P[(16 * bt + li) * LdC + 16 * bt + s2] = s2 <= li ? ap : 0.0f;
             }
           }
         }
@@ -1001,6 +1142,7 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
     // ================= segment 3 =================
     if (prep_now) {
       // operands -Kb, Qg, Kd of chunk it in place of its rows; diagonal inverses
+      prefetch_rows(cp + C < t1 ? cp + C : cp, li, gq);
       const int pb = pw % NB, pp = pw / NB;
       const int tl = 16 * pb + li;
       const int ch0 = pp * (128 / PARTS) + gq * CPL;
@@ -1021,9 +1163,8 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
         const f4 gl4 = *reinterpret_cast<const f4*>(bp.Y + row + m);
         const f4 q4 = *reinterpret_cast<const f4*>(bp.Z + row + m);
         const f4 pre = *reinterpret_cast<const f4*>(&bp.Pre[pb][ch]);
-        const f4 post = *reinterpret_cast<const f4*>(&bp.Pre[NB][ch]) -
-                        *reinterpret_cast<const f4*>(&bp.Pre[pb + 1][ch]);
-        const f4 btot = *reinterpret_cast<const f4*>(&bp.Btot[pb][ch]);
+        const f4 post = *reinterpret_cast<const f4*>(&bp.Suf[pb][ch]);
+        const f4 sf = reg[kF + m / 4];
         f4 nkb, qg, kd;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1031,11 +1172,18 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
           const float eg = exp2_fast(pre[e] + gl4[e]);
           nkb[e] = -((beta * kn) * eg);
           qg[e] = (q4[e] * rq) * eg;
-          kd[e] = kn * exp2_fast(post[e] + (btot[e] - gl4[e]));
+          kd[e] = kn * exp2_fast(post[e] + sf[e]);
         }
         *reinterpret_cast<f4*>(bp.X + row + m) = nkb;
         *reinterpret_cast<f4*>(bp.Y + row + m) = qg;
         *reinterpret_cast<f4*>(bp.Z + row + m) = kd;
+      }
+      // P_tt = qn_t . kn_t (no decay) in place of the chain's value
+      if (pp == 0 && gq == 0) {
+        float qk = 0.0f;
+#pragma unroll
+        for (int u = 0; u < PARTS; ++u) qk += bp.Sqk[u][tl];
+        bp.P[tl * LdC + tl] = (qk * rq) * rk;
       }
       if (pw < NB && gq == 0) {
         const int b = pw;

