@@ -272,7 +272,8 @@ void kda_prefill_kernel(PrefillArgs a) {
   __shared__ float sSk[PARTS][C];
   __shared__ float sSqk[PARTS][C];  // partial sums of q k
 
-  const int wave = threadIdx.x / 64;
+  // wave-uniform: in scalar registers, and so everything derived from it
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
   const int seq = seq_of_rank(a.cu, a.n_seq, blockIdx.x / a.H);
   const int h = blockIdx.x % a.H;
 
