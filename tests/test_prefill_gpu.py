@@ -9,9 +9,10 @@ bounds are the decode ones carried over: fp32 pools, max abs state error
 ||o_ref|| <= 1e-5.  fp16 pools: every stored element must be the RNE of some
 fp32 value within 1e-6 of the oracle's fp32 state (the fp32 bound, then the
 store's rounding), which for states of ordinary size is "within 1 fp16
-ulp".  The strong-decay stress case is graded against the fp64 oracle with
-a 1e-4 output bound: there the fp32 oracle itself is 2e-5 from fp64
-(outputs are a small difference of large terms)."""
+ulp".  The strong-decay stress case is graded against the fp64 oracle:
+1e-5 at 32-token chunks, and at 64-token chunks 1.5 times the fp32
+oracle's own error there (about 2e-5: outputs are a small difference of
+large terms)."""
 import numpy as np
 import pytest
 
@@ -129,19 +130,30 @@ def test_prefill_empty_sequences_copy_the_state(dtype):
         np.testing.assert_array_equal(gp[inp.dst_slot_ids[s]], inp.pool[inp.init_slot_ids[s]])
 
 
-def test_prefill_strong_decay_takes_the_exact_path(oracle):
-    # log-decays of -3 .. -8 per token: the in-block decay passes e^80, so
-    # the diagonal blocks go pair by pair; results stay finite and accurate
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_prefill_strong_decay_takes_the_exact_path(oracle, chunk):
+    """Log-decays of -3 .. -8 per token: the in-block decay passes e^80, so
+    the diagonal blocks go pair by pair; results stay finite and accurate.
+    Outputs here are small differences of large terms, and the fp32 oracle
+    itself is about 2e-5 from fp64.  With 32-token chunks (compensated
+    in-block decay sums) the kernel is held to 1e-5 from fp64 all the same;
+    with 64-token chunks (plain sums) to 1.5 times the oracle's own error."""
     inp = kda_inputs.make_prefill_inputs("prefill strong decay", [130, 40], 8, "f32", H=2, seed=12)
     inp.g[:] = -np.random.default_rng(0).uniform(3.0, 8.0, inp.g.shape).astype(np.float32)
-    gp, go = run_gpu(inp)
+    gp, go = run_gpu(inp, chunk=chunk)
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gp))
     p64 = inp.pool.astype(np.float64)
     o64 = oracle.prefill_f64(p64, inp.init_slot_ids, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.g,
                              inp.b, scale=inp.scale)
+    p32 = inp.pool.copy()
+    o32 = oracle.prefill_f32(p32, inp.init_slot_ids, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.g,
+                             inp.b, scale=inp.scale)
     for s in inp.init_slot_ids:
         assert np.max(np.abs(gp[s] - p64[s])) <= STATE_ABS
-    assert out_rel(go, o64) <= 1e-4
+    err, own = out_rel(go, o64), out_rel(np.asarray(o32), o64)
+    print("strong decay, chunk %d: outputs %.3g from fp64 (the fp32 oracle %.3g)" % (chunk, err, own),
+          flush=True)
+    assert err <= (OUT_REL if chunk == 32 else max(OUT_REL, 1.5 * own))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
