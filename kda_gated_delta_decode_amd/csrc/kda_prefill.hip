@@ -264,7 +264,7 @@ void kda_prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) float sP[C * LdC];      // P (lower)
   __shared__ __attribute__((aligned(16))) float sTd[NB][16 * 20]; // (I + A_bb)^-1
   __shared__ __attribute__((aligned(16))) float sBtot[NB][128];   // per block: sum of g log2 e
-  __shared__ __attribute__((aligned(16))) float sPre[NB + 1][128];  // sums of Btot over blocks < u
+  __shared__ __attribute__((aligned(16))) float sPre[NB][128];      // sums of Btot over blocks < u
   __shared__ __attribute__((aligned(16))) float sSuf[NB][128];      // sums of Btot over blocks > u
   __shared__ float sGC[128];                                      // 2^(G_C)
   __shared__ float sBeta[C];
@@ -418,7 +418,7 @@ void kda_prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           acc += sBtot[u][ch];
-          sPre[u + 1][ch] = acc;
+          if (u + 1 < NB) sPre[u + 1][ch] = acc;
         }
         sGC[ch] = exp2_fast(acc);
         float later = 0.0f;
@@ -758,7 +758,7 @@ struct __attribute__((aligned(16))) WsBuf {
   float P[kWsC * kWsLdC];  // P (lower)
   float Td[kWsNB][16 * 20];  // (I + A_bb)^-1
   float Btot[kWsNB][128];
-  float Pre[kWsNB + 1][128];
+  float Pre[kWsNB][128];   // sums of Btot over earlier blocks
   float Suf[kWsNB][128];   // sums of Btot over later blocks
   float GC[128];
   float Beta[kWsC];
@@ -961,7 +961,7 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
 #pragma unroll
           for (int u = 0; u < NB; ++u) {
             acc += bp.Btot[u][ch];
-            bp.Pre[u + 1][ch] = acc;
+            if (u + 1 < NB) bp.Pre[u + 1][ch] = acc;
           }
           bp.GC[ch] = exp2_fast(acc);
           float later = 0.0f;
