@@ -183,6 +183,44 @@ def test_prefill_full_batch(oracle, dtype):
     assert out_rel(go[:T], oo[:T]) <= OUT_REL
 
 
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_prefill_long_prompt(oracle, chunk):
+    """One 8192-token prompt (H = 2): 256 chunks of 32 tokens, or 128 of 64,
+    chained through the state.  The final state and every output row are
+    graded against the fp64 oracle (outputs at 64-token chunks, whose in-block
+    decay sums are plain, against 1.5 times the fp32 oracle's own error), and
+    the final state against the same tokens run one at a time through the
+    decode kernel."""
+    inp = kda_inputs.make_prefill_inputs("prefill 8192 tokens", [8192], 2, "f32", H=2, seed=21)
+    gp, go = run_gpu(inp, chunk=chunk)
+    assert np.all(np.isfinite(go))
+    p64 = inp.pool.astype(np.float64)
+    o64 = oracle.prefill_f64(p64, inp.init_slot_ids, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.g,
+                             inp.b, scale=inp.scale)
+    p32 = inp.pool.copy()
+    o32 = oracle.prefill_f32(p32, inp.init_slot_ids, inp.cu_seqlens, inp.q, inp.k, inp.v, inp.g,
+                             inp.b, scale=inp.scale)
+    s = int(inp.init_slot_ids[0])
+    err_state = float(np.max(np.abs(gp[s] - p64[s])))
+    err_out, own = out_rel(go, o64), out_rel(np.asarray(o32), o64)
+    # the decode kernel, token after token, from the same initial state
+    dev = torch.device("cuda", 0)
+    pool = torch.from_numpy(inp.pool).to(dev)
+    ids = torch.tensor([s], dtype=torch.int32, device=dev)
+    t = {n: torch.from_numpy(getattr(inp, n)).to(dev) for n in ("q", "k", "v", "g", "b")}
+    out = torch.empty((1, 2, 128), device=dev)
+    for i in range(inp.n_tokens):
+        B.kda_decode_step(pool, ids, t["q"][i:i + 1], t["k"][i:i + 1], t["v"][i:i + 1],
+                          t["g"][i:i + 1], t["b"][i:i + 1], out, scale=inp.scale)
+    torch.cuda.synchronize()
+    dec = pool_to_host(pool)[s]
+    print("8192-token prompt, chunk %d: state %.3g from fp64 (decode %.3g), outputs %.3g (fp32 oracle "
+          "%.3g)" % (chunk, err_state, float(np.max(np.abs(dec - p64[s]))), err_out, own), flush=True)
+    assert err_state <= STATE_ABS
+    assert float(np.max(np.abs(gp[s] - dec))) <= 2 * STATE_ABS
+    assert err_out <= (OUT_REL if chunk == 32 else max(OUT_REL, 1.5 * own))
+
+
 @pytest.mark.parametrize("n_seq,in_place", [(100, False), (300, True)])
 def test_prefill_many_sequences_with_equal_lengths(oracle, n_seq, in_place):
     """Workgroups take the sequences longest first (ties by index) when there
