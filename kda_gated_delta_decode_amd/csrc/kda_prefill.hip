@@ -787,6 +787,11 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / 64));
   const bool state_wave = wave < kWsState;
   const int pw = wave - kWsState;  // preparation wave index (prep waves only)
+  // The preparation waves issue ahead of the state waves on their SIMDs: the
+  // state waves' matrix-core products then fill the gaps in the preparation
+  // waves' vector work rather than delaying it (34K-token batch: 761 -> 720
+  // us; raising the state waves instead changes nothing).
+  if (!state_wave) __builtin_amdgcn_s_setprio(1);
   const int seq = seq_of_rank(a.cu, a.n_seq, blockIdx.x / a.H);
   const int h = blockIdx.x % a.H;
 
