@@ -373,8 +373,10 @@ int32_t kda_tile_bv(kda_dtype dtype);
  * solve per chunk, matrix-core products) equals the token-by-token
  * recurrence up to rounding.  Device-side, a sequence whose table entries
  * are out of range is skipped (nothing written for it).
- * Errors: as kda_decode_step (KDA_ERR_SLOT: n_seq > n_slots), KDA_ERR_ARG
- * (bad chunk, n_tokens < 0, non-finite scale).  Asynchronous on stream.
+ * Errors: as kda_decode_step (KDA_ERR_SLOT: n_seq > n_slots; KDA_ERR_SHAPE
+ * also for H > 16384, which keeps byte offsets within a chunk below 2^31),
+ * KDA_ERR_ARG (bad chunk, n_tokens < 0, n_seq * H > INT32_MAX, non-finite
+ * scale).  Asynchronous on stream.
  */
 typedef struct kda_prefill_opts {
   int32_t chunk;

@@ -383,6 +383,9 @@ def test_prefill_refusals():
     assert prefill(pool(n_slots=16, dtype=B.KDA_BF16)) == B.KDA_ERR_DTYPE_REFUSED
     assert prefill(P, dtype=B.KDA_F16) == B.KDA_ERR_DTYPE_MISMATCH
     assert prefill(pool(n_slots=16, Kd=64)) == B.KDA_ERR_SHAPE
+    # byte offsets within a chunk stay below 2^31: at most 16384 heads (refused
+    # before any launch; the accepted side would launch, so it is not called here)
+    assert prefill(pool(n_slots=16, H=16385)) == B.KDA_ERR_SHAPE
     assert prefill(P, n_seq=17) == B.KDA_ERR_SLOT          # more sequences than slots
     assert prefill(P, n_seq=-1) == B.KDA_ERR_ARG
     assert prefill(P, n_tokens=-1) == B.KDA_ERR_ARG
