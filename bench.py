@@ -424,6 +424,11 @@ def main():
                 # unless the committed summary matches the kernel source)
                 extras[name]["traffic"] = pmc_traffic("%s_n64_rows1_spec_verify_8x8" % args.dtype)
             del w
+        rp = extras.get("bandwidth_probes", {}).get("rows_pattern_f16_8x8")
+        if rp is not None and "spec_verify_f16" in extras:
+            sv = extras["spec_verify_f16"]
+            sv["rows_pattern_us"] = rp["us"]
+            sv["pct_of_rows_pattern"] = round(100.0 * rp["us"] / sv["us_per_step"], 2)
         if args.extras == "all":
             # the same batched step out of place: each request reads slot A
             # and writes slot B of a 128-slot pool (init_slot_ids), as a
@@ -477,7 +482,9 @@ def bandwidth_probes(B, torch, step_state_bytes):
     write-only streams at 1 GiB and at one decode step's bytes, and the decode
     launch's own tile traffic (kda_tile_probe: same grid, layout and
     nontemporal loads and stores, no arithmetic) on the batched workloads'
-    rotated pools.  GB/s counts every byte read plus every byte written."""
+    rotated pools, and the 8 x 8 chained rows' own traffic (kda_rows_probe)
+    on the spec-verify workload's.  GB/s counts every byte read plus every
+    byte written."""
     import kda_inputs
     GiB = 1 << 30
     res = {}
@@ -528,6 +535,18 @@ def bandwidth_probes(B, torch, step_state_bytes):
                                         "us": round(us, 2), "GB/s": round(inp.state_bytes() / us / 1e3, 1)}
         del w
         torch.cuda.empty_cache()
+    # the 8 x 8 chained rows' own traffic (kda_rows_probe: the matrix-core
+    # block form's grid, layout, slot id loads, state loads and snapshot
+    # stores, no arithmetic) on the spec-verify workload's rotated pools
+    inp = kda_inputs.spec_verify_f16(0)
+    w = Workload(inp, ROT, torch)
+    tc = time_launches(lambda i: B.kda_rows_probe(w.pools[i % len(w.pools)], w.ids, inp.n_rows), 100, 10,
+                       torch)
+    us = tc["launch_ms_mean"] * 1e3
+    res["rows_pattern_f16_8x8"] = {"bytes_moved": inp.state_bytes(), "pools_rotated": len(w.pools),
+                                   "us": round(us, 2), "GB/s": round(inp.state_bytes() / us / 1e3, 1)}
+    del w
+    torch.cuda.empty_cache()
     return res
 
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6  /* 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
+#define KDA_ABI_VERSION 7  /* 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -472,6 +472,23 @@ int kda_bw_probe(void* dst, const void* src, size_t bytes, int32_t mode,
  */
 int kda_tile_probe(const kda_pool* pool, const int32_t* slot_ids, int32_t n_req,
                    kda_dtype state_dtype, void* stream);
+
+/*
+ * kda_rows_probe -- measurement helper: the memory traffic of a chained-row
+ * launch in the matrix-core block form (KDA_ROWS_MATRIX at its default 8
+ * waves: 64-column halves, K over the waves) with the arithmetic taken out.
+ * Same grid, block-to-tile map, slot id loads, lane layout and nontemporal
+ * loads and stores as kda_decode_step there; each request's initial state
+ * (init_slot_ids[r], or slot_ids[r * n_rows] if init_slot_ids is NULL) is
+ * written unchanged to each of its rows' slots slot_ids[r * n_rows + t].
+ *  slot_ids       device int32 [n_req * n_rows]; init_slot_ids: NULL or
+ *                 device int32 [n_req].  A request with an id out of range
+ *                 is skipped.
+ * Errors: as kda_tile_probe; KDA_ERR_ROWS (n_rows outside [1,
+ * KDA_MAX_ROWS]); KDA_ERR_ARG (n_req < 0 or n_req * n_rows > n_slots).
+ */
+int kda_rows_probe(const kda_pool* pool, const int32_t* slot_ids, const int32_t* init_slot_ids,
+                   int32_t n_req, int32_t n_rows, kda_dtype state_dtype, void* stream);
 
 /* Message for a kda_status code (static string, never NULL). */
 const char* kda_strerror(int code);

@@ -108,6 +108,7 @@ SIGNATURES = {
     "kda_copy_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     "kda_bw_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _I32, _I32, _I32, _P]),
     "kda_tile_probe": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _I32, ctypes.c_int, _P]),
+    "kda_rows_probe": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, ctypes.c_int, _P]),
     "kda_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_abi_version": (ctypes.c_int, []),
 }
@@ -459,6 +460,24 @@ def kda_tile_probe(pool, slot_ids, stream=None) -> None:
     n_req = slot_ids.numel()
     _check(library().kda_tile_probe(ctypes.byref(P), _dev(slot_ids, "slot_ids", torch.int32, pool.device),
                                     n_req, P.dtype, _stream_ptr(stream)), "kda_tile_probe")
+
+
+def kda_rows_probe(pool, slot_ids, n_rows: int, init_slot_ids=None, stream=None) -> None:
+    """The chained-row launch's state traffic (matrix-core block form)
+    without its arithmetic (see kda_rows_probe in include/kda_decode.h): each
+    request's initial state is written unchanged to its rows' slots."""
+    import torch
+    P = make_pool(pool)
+    n_rows = int(n_rows)
+    if n_rows < 1 or slot_ids.numel() % n_rows:
+        raise ValueError("slot_ids holds %d ids, not a multiple of n_rows = %d" % (slot_ids.numel(), n_rows))
+    n_req = slot_ids.numel() // n_rows
+    if init_slot_ids is not None:
+        _need_numel(init_slot_ids, "init_slot_ids", n_req)
+    dv = pool.device
+    _check(library().kda_rows_probe(ctypes.byref(P), _dev(slot_ids, "slot_ids", torch.int32, dv),
+                                    _dev(init_slot_ids, "init_slot_ids", torch.int32, dv), n_req, n_rows,
+                                    P.dtype, _stream_ptr(stream)), "kda_rows_probe")
 
 
 def kda_strerror(code: int) -> str:

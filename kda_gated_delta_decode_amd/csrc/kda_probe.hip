@@ -127,6 +127,59 @@ __global__ __launch_bounds__(kWave * NW) void kda_tile_probe_kernel(T* pool, con
   for (int m = 0; m < RPL; ++m) __builtin_nontemporal_store(raw[m] ^ zero, p + m * (kHeadV / CPL));
 }
 
+// The chained rows' memory traffic in the matrix-core block form with the
+// arithmetic taken out: the grid, block-to-tile map, slot id loads, lane
+// layout (wave w: key rows 16 w + 4 gq + j, j < 4; lane li: columns 4 li ..
+// 4 li + 3 of the 64-column half) and nontemporal loads and stores of
+// kda_rows_mfma8_kernel.  The initial state is written unchanged to every
+// row's slot (xor with a zero the compiler cannot see, so the stores stay).
+template <typename T>
+__global__ __launch_bounds__(kWave * kMatrixWaves) void kda_rows_probe_kernel(
+    T* pool, const int32_t* slot_ids, const int32_t* init_ids, int32_t n_slots, int32_t H,
+    int32_t n_rows, uint32_t zero) {
+  constexpr int NW = kMatrixWaves;
+  constexpr int BH = kMatrixBV;
+  constexpr int RPW = kHeadK / NW;
+  constexpr int J = RPW / 4;
+  constexpr int TMAX = KDA_MAX_ROWS;
+  // 4 columns of one row: 8 bytes (fp16) or 16 (fp32)
+  using piece = uint32_t __attribute__((ext_vector_type(sizeof(T))));
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int gq = lane / 16, li = lane % 16;
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int vt = tile % (kHeadV / BH);
+  const int rh = tile / (kHeadV / BH);
+  const int h = rh % H;
+  const int r = rh / H;
+  const int32_t* ids = slot_ids + static_cast<int64_t>(r) * n_rows;
+  int32_t sid[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
+  const int32_t init = init_ids != nullptr ? init_ids[r] : sid[0];
+  bool ok = init >= 0 && init < n_slots;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) ok = ok && (t >= n_rows || (sid[t] >= 0 && sid[t] < n_slots));
+  if (!ok) return;  // as the kernel: a request with a bad id is skipped
+  const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
+  const int64_t slot_elems = static_cast<int64_t>(H) * head_elems;
+  const int row0 = RPW * wave + J * gq;
+  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + vt * BH + 4 * li;
+  piece raw[J];
+  {
+    const piece* src = reinterpret_cast<const piece*>(pool + static_cast<int64_t>(init) * slot_elems + lane_off);
+#pragma unroll
+    for (int j = 0; j < J; ++j) raw[j] = __builtin_nontemporal_load(src + j * (kHeadV / 4));
+  }
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    if (t >= n_rows) break;
+    piece* dst = reinterpret_cast<piece*>(pool + static_cast<int64_t>(sid[t]) * slot_elems + lane_off);
+#pragma unroll
+    for (int j = 0; j < J; ++j) __builtin_nontemporal_store(raw[j] ^ zero, dst + j * (kHeadV / 4));
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -184,5 +237,32 @@ extern "C" int kda_tile_probe(const kda_pool* pool, const int32_t* slot_ids, int
                        kHeadV / bv, 0u);
   else
     return KDA_ERR_ARG;  // the default shapes changed: this probe follows them
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+extern "C" int kda_rows_probe(const kda_pool* pool, const int32_t* slot_ids, const int32_t* init_slot_ids,
+                              int32_t n_req, int32_t n_rows, kda_dtype state_dtype, void* stream) {
+  if (pool == nullptr || pool->base == nullptr) return KDA_ERR_NULL;
+  if (state_dtype != KDA_F32 && state_dtype != KDA_F16) return KDA_ERR_DTYPE_REFUSED;
+  if (pool->dtype != state_dtype) return KDA_ERR_DTYPE_MISMATCH;
+  if (pool->K != kHeadK || pool->V != kHeadV || pool->H < 1 || pool->n_slots < 1) return KDA_ERR_SHAPE;
+  if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
+  if (n_req < 0 || static_cast<int64_t>(n_req) * n_rows > pool->n_slots) return KDA_ERR_ARG;
+  if (n_req == 0) return KDA_OK;
+  if (slot_ids == nullptr) return KDA_ERR_NULL;
+  if (!aligned16(pool->base) || (reinterpret_cast<uintptr_t>(slot_ids) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(init_slot_ids) & 3u) != 0)
+    return KDA_ERR_ALIGN;
+  const int64_t blocks = static_cast<int64_t>(n_req) * pool->H * (kHeadV / kMatrixBV);
+  if (blocks > INT32_MAX) return KDA_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(kWave * kMatrixWaves);
+  if (state_dtype == KDA_F32)
+    hipLaunchKernelGGL((kda_rows_probe_kernel<float>), grid, block, 0, s, static_cast<float*>(pool->base),
+                       slot_ids, init_slot_ids, pool->n_slots, pool->H, n_rows, 0u);
+  else
+    hipLaunchKernelGGL((kda_rows_probe_kernel<_Float16>), grid, block, 0, s,
+                       static_cast<_Float16*>(pool->base), slot_ids, init_slot_ids, pool->n_slots, pool->H,
+                       n_rows, 0u);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -34,7 +34,8 @@ def test_header_declares_the_abi():
                      "kda_state_copy", "kda_decode_step_conv", "kda_prefill",
                      "kda_prefill_validate",
                      "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
-                     "kda_copy_probe", "kda_bw_probe", "kda_tile_probe", "kda_strerror",
+                     "kda_copy_probe", "kda_bw_probe", "kda_tile_probe", "kda_rows_probe",
+                     "kda_strerror",
                      "kda_abi_version"]:
         assert expected in names
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 6
+    assert B.kda_abi_version() == 7
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -460,3 +461,17 @@ def test_probe_refusals_before_any_hip_call():
     assert lib.kda_tile_probe(ctypes.byref(pool(n_slots=3)), ids, 4, B.KDA_F32, None) == B.KDA_ERR_ARG
     assert lib.kda_tile_probe(ctypes.byref(pool()), None, 4, B.KDA_F32, None) == B.KDA_ERR_NULL
     assert lib.kda_tile_probe(ctypes.byref(pool()), ids, 0, B.KDA_F32, None) == B.KDA_OK
+    rp = lambda P, n_req=4, n_rows=8, ids=ids, init=None, dt=None: lib.kda_rows_probe(
+        ctypes.byref(P) if P is not None else None, ids, init, n_req, n_rows,
+        P.dtype if dt is None else dt, None)
+    assert rp(None, dt=B.KDA_F16) == B.KDA_ERR_NULL
+    assert rp(pool(dtype=B.KDA_BF16)) == B.KDA_ERR_DTYPE_REFUSED
+    assert rp(pool(), dt=B.KDA_F16) == B.KDA_ERR_DTYPE_MISMATCH
+    assert rp(pool(Kd=64)) == B.KDA_ERR_SHAPE
+    assert rp(pool(), n_rows=0) == B.KDA_ERR_ROWS
+    assert rp(pool(), n_rows=9) == B.KDA_ERR_ROWS
+    assert rp(pool(n_slots=31), n_rows=8) == B.KDA_ERR_ARG              # 4 x 8 rows need 32 slots
+    assert rp(pool(), n_req=-1) == B.KDA_ERR_ARG
+    assert rp(pool(), ids=None) == B.KDA_ERR_NULL
+    assert rp(pool(), init=ctypes.c_void_p(FAKE + 2)) == B.KDA_ERR_ALIGN
+    assert rp(pool(), n_req=0) == B.KDA_OK                              # no launch
