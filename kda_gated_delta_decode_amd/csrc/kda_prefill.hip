@@ -37,8 +37,8 @@
 // last tokens of a chunk, whose Kd rows are the largest, it is then exactly 0
 // or small, where a difference would leave about one ulp of the chunk's total
 // decay (a relative error of 1e-6 in Kd at a total of 25 in log2 units).
-// In the 32-token kernel the block-local cumulative decays are compensated
-// sums (fp32 high and low parts, see row_scan2), and A and P take both parts:
+// In the 32-token kernel the block-local cumulative decays are summed in fp64
+// and kept as fp32 high and low parts (see row_scan2), and A and P take both:
 // their in-block factors 2^(G_t - G_s) are products of 2^(+-G) factors whose
 // exponents are large where the decay between t and s is small, so one ulp of
 // G would be a relative error of 1e-6 in an O(1) factor.  (The 64-token
@@ -777,9 +777,10 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
   constexpr int CPL = kWsCpl;
   constexpr int NPAIR = NB * (NB + 1) / 2;
   __shared__ WsBuf sb[2];
-  // low parts of the compensated block-local cumulative decays (the high
-  // parts are the rows of Y) and of the block totals: read only by the
-  // preparation waves within the chunk that wrote them, so single-buffered
+  // low parts (fp64 sum minus its fp32 rounding) of the block-local
+  // cumulative decays (the high parts are the rows of Y) and of the block
+  // totals: read only by the preparation waves within the chunk that wrote
+  // them, so single-buffered
   __shared__ __attribute__((aligned(16))) float sYlo[kWsC * kLdK];
   __shared__ __attribute__((aligned(16))) float sBlo[kWsNB][128];
 
@@ -1009,8 +1010,8 @@ void kda_prefill_ws_kernel(PrefillArgs a) {
         }
         if (!exact) {
           // Step (m, e): channel 32 gq + m + e of both operands.  Diagonal
-          // block: t-factor 2^(gl_t), s-factor 2^(-gl_s), each from the
-          // compensated sums (their exponents cancel to the small in-block
+          // block: t-factor 2^(gl_t), s-factor 2^(-gl_s), each from the high
+          // and low parts (their exponents cancel to the small in-block
           // decay).  Block bt > bsb: t-factor 2^(gl_t), whose exponent is the
           // product's own order (no low part needed), s-factor
           // 2^(Btot_bsb - gl_s), the difference taken in high and low parts.

@@ -135,8 +135,9 @@ def test_prefill_strong_decay_takes_the_exact_path(oracle, chunk):
     """Log-decays of -3 .. -8 per token: the in-block decay passes e^80, so
     the diagonal blocks go pair by pair; results stay finite and accurate.
     Outputs here are small differences of large terms, and the fp32 oracle
-    itself is about 2e-5 from fp64.  With 32-token chunks (compensated
-    in-block decay sums) the kernel is held to 1e-5 from fp64 all the same;
+    itself is about 2e-5 from fp64.  With 32-token chunks (in-block decay
+    sums in fp64, kept as high and low parts) the kernel is held to 1e-5
+    from fp64 all the same;
     with 64-token chunks (plain sums) to 1.5 times the oracle's own error."""
     inp = kda_inputs.make_prefill_inputs("prefill strong decay", [130, 40], 8, "f32", H=2, seed=12)
     inp.g[:] = -np.random.default_rng(0).uniform(3.0, 8.0, inp.g.shape).astype(np.float32)
