@@ -561,10 +561,11 @@ def summarize(inp, tt):
 
 def fused_conv(n_req, n_rows, dtype, B, torch, steps, **launch):
     """Time the decode step with the short convolution fused in front
-    (kda_decode_step_conv) on a 96-slot pool; state pools and conv pools both
-    rotate over >= 1 GiB.  Algorithmic bytes add to the plain step's the raw
-    q|k|v rows, the taps, and the conv history (3 bf16 entries of 3*H*128
-    channels) read once per request and written once per row."""
+    (kda_decode_step_conv, with pair counters: kda_decode_step_conv_ws) on a
+    96-slot pool; state pools and conv pools both rotate over >= 1 GiB.
+    Algorithmic bytes add to the plain step's the raw q|k|v rows, the taps,
+    and the conv history (3 bf16 entries of 3*H*128 channels) read once per
+    request and written once per row."""
     import kda_inputs
     ci = kda_inputs.make_conv_inputs("fused conv + decode, %d req x %d rows, %s pool, H=12"
                                      % (n_req, n_rows, dtype), 96, n_req, n_rows, dtype, seed=0)
@@ -574,6 +575,7 @@ def fused_conv(n_req, n_rows, dtype, B, torch, steps, **launch):
     convs = [conv0] + [conv0.clone() for _ in range(len(w.pools) - 1)]
     x = torch.from_numpy(ci.x).cuda()
     cw = torch.from_numpy(ci.w).cuda()
+    launch.setdefault("pair_counts", B.conv_pair_counts(n_req, inp.pool.shape[1], x.device))
 
     def step(i):
         B.kda_decode_step_conv(w.pools[i % len(w.pools)], convs[i % len(convs)], w.ids, x, cw,

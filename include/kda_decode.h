@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7  /* 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
+#define KDA_ABI_VERSION 8  /* 8: kda_decode_step_conv_ws; 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -177,13 +177,15 @@ int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids,
  *  rows_layout     chained rows only: KDA_ROWS_DEFAULT, KDA_ROWS_K_SPLIT,
  *                  KDA_ROWS_WAVE_K or KDA_ROWS_MATRIX (a block form
  *                  whatever block_rows says); ignored for one row.  The
- *                  default: for fp16 pools the matrix-core block form, or,
- *                  when bv or waves_per_tile is set, the whole-K layout (bv
- *                  64 over 4 waves unless set); for fp32 pools the K split
- *                  (bv 64 over 8 waves), or the matrix-core block form for
- *                  launches of at most 48 requests x heads with no bv or
- *                  waves option; block_rows alone selects the K-split block
- *                  form.
+ *                  default, with units = requests x heads: for fp16 pools
+ *                  the matrix-core block form for 3 rows or more up to 240
+ *                  units, else the whole-K layout up to 48 units and the K
+ *                  split beyond; when bv or waves_per_tile is set, the
+ *                  whole-K layout (bv 64 over 4 waves unless set).  For
+ *                  fp32 pools the matrix-core block form for 6 rows or
+ *                  more up to 48 units with no bv or waves option, else the
+ *                  K split (bv 64 over 8 waves).  block_rows alone selects
+ *                  the K-split block form.
  * Supported K-split combinations keep 2..32 key rows per lane (rows per
  * lane = 2 * lanes per row / waves).  The shape changes the order of the
  * fp32 column sums over K (so results may differ in the last bits), never
@@ -261,13 +263,14 @@ typedef struct kda_conv_pool {
  * then the decode update.  Row t's snapshot slot receives both the state and
  * the history after row t (its last 3 raw inputs, rounded to bfloat16 to
  * nearest even); rows of one launch use their fp32 inputs directly.
- * Launch shapes: whole heads only (opts->bv 0 or 128).  Chained rows take
- * the matrix-core block form (KDA_ROWS_MATRIX: 8 waves, two 64-column
- * halves) when rows_layout asks for it, or by default for fp16 pools and
- * for fp32 launches of at most 48 requests x heads, unless waves_per_tile or
- * block_rows is set; otherwise the K-split kernel with 2,
- * 4 or 8 waves.  KDA_ROWS_WAVE_K is refused; rows_layout is ignored for one
- * row.
+ * Launch shapes: whole heads only (opts->bv 0 or 128), since a head's
+ * history at the initial slot is read and may be rewritten in place by one
+ * workgroup.  Chained rows take the matrix-core block form (KDA_ROWS_MATRIX:
+ * 16 waves, two 64-column halves of 8; waves_per_tile 8: two halves of 4)
+ * when rows_layout asks for it, or by default for 3 rows or more up to 192
+ * (fp16) or 48 (fp32) requests x heads unless waves_per_tile or block_rows
+ * is set; otherwise the K-split kernel with 2, 4 or 8 waves.
+ * KDA_ROWS_WAVE_K is refused; rows_layout is ignored for one row.
  * Errors: as kda_decode_step_ex, plus KDA_ERR_NULL for a missing conv pool,
  * x or conv_w, KDA_ERR_SHAPE if the pools' n_slots or H differ.
  */
@@ -277,6 +280,48 @@ int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
                          const float* b, float* out, int32_t n_req,
                          int32_t n_rows_per_slot, kda_dtype state_dtype,
                          float scale, const kda_launch_opts* opts, void* stream);
+
+/*
+ * kda_decode_step_conv_ws -- kda_decode_step_conv with pair counters, which
+ * let chained rows in the matrix-core block form split each head into two
+ * 64-column workgroups of 8 waves (twice the workgroups: with fewer heads
+ * than compute units, a unit's store throughput bounds the whole-head form).
+ * Both halves read the initial slot's q and k history; the row whose slot
+ * is the initial slot may overwrite it only after both have read it, so each
+ * half adds 1 to the counter of its (request, head) once its reads are done,
+ * and the half that finds an odd count writes that row's q and k history.
+ * No workgroup waits for another.
+ *
+ *  pair_counts    NULL (then exactly kda_decode_step_conv), or device
+ *                 uint32 [n_pair_counts], n_pair_counts >= n_req * H,
+ *                 4-byte aligned: counter r * H + h serves request r, head
+ *                 h.  Owned by the caller.  Every entry must be even
+ *                 (zero-fill once) before the first call; each call adds 0
+ *                 or 2 to an entry, so entries stay even and one buffer
+ *                 serves any number of calls in sequence.  Calls that may run
+ *                 at the same time (other streams, concurrent graphs) need
+ *                 buffers of their own.
+ *  n_pair_counts  entries of pair_counts (0 with NULL).
+ *  opts           as kda_decode_step_conv, plus bv 64: the halves, which
+ *                 need pair_counts.  With pair_counts, chained rows take
+ *                 the halves when rows_layout is KDA_ROWS_MATRIX or by
+ *                 default up to 96 (fp16) requests x heads, or for fp32 up
+ *                 to 48, or 96 with 6 rows or more, unless waves_per_tile or
+ *                 block_rows is set; bv 128 keeps whole heads; beyond, the
+ *                 defaults of kda_decode_step_conv.
+ * Errors: as kda_decode_step_conv, plus KDA_ERR_NULL for NULL pair_counts
+ * with n_pair_counts != 0, KDA_ERR_ARG for n_pair_counts < 0 or, with
+ * counters given, n_pair_counts < n_req * H, or bv 64 without counters,
+ * KDA_ERR_ALIGN for misaligned counters.
+ */
+int kda_decode_step_conv_ws(const kda_pool* pool, const kda_conv_pool* conv,
+                            const int32_t* slot_ids, const int32_t* init_slot_ids,
+                            const float* x, const float* conv_w, const float* g,
+                            const float* b, float* out, int32_t n_req,
+                            int32_t n_rows_per_slot, kda_dtype state_dtype,
+                            float scale, uint32_t* pair_counts,
+                            int32_t n_pair_counts, const kda_launch_opts* opts,
+                            void* stream);
 
 /*
  * kda_validate -- host-side check of a launch's arguments and slot tables

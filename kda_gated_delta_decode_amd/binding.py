@@ -91,6 +91,10 @@ SIGNATURES = {
     "kda_decode_step_conv": (ctypes.c_int, [ctypes.POINTER(kda_pool), ctypes.POINTER(kda_conv_pool),
                                             _P, _P, _P, _P, _P, _P, _P, _I32, _I32, ctypes.c_int,
                                             ctypes.c_float, ctypes.POINTER(kda_launch_opts), _P]),
+    "kda_decode_step_conv_ws": (ctypes.c_int, [ctypes.POINTER(kda_pool), ctypes.POINTER(kda_conv_pool),
+                                               _P, _P, _P, _P, _P, _P, _P, _I32, _I32, ctypes.c_int,
+                                               ctypes.c_float, _P, _I32, ctypes.POINTER(kda_launch_opts),
+                                               _P]),
     "kda_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, ctypes.c_int]),
     "kda_state_copy": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, ctypes.c_int, _P]),
     "kda_prefill": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -281,14 +285,25 @@ def make_conv_pool(conv) -> kda_conv_pool:
     return kda_conv_pool(ctypes.c_void_p(conv.data_ptr()), conv.shape[0], conv.shape[3])
 
 
+def conv_pair_counts(n_req: int, H: int, device):
+    """Zeroed pair counters for kda_decode_step_conv(pair_counts=...): one
+    int32 per (request, head) of the largest launch they serve.  Launches
+    leave them even, so one buffer serves any number of launches in a row,
+    but not launches that may overlap (another stream, a concurrent graph)."""
+    import torch
+    return torch.zeros(int(n_req) * int(H), dtype=torch.int32, device=device)
+
+
 def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot: int = 1,
                          state_dtype=None, scale: float | None = None, stream=None,
                          init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0,
-                         block_rows: bool = False, rows_layout: int = 0) -> None:
+                         block_rows: bool = False, rows_layout: int = 0, pair_counts=None) -> None:
     """Decode step with the short causal convolution fused in front (see
     kda_decode_step_conv in include/kda_decode.h).  conv: bfloat16 history
     [n_slots, 3, 3, H, 128]; x: fp32 raw q|k|v [R, 3, H, 128]; conv_w: fp32
-    taps [3, H, 128, 4]; the other arguments as kda_decode_step."""
+    taps [3, H, 128, 4]; pair_counts: None, or device int32 counters from
+    conv_pair_counts (kda_decode_step_conv_ws: chained rows then take
+    64-column halves); the other arguments as kda_decode_step."""
     import torch
     P = make_pool(pool)
     Cv = make_conv_pool(conv)
@@ -306,13 +321,18 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
                        (b, "b", R * H), (init_slot_ids, "init_slot_ids", n_req)):
         _need_numel(t, name, n)
     opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout))
-    rc = library().kda_decode_step_conv(
-        ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32, dv),
-        _dev(init_slot_ids, "init_slot_ids", torch.int32, dv), _dev(x, "x", torch.float32, dv),
-        _dev(conv_w, "conv_w", torch.float32, dv), _dev(g, "g", torch.float32, dv),
-        _dev(b, "b", torch.float32, dv), _dev(out, "out", torch.float32, dv), n_req,
-        n_rows_per_slot, sd, float(scale), ctypes.byref(opts), _stream_ptr(stream))
-    _check(rc, "kda_decode_step_conv")
+    args = (ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32, dv),
+            _dev(init_slot_ids, "init_slot_ids", torch.int32, dv), _dev(x, "x", torch.float32, dv),
+            _dev(conv_w, "conv_w", torch.float32, dv), _dev(g, "g", torch.float32, dv),
+            _dev(b, "b", torch.float32, dv), _dev(out, "out", torch.float32, dv), n_req,
+            n_rows_per_slot, sd, float(scale))
+    if pair_counts is None:
+        rc = library().kda_decode_step_conv(*args, ctypes.byref(opts), _stream_ptr(stream))
+        _check(rc, "kda_decode_step_conv")
+    else:
+        rc = library().kda_decode_step_conv_ws(*args, _dev(pair_counts, "pair_counts", torch.int32, dv),
+                                               pair_counts.numel(), ctypes.byref(opts), _stream_ptr(stream))
+        _check(rc, "kda_decode_step_conv_ws")
 
 
 def kda_prefill(pool, init_slot_ids, cu_seqlens, q, k, v, g, b, out, dst_slot_ids=None,

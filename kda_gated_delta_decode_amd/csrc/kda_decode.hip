@@ -57,6 +57,7 @@ struct Args {
   const float* x;          // raw q|k|v inputs [R, 3, H, 128]
   const float* conv_w;     // taps [3, H, 128, 4], tap 3 on the newest input
   uint16_t* conv_pool;     // bf16 history [n_slots, 3, 3 * H * 128], entry 0 oldest
+  uint32_t* pair_counts;   // per (request, head) arrival counters (convolution in halves)
   int32_t n_slots;
   int32_t H;
   int32_t n_rows;
@@ -1571,60 +1572,98 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
 }
 
 // ---------------------------------------------------------------------------
-// The same block form with K split over 8 waves (kda_rows_mfma8_kernel<T>,
-// the default layout of chained rows on the matrix cores, without the
-// convolution).  Workgroup = (request, head, 64-column half), 8 waves: wave w
-// holds key rows 16 w .. 16 w + 15, lane (gq, li) rows 16 w + 4 gq + j (j <
-// 4) and columns 4 li .. 4 li + 3 of the half, so each state load or store
-// instruction still covers whole 128-byte (fp16) or 256-byte (fp32) rows of
-// the half.  Against the 4-wave form, each wave runs half the matrix-core
-// steps (16 instead of 32 of v_mfma_f32_16x16x4_f32) and half the snapshot
-// work per row, and two waves share each SIMD, so one wave's vector work
-// runs while the other's products or stores are in flight.  Each wave loads
-// and normalises one row of the request (one 8-byte q, k and g vector per
-// lane): the prologue issues 4 row loads per wave instead of 22.  The eight
-// waves' partial column sums meet in LDS in two steps (each thread sums one
-// 8-byte piece over the waves, then every lane reads the 16 totals of its
-// column), which keeps the LDS traffic of the 4-wave form.
+// The same block form with K split over 8 waves (kda_rows_mfma8_kernel<T,
+// FORM>, the default layout of chained rows on the matrix cores).  Workgroup
+// = (request, head, 64-column half), 8 waves: wave w holds key rows 16 w ..
+// 16 w + 15, lane (gq, li) rows 16 w + 4 gq + j (j < 4) and columns 4 li ..
+// 4 li + 3 of the half, so each state load or store instruction still covers
+// whole 128-byte (fp16) or 256-byte (fp32) rows of the half.  Against the
+// 4-wave form, each wave runs half the matrix-core steps (16 instead of 32 of
+// v_mfma_f32_16x16x4_f32) and half the snapshot work per row, and two waves
+// share each SIMD, so one wave's vector work runs while the other's products
+// or stores are in flight.  Each wave loads and normalises one row of the
+// request (one 8-byte q, k and g vector per lane): the prologue issues 4 row
+// loads per wave instead of 22.  The eight waves' partial column sums meet in
+// LDS in two steps (each thread sums one 8-byte piece over the waves, then
+// every lane reads the 16 totals of its column), which keeps the LDS traffic
+// of the 4-wave form.
 //
+// Three forms:
+//  kRowsPlain     the decode step as described.
+//  kRowsConvHead  the short convolution fused in front, a whole head per
+//                 workgroup: two 64-column halves of 8 waves, 16 waves in
+//                 all.  Wave w of each half takes row w: in half 0 its q,
+//                 in half 1 its k (2 channels per lane), and in both its
+//                 half's 64 v channels (one per lane), so the 16 waves share
+//                 the convolution's loads and arithmetic evenly; half 0
+//                 stages beta, half 1 the decays.  One workgroup owns all of
+//                 a head's history, so the history it reads at the initial
+//                 slot may be rewritten at row 0's slot with a barrier
+//                 between the two.
+//  kRowsConvHalf  the convolution fused in front, 64-column halves as in
+//                 the plain form (twice the workgroups: on MI355X a CU's
+//                 store throughput, not the HBM, bounds the whole-head
+//                 form's snapshots when a launch has fewer heads than CUs).
+//                 Both halves of a head form its q and k (wave w: row w, 2
+//                 channels of each per lane) and their own v channels.  The
+//                 history is written by channel owner: v by its half, q by
+//                 half 0, k by half 1, except at a row whose slot is the
+//                 initial slot (at most one per request, slots being
+//                 distinct): both halves read q and k there, so neither may
+//                 overwrite them before the other has read them.  That row's
+//                 wave in each half counts its half's arrival on the
+//                 request's and head's counter once the workgroup's history
+//                 reads are done (after the first barrier); the half that
+//                 arrives second (odd count before its increment) writes that
+//                 row's q and k history.  No wave waits on another
+//                 workgroup.  Each launch adds 2 per such counter, so counters
+//                 that start even stay even.
 // ---------------------------------------------------------------------------
-constexpr int kMfma8Waves = 8;
+constexpr int kMfma8Waves = 8;  // waves per 64-column half
+constexpr int kRowsPlain = 0, kRowsConvHead = 1, kRowsConvHalf = 2;
 
-template <typename T>
-__global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA_HOT_PARAMS, Args a) {
+template <typename T, int FORM>
+__global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 1)) void kda_rows_mfma8_kernel(
+    KDA_HOT_PARAMS, Args a) {
   const int init_stride = unpack_hot(a, hot_ids, hot_pool, hot_q, hot_k, hot_slots, hot_dims);
   using vec = typename Piece4<T>::vec;
+  constexpr bool CONV = FORM != kRowsPlain;
+  constexpr bool HEAD = FORM == kRowsConvHead;
   constexpr int TMAX = KDA_MAX_ROWS;
-  constexpr int NW = kMfma8Waves;
-  constexpr int BH = kMfmaBV;          // columns per workgroup (one half of a head)
-  constexpr int RPW = kHeadK / NW;     // key rows per wave
-  constexpr int J = RPW / 4;           // key rows per lane (= matrix-core steps)
-  static_assert(TMAX == NW, "one row of the request per wave");
+  constexpr int HALVES = HEAD ? 2 : 1;  // 64-column halves per workgroup
+  constexpr int NW = kMfma8Waves;       // waves per half
+  constexpr int BH = kMfmaBV;           // columns per half
+  constexpr int BV = BH * HALVES;       // columns per workgroup
+  constexpr int RPW = kHeadK / NW;      // key rows per wave
+  constexpr int J = RPW / 4;            // key rows per lane (= matrix-core steps)
+  static_assert(TMAX == NW, "one row of the request per wave of a half");
 
   __shared__ __attribute__((aligned(16))) float s_kn[TMAX][kLdRow];
   __shared__ __attribute__((aligned(16))) float s_qn[TMAX][kLdRow];
   __shared__ __attribute__((aligned(16))) float s_a[TMAX][kLdRow];
-  __shared__ __attribute__((aligned(16))) float s_v[TMAX][BH];
-  // [wave][gq][column] = the wave's D[4 gq + r][column], r = 0..3
-  __shared__ __attribute__((aligned(16))) f4 s_part[NW][4][BH];
-  // [gq][column] = the totals over the waves
-  __shared__ __attribute__((aligned(16))) f4 s_tot[4][BH];
+  __shared__ __attribute__((aligned(16))) float s_v[TMAX][BV];
+  // [half][wave of the half][gq][column of the half] = the wave's D[4 gq + r][column], r = 0..3
+  __shared__ __attribute__((aligned(16))) f4 s_part[HALVES][NW][4][BH];
+  // [half][gq][column of the half] = the totals over the half's waves
+  __shared__ __attribute__((aligned(16))) f4 s_tot[HALVES][4][BH];
   __shared__ __attribute__((aligned(16))) float s_cP[TMAX][TMAX];
   __shared__ __attribute__((aligned(16))) float s_cA[TMAX][TMAX];
   __shared__ __attribute__((aligned(16))) float s_beta[TMAX];
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
+  const int half = HEAD ? wave / NW : 0;
+  const int rw = HEAD ? wave % NW : wave;  // the wave's place in its half, and its row
   const int gq = lane / 16, li = lane % 16;
   const int H = a.H;
   const int n_rows = a.n_rows;
 
   const int tile = tile_of_block(blockIdx.x, hot_blocks);
-  const int vt = tile % (kHeadV / BH);
-  const int rh = tile / (kHeadV / BH);
+  const int vt = tile % (kHeadV / BV);
+  const int rh = tile / (kHeadV / BV);
   const int h = rh % H;
   const int r = rh / H;
-  const int hcol = vt * BH;
+  const int hcol = vt * BV + half * BH;  // the first column of this wave's half
 
   const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
   int32_t sid[TMAX];
@@ -1636,24 +1675,74 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA
   // last one and stages zeros).
   int zero_v;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
-  const int trow = min(wave, n_rows - 1);
+  const int trow = min(rw, n_rows - 1);
   const int64_t rho = static_cast<int64_t>(r) * n_rows + trow;
   const int64_t roff = (rho * H + h) * kHeadK;
-  const f2 q2 = reinterpret_cast<const f2*>(a.q + roff)[lane];
-  const f2 k2 = reinterpret_cast<const f2*>(a.k + roff)[lane];
-  const f2 g2 = reinterpret_cast<const f2*>(a.g + roff)[lane];
-  const float v1 = a.v[roff + hcol + lane];
-  const float braw = a.b[rho * H + h + zero_v];
+  f2 q2, k2, g2;
+  float v1, braw;
+  // fused convolution: the window win[trow + m], m = 0..3 (the 3-entry
+  // history, then this request's rows) of the lane's 2 q channels (eq; the
+  // whole-head form: q or k by half), 2 k channels (ek; halves form only)
+  // and its v channel, and their taps
+  f2 eq[4], ek[4];
+  float ev[4];
+  f4 wq0, wq1, wk0, wk1, wv;
+  const int64_t conv_c = static_cast<int64_t>(3) * H * kHeadK;  // channels per history entry
+  const int64_t chq = static_cast<int64_t>(half * H + h) * kHeadK + 2 * lane;
+  const int64_t chk = static_cast<int64_t>(H + h) * kHeadK + 2 * lane;
+  const int64_t chv = static_cast<int64_t>(2 * H + h) * kHeadK + hcol + lane;
+  if constexpr (!CONV) {
+    q2 = reinterpret_cast<const f2*>(a.q + roff)[lane];
+    k2 = reinterpret_cast<const f2*>(a.k + roff)[lane];
+    g2 = reinterpret_cast<const f2*>(a.g + roff)[lane];
+    v1 = a.v[roff + hcol + lane];
+    braw = a.b[rho * H + h + zero_v];
+  } else {
+    // the history is read at the initial slot (slot 0 for a request with a
+    // bad id, which is skipped below, so every address stays valid)
+    bool ok0 = init_slot >= 0 && init_slot < a.n_slots;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) ok0 = ok0 && sid[t] >= 0 && sid[t] < a.n_slots;
+    const int64_t hslot = ok0 ? init_slot : 0;
+    wq0 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4);
+    wq1 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4 + 4);
+    if constexpr (!HEAD) {
+      wk0 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4);
+      wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
+    }
+    wv = *reinterpret_cast<const f4*>(a.conv_w + chv * 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int pos = trow + m;  // window index (wave-uniform)
+      if (pos < 3) {
+        const uint16_t* hb = a.conv_pool + (hslot * 3 + pos) * conv_c;
+        const uint32_t pq = *reinterpret_cast<const uint32_t*>(hb + chq);
+        eq[m] = f2{bf16_lo(pq), bf16_hi(pq)};
+        if constexpr (!HEAD) {
+          const uint32_t pk = *reinterpret_cast<const uint32_t*>(hb + chk);
+          ek[m] = f2{bf16_lo(pk), bf16_hi(pk)};
+        }
+        ev[m] = bf16_lo(hb[chv]);
+      } else {
+        const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * conv_c;
+        eq[m] = *reinterpret_cast<const f2*>(xr + chq);
+        if constexpr (!HEAD) ek[m] = *reinterpret_cast<const f2*>(xr + chk);
+        ev[m] = xr[chv];
+      }
+    }
+    if (!HEAD || half == 0) braw = a.b[rho * H + h + zero_v];
+    if (!HEAD || half == 1) g2 = reinterpret_cast<const f2*>(a.g + roff)[lane];
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   bool ids_ok = init_slot >= 0 && init_slot < a.n_slots;
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
 
-  // The initial state: rows 16 wave + 4 gq + j, columns 4 li .. 4 li + 3 of the half.
+  // The initial state: rows 16 rw + 4 gq + j, columns 4 li .. 4 li + 3 of the half.
   const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
   const int64_t slot_elems = static_cast<int64_t>(H) * head_elems;
-  const int row0 = RPW * wave + J * gq;
+  const int row0 = RPW * rw + J * gq;
   const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + hcol + 4 * li;
   T* const pool = static_cast<T*>(a.pool);
   vec raw[J];
@@ -1665,27 +1754,104 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  const bool live = rw < n_rows;
   {
-    const bool live = wave < n_rows;
-    const float sq = wave_sum(fmaf(q2[1], q2[1], q2[0] * q2[0]));
-    const float sk = wave_sum(fmaf(k2[1], k2[1], k2[0] * k2[0]));
-    const float rq = live ? 1.0f / sqrtf(sq + 1e-6f) : 0.0f;
-    const float rk = live ? 1.0f / sqrtf(sk + 1e-6f) : 0.0f;
-    *reinterpret_cast<f2*>(&s_qn[wave][2 * lane]) = f2{q2[0] * rq, q2[1] * rq};
-    *reinterpret_cast<f2*>(&s_kn[wave][2 * lane]) = f2{k2[0] * rk, k2[1] * rk};
-    *reinterpret_cast<f2*>(&s_a[wave][2 * lane]) =
-        live ? f2{expf(g2[0]), expf(g2[1])} : f2{0.0f, 0.0f};
-    s_v[wave][lane] = live ? v1 : 0.0f;
-    if (lane == 0) s_beta[wave] = live ? 1.0f / (1.0f + expf(-braw)) : 0.0f;
+    if constexpr (CONV) {
+      // y = silu(sum_m w_m win[trow + m]), the sum taken in window order
+      float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f, sv = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        sq0 = fmaf(wq0[m], eq[m][0], sq0);
+        sq1 = fmaf(wq1[m], eq[m][1], sq1);
+        if constexpr (!HEAD) {
+          sk0 = fmaf(wk0[m], ek[m][0], sk0);
+          sk1 = fmaf(wk1[m], ek[m][1], sk1);
+        }
+        sv = fmaf(wv[m], ev[m], sv);
+      }
+      q2 = f2{silu(sq0), silu(sq1)};
+      if constexpr (!HEAD) k2 = f2{silu(sk0), silu(sk1)};
+      v1 = silu(sv);
+    }
+    if constexpr (!HEAD) {
+      const float sq = wave_sum(fmaf(q2[1], q2[1], q2[0] * q2[0]));
+      const float sk = wave_sum(fmaf(k2[1], k2[1], k2[0] * k2[0]));
+      const float rq = live ? 1.0f / sqrtf(sq + 1e-6f) : 0.0f;
+      const float rk = live ? 1.0f / sqrtf(sk + 1e-6f) : 0.0f;
+      *reinterpret_cast<f2*>(&s_qn[rw][2 * lane]) = f2{q2[0] * rq, q2[1] * rq};
+      *reinterpret_cast<f2*>(&s_kn[rw][2 * lane]) = f2{k2[0] * rk, k2[1] * rk};
+      *reinterpret_cast<f2*>(&s_a[rw][2 * lane]) =
+          live ? f2{expf(g2[0]), expf(g2[1])} : f2{0.0f, 0.0f};
+      s_v[rw][lane] = live ? v1 : 0.0f;
+      if (lane == 0) s_beta[rw] = live ? 1.0f / (1.0f + expf(-braw)) : 0.0f;
+    } else {
+      // half 0 normalises q, half 1 k
+      const float ss = wave_sum(fmaf(q2[1], q2[1], q2[0] * q2[0]));
+      const float rn = live ? 1.0f / sqrtf(ss + 1e-6f) : 0.0f;
+      float* xn = half == 0 ? &s_qn[rw][2 * lane] : &s_kn[rw][2 * lane];
+      *reinterpret_cast<f2*>(xn) = f2{q2[0] * rn, q2[1] * rn};
+      s_v[rw][half * BH + lane] = live ? v1 : 0.0f;
+      if (half == 0) {
+        if (lane == 0) s_beta[rw] = live ? 1.0f / (1.0f + expf(-braw)) : 0.0f;
+      } else {
+        *reinterpret_cast<f2*>(&s_a[rw][2 * lane]) =
+            live ? f2{expf(g2[0]), expf(g2[1])} : f2{0.0f, 0.0f};
+      }
+    }
   }
   if (!ids_ok) {  // uniform over the workgroup: no wave waits at the barrier
-    if (wave < n_rows) {
-      const int64_t orow = static_cast<int64_t>(r) * n_rows + wave;
+    if (live) {
+      const int64_t orow = static_cast<int64_t>(r) * n_rows + rw;
       a.out[(orow * H + h) * kHeadV + hcol + lane] = NAN;
     }
     return;
   }
   __syncthreads();
+
+  // -- history snapshots: row t keeps win[t + 1 .. t + 3] ----------------------
+  // After the barrier every wave of the workgroup has read the history it
+  // needs (its values are in LDS).
+  int32_t st = sid[0];  // this wave's row's slot
+#pragma unroll
+  for (int u = 1; u < TMAX; ++u)
+    if (u == rw) st = sid[u];
+  uint16_t* const hrow = CONV ? a.conv_pool + static_cast<int64_t>(st) * 3 * conv_c : nullptr;
+  auto store_pair = [&](int64_t ch, const f2 (&e)[4]) {
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      *reinterpret_cast<uint32_t*>(hrow + m * conv_c + ch) = bf16_pack(e[m + 1][0], e[m + 1][1]);
+  };
+  // the initial slot's row, if any (kRowsConvHalf): its q and k wait for the
+  // pair counter.  What must be ordered is the first half's history reads
+  // before the second half's history stores, and nothing else: every read
+  // of this workgroup has returned its data before the barrier above (the
+  // values are in LDS), the increment is issued after it and performed at
+  // device scope, and the second half's stores depend on the value its
+  // increment returns.  The increment is therefore relaxed: an agent-scope
+  // release would also write back this XCD's L2 (buffer_wbl2), which
+  // measured 14.2 against 10.9 us for 8 requests x 8 rows and 58 against
+  // 24 us for 48 x 2 (fp16), for stores no other workgroup reads.
+  const bool handover = !HEAD && CONV && live && st == init_slot;
+  uint32_t arrival = 0;
+  if constexpr (CONV && !HEAD) {
+    if (handover && lane == 0)
+      arrival = __hip_atomic_fetch_add(a.pair_counts + static_cast<int64_t>(r) * H + h, 1u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if constexpr (CONV) {
+    if (live) {
+#pragma unroll
+      for (int m = 0; m < 3; ++m) hrow[m * conv_c + chv] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(ev[m + 1]));
+      if constexpr (HEAD) {
+        store_pair(chq, eq);  // q (half 0) or k (half 1)
+      } else if (!handover) {
+        if (vt == 0)
+          store_pair(chq, eq);
+        else
+          store_pair(chk, ek);
+      }
+    }
+  }
 
   // couplings (waves 0..3: two columns of the n x n matrices each), then
   // this wave's share of w0 and p0 on the matrix cores
@@ -1726,27 +1892,29 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA
       for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(wj, S[j][e], acc[e], 0, 0, 0);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_part[wave][gq][4 * li + e] = acc[e];
+    for (int e = 0; e < 4; ++e) s_part[half][rw][gq][4 * li + e] = acc[e];
   }
   __syncthreads();
-  // totals over the waves: thread i sums the 8-byte piece (i mod 2) of entry
-  // i / 2 of the [4][64] f4 array, in a fixed tree order
+  // totals over a half's waves: thread i of the half sums the 8-byte piece
+  // (i mod 2) of entry i / 2 of the half's [4][64] f4 array, in a fixed tree
+  // order
   {
-    const int ent = threadIdx.x >> 1, pc = threadIdx.x & 1;
+    const int ti = HEAD ? threadIdx.x % (kWave * NW) : threadIdx.x;
+    const int ent = ti >> 1, pc = ti & 1;
     const int eg = ent / BH, ec = ent % BH;
     f2 x[NW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) x[w] = reinterpret_cast<const f2*>(&s_part[w][eg][ec])[pc];
+    for (int w = 0; w < NW; ++w) x[w] = reinterpret_cast<const f2*>(&s_part[half][w][eg][ec])[pc];
     const f2 t01 = x[0] + x[1], t23 = x[2] + x[3], t45 = x[4] + x[5], t67 = x[6] + x[7];
-    reinterpret_cast<f2*>(&s_tot[eg][ec])[pc] = (t01 + t23) + (t45 + t67);
+    reinterpret_cast<f2*>(&s_tot[half][eg][ec])[pc] = (t01 + t23) + (t45 + t67);
   }
   __syncthreads();
 
-  // Every wave solves the 64 columns of the half (lane l: column l) and
-  // writes row t's snapshot as soon as Delta_t is known; wave t writes row
-  // t's outputs.  The couplings and beta are the same for every column: each
-  // lane reads one and the solve takes them with readlane (the empty
-  // volatile asm keeps those reads in every lane).
+  // Every wave solves the 64 columns of its half (lane l: column l) and
+  // writes row t's snapshot as soon as Delta_t is known; wave t of the half
+  // writes row t's outputs.  The couplings and beta are the same for every
+  // column: each lane reads one and the solve takes them with readlane (the
+  // empty volatile asm keeps those reads in every lane).
   float cA_l = s_cA[lane >> 3][lane & 7];
   float cP_l = s_cP[lane >> 3][lane & 7];
   float bt_l = s_beta[lane & 7];
@@ -1756,12 +1924,12 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA
   float tot[16], vv[TMAX];
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
-    const f4 x = s_tot[gi][lane];
+    const f4 x = s_tot[half][gi][lane];
 #pragma unroll
     for (int e = 0; e < 4; ++e) tot[4 * gi + e] = x[e];
   }
 #pragma unroll
-  for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][lane];
+  for (int t = 0; t < TMAX; ++t) vv[t] = s_v[t][half * BH + lane];
   float* op = a.out + (static_cast<int64_t>(r) * n_rows * H + h) * kHeadV + hcol + lane;
   const int64_t o_row = static_cast<int64_t>(H) * kHeadV;
   float dl[TMAX];
@@ -1772,7 +1940,7 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA
 #pragma unroll
     for (int s2 = 0; s2 < t; ++s2) d = fmaf(-cA(t, s2), dl[s2], d);
     dl[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bt_l), t)) * d;
-    if (t == wave) {  // this wave writes row t's outputs of the half
+    if (t == rw) {  // this wave writes row t's outputs of the half
       float o = tot[8 + t];
 #pragma unroll
       for (int s2 = 0; s2 <= t; ++s2) o = fmaf(cP(t, s2), dl[s2], o);
@@ -1798,6 +1966,15 @@ __global__ __launch_bounds__(kWave * kMfma8Waves) void kda_rows_mfma8_kernel(KDA
         o[e] = static_cast<T>(s1);
       }
       __builtin_nontemporal_store(o, reinterpret_cast<vec*>(dst + j * kHeadV));
+    }
+  }
+
+  // the half that arrived second writes the initial slot's row's q and k
+  // history (the other half has read them by now)
+  if constexpr (CONV && !HEAD) {
+    if (handover && (__builtin_amdgcn_readlane(static_cast<int>(arrival), 0) & 1) != 0) {
+      store_pair(chq, eq);
+      store_pair(chk, ek);
     }
   }
 }
@@ -1926,7 +2103,7 @@ static hipError_t dispatch(const Args& a, const Shape& sh, int32_t blocks, hipSt
   if (sh.layout == KDA_ROWS_MATRIX) {
     const Hot h = hot_of(a, blocks);
     if (sh.nw == kMatrixWaves)
-      hipLaunchKernelGGL((kda_rows_mfma8_kernel<T>), dim3(blocks), dim3(kWave * kMatrixWaves), 0, s,
+      hipLaunchKernelGGL((kda_rows_mfma8_kernel<T, kRowsPlain>), dim3(blocks), dim3(kWave * kMatrixWaves), 0, s,
                          KDA_HOT_ARGS(h), a);
     else
       hipLaunchKernelGGL((kda_rows_mfma_kernel<T, false>), dim3(blocks), dim3(kWave * kMfmaWaves), 0, s,
@@ -1990,6 +2167,7 @@ extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
   a.x = nullptr;
   a.conv_w = nullptr;
   a.conv_pool = nullptr;
+  a.pair_counts = nullptr;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -2018,12 +2196,14 @@ extern "C" int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids, co
                             state_dtype, scale, nullptr, stream);
 }
 
-extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
-                                    const int32_t* slot_ids, const int32_t* init_slot_ids,
-                                    const float* x, const float* conv_w, const float* g,
-                                    const float* b, float* out, int32_t n_req,
-                                    int32_t n_rows_per_slot, kda_dtype state_dtype, float scale,
-                                    const kda_launch_opts* opts, void* stream) {
+// The fused step; pair_counts (nullable, n_pairs entries) lets chained rows
+// in the matrix-core form take 64-column halves.
+static int decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv, const int32_t* slot_ids,
+                            const int32_t* init_slot_ids, const float* x, const float* conv_w,
+                            const float* g, const float* b, float* out, int32_t n_req,
+                            int32_t n_rows_per_slot, kda_dtype state_dtype, float scale,
+                            uint32_t* pair_counts, int64_t n_pairs, const kda_launch_opts* opts,
+                            void* stream) {
   const int rc = check_common(pool, n_req, n_rows_per_slot, state_dtype);
   if (rc != KDA_OK) return rc;
   if (conv == nullptr || conv->base == nullptr) return KDA_ERR_NULL;
@@ -2033,13 +2213,17 @@ extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* c
       out == nullptr)
     return KDA_ERR_NULL;
   if (!std::isfinite(scale)) return KDA_ERR_ARG;
+  const int64_t units = static_cast<int64_t>(n_req) * pool->H;
+  if (pair_counts != nullptr && n_pairs < units) return KDA_ERR_ARG;
   Shape shape;
-  if (!resolve_conv_shape(state_dtype, n_rows_per_slot, static_cast<int64_t>(n_req) * pool->H, opts, &shape))
+  if (!resolve_conv_shape(state_dtype, n_rows_per_slot, units, opts, pair_counts != nullptr, &shape))
     return KDA_ERR_ARG;
   if (!aligned16(pool->base) || !aligned16(conv->base) || !aligned16(x) || !aligned16(conv_w) ||
       !aligned16(g) || !aligned16(out) || !aligned4(b) || !aligned4(slot_ids) ||
-      !aligned4(init_slot_ids))
+      !aligned4(init_slot_ids) || !aligned4(pair_counts))
     return KDA_ERR_ALIGN;
+  const int64_t tiles = units * (kHeadV / shape.bv);
+  if (tiles > INT32_MAX) return KDA_ERR_ARG;
   Args a;
   a.pool = pool->base;
   a.slot_ids = slot_ids;
@@ -2053,29 +2237,65 @@ extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* c
   a.x = x;
   a.conv_w = conv_w;
   a.conv_pool = static_cast<uint16_t*>(conv->base);
+  a.pair_counts = pair_counts;
   a.n_slots = pool->n_slots;
   a.H = pool->H;
   a.n_rows = n_rows_per_slot;
-  a.n_vt = 1;
+  a.n_vt = kHeadV / shape.bv;
   a.rows_block = opts != nullptr && opts->block_rows != 0 ? 1 : 0;
   a.scale = scale;
-  const int32_t blocks = n_req * pool->H;
+  const int32_t blocks = static_cast<int32_t>(tiles);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (shape.layout == KDA_ROWS_MATRIX) {
     const Hot h = hot_of(a, blocks);
-    if (state_dtype == KDA_F32)
-      hipLaunchKernelGGL((kda_rows_mfma_kernel<float, true>), dim3(blocks), dim3(kWave * kMatrixConvWaves),
-                         0, s, KDA_HOT_ARGS(h), a);
-    else
-      hipLaunchKernelGGL((kda_rows_mfma_kernel<_Float16, true>), dim3(blocks),
-                         dim3(kWave * kMatrixConvWaves), 0, s, KDA_HOT_ARGS(h), a);
+    const dim3 grid(blocks), block(kWave * shape.nw);
+    const bool f32 = state_dtype == KDA_F32;
+    if (shape.bv == kMatrixBV) {
+      if (f32)
+        hipLaunchKernelGGL((kda_rows_mfma8_kernel<float, kRowsConvHalf>), grid, block, 0, s, KDA_HOT_ARGS(h), a);
+      else
+        hipLaunchKernelGGL((kda_rows_mfma8_kernel<_Float16, kRowsConvHalf>), grid, block, 0, s, KDA_HOT_ARGS(h), a);
+    } else if (shape.nw == kMatrixConvWaves) {
+      if (f32)
+        hipLaunchKernelGGL((kda_rows_mfma8_kernel<float, kRowsConvHead>), grid, block, 0, s, KDA_HOT_ARGS(h), a);
+      else
+        hipLaunchKernelGGL((kda_rows_mfma8_kernel<_Float16, kRowsConvHead>), grid, block, 0, s, KDA_HOT_ARGS(h), a);
+    } else {
+      if (f32)
+        hipLaunchKernelGGL((kda_rows_mfma_kernel<float, true>), grid, block, 0, s, KDA_HOT_ARGS(h), a);
+      else
+        hipLaunchKernelGGL((kda_rows_mfma_kernel<_Float16, true>), grid, block, 0, s, KDA_HOT_ARGS(h), a);
+    }
     err = hipGetLastError();
   } else {
     err = state_dtype == KDA_F32 ? dispatch_conv<float>(a, shape.nw, blocks, s)
                                  : dispatch_conv<_Float16>(a, shape.nw, blocks, s);
   }
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
+                                    const int32_t* slot_ids, const int32_t* init_slot_ids,
+                                    const float* x, const float* conv_w, const float* g,
+                                    const float* b, float* out, int32_t n_req,
+                                    int32_t n_rows_per_slot, kda_dtype state_dtype, float scale,
+                                    const kda_launch_opts* opts, void* stream) {
+  return decode_step_conv(pool, conv, slot_ids, init_slot_ids, x, conv_w, g, b, out, n_req,
+                          n_rows_per_slot, state_dtype, scale, nullptr, 0, opts, stream);
+}
+
+extern "C" int kda_decode_step_conv_ws(const kda_pool* pool, const kda_conv_pool* conv,
+                                       const int32_t* slot_ids, const int32_t* init_slot_ids,
+                                       const float* x, const float* conv_w, const float* g,
+                                       const float* b, float* out, int32_t n_req,
+                                       int32_t n_rows_per_slot, kda_dtype state_dtype, float scale,
+                                       uint32_t* pair_counts, int32_t n_pair_counts,
+                                       const kda_launch_opts* opts, void* stream) {
+  if (pair_counts == nullptr && n_pair_counts != 0) return KDA_ERR_NULL;
+  if (n_pair_counts < 0) return KDA_ERR_ARG;
+  return decode_step_conv(pool, conv, slot_ids, init_slot_ids, x, conv_w, g, b, out, n_req,
+                          n_rows_per_slot, state_dtype, scale, pair_counts, n_pair_counts, opts, stream);
 }
 
 extern "C" int kda_state_copy(const kda_pool* pool, const int32_t* src_slot_ids,

@@ -90,26 +90,33 @@ inline bool wave_k_supported(kda_dtype dt, int32_t bv, int32_t nw) {
   return lpr == 2 || lpr == 4;
 }
 
-// The chained-row layout of a launch.  An explicit rows_layout wins; the
-// block_rows option alone means the K-split block form.  Otherwise, chosen by
-// measurement on MI355X (8 requests x 8 rows x 12 heads, graph-replayed
-// launches, 1 GiB of rotating pools): fp16 pools take the matrix-core block
-// form (8.95 us, against 11.8 us row after row with the whole of K in each
-// wave and 12.3 us with K split) unless a bv or waves option asks for a
-// row-after-row shape (then the whole-K layout, as before the block form
-// existed); fp32 pools keep the K split (11.5-11.6 us; the block form 13.3
-// us: its twice larger snapshot stores start only after the column sums
-// and the couplings, while the row-after-row chain stores from its first row
-// on) except for launches of at most 48 requests x heads, where the block
-// form is the faster (8 rows of 1, 2, 4 requests: 8.4, 8.5, 9.0 us against
-// 9.5, 9.6, 10.0 us; 6 requests: 11.2 against 10.4 us).
-inline int32_t chained_rows_layout(kda_dtype dt, const kda_launch_opts* opts, int64_t units) {
+// The chained-row layout of a launch of `units` = requests x heads with
+// n_rows rows each.  An explicit rows_layout wins; the block_rows option
+// alone means the K-split block form; a bv or waves option asks for a
+// row-after-row shape (the whole-K layout for fp16, the K split for fp32).
+// Otherwise, chosen by measurement on MI355X (H = 12, graph-replayed
+// launches over 1 GiB of rotating pools; microseconds):
+//   fp16: the matrix-core block form for 3 rows or more up to 240 units
+//     (8 x 8: 8.4 against 12.0 with K split; 20 x 8: 15.0 against 15.6;
+//     16 x 4: 8.8 against 9.1), the K split beyond (24 x 8: 19.6 against
+//     20.9; 24 x 4: 11.6 against 13.9); for 2 rows the whole-K layout up to
+//     48 units (1 x 2, 4 x 2: 4.3, 4.6 against 4.7, 5.0 with K split), the
+//     K split beyond (16 x 2: 6.7 against 7.8 as a block, 7.7 whole-K).
+//   fp32: the block form for 6 rows or more up to 48 units (1 x 8, 4 x 8:
+//     7.5, 9.2 against 9.4, 10.6 with K split), the K split otherwise (8 x 8:
+//     11.6 against 12.8; 8 x 6: 9.6 against 10.6; 1 x 2: 4.4 against 5.2).
+inline int32_t chained_rows_layout(kda_dtype dt, int32_t n_rows, const kda_launch_opts* opts,
+                                   int64_t units) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked != KDA_ROWS_DEFAULT) return asked;
   if (opts != nullptr && opts->block_rows != 0) return KDA_ROWS_K_SPLIT;
   const bool shaped = opts != nullptr && (opts->bv != 0 || opts->waves_per_tile != 0);
-  if (dt == KDA_F16) return shaped ? KDA_ROWS_WAVE_K : KDA_ROWS_MATRIX;
-  return !shaped && units <= 48 ? KDA_ROWS_MATRIX : KDA_ROWS_K_SPLIT;
+  if (dt == KDA_F16) {
+    if (shaped) return KDA_ROWS_WAVE_K;
+    if (n_rows >= 3 && units <= 240) return KDA_ROWS_MATRIX;
+    return units <= 48 ? KDA_ROWS_WAVE_K : KDA_ROWS_K_SPLIT;
+  }
+  return !shaped && n_rows >= 6 && units <= 48 ? KDA_ROWS_MATRIX : KDA_ROWS_K_SPLIT;
 }
 inline int32_t default_wave_k_bv(kda_dtype /*dt*/) { return 64; }
 inline int32_t default_wave_k_waves(kda_dtype /*dt*/) { return 4; }
@@ -119,13 +126,13 @@ inline bool block_supported(kda_dtype dt, int32_t nw) { return dt != KDA_F16 || 
 
 // The matrix-core block form of chained rows: 64 columns per workgroup, K
 // over 8 waves by default or over 4 (the first form, kept selectable); with
-// the fused convolution, whole heads: two 64-column halves of 4 waves.
-// Measured on MI355X (8 requests x 8 rows x 12 heads, fp16, graph replay,
-// rotated pools): see the kernel's header for the figures.
+// the fused convolution, whole heads: two 64-column halves of 8 waves by
+// default, or of 4.
 constexpr int32_t kMatrixBV = 64;
 constexpr int32_t kMatrixWaves = 8;
 constexpr int32_t kMatrixWaves4 = 4;
-constexpr int32_t kMatrixConvWaves = 2 * kMatrixWaves4;
+constexpr int32_t kMatrixConvWaves = 2 * kMatrixWaves;
+constexpr int32_t kMatrixConvWaves4 = 2 * kMatrixWaves4;
 // The kernels take H packed into 16 bits of a kernel argument.
 constexpr int32_t kMaxHeads = 0xFFFF;
 
@@ -142,7 +149,7 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, int64_t units, const kda
                           Shape* out) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX) return false;
-  const int32_t layout = n_rows > 1 ? chained_rows_layout(dt, opts, units) : KDA_ROWS_K_SPLIT;
+  const int32_t layout = n_rows > 1 ? chained_rows_layout(dt, n_rows, opts, units) : KDA_ROWS_K_SPLIT;
   if (layout == KDA_ROWS_MATRIX) {
     // 64 columns over 8 waves (default) or 4; a block form whatever
     // block_rows says
@@ -199,30 +206,55 @@ inline int32_t lds_bytes(int32_t bv, int32_t nw, int32_t n_rows, bool rows_block
 }
 
 // Fused-convolution launches take whole heads (bv = 128) so that a head's
-// convolution history is read and rewritten inside one workgroup.  Chained
-// rows take the matrix-core block form (8 waves: two 64-column halves) when
-// rows_layout asks for it or, by default for fp16 pools and for fp32 launches
-// of at most 48 requests x heads, when no waves or block_rows option asks
-// for a K-split shape (measured on MI355X: 8 x 8 rows, fp16 13.4 us against
-// 17.6 us K-split, fp32 16.5 against 16.4 us; 1 and 4 requests x 8 rows,
-// fp32 13.0 and 14.0 us against 14.9 and 15.7 us); otherwise the K-split
-// kernel with 2, 4 or 8 waves per tile (default: 2 fp32 / 4 fp16 for one
-// row, 8 / 4 for chained rows).  A bv option other than 0 or 128, or the
-// whole-K row layout, is refused; rows_layout is ignored for one row.
+// convolution history is read and rewritten inside one workgroup, except
+// chained rows in the matrix-core block form with pair counters: those may
+// take 64-column halves (bv = 64, 8 waves; the two halves of a head hand the
+// initial slot's history over through the request's and head's counter).
+// An explicit rows_layout wins (the matrix-core form: halves with counters,
+// whole heads without, unless bv says which); bv 64 alone asks for the
+// halves; a waves or block_rows option asks for the K split.  Otherwise,
+// measured on MI355X (H = 12, graph-replayed launches over 1 GiB of rotating
+// pools; microseconds):
+//   halves, with counters: fp16 up to 96 units (8 x 8: 10.9 against 13.2
+//     whole heads and 17.4 with K split; 8 x 2: 7.5 against 8.1 K split),
+//     fp32 up to 48 units, or up to 96 with 6 rows or more (4 x 8: 11.2
+//     against 13.2 and 15.8; 8 x 8: 15.7 against 16.0 and 16.3; 8 x 4: 11.2
+//     against 10.9 with K split);
+//   whole heads over 16 waves, for 3 rows or more: fp16 up to 192 units
+//     (12 x 8: 14.3 against 14.9 in halves and 17.8 K split; 16 x 4: 11.7
+//     against 11.5 K split), fp32 up to 48 (4 x 4: 10.4 against 10.7);
+//   the K split beyond (fp16 24 x 4: 15.1 against 19.3 in halves; 48 x 2:
+//     14.0 against 24.0; fp32 12 x 8: 19.4 against 21.1 whole heads).
+// The K split takes 2, 4 or 8 waves per tile (default: 2 fp32 / 4 fp16 for
+// one row, 8 / 4 for chained rows).  A bv option other than 0, 64 (the
+// halves, which need counters) or 128, or the whole-K row layout, is
+// refused; rows_layout is ignored for one row.
 inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, int64_t units, const kda_launch_opts* opts,
-                               Shape* out) {
+                               bool pairs, Shape* out) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX || asked == KDA_ROWS_WAVE_K) return false;
-  if (opts != nullptr && opts->bv != 0 && opts->bv != kHeadV) return false;
+  const int32_t bv = opts != nullptr ? opts->bv : 0;
+  if (bv != 0 && bv != kHeadV && bv != kMatrixBV) return false;
   if (n_rows > 1) {
     const bool shaped = opts != nullptr && (opts->waves_per_tile != 0 || opts->block_rows != 0);
-    const bool matrix = asked == KDA_ROWS_MATRIX ||
-                        (asked == KDA_ROWS_DEFAULT && !shaped && (dt == KDA_F16 || units <= 48));
-    if (matrix) {
-      *out = Shape{kHeadV, kMatrixConvWaves, KDA_ROWS_MATRIX};
-      return opts == nullptr || opts->waves_per_tile == 0 || opts->waves_per_tile == kMatrixConvWaves;
+    int32_t bvm = 0;  // columns per workgroup of the matrix-core form; 0: the K split
+    if (asked == KDA_ROWS_MATRIX || (asked == KDA_ROWS_DEFAULT && bv == kMatrixBV)) {
+      bvm = bv != 0 ? bv : (pairs ? kMatrixBV : kHeadV);
+    } else if (asked == KDA_ROWS_DEFAULT && !shaped) {
+      const bool f16 = dt == KDA_F16;
+      const bool halves = pairs && bv == 0 && (f16 ? units <= 96 : units <= 48 || (units <= 96 && n_rows >= 6));
+      const bool head = n_rows >= 3 && units <= (f16 ? 192 : 48);
+      bvm = halves ? kMatrixBV : head ? kHeadV : 0;
+    }
+    if (bvm != 0) {
+      const int32_t nw_default = bvm == kMatrixBV ? kMatrixWaves : kMatrixConvWaves;
+      const int32_t nw = opts == nullptr || opts->waves_per_tile == 0 ? nw_default : opts->waves_per_tile;
+      *out = Shape{bvm, nw, KDA_ROWS_MATRIX};
+      if (bvm == kMatrixBV) return pairs && nw == kMatrixWaves;
+      return nw == kMatrixConvWaves || nw == kMatrixConvWaves4;
     }
   }
+  if (bv == kMatrixBV) return false;  // halves: the matrix-core form only
   Shape s{kHeadV, n_rows == 1 ? (dt == KDA_F32 ? 2 : 4) : (dt == KDA_F32 ? 8 : 4), KDA_ROWS_K_SPLIT};
   if (opts != nullptr && opts->waves_per_tile != 0) s.nw = opts->waves_per_tile;
   *out = s;

@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "kda_decode.h"
+#include "kda_launch.h"
 
 static int g_failures = 0;
 
@@ -252,6 +253,75 @@ static void describe_launch() {
               }
 }
 
+// The fused convolution's launch shapes (resolve_conv_shape): the defaults
+// the layout header states, and every option combination consistent.
+static bool conv_shape(kda_dtype dt, int32_t n_req, int32_t n_rows, bool pairs, kda::Shape* s,
+                       int32_t nw = 0, int32_t bv = 0, int32_t blk = 0, int32_t layout = 0) {
+  const kda_launch_opts o{nw, bv, blk, layout};
+  return kda::resolve_conv_shape(dt, n_rows, static_cast<int64_t>(n_req) * 12, &o, pairs, s);
+}
+
+static bool is_shape(const kda::Shape& s, int32_t bv, int32_t nw, int32_t layout) {
+  return s.bv == bv && s.nw == nw && s.layout == layout;
+}
+
+static void conv_shapes() {
+  using kda::Shape;
+  Shape s{};
+  const int32_t M = KDA_ROWS_MATRIX, KS = KDA_ROWS_K_SPLIT;
+  // halves with counters: fp16 up to 96 units, fp32 up to 48 (96 from 6 rows)
+  CHECK(conv_shape(KDA_F16, 8, 8, true, &s) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F16, 8, 2, true, &s) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F16, 9, 8, true, &s) && is_shape(s, 128, 16, M));   // whole heads
+  CHECK(conv_shape(KDA_F16, 17, 8, true, &s) && is_shape(s, 128, 4, KS));  // K split
+  CHECK(conv_shape(KDA_F16, 9, 2, true, &s) && is_shape(s, 128, 4, KS));
+  CHECK(conv_shape(KDA_F32, 4, 2, true, &s) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F32, 8, 8, true, &s) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F32, 8, 4, true, &s) && is_shape(s, 128, 8, KS));
+  CHECK(conv_shape(KDA_F32, 9, 8, true, &s) && is_shape(s, 128, 8, KS));
+  // without counters: whole heads from 3 rows, up to 192 (fp16) or 48 units
+  CHECK(conv_shape(KDA_F16, 8, 8, false, &s) && is_shape(s, 128, 16, M));
+  CHECK(conv_shape(KDA_F16, 16, 3, false, &s) && is_shape(s, 128, 16, M));
+  CHECK(conv_shape(KDA_F16, 8, 2, false, &s) && is_shape(s, 128, 4, KS));
+  CHECK(conv_shape(KDA_F16, 17, 8, false, &s) && is_shape(s, 128, 4, KS));
+  CHECK(conv_shape(KDA_F32, 4, 4, false, &s) && is_shape(s, 128, 16, M));
+  CHECK(conv_shape(KDA_F32, 8, 8, false, &s) && is_shape(s, 128, 8, KS));
+  // one row: the single-row kernel over whole heads whatever the counters
+  CHECK(conv_shape(KDA_F16, 8, 1, true, &s) && is_shape(s, 128, 4, KS));
+  CHECK(conv_shape(KDA_F32, 8, 1, true, &s) && is_shape(s, 128, 2, KS));
+  // explicit choices
+  CHECK(conv_shape(KDA_F16, 64, 8, true, &s, 0, 0, 0, M) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F16, 64, 8, false, &s, 0, 0, 0, M) && is_shape(s, 128, 16, M));
+  CHECK(conv_shape(KDA_F16, 64, 8, true, &s, 0, 64) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F16, 8, 8, true, &s, 0, 128) && is_shape(s, 128, 16, M));
+  CHECK(conv_shape(KDA_F16, 8, 8, true, &s, 8, 128, 0, M) && is_shape(s, 128, 8, M));
+  CHECK(conv_shape(KDA_F16, 8, 8, true, &s, 8) && is_shape(s, 128, 8, KS));
+  CHECK(!conv_shape(KDA_F16, 8, 8, false, &s, 0, 64));      // halves need counters
+  CHECK(!conv_shape(KDA_F16, 8, 8, true, &s, 16, 64, 0, M));
+  CHECK(!conv_shape(KDA_F16, 8, 8, true, &s, 0, 64, 0, KS));
+  CHECK(!conv_shape(KDA_F16, 8, 1, true, &s, 0, 64));
+  // every combination: an admitted shape is one a kernel exists for
+  const kda_dtype dts[2] = {KDA_F32, KDA_F16};
+  for (kda_dtype dt : dts)
+    for (int32_t n_rows = 1; n_rows <= 8; ++n_rows)
+      for (int32_t n_req : {1, 2, 4, 8, 9, 16, 17, 64})
+        for (bool pairs : {false, true})
+          for (int32_t nw : {0, 2, 4, 8, 16, 3})
+            for (int32_t bv : {0, 64, 128, 32})
+              for (int32_t blk : {0, 1})
+                for (int32_t layout : {0, 1, 2, 3, 4}) {
+                  if (!conv_shape(dt, n_req, n_rows, pairs, &s, nw, bv, blk, layout)) continue;
+                  if (s.layout == M) {
+                    CHECK(n_rows > 1);
+                    CHECK(is_shape(s, 64, 8, M) || is_shape(s, 128, 16, M) || is_shape(s, 128, 8, M));
+                    if (s.bv == 64) CHECK(pairs);
+                  } else {
+                    CHECK(s.layout == KS && s.bv == 128 && (s.nw == 2 || s.nw == 4 || s.nw == 8));
+                  }
+                  CHECK(nw != 3 && bv != 32 && layout != 2 && layout != 4);
+                }
+}
+
 static void tile_map_and_strings() {
   for (int32_t n = 1; n <= 3100; n += (n < 64 ? 1 : 37)) {
     std::vector<char> hit(static_cast<size_t>(n), 0);
@@ -280,6 +350,7 @@ int main() {
   prefill_validate();
   state_at_and_sizes();
   describe_launch();
+  conv_shapes();
   tile_map_and_strings();
   if (g_failures != 0) {
     std::fprintf(stderr, "%d check(s) failed\n", g_failures);

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for expected in ["kda_decode_step", "kda_decode_step_ex", "kda_validate", "kda_state_at",
-                     "kda_state_copy", "kda_decode_step_conv", "kda_prefill",
+                     "kda_state_copy", "kda_decode_step_conv", "kda_decode_step_conv_ws", "kda_prefill",
                      "kda_prefill_validate",
                      "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
                      "kda_copy_probe", "kda_bw_probe", "kda_tile_probe", "kda_rows_probe",
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 7
+    assert B.kda_abi_version() == 8
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -289,9 +289,20 @@ def test_describe_launch():
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (128, 4, "kda_rows_kernel")
     d = B.kda_describe_launch(8, 8, 12, "f32")
     assert (d["bv"], d["waves_per_tile"], d["kernel"]) == (64, 8, "kda_decode_tile")
-    # small fp32 chained-row launches take the matrix-core block form
+    # small fp32 chained-row launches of 6 rows or more take the matrix-core
+    # block form
     assert B.kda_describe_launch(4, 8, 12, "f32")["kernel"] == "kda_rows_mfma8_kernel"
+    assert B.kda_describe_launch(4, 6, 12, "f32")["kernel"] == "kda_rows_mfma8_kernel"
+    assert B.kda_describe_launch(4, 5, 12, "f32")["kernel"] == "kda_decode_tile"
+    assert B.kda_describe_launch(1, 2, 12, "f32")["kernel"] == "kda_decode_tile"
     assert B.kda_describe_launch(5, 8, 12, "f32")["kernel"] == "kda_decode_tile"
+    # fp16: the block form from 3 rows up to 240 requests x heads; 2 rows
+    # whole-K up to 48, then the K split, as are larger launches
+    assert B.kda_describe_launch(20, 8, 12, "f16")["kernel"] == "kda_rows_mfma8_kernel"
+    assert B.kda_describe_launch(20, 3, 12, "f16")["kernel"] == "kda_rows_mfma8_kernel"
+    assert B.kda_describe_launch(21, 8, 12, "f16")["rows_layout"] == B.KDA_ROWS_K_SPLIT
+    assert B.kda_describe_launch(4, 2, 12, "f16")["rows_layout"] == B.KDA_ROWS_WAVE_K
+    assert B.kda_describe_launch(5, 2, 12, "f16")["rows_layout"] == B.KDA_ROWS_K_SPLIT
     assert B.kda_describe_launch(4, 8, 12, "f32", waves_per_tile=8)["kernel"] == "kda_decode_tile"
     d = B.kda_describe_launch(8, 8, 12, "f16", waves_per_tile=8, rows_layout=B.KDA_ROWS_K_SPLIT)
     assert (d["waves_per_tile"], d["threads"], d["kernel"]) == (8, 512, "kda_decode_tile")
@@ -362,12 +373,45 @@ def test_conv_step_refusals():
     assert conv_step(P, Cv, opts=B.kda_launch_opts(0, 64)) == B.KDA_ERR_ARG   # whole heads only
     assert conv_step(P, Cv, opts=B.kda_launch_opts(1, 0)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 0, 0, B.KDA_ROWS_WAVE_K)) == B.KDA_ERR_ARG
-    # the matrix-core block form with the convolution: whole heads over 8 waves only
-    assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(4, 0, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    # the matrix-core block form with the convolution: whole heads over 16
+    # waves (or 8: two halves of 4) only
+    for nw in (2, 4, 32):
+        assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(nw, 0, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    # 16 waves ask for the matrix-core form: refused in the K-split layout
+    assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(16, 0, 0, B.KDA_ROWS_K_SPLIT)) == B.KDA_ERR_ARG
+    assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(16, 0)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 64, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 0, 0, 4)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, scale=float("nan")) == B.KDA_ERR_ARG
     assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE + 8), 16, 12)) == B.KDA_ERR_ALIGN
+
+
+def conv_step_ws(P, conv, counts, n_counts, n_req=4, n_rows=2, opts=None, ptrs=None):
+    p = [FAKE] * 7 if ptrs is None else ptrs     # slot_ids, x, conv_w, g, b, out, init
+    f = [ctypes.c_void_p(v) for v in p]
+    return B.library().kda_decode_step_conv_ws(
+        ctypes.byref(P), ctypes.byref(conv), f[0], f[6], f[1], f[2], f[3], f[4], f[5], n_req, n_rows,
+        P.dtype, 0.0883883, None if counts is None else ctypes.c_void_p(counts), n_counts,
+        None if opts is None else ctypes.byref(opts), None)
+
+
+def test_conv_step_with_pair_counters_refusals():
+    P = pool(n_slots=16)
+    Cv = B.kda_conv_pool(ctypes.c_void_p(FAKE), 16, 12)
+    M = B.KDA_ROWS_MATRIX
+    assert conv_step_ws(P, Cv, None, 48) == B.KDA_ERR_NULL          # no counters but a count
+    assert conv_step_ws(P, Cv, FAKE, -1) == B.KDA_ERR_ARG
+    assert conv_step_ws(P, Cv, FAKE, 4 * 12 - 1) == B.KDA_ERR_ARG   # one per (request, head)
+    assert conv_step_ws(P, Cv, FAKE + 2, 48) == B.KDA_ERR_ALIGN
+    assert conv_step_ws(P, Cv, FAKE, 48, n_req=0) == B.KDA_OK
+    # the halves: the matrix-core form over 8 waves, chained rows only
+    assert conv_step_ws(P, Cv, FAKE, 48, opts=B.kda_launch_opts(16, 64, 0, M)) == B.KDA_ERR_ARG
+    assert conv_step_ws(P, Cv, FAKE, 48, opts=B.kda_launch_opts(4, 64, 0, M)) == B.KDA_ERR_ARG
+    assert conv_step_ws(P, Cv, FAKE, 48, n_rows=1, opts=B.kda_launch_opts(0, 64)) == B.KDA_ERR_ARG
+    assert conv_step_ws(P, Cv, FAKE, 48, opts=B.kda_launch_opts(0, 64, 0, B.KDA_ROWS_K_SPLIT)) == B.KDA_ERR_ARG
+    assert conv_step_ws(P, Cv, FAKE, 48, opts=B.kda_launch_opts(0, 32, 0, M)) == B.KDA_ERR_ARG
+    # without counters the halves are refused
+    assert conv_step_ws(P, Cv, None, 0, opts=B.kda_launch_opts(0, 64, 0, M)) == B.KDA_ERR_ARG
 
 
 def prefill(P, n_seq=4, n_tokens=100, ptrs=None, chunk=0, scale=0.0883883, dtype=None):

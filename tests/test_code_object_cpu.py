@@ -153,7 +153,9 @@ def by_prefix(table, prefix):
     return hits[0]
 
 
-MFMA8 = ("_ZN3kda21kda_rows_mfma8_kernelIfEE", "_ZN3kda21kda_rows_mfma8_kernelIDF16_EE")
+MFMA8 = ("_ZN3kda21kda_rows_mfma8_kernelIfLi0EEE", "_ZN3kda21kda_rows_mfma8_kernelIDF16_Li0EEE")
+MFMA8_CONV = ("_ZN3kda21kda_rows_mfma8_kernelIfLi1EEE", "_ZN3kda21kda_rows_mfma8_kernelIDF16_Li1EEE")
+MFMA8_CONV_HALF = ("_ZN3kda21kda_rows_mfma8_kernelIfLi2EEE", "_ZN3kda21kda_rows_mfma8_kernelIDF16_Li2EEE")
 MFMA4 = ("_ZN3kda20kda_rows_mfma_kernelIfLb0EEE", "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb0EEE")
 MFMA4_CONV = ("_ZN3kda20kda_rows_mfma_kernelIfLb1EEE", "_ZN3kda20kda_rows_mfma_kernelIDF16_Lb1EEE")
 
@@ -162,12 +164,28 @@ def test_matrix_block_form_lds_matches_the_launch_description(kernels):
     # the host's LDS figure for the matrix-core block form is the kernel's
     # static LDS, for both pool dtypes and both wave counts
     import kda_gated_delta_decode_amd.binding as B
-    for names, nw in ((MFMA8, 8), (MFMA4, 4)):
+    for names, nw in ((MFMA8 + MFMA8_CONV_HALF, 8), (MFMA4, 4)):
         want = B.kda_describe_launch(8, 8, 12, "f16", rows_layout=B.KDA_ROWS_MATRIX,
                                      waves_per_tile=nw)["lds_bytes"]
         for prefix in names:
             name = by_prefix(kernels, prefix)
             assert kernels[name][".group_segment_fixed_size"] == want, name
+    # with the fused convolution, 8 waves per half: the same arrays with v,
+    # the partial sums and their totals for two 64-column halves
+    t, k, bh = 8, 128, 64
+    conv16 = 4 * (3 * t * (k + 4) + t * 2 * bh + 2 * (8 + 1) * 16 * bh + 2 * t * t + t)
+    for prefix in MFMA8_CONV:
+        name = by_prefix(kernels, prefix)
+        assert kernels[name][".group_segment_fixed_size"] == conv16 <= 160 * 1024, name
+
+
+def test_fused_sixteen_wave_form_fits_four_waves_per_simd(kernels):
+    # 1024 threads: 4 waves per SIMD, at most 128 registers each
+    for prefix in MFMA8_CONV:
+        name = by_prefix(kernels, prefix)
+        k = kernels[name]
+        assert k[".max_flat_workgroup_size"] == 1024, name
+        assert k[".vgpr_count"] + k.get(".agpr_count", 0) <= 128, (name, k[".vgpr_count"])
 
 
 def test_matrix_block_form_runs_its_column_sums_on_the_matrix_cores(disassembly):
@@ -176,9 +194,23 @@ def test_matrix_block_form_runs_its_column_sums_on_the_matrix_cores(disassembly)
     for prefix in MFMA4 + MFMA4_CONV:
         name = by_prefix(disassembly, prefix)
         assert disassembly[name].count("v_mfma_f32_16x16x4_f32") == 32, name
-    for prefix in MFMA8:
+    for prefix in MFMA8 + MFMA8_CONV + MFMA8_CONV_HALF:
         name = by_prefix(disassembly, prefix)
         assert disassembly[name].count("v_mfma_f32_16x16x4_f32") == 16, name
+
+
+def test_convolution_in_halves_hands_the_history_over_with_one_counter(disassembly):
+    # one relaxed atomic add per workgroup on the pair counter, with no L2
+    # write-back or invalidate around it (an agent-scope release would write
+    # back the whole L2 of the XCD); the other forms have no atomics
+    for prefix in MFMA8_CONV_HALF:
+        ops = disassembly[by_prefix(disassembly, prefix)]
+        atomics = [op for op in ops if "atomic" in op]
+        assert atomics == ["global_atomic_add"], (prefix, atomics)
+        assert "buffer_wbl2" not in ops and "buffer_inv" not in ops, prefix
+    for prefix in MFMA8 + MFMA8_CONV + MFMA4 + MFMA4_CONV:
+        ops = disassembly[by_prefix(disassembly, prefix)]
+        assert not any("atomic" in op for op in ops), prefix
 
 
 def kernel_descriptor(code_object, name):
