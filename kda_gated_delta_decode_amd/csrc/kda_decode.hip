@@ -2196,14 +2196,18 @@ extern "C" int kda_decode_step(const kda_pool* pool, const int32_t* slot_ids, co
                             state_dtype, scale, nullptr, stream);
 }
 
-// The fused step; pair_counts (nullable, n_pairs entries) lets chained rows
-// in the matrix-core form take 64-column halves.
-static int decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv, const int32_t* slot_ids,
-                            const int32_t* init_slot_ids, const float* x, const float* conv_w,
-                            const float* g, const float* b, float* out, int32_t n_req,
-                            int32_t n_rows_per_slot, kda_dtype state_dtype, float scale,
-                            uint32_t* pair_counts, int64_t n_pairs, const kda_launch_opts* opts,
-                            void* stream) {
+// The fused step's host half: every check, the shape and the kernel
+// arguments, before any HIP call.  pairs says whether pair counters will be
+// there (n_pairs of them; pair_counts may still be NULL when the caller
+// supplies them later), which lets chained rows in the matrix-core form take
+// 64-column halves.  *blocks = 0: nothing to launch.
+static int conv_prepare(const kda_pool* pool, const kda_conv_pool* conv, const int32_t* slot_ids,
+                        const int32_t* init_slot_ids, const float* x, const float* conv_w,
+                        const float* g, const float* b, float* out, int32_t n_req,
+                        int32_t n_rows_per_slot, kda_dtype state_dtype, float scale, bool pairs,
+                        uint32_t* pair_counts, int64_t n_pairs, const kda_launch_opts* opts, Args* a,
+                        Shape* shape, int32_t* blocks) {
+  *blocks = 0;
   const int rc = check_common(pool, n_req, n_rows_per_slot, state_dtype);
   if (rc != KDA_OK) return rc;
   if (conv == nullptr || conv->base == nullptr) return KDA_ERR_NULL;
@@ -2214,37 +2218,39 @@ static int decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv, con
     return KDA_ERR_NULL;
   if (!std::isfinite(scale)) return KDA_ERR_ARG;
   const int64_t units = static_cast<int64_t>(n_req) * pool->H;
-  if (pair_counts != nullptr && n_pairs < units) return KDA_ERR_ARG;
-  Shape shape;
-  if (!resolve_conv_shape(state_dtype, n_rows_per_slot, units, opts, pair_counts != nullptr, &shape))
-    return KDA_ERR_ARG;
+  if (pairs && n_pairs < units) return KDA_ERR_ARG;
+  if (!resolve_conv_shape(state_dtype, n_rows_per_slot, units, opts, pairs, shape)) return KDA_ERR_ARG;
   if (!aligned16(pool->base) || !aligned16(conv->base) || !aligned16(x) || !aligned16(conv_w) ||
       !aligned16(g) || !aligned16(out) || !aligned4(b) || !aligned4(slot_ids) ||
       !aligned4(init_slot_ids) || !aligned4(pair_counts))
     return KDA_ERR_ALIGN;
-  const int64_t tiles = units * (kHeadV / shape.bv);
+  const int64_t tiles = units * (kHeadV / shape->bv);
   if (tiles > INT32_MAX) return KDA_ERR_ARG;
-  Args a;
-  a.pool = pool->base;
-  a.slot_ids = slot_ids;
-  a.init_slot_ids = init_slot_ids;
-  a.q = nullptr;
-  a.k = nullptr;
-  a.v = nullptr;
-  a.g = g;
-  a.b = b;
-  a.out = out;
-  a.x = x;
-  a.conv_w = conv_w;
-  a.conv_pool = static_cast<uint16_t*>(conv->base);
-  a.pair_counts = pair_counts;
-  a.n_slots = pool->n_slots;
-  a.H = pool->H;
-  a.n_rows = n_rows_per_slot;
-  a.n_vt = kHeadV / shape.bv;
-  a.rows_block = opts != nullptr && opts->block_rows != 0 ? 1 : 0;
-  a.scale = scale;
-  const int32_t blocks = static_cast<int32_t>(tiles);
+  a->pool = pool->base;
+  a->slot_ids = slot_ids;
+  a->init_slot_ids = init_slot_ids;
+  a->q = nullptr;
+  a->k = nullptr;
+  a->v = nullptr;
+  a->g = g;
+  a->b = b;
+  a->out = out;
+  a->x = x;
+  a->conv_w = conv_w;
+  a->conv_pool = static_cast<uint16_t*>(conv->base);
+  a->pair_counts = pair_counts;
+  a->n_slots = pool->n_slots;
+  a->H = pool->H;
+  a->n_rows = n_rows_per_slot;
+  a->n_vt = kHeadV / shape->bv;
+  a->rows_block = opts != nullptr && opts->block_rows != 0 ? 1 : 0;
+  a->scale = scale;
+  *blocks = static_cast<int32_t>(tiles);
+  return KDA_OK;
+}
+
+static int conv_launch(const Args& a, const Shape& shape, int32_t blocks, kda_dtype state_dtype,
+                       void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (shape.layout == KDA_ROWS_MATRIX) {
@@ -2273,6 +2279,24 @@ static int decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv, con
                                  : dispatch_conv<_Float16>(a, shape.nw, blocks, s);
   }
   return err == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// The fused step; pair_counts (nullable, n_pairs entries) lets chained rows
+// in the matrix-core form take 64-column halves.
+static int decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv, const int32_t* slot_ids,
+                            const int32_t* init_slot_ids, const float* x, const float* conv_w,
+                            const float* g, const float* b, float* out, int32_t n_req,
+                            int32_t n_rows_per_slot, kda_dtype state_dtype, float scale,
+                            uint32_t* pair_counts, int64_t n_pairs, const kda_launch_opts* opts,
+                            void* stream) {
+  Args a;
+  Shape shape;
+  int32_t blocks = 0;
+  const int rc = conv_prepare(pool, conv, slot_ids, init_slot_ids, x, conv_w, g, b, out, n_req,
+                              n_rows_per_slot, state_dtype, scale, pair_counts != nullptr, pair_counts,
+                              n_pairs, opts, &a, &shape, &blocks);
+  if (rc != KDA_OK || blocks == 0) return rc;
+  return conv_launch(a, shape, blocks, state_dtype, stream);
 }
 
 extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
