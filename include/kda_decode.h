@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 8  /* 8: kda_decode_step_conv_ws; 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
+#define KDA_ABI_VERSION 9  /* 9: kda_decode_step_conv_noalloc; 8: kda_decode_step_conv_ws; 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -322,6 +322,31 @@ int kda_decode_step_conv_ws(const kda_pool* pool, const kda_conv_pool* conv,
                             float scale, uint32_t* pair_counts,
                             int32_t n_pair_counts, const kda_launch_opts* opts,
                             void* stream);
+
+/*
+ * kda_decode_step_conv_noalloc -- kda_decode_step_conv_ws for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the pair counters live in a
+ * static device array of KDA_NOALLOC_MAX_PAIRS entries inside the library,
+ * one per GPU it runs on, held until the process ends.  The call allocates
+ * nothing; its first call on a device looks the array's address up on that
+ * device (the stream's device, or the current one for the null stream).
+ * Arguments and launch shapes as kda_decode_step_conv_ws with counters given.
+ * Every call on a GPU shares that GPU's counters: calls that overlap on one
+ * GPU race (results of chained rows in halves are then undefined), calls in
+ * sequence do not.  Nothing needs clearing between calls: the counters stay
+ * even.
+ * Errors: as kda_decode_step_conv_ws, plus KDA_ERR_ARG when n_req * H exceeds
+ * KDA_NOALLOC_MAX_PAIRS (checked before any device work), KDA_ERR_LAUNCH if
+ * the counters' address cannot be found on the device.
+ */
+#define KDA_NOALLOC_MAX_PAIRS 4096
+int kda_decode_step_conv_noalloc(const kda_pool* pool, const kda_conv_pool* conv,
+                                 const int32_t* slot_ids, const int32_t* init_slot_ids,
+                                 const float* x, const float* conv_w, const float* g,
+                                 const float* b, float* out, int32_t n_req,
+                                 int32_t n_rows_per_slot, kda_dtype state_dtype,
+                                 float scale, const kda_launch_opts* opts, void* stream);
 
 /*
  * kda_validate -- host-side check of a launch's arguments and slot tables

@@ -43,6 +43,7 @@ KDA_ROWS_DEFAULT = 0
 KDA_ROWS_K_SPLIT = 1
 KDA_ROWS_WAVE_K = 2
 KDA_ROWS_MATRIX = 3
+KDA_NOALLOC_MAX_PAIRS = 4096  # pair counters of kda_decode_step_conv_noalloc
 KDA_PROBE_COPY = 0
 KDA_PROBE_READ = 1
 KDA_PROBE_WRITE = 2
@@ -95,6 +96,9 @@ SIGNATURES = {
                                                _P, _P, _P, _P, _P, _P, _P, _I32, _I32, ctypes.c_int,
                                                ctypes.c_float, _P, _I32, ctypes.POINTER(kda_launch_opts),
                                                _P]),
+    "kda_decode_step_conv_noalloc": (ctypes.c_int, [ctypes.POINTER(kda_pool), ctypes.POINTER(kda_conv_pool),
+                                                    _P, _P, _P, _P, _P, _P, _P, _I32, _I32, ctypes.c_int,
+                                                    ctypes.c_float, ctypes.POINTER(kda_launch_opts), _P]),
     "kda_validate": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, ctypes.c_int]),
     "kda_state_copy": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, ctypes.c_int, _P]),
     "kda_prefill": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -304,6 +308,24 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
     taps [3, H, 128, 4]; pair_counts: None, or device int32 counters from
     conv_pair_counts (kda_decode_step_conv_ws: chained rows then take
     64-column halves); the other arguments as kda_decode_step."""
+    _conv_step(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot, state_dtype, scale, stream,
+               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, pair_counts, False)
+
+
+def kda_decode_step_conv_noalloc(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot: int = 1,
+                                 state_dtype=None, scale: float | None = None, stream=None,
+                                 init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0,
+                                 block_rows: bool = False, rows_layout: int = 0) -> None:
+    """kda_decode_step_conv with the library's own pair counters (see
+    kda_decode_step_conv_noalloc in include/kda_decode.h): allocates nothing;
+    at most KDA_NOALLOC_MAX_PAIRS requests x heads; calls that overlap on one
+    GPU race."""
+    _conv_step(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot, state_dtype, scale, stream,
+               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, None, True)
+
+
+def _conv_step(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot, state_dtype, scale, stream,
+               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, pair_counts, noalloc):
     import torch
     P = make_pool(pool)
     Cv = make_conv_pool(conv)
@@ -326,7 +348,10 @@ def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_
             _dev(conv_w, "conv_w", torch.float32, dv), _dev(g, "g", torch.float32, dv),
             _dev(b, "b", torch.float32, dv), _dev(out, "out", torch.float32, dv), n_req,
             n_rows_per_slot, sd, float(scale))
-    if pair_counts is None:
+    if noalloc:
+        rc = library().kda_decode_step_conv_noalloc(*args, ctypes.byref(opts), _stream_ptr(stream))
+        _check(rc, "kda_decode_step_conv_noalloc")
+    elif pair_counts is None:
         rc = library().kda_decode_step_conv(*args, ctypes.byref(opts), _stream_ptr(stream))
         _check(rc, "kda_decode_step_conv")
     else:

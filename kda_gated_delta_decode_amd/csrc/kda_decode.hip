@@ -32,8 +32,10 @@
 // for a second reduction.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_decode.h"
@@ -2299,6 +2301,48 @@ static int decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv, con
   return conv_launch(a, shape, blocks, state_dtype, stream);
 }
 
+// Pair counters of kda_decode_step_conv_noalloc, for callers that cannot
+// allocate: one per (request, head) of a launch, at most
+// KDA_NOALLOC_MAX_PAIRS; every GPU the library runs on holds its own copy
+// until the process ends.  They need only be even between calls, never
+// cleared: zero when the code object loads, and every call adds 0 or 2 to
+// each (calls that overlap on one GPU still add 2 each, though they race on
+// which half writes the handed-over history).
+static __device__ __align__(256) uint32_t scratch[KDA_NOALLOC_MAX_PAIRS];
+
+// The device address of `scratch` on each device, looked up once per device
+// with that device current.  In host code the array's name stands for a
+// host-side shadow, not a device address: kernels get only these pointers.
+constexpr int kMaxDevices = 64;
+static std::atomic<uint32_t*> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mutex;
+
+static hipError_t scratch_on_device(int dev, uint32_t** out) {
+  uint32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = -1;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (cur != dev) {
+        const hipError_t back = hipSetDevice(cur);
+        if (e == hipSuccess) e = back;
+      }
+      if (e != hipSuccess) return e;
+      if (addr == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<uint32_t*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 extern "C" int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
                                     const int32_t* slot_ids, const int32_t* init_slot_ids,
                                     const float* x, const float* conv_w, const float* g,
@@ -2320,6 +2364,31 @@ extern "C" int kda_decode_step_conv_ws(const kda_pool* pool, const kda_conv_pool
   if (n_pair_counts < 0) return KDA_ERR_ARG;
   return decode_step_conv(pool, conv, slot_ids, init_slot_ids, x, conv_w, g, b, out, n_req,
                           n_rows_per_slot, state_dtype, scale, pair_counts, n_pair_counts, opts, stream);
+}
+
+extern "C" int kda_decode_step_conv_noalloc(const kda_pool* pool, const kda_conv_pool* conv,
+                                            const int32_t* slot_ids, const int32_t* init_slot_ids,
+                                            const float* x, const float* conv_w, const float* g,
+                                            const float* b, float* out, int32_t n_req,
+                                            int32_t n_rows_per_slot, kda_dtype state_dtype,
+                                            float scale, const kda_launch_opts* opts, void* stream) {
+  Args a;
+  Shape shape;
+  int32_t blocks = 0;
+  const int rc = conv_prepare(pool, conv, slot_ids, init_slot_ids, x, conv_w, g, b, out, n_req,
+                              n_rows_per_slot, state_dtype, scale, true, nullptr, KDA_NOALLOC_MAX_PAIRS,
+                              opts, &a, &shape, &blocks);
+  if (rc != KDA_OK || blocks == 0) return rc;
+  // the device the launch runs on: the stream's (the current one for the
+  // null stream)
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return KDA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_LAUNCH;
+  uint32_t* counters = nullptr;
+  if (scratch_on_device(dev, &counters) != hipSuccess) return KDA_ERR_LAUNCH;
+  a.pair_counts = counters;
+  return conv_launch(a, shape, blocks, state_dtype, stream);
 }
 
 extern "C" int kda_state_copy(const kda_pool* pool, const int32_t* src_slot_ids,

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for expected in ["kda_decode_step", "kda_decode_step_ex", "kda_validate", "kda_state_at",
-                     "kda_state_copy", "kda_decode_step_conv", "kda_decode_step_conv_ws", "kda_prefill",
+                     "kda_state_copy", "kda_decode_step_conv", "kda_decode_step_conv_ws",
+                     "kda_decode_step_conv_noalloc", "kda_prefill",
                      "kda_prefill_validate",
                      "kda_pool_bytes", "kda_tile_bv", "kda_describe_launch", "kda_tile_of_block",
                      "kda_copy_probe", "kda_bw_probe", "kda_tile_probe", "kda_rows_probe",
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 8
+    assert B.kda_abi_version() == 9
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -414,6 +415,30 @@ def test_conv_step_with_pair_counters_refusals():
     assert conv_step_ws(P, Cv, None, 0, opts=B.kda_launch_opts(0, 64, 0, M)) == B.KDA_ERR_ARG
 
 
+def conv_step_noalloc(P, conv, n_req=4, n_rows=2, opts=None, ptrs=None):
+    p = [FAKE] * 7 if ptrs is None else ptrs     # slot_ids, x, conv_w, g, b, out, init
+    f = [ctypes.c_void_p(v) for v in p]
+    return B.library().kda_decode_step_conv_noalloc(
+        ctypes.byref(P), None if conv is None else ctypes.byref(conv), f[0], f[6], f[1], f[2], f[3], f[4],
+        f[5], n_req, n_rows, P.dtype, 0.0883883, None if opts is None else ctypes.byref(opts), None)
+
+
+def test_conv_step_noalloc_refusals():
+    # every refusal comes before any device work (no GPU here)
+    P = pool(n_slots=1024, H=12)
+    Cv = B.kda_conv_pool(ctypes.c_void_p(FAKE), 1024, 12)
+    assert B.KDA_NOALLOC_MAX_PAIRS == 4096
+    assert conv_step_noalloc(P, Cv, n_req=4096 // 12 + 1) == B.KDA_ERR_ARG   # beyond the counters
+    assert conv_step_noalloc(P, Cv, n_req=0) == B.KDA_OK
+    assert conv_step_noalloc(P, None) == B.KDA_ERR_NULL
+    assert conv_step_noalloc(pool(n_slots=1024, H=12, dtype=B.KDA_BF16), Cv) == B.KDA_ERR_DTYPE_REFUSED
+    assert conv_step_noalloc(P, Cv, n_rows=9) == B.KDA_ERR_ROWS
+    assert conv_step_noalloc(P, Cv, opts=B.kda_launch_opts(16, 64, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    ptrs = [FAKE] * 7
+    ptrs[1] = FAKE + 4                                                          # x misaligned
+    assert conv_step_noalloc(P, Cv, ptrs=ptrs) == B.KDA_ERR_ALIGN
+
+
 def prefill(P, n_seq=4, n_tokens=100, ptrs=None, chunk=0, scale=0.0883883, dtype=None):
     p = [FAKE] * 9 if ptrs is None else ptrs     # init, cu, q, k, v, g, b, out, dst
     f = [ctypes.c_void_p(v) for v in p]
@@ -519,3 +544,12 @@ def test_probe_refusals_before_any_hip_call():
     assert rp(pool(), ids=None) == B.KDA_ERR_NULL
     assert rp(pool(), init=ctypes.c_void_p(FAKE + 2)) == B.KDA_ERR_ALIGN
     assert rp(pool(), n_req=0) == B.KDA_OK                              # no launch
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defines = dict(re.findall(r"^#define (KDA_\w+) (-?\d+)", text, flags=re.M))
+    assert "KDA_NOALLOC_MAX_PAIRS" in defines
+    for name, val in defines.items():
+        if hasattr(B, name):
+            assert getattr(B, name) == int(val), name
