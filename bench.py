@@ -537,14 +537,20 @@ def bandwidth_probes(B, torch, step_state_bytes):
         torch.cuda.empty_cache()
     # the 8 x 8 chained rows' own traffic (kda_rows_probe: the matrix-core
     # block form's grid, layout, slot id loads, state loads and snapshot
-    # stores, no arithmetic) on the spec-verify workload's rotated pools
+    # stores, no arithmetic) on the spec-verify workload's rotated pools; then
+    # the same traffic in the tiles the block form was weighed against: 32 and
+    # 128 columns over 8 waves, and the fused convolution's whole heads (128
+    # columns, two halves of 8 waves)
     inp = kda_inputs.spec_verify_f16(0)
     w = Workload(inp, ROT, torch)
-    tc = time_launches(lambda i: B.kda_rows_probe(w.pools[i % len(w.pools)], w.ids, inp.n_rows), 100, 10,
-                       torch)
-    us = tc["launch_ms_mean"] * 1e3
-    res["rows_pattern_f16_8x8"] = {"bytes_moved": inp.state_bytes(), "pools_rotated": len(w.pools),
-                                   "us": round(us, 2), "GB/s": round(inp.state_bytes() / us / 1e3, 1)}
+    for name, cols, nw in (("rows_pattern_f16_8x8", 0, 0), ("rows_pattern_f16_8x8_cols32", 32, 8),
+                           ("rows_pattern_f16_8x8_cols128", 128, 8),
+                           ("rows_pattern_f16_8x8_cols128_waves16", 128, 16)):
+        tc = time_launches(lambda i, cols=cols, nw=nw: B.kda_rows_probe(
+            w.pools[i % len(w.pools)], w.ids, inp.n_rows, tile_cols=cols, waves=nw), 100, 10, torch)
+        us = tc["launch_ms_mean"] * 1e3
+        res[name] = {"bytes_moved": inp.state_bytes(), "pools_rotated": len(w.pools), "tile_cols": cols or 64,
+                     "waves": nw or 8, "us": round(us, 2), "GB/s": round(inp.state_bytes() / us / 1e3, 1)}
     del w
     torch.cuda.empty_cache()
     return res

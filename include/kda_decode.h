@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 9  /* 9: kda_decode_step_conv_noalloc; 8: kda_decode_step_conv_ws; 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
+#define KDA_ABI_VERSION 10  /* 10: kda_rows_probe tile shapes; 9: kda_decode_step_conv_noalloc; 8: kda_decode_step_conv_ws; 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -554,11 +554,18 @@ int kda_tile_probe(const kda_pool* pool, const int32_t* slot_ids, int32_t n_req,
  *  slot_ids       device int32 [n_req * n_rows]; init_slot_ids: NULL or
  *                 device int32 [n_req].  A request with an id out of range
  *                 is skipped.
+ *  tile_cols, waves  the workgroup's value columns and waves: 0, 0 or 64, 8
+ *                 (the block form), 32 or 128 over 8 waves (narrower and
+ *                 wider tiles, each lane still 4 columns of a row), or 128
+ *                 over 16 waves (two 64-column halves of 8, the fused
+ *                 convolution's whole-head form).
  * Errors: as kda_tile_probe; KDA_ERR_ROWS (n_rows outside [1,
- * KDA_MAX_ROWS]); KDA_ERR_ARG (n_req < 0 or n_req * n_rows > n_slots).
+ * KDA_MAX_ROWS]); KDA_ERR_ARG (n_req < 0, n_req * n_rows > n_slots, or
+ * another tile shape).
  */
 int kda_rows_probe(const kda_pool* pool, const int32_t* slot_ids, const int32_t* init_slot_ids,
-                   int32_t n_req, int32_t n_rows, kda_dtype state_dtype, void* stream);
+                   int32_t n_req, int32_t n_rows, int32_t tile_cols, int32_t waves,
+                   kda_dtype state_dtype, void* stream);
 
 /* Message for a kda_status code (static string, never NULL). */
 const char* kda_strerror(int code);

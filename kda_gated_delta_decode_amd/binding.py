@@ -116,7 +116,8 @@ SIGNATURES = {
     "kda_copy_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     "kda_bw_probe": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _I32, _I32, _I32, _P]),
     "kda_tile_probe": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _I32, ctypes.c_int, _P]),
-    "kda_rows_probe": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, ctypes.c_int, _P]),
+    "kda_rows_probe": (ctypes.c_int, [ctypes.POINTER(kda_pool), _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int,
+                                      _P]),
     "kda_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_abi_version": (ctypes.c_int, []),
 }
@@ -507,10 +508,13 @@ def kda_tile_probe(pool, slot_ids, stream=None) -> None:
                                     n_req, P.dtype, _stream_ptr(stream)), "kda_tile_probe")
 
 
-def kda_rows_probe(pool, slot_ids, n_rows: int, init_slot_ids=None, stream=None) -> None:
+def kda_rows_probe(pool, slot_ids, n_rows: int, init_slot_ids=None, tile_cols: int = 0, waves: int = 0,
+                   stream=None) -> None:
     """The chained-row launch's state traffic (matrix-core block form)
     without its arithmetic (see kda_rows_probe in include/kda_decode.h): each
-    request's initial state is written unchanged to its rows' slots."""
+    request's initial state is written unchanged to its rows' slots.
+    tile_cols, waves: 0, 0 for the block form's 64 columns over 8 waves, or
+    32 / 128 over 8, or 128 over 16."""
     import torch
     P = make_pool(pool)
     n_rows = int(n_rows)
@@ -522,7 +526,7 @@ def kda_rows_probe(pool, slot_ids, n_rows: int, init_slot_ids=None, stream=None)
     dv = pool.device
     _check(library().kda_rows_probe(ctypes.byref(P), _dev(slot_ids, "slot_ids", torch.int32, dv),
                                     _dev(init_slot_ids, "init_slot_ids", torch.int32, dv), n_req, n_rows,
-                                    P.dtype, _stream_ptr(stream)), "kda_rows_probe")
+                                    int(tile_cols), int(waves), P.dtype, _stream_ptr(stream)), "kda_rows_probe")
 
 
 def kda_strerror(code: int) -> str:

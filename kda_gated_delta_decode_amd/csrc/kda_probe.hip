@@ -129,27 +129,36 @@ __global__ __launch_bounds__(kWave * NW) void kda_tile_probe_kernel(T* pool, con
 
 // The chained rows' memory traffic in the matrix-core block form with the
 // arithmetic taken out: the grid, block-to-tile map, slot id loads, lane
-// layout (wave w: key rows 16 w + 4 gq + j, j < 4; lane li: columns 4 li ..
-// 4 li + 3 of the 64-column half) and nontemporal loads and stores of
-// kda_rows_mfma8_kernel.  The initial state is written unchanged to every
-// row's slot (xor with a zero the compiler cannot see, so the stores stay).
-template <typename T>
-__global__ __launch_bounds__(kWave * kMatrixWaves) void kda_rows_probe_kernel(
+// layout and nontemporal loads and stores of kda_rows_mfma8_kernel, with the
+// initial state written unchanged to every row's slot (xor with a zero the
+// compiler cannot see, so the stores stay).  A workgroup takes NH column
+// groups of BH columns, 8 waves each; wave w holds key rows 16 w .. 16 w +
+// 15, lane (gq, li) 4-column piece li of the group's row 16 w + J gq + j
+// (j < J), so one instruction covers 64 / (BH / 4) whole rows of the group.
+// BH = 64, NH = 1 is the block form's layout and BH = 64, NH = 2 its
+// whole-head form with the convolution fused; BH = 32 and BH = 128 are the
+// narrower and wider tiles it was weighed against.
+template <typename T, int BH, int NH>
+__global__ __launch_bounds__(kWave * kMatrixWaves * NH) void kda_rows_probe_kernel(
     T* pool, const int32_t* slot_ids, const int32_t* init_ids, int32_t n_slots, int32_t H,
     int32_t n_rows, uint32_t zero) {
-  constexpr int NW = kMatrixWaves;
-  constexpr int BH = kMatrixBV;
-  constexpr int RPW = kHeadK / NW;
-  constexpr int J = RPW / 4;
+  constexpr int NW = kMatrixWaves;  // waves per column group
+  constexpr int LPR = BH / 4;       // lanes per row
+  constexpr int RPI = kWave / LPR;  // rows per instruction
+  constexpr int RPW = kHeadK / NW;  // key rows per wave
+  constexpr int J = RPW / RPI;      // rows per lane
+  constexpr int BW = BH * NH;       // columns per workgroup
   constexpr int TMAX = KDA_MAX_ROWS;
+  static_assert(J >= 1 && RPW % RPI == 0 && kHeadV % BW == 0, "a tile the lanes cover exactly");
   // 4 columns of one row: 8 bytes (fp16) or 16 (fp32)
   using piece = uint32_t __attribute__((ext_vector_type(sizeof(T))));
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int gq = lane / 16, li = lane % 16;
+  const int wave = (threadIdx.x / kWave) % NW;
+  const int grp = threadIdx.x / (kWave * NW);
+  const int gq = lane / LPR, li = lane % LPR;
   const int tile = tile_of_block(blockIdx.x, gridDim.x);
-  const int vt = tile % (kHeadV / BH);
-  const int rh = tile / (kHeadV / BH);
+  const int vt = tile % (kHeadV / BW);
+  const int rh = tile / (kHeadV / BW);
   const int h = rh % H;
   const int r = rh / H;
   const int32_t* ids = slot_ids + static_cast<int64_t>(r) * n_rows;
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(kWave * kMatrixWaves) void kda_rows_probe_kernel(
   const int64_t head_elems = static_cast<int64_t>(kHeadK) * kHeadV;
   const int64_t slot_elems = static_cast<int64_t>(H) * head_elems;
   const int row0 = RPW * wave + J * gq;
-  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + vt * BH + 4 * li;
+  const int64_t lane_off = h * head_elems + static_cast<int64_t>(row0) * kHeadV + vt * BW + grp * BH + 4 * li;
   piece raw[J];
   {
     const piece* src = reinterpret_cast<const piece*>(pool + static_cast<int64_t>(init) * slot_elems + lane_off);
@@ -178,6 +187,29 @@ __global__ __launch_bounds__(kWave * kMatrixWaves) void kda_rows_probe_kernel(
 #pragma unroll
     for (int j = 0; j < J; ++j) __builtin_nontemporal_store(raw[j] ^ zero, dst + j * (kHeadV / 4));
   }
+}
+
+template <typename T, int BH, int NH>
+hipError_t launch_rows_probe(const kda_pool* pool, const int32_t* slot_ids, const int32_t* init_slot_ids,
+                             int32_t n_req, int32_t n_rows, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(n_req) * pool->H * (kHeadV / (BH * NH));
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((kda_rows_probe_kernel<T, BH, NH>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(kWave * kMatrixWaves * NH), 0, s, static_cast<T*>(pool->base), slot_ids, init_slot_ids,
+                     pool->n_slots, pool->H, n_rows, 0u);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_rows_probe(int32_t cols, int32_t waves, const kda_pool* pool, const int32_t* slot_ids,
+                               const int32_t* init_slot_ids, int32_t n_req, int32_t n_rows, hipStream_t s) {
+  if (waves == kMatrixWaves && cols == 32)
+    return launch_rows_probe<T, 32, 1>(pool, slot_ids, init_slot_ids, n_req, n_rows, s);
+  if (waves == kMatrixWaves && cols == 64)
+    return launch_rows_probe<T, 64, 1>(pool, slot_ids, init_slot_ids, n_req, n_rows, s);
+  if (waves == kMatrixWaves && cols == 128)
+    return launch_rows_probe<T, 128, 1>(pool, slot_ids, init_slot_ids, n_req, n_rows, s);
+  return launch_rows_probe<T, 64, 2>(pool, slot_ids, init_slot_ids, n_req, n_rows, s);  // 128 columns, 16 waves
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -241,28 +273,28 @@ extern "C" int kda_tile_probe(const kda_pool* pool, const int32_t* slot_ids, int
 }
 
 extern "C" int kda_rows_probe(const kda_pool* pool, const int32_t* slot_ids, const int32_t* init_slot_ids,
-                              int32_t n_req, int32_t n_rows, kda_dtype state_dtype, void* stream) {
+                              int32_t n_req, int32_t n_rows, int32_t tile_cols, int32_t waves,
+                              kda_dtype state_dtype, void* stream) {
   if (pool == nullptr || pool->base == nullptr) return KDA_ERR_NULL;
   if (state_dtype != KDA_F32 && state_dtype != KDA_F16) return KDA_ERR_DTYPE_REFUSED;
   if (pool->dtype != state_dtype) return KDA_ERR_DTYPE_MISMATCH;
   if (pool->K != kHeadK || pool->V != kHeadV || pool->H < 1 || pool->n_slots < 1) return KDA_ERR_SHAPE;
   if (n_rows < 1 || n_rows > KDA_MAX_ROWS) return KDA_ERR_ROWS;
   if (n_req < 0 || static_cast<int64_t>(n_req) * n_rows > pool->n_slots) return KDA_ERR_ARG;
+  const int32_t cols = tile_cols == 0 ? kMatrixBV : tile_cols;
+  const int32_t nw = waves == 0 ? kMatrixWaves : waves;
+  const bool shape_ok = (nw == kMatrixWaves && (cols == 32 || cols == 64 || cols == 128)) ||
+                        (nw == 2 * kMatrixWaves && cols == 128);
+  if (!shape_ok) return KDA_ERR_ARG;
   if (n_req == 0) return KDA_OK;
   if (slot_ids == nullptr) return KDA_ERR_NULL;
   if (!aligned16(pool->base) || (reinterpret_cast<uintptr_t>(slot_ids) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(init_slot_ids) & 3u) != 0)
     return KDA_ERR_ALIGN;
-  const int64_t blocks = static_cast<int64_t>(n_req) * pool->H * (kHeadV / kMatrixBV);
-  if (blocks > INT32_MAX) return KDA_ERR_ARG;
+  if (static_cast<int64_t>(n_req) * pool->H * (kHeadV / cols) > INT32_MAX) return KDA_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<uint32_t>(blocks)), block(kWave * kMatrixWaves);
-  if (state_dtype == KDA_F32)
-    hipLaunchKernelGGL((kda_rows_probe_kernel<float>), grid, block, 0, s, static_cast<float*>(pool->base),
-                       slot_ids, init_slot_ids, pool->n_slots, pool->H, n_rows, 0u);
-  else
-    hipLaunchKernelGGL((kda_rows_probe_kernel<_Float16>), grid, block, 0, s,
-                       static_cast<_Float16*>(pool->base), slot_ids, init_slot_ids, pool->n_slots, pool->H,
-                       n_rows, 0u);
-  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  const hipError_t e = state_dtype == KDA_F32
+                           ? dispatch_rows_probe<float>(cols, nw, pool, slot_ids, init_slot_ids, n_req, n_rows, s)
+                           : dispatch_rows_probe<_Float16>(cols, nw, pool, slot_ids, init_slot_ids, n_req, n_rows, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 9
+    assert B.kda_abi_version() == 10
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -530,8 +530,8 @@ def test_probe_refusals_before_any_hip_call():
     assert lib.kda_tile_probe(ctypes.byref(pool(n_slots=3)), ids, 4, B.KDA_F32, None) == B.KDA_ERR_ARG
     assert lib.kda_tile_probe(ctypes.byref(pool()), None, 4, B.KDA_F32, None) == B.KDA_ERR_NULL
     assert lib.kda_tile_probe(ctypes.byref(pool()), ids, 0, B.KDA_F32, None) == B.KDA_OK
-    rp = lambda P, n_req=4, n_rows=8, ids=ids, init=None, dt=None: lib.kda_rows_probe(
-        ctypes.byref(P) if P is not None else None, ids, init, n_req, n_rows,
+    rp = lambda P, n_req=4, n_rows=8, ids=ids, init=None, dt=None, cols=0, nw=0: lib.kda_rows_probe(
+        ctypes.byref(P) if P is not None else None, ids, init, n_req, n_rows, cols, nw,
         P.dtype if dt is None else dt, None)
     assert rp(None, dt=B.KDA_F16) == B.KDA_ERR_NULL
     assert rp(pool(dtype=B.KDA_BF16)) == B.KDA_ERR_DTYPE_REFUSED
@@ -544,6 +544,11 @@ def test_probe_refusals_before_any_hip_call():
     assert rp(pool(), ids=None) == B.KDA_ERR_NULL
     assert rp(pool(), init=ctypes.c_void_p(FAKE + 2)) == B.KDA_ERR_ALIGN
     assert rp(pool(), n_req=0) == B.KDA_OK                              # no launch
+    # tile shapes: 32, 64 or 128 columns over 8 waves, 128 over 16
+    for cols, nw in ((32, 8), (64, 8), (128, 8), (128, 16), (0, 0), (64, 0), (0, 8)):
+        assert rp(pool(), n_req=0, cols=cols, nw=nw) == B.KDA_OK
+    for cols, nw in ((16, 8), (64, 16), (32, 16), (128, 4), (96, 8), (64, 4)):
+        assert rp(pool(), n_req=0, cols=cols, nw=nw) == B.KDA_ERR_ARG, (cols, nw)
 
 
 def test_binding_constants_match_the_header():

@@ -2,7 +2,7 @@
 kda_bw_probe (streaming copy, read-only and write-only streams),
 kda_tile_probe (the single-row decode's state traffic, written back in
 place) and kda_rows_probe (the chained rows' traffic: the initial state
-written to every row's slot).  Each must move exactly the bytes it claims
+written to every row's slot, in every tile shape it takes).  Each must move exactly the bytes it claims
 and touch nothing else, or the ceilings the bench reports would be wrong."""
 import numpy as np
 import pytest
@@ -70,7 +70,8 @@ def test_tile_probe_writes_every_tile_back_unchanged(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("with_init", [False, True])
-def test_rows_probe_copies_the_initial_state_to_every_row(dtype, with_init):
+@pytest.mark.parametrize("cols,waves", [(0, 0), (32, 8), (128, 8), (128, 16)])
+def test_rows_probe_copies_the_initial_state_to_every_row(dtype, with_init, cols, waves):
     tdt = torch.float32 if dtype == "f32" else torch.float16
     itype = torch.int32 if dtype == "f32" else torch.int16
     n_slots, H, n_rows = 40, 3, 8
@@ -83,7 +84,8 @@ def test_rows_probe_copies_the_initial_state_to_every_row(dtype, with_init):
     init = perm[3 * n_rows:3 * n_rows + 3].copy() if with_init else ids[:, 0].copy()
     ids[2, 5] = n_slots                       # request 2 has a bad id: skipped
     B.kda_rows_probe(pool, torch.from_numpy(ids.reshape(-1)).cuda(), n_rows,
-                     init_slot_ids=torch.from_numpy(init).cuda() if with_init else None)
+                     init_slot_ids=torch.from_numpy(init).cuda() if with_init else None,
+                     tile_cols=cols, waves=waves)
     torch.cuda.synchronize()
     got, ref = pool.view(itype).cpu(), before.view(itype).cpu()
     expect = ref.clone()
