@@ -51,6 +51,11 @@ def flags() -> list[str]:
         # kernels whose leading arguments are plain pointers and integers get
         # the first 14 argument dwords preloaded into scalar registers
         "-mllvm", "-amdgpu-kernarg-preload-count=14",
+        # atomics stay as written: the optimizer's rewrite of a one-lane
+        # atomic reads its result back at once, which would stall the
+        # chained-row kernel's pair-counter increment (issued early, its
+        # result used only at the end)
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-Wall",
         "-I", INCLUDE,
         "-I", CSRC,

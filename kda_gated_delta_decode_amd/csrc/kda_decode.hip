@@ -1614,12 +1614,12 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
 //                 distinct): both halves read q and k there, so neither may
 //                 overwrite them before the other has read them.  That row's
 //                 wave in each half counts its half's arrival on the
-//                 request's and head's counter once the workgroup's history
-//                 reads are done (after the first barrier); the half that
-//                 arrives second (odd count before its increment) writes that
-//                 row's q and k history.  No wave waits on another
-//                 workgroup.  Each launch adds 2 per such counter, so counters
-//                 that start even stay even.
+//                 request's and head's counter after the third barrier (the
+//                 workgroup's history reads were done before the first);
+//                 the half that arrives second (odd count before its
+//                 increment) writes that row's q and k history at the end.  No wave
+//                 waits on another workgroup.  Each launch adds 2 per such
+//                 counter, so counters that start even stay even.
 // ---------------------------------------------------------------------------
 constexpr int kMfma8Waves = 8;  // waves per 64-column half
 constexpr int kRowsPlain = 0, kRowsConvHead = 1, kRowsConvHalf = 2;
@@ -1811,8 +1811,10 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
   __syncthreads();
 
   // -- history snapshots: row t keeps win[t + 1 .. t + 3] ----------------------
-  // After the barrier every wave of the workgroup has read the history it
-  // needs (its values are in LDS).
+  // After the first barrier every wave of the workgroup has read the history
+  // it needs (its values are in LDS); the stores are issued after the third
+  // barrier: a store issued earlier would hold up the waits for the state
+  // loads before the products (loads and stores share one counter).
   int32_t st = sid[0];  // this wave's row's slot
 #pragma unroll
   for (int u = 1; u < TMAX; ++u)
@@ -1823,37 +1825,9 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
     for (int m = 0; m < 3; ++m)
       *reinterpret_cast<uint32_t*>(hrow + m * conv_c + ch) = bf16_pack(e[m + 1][0], e[m + 1][1]);
   };
-  // the initial slot's row, if any (kRowsConvHalf): its q and k wait for the
-  // pair counter.  What must be ordered is the first half's history reads
-  // before the second half's history stores, and nothing else: every read
-  // of this workgroup has returned its data before the barrier above (the
-  // values are in LDS), the increment is issued after it and performed at
-  // device scope, and the second half's stores depend on the value its
-  // increment returns.  The increment is therefore relaxed: an agent-scope
-  // release would also write back this XCD's L2 (buffer_wbl2), which
-  // measured 14.2 against 10.9 us for 8 requests x 8 rows and 58 against
-  // 24 us for 48 x 2 (fp16), for stores no other workgroup reads.
+  // the initial slot's row, if any (kRowsConvHalf): its q and k history
+  // waits for the pair counter
   const bool handover = !HEAD && CONV && live && st == init_slot;
-  uint32_t arrival = 0;
-  if constexpr (CONV && !HEAD) {
-    if (handover && lane == 0)
-      arrival = __hip_atomic_fetch_add(a.pair_counts + static_cast<int64_t>(r) * H + h, 1u,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if constexpr (CONV) {
-    if (live) {
-#pragma unroll
-      for (int m = 0; m < 3; ++m) hrow[m * conv_c + chv] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(ev[m + 1]));
-      if constexpr (HEAD) {
-        store_pair(chq, eq);  // q (half 0) or k (half 1)
-      } else if (!handover) {
-        if (vt == 0)
-          store_pair(chq, eq);
-        else
-          store_pair(chk, ek);
-      }
-    }
-  }
 
   // couplings (waves 0..3: two columns of the n x n matrices each), then
   // this wave's share of w0 and p0 on the matrix cores
@@ -1911,6 +1885,29 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
     reinterpret_cast<f2*>(&s_tot[half][eg][ec])[pc] = (t01 + t23) + (t45 + t67);
   }
   __syncthreads();
+
+  // The in-place row's pair-counter increment (its result is used at the
+  // end, where the second half writes the q and k history).
+  uint32_t arrival = 0;
+  if constexpr (CONV && !HEAD) {
+    if (handover && lane == 0)
+      arrival = __hip_atomic_fetch_add(a.pair_counts + static_cast<int64_t>(r) * H + h, 1u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if constexpr (CONV) {
+    if (live) {
+#pragma unroll
+      for (int m = 0; m < 3; ++m) hrow[m * conv_c + chv] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(ev[m + 1]));
+      if constexpr (HEAD) {
+        store_pair(chq, eq);  // q (half 0) or k (half 1)
+      } else if (!handover) {
+        if (vt == 0)
+          store_pair(chq, eq);
+        else
+          store_pair(chk, ek);
+      }
+    }
+  }
 
   // Every wave solves the 64 columns of its half (lane l: column l) and
   // writes row t's snapshot as soon as Delta_t is known; wave t of the half
@@ -1971,8 +1968,18 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
     }
   }
 
-  // the half that arrived second writes the initial slot's row's q and k
-  // history (the other half has read them by now)
+  // The initial slot's row: the half that arrives second on the pair
+  // counter writes its q and k history.  What must be ordered is the first
+  // half's history reads before the second half's history stores, and
+  // nothing else: every read of this workgroup returned its data before the
+  // first barrier (the values are in LDS), the increment is issued after the
+  // third (and read back only here, so that no wave waits for it earlier)
+  // and performed at device scope, and the second half's stores depend on
+  // the value its increment returns.  The increment is therefore relaxed:
+  // an agent-scope release would also write back this XCD's L2
+  // (buffer_wbl2), which measured 14.2 against 10.9 us for 8 requests x 8
+  // rows and 58 against 24 us for 48 x 2 (fp16), for stores no other
+  // workgroup reads.
   if constexpr (CONV && !HEAD) {
     if (handover && (__builtin_amdgcn_readlane(static_cast<int>(arrival), 0) & 1) != 0) {
       store_pair(chq, eq);

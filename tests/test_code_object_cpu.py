@@ -208,9 +208,34 @@ def test_convolution_in_halves_hands_the_history_over_with_one_counter(disassemb
         atomics = [op for op in ops if "atomic" in op]
         assert atomics == ["global_atomic_add"], (prefix, atomics)
         assert "buffer_wbl2" not in ops and "buffer_inv" not in ops, prefix
+        # issued after the last barrier
+        i = ops.index("global_atomic_add")
+        barriers = [j for j, op in enumerate(ops) if op == "s_barrier"]
+        assert barriers and barriers[-1] < i, prefix
     for prefix in MFMA8 + MFMA8_CONV + MFMA4 + MFMA4_CONV:
         ops = disassembly[by_prefix(disassembly, prefix)]
         assert not any("atomic" in op for op in ops), prefix
+
+
+def test_pair_counter_result_is_waited_for_only_after_the_snapshots(code_object):
+    # no vector-memory wait between the increment and the snapshot stores:
+    # the wave that issues it goes on with its solve (the atomic optimizer's
+    # rewrite would read the result back at once)
+    for prefix in MFMA8_CONV_HALF:
+        lines = None
+        for path in code_object["paths"]:
+            text = subprocess.run([tool("llvm-objdump"), "-d", "--no-show-raw-insn", path],
+                                  check=True, capture_output=True, text=True).stdout
+            blocks = re.split(r"^[0-9a-f]+ <", text, flags=re.M)
+            hit = [b for b in blocks if b.startswith(prefix)]
+            if hit:
+                lines = [l.split("//")[0].strip() for l in hit[0].splitlines()[1:] if l.strip()]
+                break
+        assert lines is not None, prefix
+        i = next(j for j, l in enumerate(lines) if l.startswith("global_atomic_add"))
+        w = next(j for j in range(i, len(lines)) if lines[j].startswith("s_waitcnt") and "vmcnt" in lines[j])
+        stores = sum(1 for l in lines[i:w] if l.startswith("global_store_dwordx"))
+        assert stores >= 8 * 4, (prefix, stores)   # 8 rows x 4 snapshot pieces per lane
 
 
 def kernel_descriptor(code_object, name):
