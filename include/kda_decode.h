@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 10  /* 10: kda_rows_probe tile shapes; 9: kda_decode_step_conv_noalloc; 8: kda_decode_step_conv_ws; 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
+#define KDA_ABI_VERSION 11  /* 11: kda_launch_opts.g_raw; 10: kda_rows_probe tile shapes; 9: kda_decode_step_conv_noalloc; 8: kda_decode_step_conv_ws; 7: kda_rows_probe; 6: kda_bw_probe and kda_tile_probe; 5: KDA_ROWS_MATRIX */
 
 /* Head dimensions this build supports (the Kimi-K3 KDA layer shape). */
 #define KDA_HEAD_K 128
@@ -196,6 +196,7 @@ typedef struct kda_launch_opts {
   int32_t bv;
   int32_t block_rows;
   int32_t rows_layout;
+  int32_t g_raw;  /* fused convolution entries only (0 elsewhere): see kda_decode_step_conv */
 } kda_launch_opts;
 
 /*
@@ -271,6 +272,12 @@ typedef struct kda_conv_pool {
  * (fp16) or 48 (fp32) requests x heads unless waves_per_tile or block_rows
  * is set; otherwise the K-split kernel with 2, 4 or 8 waves.
  * KDA_ROWS_WAVE_K is refused; rows_layout is ignored for one row.
+ * opts->g_raw: 0 (default), g is the log-decay as in kda_decode_step; 1, g
+ * holds the raw gate x of each key channel and the step takes the
+ * log-decay g = -softplus(x) = -log(1 + e^x), computing the decay as
+ * 1 / (1 + e^x), so the gate is fused into the front end beside the
+ * convolution.  Other values are refused, as is g_raw != 0 on the entries
+ * without the convolution.
  * Errors: as kda_decode_step_ex, plus KDA_ERR_NULL for a missing conv pool,
  * x or conv_w, KDA_ERR_SHAPE if the pools' n_slots or H differ.
  */

@@ -60,7 +60,8 @@ class kda_conv_pool(ctypes.Structure):
 
 class kda_launch_opts(ctypes.Structure):
     _fields_ = [("waves_per_tile", ctypes.c_int32), ("bv", ctypes.c_int32),
-                ("block_rows", ctypes.c_int32), ("rows_layout", ctypes.c_int32)]
+                ("block_rows", ctypes.c_int32), ("rows_layout", ctypes.c_int32),
+                ("g_raw", ctypes.c_int32)]
 
 
 class kda_prefill_opts(ctypes.Structure):
@@ -302,31 +303,33 @@ def conv_pair_counts(n_req: int, H: int, device):
 def kda_decode_step_conv(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot: int = 1,
                          state_dtype=None, scale: float | None = None, stream=None,
                          init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0,
-                         block_rows: bool = False, rows_layout: int = 0, pair_counts=None) -> None:
+                         block_rows: bool = False, rows_layout: int = 0, pair_counts=None,
+                         g_raw: bool = False) -> None:
     """Decode step with the short causal convolution fused in front (see
     kda_decode_step_conv in include/kda_decode.h).  conv: bfloat16 history
     [n_slots, 3, 3, H, 128]; x: fp32 raw q|k|v [R, 3, H, 128]; conv_w: fp32
     taps [3, H, 128, 4]; pair_counts: None, or device int32 counters from
     conv_pair_counts (kda_decode_step_conv_ws: chained rows then take
-    64-column halves); the other arguments as kda_decode_step."""
+    64-column halves); g_raw: g holds the raw gate x, the log-decay being
+    -softplus(x); the other arguments as kda_decode_step."""
     _conv_step(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot, state_dtype, scale, stream,
-               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, pair_counts, False)
+               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, pair_counts, False, g_raw)
 
 
 def kda_decode_step_conv_noalloc(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot: int = 1,
                                  state_dtype=None, scale: float | None = None, stream=None,
                                  init_slot_ids=None, waves_per_tile: int = 0, bv: int = 0,
-                                 block_rows: bool = False, rows_layout: int = 0) -> None:
+                                 block_rows: bool = False, rows_layout: int = 0, g_raw: bool = False) -> None:
     """kda_decode_step_conv with the library's own pair counters (see
     kda_decode_step_conv_noalloc in include/kda_decode.h): allocates nothing;
     at most KDA_NOALLOC_MAX_PAIRS requests x heads; calls that overlap on one
     GPU race."""
     _conv_step(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot, state_dtype, scale, stream,
-               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, None, True)
+               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, None, True, g_raw)
 
 
 def _conv_step(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot, state_dtype, scale, stream,
-               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, pair_counts, noalloc):
+               init_slot_ids, waves_per_tile, bv, block_rows, rows_layout, pair_counts, noalloc, g_raw):
     import torch
     P = make_pool(pool)
     Cv = make_conv_pool(conv)
@@ -343,7 +346,8 @@ def _conv_step(pool, conv, slot_ids, x, conv_w, g, b, out, n_rows_per_slot, stat
                        (g, "g", R * H * KDA_HEAD_K), (out, "out", R * H * KDA_HEAD_K),
                        (b, "b", R * H), (init_slot_ids, "init_slot_ids", n_req)):
         _need_numel(t, name, n)
-    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout))
+    opts = kda_launch_opts(int(waves_per_tile), int(bv), int(bool(block_rows)), int(rows_layout),
+                           int(bool(g_raw)))
     args = (ctypes.byref(P), ctypes.byref(Cv), _dev(slot_ids, "slot_ids", torch.int32, dv),
             _dev(init_slot_ids, "init_slot_ids", torch.int32, dv), _dev(x, "x", torch.float32, dv),
             _dev(conv_w, "conv_w", torch.float32, dv), _dev(g, "g", torch.float32, dv),

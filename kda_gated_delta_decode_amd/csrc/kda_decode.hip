@@ -66,6 +66,7 @@ struct Args {
   int32_t n_vt;  // V-tiles per head
   int32_t rows_block;  // chained rows: 1 = as one block, 0 = row after row (default)
   float scale;
+  int32_t g_raw;  // fused front end: g holds the raw gate x, g = -softplus(x)
 };
 
 // Every decode kernel takes the values its first memory requests depend on
@@ -174,6 +175,14 @@ __device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
   return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
 }
 __device__ __forceinline__ float silu(float s) { return s / (1.0f + expf(-s)); }
+
+// The decay a = e^g of a log-decay input g, or, when the input is the raw
+// gate x of g = -softplus(x) = -log(1 + e^x), the same decay 1 / (1 + e^x)
+// without forming the logarithm.
+__device__ __forceinline__ float decay_of(float x, bool raw) {
+  const float e = expf(x);
+  return raw ? 1.0f / (1.0f + e) : e;
+}
 
 // ---------------------------------------------------------------------------
 // Reads of N consecutive fp32 values from LDS (N a multiple of 2; 16-byte
@@ -416,7 +425,8 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
       const float rk = 1.0f / sqrtf(sk + 1e-6f);
       *reinterpret_cast<f2*>(&s_qn[t][2 * lane]) = f2{q2[j][0] * rq, q2[j][1] * rq};
       *reinterpret_cast<f2*>(&s_kn[t][2 * lane]) = f2{k2[j][0] * rk, k2[j][1] * rk};
-      *reinterpret_cast<f2*>(&s_a[t][2 * lane]) = f2{expf(g2[j][0]), expf(g2[j][1])};
+      const bool raw = CONV && a.g_raw != 0;
+      *reinterpret_cast<f2*>(&s_a[t][2 * lane]) = f2{decay_of(g2[j][0], raw), decay_of(g2[j][1], raw)};
       if (lane < BV / 4) *reinterpret_cast<f4*>(&s_v[t][4 * lane]) = v4[j];
       if (lane == 0) {
         s_beta[t] = 1.0f / (1.0f + expf(-braw[j]));
@@ -1423,7 +1433,7 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
     float gam = 1.0f;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
-      const float at = t < n_rows ? expf(graw[t]) : 0.0f;
+      const float at = t < n_rows ? decay_of(graw[t], CONV && a.g_raw != 0) : 0.0f;
       gam *= at;
       s_a[t][chan] = at;
       s_gam[t][chan] = gam;
@@ -1782,8 +1792,9 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
       const float rk = live ? 1.0f / sqrtf(sk + 1e-6f) : 0.0f;
       *reinterpret_cast<f2*>(&s_qn[rw][2 * lane]) = f2{q2[0] * rq, q2[1] * rq};
       *reinterpret_cast<f2*>(&s_kn[rw][2 * lane]) = f2{k2[0] * rk, k2[1] * rk};
+      const bool raw = CONV && a.g_raw != 0;
       *reinterpret_cast<f2*>(&s_a[rw][2 * lane]) =
-          live ? f2{expf(g2[0]), expf(g2[1])} : f2{0.0f, 0.0f};
+          live ? f2{decay_of(g2[0], raw), decay_of(g2[1], raw)} : f2{0.0f, 0.0f};
       s_v[rw][lane] = live ? v1 : 0.0f;
       if (lane == 0) s_beta[rw] = live ? 1.0f / (1.0f + expf(-braw)) : 0.0f;
     } else {
@@ -1796,8 +1807,9 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
       if (half == 0) {
         if (lane == 0) s_beta[rw] = live ? 1.0f / (1.0f + expf(-braw)) : 0.0f;
       } else {
+        const bool raw = a.g_raw != 0;
         *reinterpret_cast<f2*>(&s_a[rw][2 * lane]) =
-            live ? f2{expf(g2[0]), expf(g2[1])} : f2{0.0f, 0.0f};
+            live ? f2{decay_of(g2[0], raw), decay_of(g2[1], raw)} : f2{0.0f, 0.0f};
       }
     }
   }
@@ -2188,6 +2200,7 @@ extern "C" int kda_decode_step_ex(const kda_pool* pool, const int32_t* slot_ids,
   a.n_rows = n_rows_per_slot;
   a.n_vt = kHeadV / shape.bv;
   a.rows_block = opts != nullptr && opts->block_rows != 0 ? 1 : 0;
+  a.g_raw = 0;
   a.scale = scale;
   const int32_t blocks = n_req * pool->H * a.n_vt;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -2253,6 +2266,7 @@ static int conv_prepare(const kda_pool* pool, const kda_conv_pool* conv, const i
   a->n_rows = n_rows_per_slot;
   a->n_vt = kHeadV / shape->bv;
   a->rows_block = opts != nullptr && opts->block_rows != 0 ? 1 : 0;
+  a->g_raw = opts != nullptr ? opts->g_raw : 0;
   a->scale = scale;
   *blocks = static_cast<int32_t>(tiles);
   return KDA_OK;

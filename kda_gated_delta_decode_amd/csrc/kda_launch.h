@@ -149,6 +149,7 @@ inline bool resolve_shape(kda_dtype dt, int32_t n_rows, int64_t units, const kda
                           Shape* out) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX) return false;
+  if (opts != nullptr && opts->g_raw != 0) return false;  // the fused front end's option
   const int32_t layout = n_rows > 1 ? chained_rows_layout(dt, n_rows, opts, units) : KDA_ROWS_K_SPLIT;
   if (layout == KDA_ROWS_MATRIX) {
     // 64 columns over 8 waves (default) or 4; a block form whatever
@@ -233,6 +234,7 @@ inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, int64_t units, cons
                                bool pairs, Shape* out) {
   const int32_t asked = opts != nullptr ? opts->rows_layout : KDA_ROWS_DEFAULT;
   if (asked < KDA_ROWS_DEFAULT || asked > KDA_ROWS_MATRIX || asked == KDA_ROWS_WAVE_K) return false;
+  if (opts != nullptr && opts->g_raw != 0 && opts->g_raw != 1) return false;
   const int32_t bv = opts != nullptr ? opts->bv : 0;
   if (bv != 0 && bv != kHeadV && bv != kMatrixBV) return false;
   if (n_rows > 1) {

@@ -272,6 +272,17 @@ def conv_f32(conv_pool: np.ndarray, slot_ids, x, w, n_rows: int = 1,
     return y
 
 
+def log_decay_from_gate(x) -> np.ndarray:
+    """The log-decay g = -softplus(x) = -log(1 + e^x) of a raw gate x, taken
+    in fp64 in the overflow-free form -(max(x, 0) + log1p(e^-|x|)) and
+    rounded to fp32: the decay input of the step (a = e^g) when the fused
+    front end is given the raw gate (ROCm/ATOM PR #2894, the two-node trial:
+    the gate is computed inside the fused front end).  Test infrastructure,
+    like the rest of this module."""
+    x = np.asarray(x, dtype=np.float64)
+    return (-(np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x))))).astype(np.float32)
+
+
 def set_mutation(which: int) -> None:
     """Plant one mistake in the oracle (tests of the pins only); 0 clears."""
     lib().kdao_set_mutation(int(which))

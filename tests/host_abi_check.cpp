@@ -235,7 +235,7 @@ static void describe_launch() {
           for (int32_t bv : {0, 32, 64, 128, 48})
             for (int32_t blk : {0, 1})
               for (int32_t layout : {0, 1, 2, 3, 4, -1}) {
-                kda_launch_opts o{nw, bv, blk, layout};
+                kda_launch_opts o{nw, bv, blk, layout, 0};
                 std::memset(&d, 0, sizeof d);
                 const int rc = kda_describe_launch(n_req, n_rows, 12, dt, &o, &d);
                 CHECK(rc == KDA_OK || rc == KDA_ERR_ARG);
@@ -257,7 +257,7 @@ static void describe_launch() {
 // the layout header states, and every option combination consistent.
 static bool conv_shape(kda_dtype dt, int32_t n_req, int32_t n_rows, bool pairs, kda::Shape* s,
                        int32_t nw = 0, int32_t bv = 0, int32_t blk = 0, int32_t layout = 0) {
-  const kda_launch_opts o{nw, bv, blk, layout};
+  const kda_launch_opts o{nw, bv, blk, layout, 0};
   return kda::resolve_conv_shape(dt, n_rows, static_cast<int64_t>(n_req) * 12, &o, pairs, s);
 }
 
@@ -300,6 +300,16 @@ static void conv_shapes() {
   CHECK(!conv_shape(KDA_F16, 8, 8, true, &s, 16, 64, 0, M));
   CHECK(!conv_shape(KDA_F16, 8, 8, true, &s, 0, 64, 0, KS));
   CHECK(!conv_shape(KDA_F16, 8, 1, true, &s, 0, 64));
+  // the raw gate: 0 or 1 on the fused entries, refused on the plain ones
+  {
+    kda_launch_opts o{0, 0, 0, 0, 1};
+    CHECK(kda::resolve_conv_shape(KDA_F16, 8, 96, &o, true, &s) && is_shape(s, 64, 8, M));
+    o.g_raw = 2;
+    CHECK(!kda::resolve_conv_shape(KDA_F16, 8, 96, &o, true, &s));
+    o.g_raw = 1;
+    kda_launch_desc d;
+    CHECK(kda_describe_launch(8, 8, 12, KDA_F16, &o, &d) == KDA_ERR_ARG);
+  }
   // every combination: an admitted shape is one a kernel exists for
   const kda_dtype dts[2] = {KDA_F32, KDA_F16};
   for (kda_dtype dt : dts)

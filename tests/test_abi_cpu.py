@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in B.SIGNATURES, "binding lacks a signature for %s" % name
-    assert B.kda_abi_version() == 10
+    assert B.kda_abi_version() == 11
 
 
 def pool(n_slots=96, H=12, Kd=128, V=128, dtype=B.KDA_F32, base=FAKE):
@@ -95,6 +95,9 @@ def test_refusals_before_any_hip_call():
     # the matrix-core block form: 64 columns over 8 (default) or 4 waves
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 32, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
     assert step(pool(), n_rows=8, opts=B.kda_launch_opts(2, 0, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
+    # the raw gate belongs to the fused front end only
+    assert step(pool(), opts=B.kda_launch_opts(0, 0, 0, 0, 1)) == B.KDA_ERR_ARG
+    assert step(pool(), n_rows=8, opts=B.kda_launch_opts(0, 0, 0, B.KDA_ROWS_MATRIX, 1)) == B.KDA_ERR_ARG
     assert step(pool(base=FAKE + 4)) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE]) == B.KDA_ERR_ALIGN
     assert step(pool(), ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE]) == B.KDA_ERR_ALIGN
@@ -384,6 +387,11 @@ def test_conv_step_refusals():
     assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 64, 0, B.KDA_ROWS_MATRIX)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, n_rows=2, opts=B.kda_launch_opts(0, 0, 0, 4)) == B.KDA_ERR_ARG
     assert conv_step(P, Cv, scale=float("nan")) == B.KDA_ERR_ARG
+    # the raw gate: 0 or 1 on the fused entries, 0 elsewhere
+    assert conv_step(P, Cv, n_req=0, opts=B.kda_launch_opts(0, 0, 0, 0, 1)) == B.KDA_OK
+    for bad in (2, -1):
+        assert conv_step(P, Cv, opts=B.kda_launch_opts(0, 0, 0, 0, bad)) == B.KDA_ERR_ARG
+        assert conv_step(P, Cv, n_rows=4, opts=B.kda_launch_opts(0, 0, 0, B.KDA_ROWS_MATRIX, bad)) == B.KDA_ERR_ARG
     assert conv_step(P, B.kda_conv_pool(ctypes.c_void_p(FAKE + 8), 16, 12)) == B.KDA_ERR_ALIGN
 
 

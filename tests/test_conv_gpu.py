@@ -221,3 +221,35 @@ def test_fused_conv_matrix_skips_a_request_with_a_bad_id(oracle, form, n_rows):
     assert out_rel_err(go[sel], oo) <= OUT_REL
     assert f16_ulp_distance(gp[ids[sel]], op[ids[sel]]).max() <= F16_ULP
     np.testing.assert_array_equal(gc[ids[sel]], oc[ids[sel]])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("layout", ["single_row", "halves", "matrix16", "matrix8", "k_split"])
+def test_fused_conv_with_the_raw_gate(oracle, dtype, layout):
+    """g_raw: the launch gets the raw gate x and takes the log-decay
+    -softplus(x) itself; the oracle forms g from x (log_decay_from_gate)
+    and runs the usual composition.  Every fused layout."""
+    n_rows = 1 if layout == "single_row" else 5
+    ci = kda_inputs.make_conv_inputs("conv gate", 48, 4, n_rows, dtype, H=3, seed=221 + n_rows)
+    raw = np.random.default_rng(7).standard_normal(ci.dec.g.shape).astype(np.float32) * np.float32(2.0)
+    waves, rows_layout, pairs = (0, 0, False) if layout == "single_row" else LAYOUTS[layout]
+    d = ci.dec
+    dev = torch.device("cuda", 0)
+    pool = torch.from_numpy(d.pool if d.dtype == "f32" else d.pool.view(np.float16)).to(dev)
+    conv = torch.from_numpy(ci.conv).to(dev).view(torch.bfloat16)
+    t = {n: torch.from_numpy(getattr(src, n)).to(dev) for src, n in ((d, "slot_ids"), (ci, "x"), (ci, "w"), (d, "b"))}
+    out = torch.full((d.slot_ids.size, d.pool.shape[1], 128), float("nan"), device=dev)
+    counts = counters(ci) if pairs else None
+    B.kda_decode_step_conv(pool, conv, t["slot_ids"], t["x"], t["w"], torch.from_numpy(raw).to(dev), t["b"], out,
+                           n_rows_per_slot=n_rows, scale=d.scale, waves_per_tile=waves, rows_layout=rows_layout,
+                           pair_counts=counts, g_raw=True)
+    torch.cuda.synchronize()
+    gp, gc, go = pool_to_host(pool), conv.view(torch.int16).cpu().numpy().view(np.uint16), out.cpu().numpy()
+    d.g = oracle.log_decay_from_gate(raw)
+    op, oc, oo = oracle_conv(oracle, ci)
+    if dtype == "f32":
+        assert np.max(np.abs(gp - op)) <= STATE_ABS_F32
+    else:
+        assert f16_ulp_distance(gp, op).max() <= F16_ULP
+    assert out_rel_err(go, oo) <= OUT_REL
+    np.testing.assert_array_equal(gc, oc)

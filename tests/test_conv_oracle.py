@@ -138,3 +138,28 @@ def test_dropped_silu_is_caught(oracle):
     finally:
         oracle.set_mutation(0)
     assert not np.allclose(y, y_ref, rtol=1e-4, atol=1e-5)
+
+
+def test_log_decay_from_gate_closed_forms(oracle):
+    # softplus(0) = ln 2; softplus(ln(e - 1)) = ln e = 1; softplus(x) -> x
+    # for large x and -> e^x for very negative x
+    g = oracle.log_decay_from_gate(np.array([0.0, np.log(np.e - 1.0), 40.0, -40.0]))
+    assert g.dtype == np.float32
+    assert g[0] == np.float32(-np.log(2.0))
+    assert g[1] == np.float32(-1.0)
+    assert g[2] == np.float32(-40.0)
+    assert g[3] == np.float32(-np.exp(-40.0))
+
+
+def test_log_decay_from_gate_identities(oracle):
+    # softplus(x) - softplus(-x) = x, and e^g = 1 / (1 + e^x) (the decay the
+    # kernels form without the logarithm), over a wide range of x
+    x = np.linspace(-30.0, 30.0, 6001)
+    g_pos = oracle.log_decay_from_gate(x).astype(np.float64)
+    g_neg = oracle.log_decay_from_gate(-x).astype(np.float64)
+    ulp = np.spacing(np.maximum(np.abs(g_pos), np.abs(g_neg)).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs((g_neg - g_pos) - x) <= 2 * ulp + 1e-300)
+    a = np.exp(g_pos)
+    ref = 1.0 / (1.0 + np.exp(x))
+    assert np.all(np.abs(a - ref) <= 1.2e-7 * (1.0 + np.abs(x)) * ref)   # g's fp32 rounding, times |g|
+    assert np.all(g_pos <= 0) and np.all(np.diff(g_pos) <= 0)   # a decay in (0, 1], falling with x
