@@ -23,7 +23,9 @@ import csv
 import hashlib
 import json
 import os
+import shlex
 import statistics
+import sys
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -153,7 +155,8 @@ def pmc(args):
                    "one 16-byte vector per work-item) in the same runs: the decode's state loads "
                    "and stores carry the nontemporal hint.  The plain copy's factors are listed "
                    "beside them",
-           "commands": args.command, "kernel_source_sha256_16": kernel_hash(),
+           "commands": args.command, "summary_command": self_command(),
+           "kernel_source_sha256_16": kernel_hash(),
            "calibration_copies": calib,
            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
            "plain_copy_factors": [round(x, 4) for x in fac["plain"]] if "plain" in fac else None,
@@ -163,11 +166,17 @@ def pmc(args):
         f.write("\n")
 
 
+def self_command() -> str:
+    """This summary's own invocation, in full."""
+    return "python -m kda_gated_delta_decode_amd.profiling " + shlex.join(sys.argv[1:])
+
+
 def trace(args):
     stats = _rows(args.stats)
     lines = ["# %s" % args.title, "",
              "Command (from the repository root, `TMPDIR=/tmp`):", "", "```"]
-    lines += args.command + ["```", "",
+    lines += args.command + ["```", "", "Summary written by (from the repository root):", "", "```",
+                             self_command(), "```", "",
                              "Kernel sources (%s with %s) sha256[:16] at the time: `%s`." % (
                                  args.source, ", ".join(KERNEL_HEADERS),
                                  kernel_hash(os.path.join(HERE, "csrc", args.source))), "",
