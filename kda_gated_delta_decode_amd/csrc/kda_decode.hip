@@ -268,16 +268,16 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
   // any store (a re-read after the snapshot stores would be a vector load
   // that waits for every earlier store to retire).  A request with an id out
   // of range is skipped: its out rows become NaN, the pool is not touched.
+  // both id loads are issued before either is waited for
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
   const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
   int32_t sid[TMAX];
-  bool ids_ok = true;
 #pragma unroll
-  for (int t = 0; t < TMAX; ++t) {
-    sid[t] = t < n_rows ? ids[t] : 0;
-    ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
-  }
-  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
-  ids_ok = ids_ok && init_slot >= 0 && init_slot < a.n_slots;
+  for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
+  __builtin_amdgcn_sched_barrier(0);
+  bool ids_ok = init_slot >= 0 && init_slot < a.n_slots;
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) ids_ok = ids_ok && sid[t] >= 0 && sid[t] < a.n_slots;
   if (!ids_ok) {
     if (writer) {
       for (int t = 0; t < n_rows; ++t) {
@@ -963,11 +963,13 @@ __global__ __launch_bounds__(kWave * NWB) void kda_rows_kernel(KDA_HOT_PARAMS, A
   // every earlier store).  The initial slot is one load from a selected
   // address: a select between two loaded values would wait for the ids
   // before the row loads below go out.
+  // both id loads are issued before either is waited for
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
   const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
   int32_t sid[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
-  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
+  __builtin_amdgcn_sched_barrier(0);
 
   // Row inputs (wave w stages rows w, w + NWB, ...), issued before anything
   // waits on the ids.  Every address is valid whatever n_rows is (a row past
@@ -1257,11 +1259,13 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
   const int n_rows = a.n_rows;
   const int hcol = vt * BV + half * BH;  // the first column of this wave's half
 
+  // both id loads are issued before either is waited for
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
   const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
   int32_t sid[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
-  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
+  __builtin_amdgcn_sched_barrier(0);
 
   // Row inputs: wave w normalises rows w, w + NW, ... (a row past the last
   // re-reads the last one and is staged as zeros).
@@ -1677,11 +1681,13 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
   const int r = rh / H;
   const int hcol = vt * BV + half * BH;  // the first column of this wave's half
 
+  // both id loads are issued before either is waited for
+  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
   const int32_t* ids = a.slot_ids + static_cast<int64_t>(r) * n_rows;
   int32_t sid[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) sid[t] = t < n_rows ? ids[t] : 0;
-  const int32_t init_slot = hot_init[static_cast<int64_t>(r) * init_stride];
+  __builtin_amdgcn_sched_barrier(0);
 
   // This wave's row of the request (a wave past the last row re-reads the
   // last one and stages zeros).
