@@ -169,6 +169,13 @@ struct Lane16<_Float16> {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+// History words are loaded raw and widened only once the state tile's loads
+// are issued: widening a word next to its load makes the wave wait for that
+// load there, in front of its tile.
+__device__ __forceinline__ f2 bf16_x2(uint32_t p) { return f2{bf16_lo(p), bf16_hi(p)}; }
+__device__ __forceinline__ f4 bf16_x4(uint2 p) {
+  return f4{bf16_lo(p.x), bf16_hi(p.x), bf16_lo(p.y), bf16_hi(p.y)};
+}
 __device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
   const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
   const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
@@ -299,16 +306,19 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
   f4 v4[TPW];
   float braw[TPW];
   // fused convolution: the window win[t + m], m = 0..3 (3-entry history,
-  // then this request's rows) of this lane's 2 q, 2 k and 4 v channels, and
-  // their taps
+  // then this request's rows) of this lane's 2 q, 2 k and 4 v channels
+  // (lanes past BV / 4 repeat the v channels of the first ones, so no load
+  // sits behind a per-lane branch), and their taps
   constexpr int TC = CONV ? TPW : 1;
   f2 eq[TC][4], ek[TC][4];
   f4 ev[TC][4];
+  uint32_t hwq[TC][4], hwk[TC][4];  // history entries as loaded (bf16 pairs)
+  uint2 hwv[TC][4];
   f4 wq0, wq1, wk0, wk1, wv[4];
   const int64_t conv_c = static_cast<int64_t>(3) * a.H * kHeadK;  // channels per history entry
   const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
   const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
-  const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
+  const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * (CONV ? lane % (BV / 4) : lane);
   const bool conv_vl = lane < BV / 4;
   if constexpr (CONV) {
     if (wave < n_rows) {
@@ -316,10 +326,8 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
       wq1 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4 + 4);
       wk0 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4);
       wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
-      if (conv_vl) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
-      }
+      for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
     }
   }
 #pragma unroll
@@ -335,19 +343,14 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
           const int pos = t + m;              // window index
           if (pos < 3) {
             const uint16_t* hb = a.conv_pool + (static_cast<int64_t>(init_slot) * 3 + pos) * conv_c;
-            const uint32_t pq = *reinterpret_cast<const uint32_t*>(hb + chq);
-            const uint32_t pk = *reinterpret_cast<const uint32_t*>(hb + chk);
-            eq[j][m] = f2{bf16_lo(pq), bf16_hi(pq)};
-            ek[j][m] = f2{bf16_lo(pk), bf16_hi(pk)};
-            if (conv_vl) {
-              const uint2 pv = *reinterpret_cast<const uint2*>(hb + chv);
-              ev[j][m] = f4{bf16_lo(pv.x), bf16_hi(pv.x), bf16_lo(pv.y), bf16_hi(pv.y)};
-            }
+            hwq[j][m] = *reinterpret_cast<const uint32_t*>(hb + chq);
+            hwk[j][m] = *reinterpret_cast<const uint32_t*>(hb + chk);
+            hwv[j][m] = *reinterpret_cast<const uint2*>(hb + chv);
           } else {
             const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * conv_c;
             eq[j][m] = *reinterpret_cast<const f2*>(xr + chq);
             ek[j][m] = *reinterpret_cast<const f2*>(xr + chk);
-            if (conv_vl) ev[j][m] = *reinterpret_cast<const f4*>(xr + chv);
+            ev[j][m] = *reinterpret_cast<const f4*>(xr + chv);
           }
         }
       } else {
@@ -382,6 +385,14 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
     for (int j = 0; j < TPW; ++j) {
       const int t = wave + j * NW;
       if (t < n_rows) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if (t + m < 3) {
+            eq[j][m] = bf16_x2(hwq[j][m]);
+            ek[j][m] = bf16_x2(hwk[j][m]);
+            ev[j][m] = bf16_x4(hwv[j][m]);
+          }
+        }
         float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -392,17 +403,15 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
         }
         q2[j] = f2{silu(sq0), silu(sq1)};
         k2[j] = f2{silu(sk0), silu(sk1)};
-        if (conv_vl) {
-          f4 yv;
+        f4 yv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float sv = 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          float sv = 0.0f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) sv = fmaf(wv[e][m], ev[j][m][e], sv);
-            yv[e] = silu(sv);
-          }
-          v4[j] = yv;
+          for (int m = 0; m < 4; ++m) sv = fmaf(wv[e][m], ev[j][m][e], sv);
+          yv[e] = silu(sv);
         }
+        v4[j] = yv;
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
           hq[j][e] = eq[j][e + 1];
@@ -1277,15 +1286,18 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
   float braw[TPW];
   // fused convolution: the window win[t + m], m = 0..3 (3-entry history,
   // then this request's rows) of this lane's 2 q, 2 k and 4 v channels
-  // (lanes < 32 hold the 128 v channels), and their taps
+  // (lanes < 32 hold the 128 v channels, the others repeat theirs), and
+  // their taps
   constexpr int TC = CONV ? TPW : 1;
   f2 eq[TC][4], ek[TC][4];
   f4 ev[TC][4];
+  uint32_t hwq[TC][4], hwk[TC][4];  // history entries as loaded (bf16 pairs)
+  uint2 hwv[TC][4];
   f4 wq0, wq1, wk0, wk1, wv[4];
   const int64_t conv_c = static_cast<int64_t>(3) * a.H * kHeadK;  // channels per history entry
   const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
   const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
-  const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * lane;
+  const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * (CONV ? lane % (BV / 4) : lane);
   const bool conv_vl = lane < BV / 4;
   if constexpr (!CONV) {
 #pragma unroll
@@ -1312,10 +1324,8 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
       wq1 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4 + 4);
       wk0 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4);
       wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
-      if (conv_vl) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
-      }
+      for (int e = 0; e < 4; ++e) wv[e] = *reinterpret_cast<const f4*>(a.conv_w + (chv + e) * 4);
     }
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -1327,19 +1337,14 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
           const int pos = t + m;  // window index
           if (pos < 3) {
             const uint16_t* hb = a.conv_pool + (hslot * 3 + pos) * conv_c;
-            const uint32_t pq = *reinterpret_cast<const uint32_t*>(hb + chq);
-            const uint32_t pk = *reinterpret_cast<const uint32_t*>(hb + chk);
-            eq[j][m] = f2{bf16_lo(pq), bf16_hi(pq)};
-            ek[j][m] = f2{bf16_lo(pk), bf16_hi(pk)};
-            if (conv_vl) {
-              const uint2 pv = *reinterpret_cast<const uint2*>(hb + chv);
-              ev[j][m] = f4{bf16_lo(pv.x), bf16_hi(pv.x), bf16_lo(pv.y), bf16_hi(pv.y)};
-            }
+            hwq[j][m] = *reinterpret_cast<const uint32_t*>(hb + chq);
+            hwk[j][m] = *reinterpret_cast<const uint32_t*>(hb + chk);
+            hwv[j][m] = *reinterpret_cast<const uint2*>(hb + chv);
           } else {
             const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * conv_c;
             eq[j][m] = *reinterpret_cast<const f2*>(xr + chq);
             ek[j][m] = *reinterpret_cast<const f2*>(xr + chk);
-            if (conv_vl) ev[j][m] = *reinterpret_cast<const f4*>(xr + chv);
+            ev[j][m] = *reinterpret_cast<const f4*>(xr + chv);
           }
         }
         braw[j] = a.b[rho * a.H + h];
@@ -1389,6 +1394,14 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
       k2[j] = f2{0.0f, 0.0f};
       v4[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
       if (t < n_rows) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if (t + m < 3) {
+            eq[j][m] = bf16_x2(hwq[j][m]);
+            ek[j][m] = bf16_x2(hwk[j][m]);
+            ev[j][m] = bf16_x4(hwv[j][m]);
+          }
+        }
         float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -1399,17 +1412,15 @@ __global__ __launch_bounds__(kWave * kMfmaWaves * (CONV ? 2 : 1)) void kda_rows_
         }
         q2[j] = f2{silu(sq0), silu(sq1)};
         k2[j] = f2{silu(sk0), silu(sk1)};
-        if (conv_vl) {
-          f4 yv;
+        f4 yv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float sv = 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          float sv = 0.0f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) sv = fmaf(wv[e][m], ev[j][m][e], sv);
-            yv[e] = silu(sv);
-          }
-          v4[j] = yv;
+          for (int m = 0; m < 4; ++m) sv = fmaf(wv[e][m], ev[j][m][e], sv);
+          yv[e] = silu(sv);
         }
+        v4[j] = yv;
 #pragma unroll
         for (int e = 0; e < 3; ++e) {
           hq[j][e] = eq[j][e + 1];
@@ -1704,6 +1715,11 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
   // and its v channel, and their taps
   f2 eq[4], ek[4];
   float ev[4];
+  // both candidates of each window entry as loaded: the history's (bf16) and
+  // the request row's (fp32)
+  uint32_t hwq[4], hwk[4], hwv[4];
+  f2 xwq[4], xwk[4];
+  float xwv[4];
   f4 wq0, wq1, wk0, wk1, wv;
   const int64_t conv_c = static_cast<int64_t>(3) * H * kHeadK;  // channels per history entry
   const int64_t chq = static_cast<int64_t>(half * H + h) * kHeadK + 2 * lane;
@@ -1729,24 +1745,24 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
       wk1 = *reinterpret_cast<const f4*>(a.conv_w + chk * 4 + 4);
     }
     wv = *reinterpret_cast<const f4*>(a.conv_w + chv * 4);
+    // Entry m of the window is history entry trow + m while that is below 3,
+    // else row trow + m - 3 of the request.  Both are loaded (the one not
+    // taken from an in-range place: history entry 2, the request's row 0) and
+    // the entry is chosen once the state tile's loads are issued, so no load
+    // sits behind a branch whose arms the compiler would join by waiting.
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int pos = trow + m;  // window index (wave-uniform)
-      if (pos < 3) {
-        const uint16_t* hb = a.conv_pool + (hslot * 3 + pos) * conv_c;
-        const uint32_t pq = *reinterpret_cast<const uint32_t*>(hb + chq);
-        eq[m] = f2{bf16_lo(pq), bf16_hi(pq)};
-        if constexpr (!HEAD) {
-          const uint32_t pk = *reinterpret_cast<const uint32_t*>(hb + chk);
-          ek[m] = f2{bf16_lo(pk), bf16_hi(pk)};
-        }
-        ev[m] = bf16_lo(hb[chv]);
-      } else {
-        const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + (pos - 3)) * conv_c;
-        eq[m] = *reinterpret_cast<const f2*>(xr + chq);
-        if constexpr (!HEAD) ek[m] = *reinterpret_cast<const f2*>(xr + chk);
-        ev[m] = xr[chv];
+      const uint16_t* hb = a.conv_pool + (hslot * 3 + min(pos, 2)) * conv_c;
+      const float* xr = a.x + (static_cast<int64_t>(r) * n_rows + max(pos - 3, 0)) * conv_c;
+      hwq[m] = *reinterpret_cast<const uint32_t*>(hb + chq);
+      xwq[m] = *reinterpret_cast<const f2*>(xr + chq);
+      if constexpr (!HEAD) {
+        hwk[m] = *reinterpret_cast<const uint32_t*>(hb + chk);
+        xwk[m] = *reinterpret_cast<const f2*>(xr + chk);
       }
+      hwv[m] = hb[chv];
+      xwv[m] = xr[chv];
     }
     if (!HEAD || half == 0) braw = a.b[rho * H + h + zero_v];
     if (!HEAD || half == 1) g2 = reinterpret_cast<const f2*>(a.g + roff)[lane];
@@ -1775,6 +1791,13 @@ __global__ __launch_bounds__(kWave * kMfma8Waves * (FORM == kRowsConvHead ? 2 : 
   const bool live = rw < n_rows;
   {
     if constexpr (CONV) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bool hist = trow + m < 3;
+        eq[m] = hist ? bf16_x2(hwq[m]) : xwq[m];
+        if constexpr (!HEAD) ek[m] = hist ? bf16_x2(hwk[m]) : xwk[m];
+        ev[m] = hist ? bf16_lo(hwv[m]) : xwv[m];
+      }
       // y = silu(sum_m w_m win[trow + m]), the sum taken in window order
       float sq0 = 0.0f, sq1 = 0.0f, sk0 = 0.0f, sk1 = 0.0f, sv = 0.0f;
 #pragma unroll

@@ -238,6 +238,38 @@ def test_pair_counter_result_is_waited_for_only_after_the_snapshots(code_object)
         assert stores >= 8 * 4, (prefix, stores)   # 8 rows x 4 snapshot pieces per lane
 
 
+def kernel_lines(code_object, prefix):
+    """The disassembled instructions (with operands) of the one kernel whose
+    symbol starts with `prefix`."""
+    for path in code_object["paths"]:
+        text = subprocess.run([tool("llvm-objdump"), "-d", "--no-show-raw-insn", path],
+                              check=True, capture_output=True, text=True).stdout
+        blocks = re.split(r"^[0-9a-f]+ <", text, flags=re.M)
+        hit = [b for b in blocks if b.startswith(prefix)]
+        if hit:
+            assert len(hit) == 1, prefix
+            return [l.split("//")[0].strip() for l in hit[0].splitlines()[1:] if l.strip()]
+    raise AssertionError("no kernel " + prefix)
+
+
+# the fused launches' default kernels: single rows (fp32 over 2 waves, fp16
+# over 4), chained rows in 64-column halves and as whole heads
+FUSED_DEFAULTS = ("_ZN3kda15kda_decode_tileIfLi32ELi2ELb0ELb1ELb0EE",
+                  "_ZN3kda15kda_decode_tileIDF16_Li16ELi4ELb0ELb1ELb0EE") + MFMA8_CONV + MFMA8_CONV_HALF
+
+
+def test_fused_kernels_issue_the_state_loads_before_any_memory_wait(code_object):
+    # the history, row and tap loads of the convolution are issued first and
+    # only consumed after the state tile's (nontemporal) loads are in flight:
+    # a wait in between would put their round trip in front of the tile's
+    for prefix in FUSED_DEFAULTS:
+        lines = kernel_lines(code_object, prefix)
+        first = next(j for j, l in enumerate(lines) if l.startswith("global_load") and l.endswith(" nt"))
+        waits = [l for l in lines[:first] if l.startswith("s_waitcnt") and "vmcnt" in l]
+        assert not waits, (prefix, waits)
+        assert sum(1 for l in lines[:first] if l.startswith("global_load")) >= 8, prefix
+
+
 def kernel_descriptor(code_object, name):
     """The 64-byte kernel descriptor (symbol NAME.kd) from whichever code
     object holds it."""
