@@ -319,7 +319,8 @@ __global__ __launch_bounds__(kWave * NW) void kda_decode_tile(KDA_HOT_PARAMS, Ar
   const int64_t chq = static_cast<int64_t>(h) * kHeadK + 2 * lane;
   const int64_t chk = chq + static_cast<int64_t>(a.H) * kHeadK;
   const int64_t chv = static_cast<int64_t>(2 * a.H + h) * kHeadK + 4 * (CONV ? lane % (BV / 4) : lane);
-  const bool conv_vl = lane < BV / 4;
+  // unused here; without it the compiler orders the plain single-row kernels differently
+  [[maybe_unused]] const bool conv_vl = lane < BV / 4;
   if constexpr (CONV) {
     if (wave < n_rows) {
       wq0 = *reinterpret_cast<const f4*>(a.conv_w + chq * 4);
