@@ -270,7 +270,10 @@ typedef struct kda_conv_pool {
  * 16 waves, two 64-column halves of 8; waves_per_tile 8: two halves of 4)
  * when rows_layout asks for it, or by default for 3 rows or more up to 192
  * (fp16) or 48 (fp32) requests x heads unless waves_per_tile or block_rows
- * is set; otherwise the K-split kernel with 2, 4 or 8 waves.
+ * is set; otherwise the K-split kernel with 2, 4 or 8 waves.  One row per
+ * request: the single-row kernel over whole heads, by default 4 waves for
+ * fp16 pools, and for fp32 pools 2 waves below 384 requests x heads and 4
+ * from there.
  * KDA_ROWS_WAVE_K is refused; rows_layout is ignored for one row.
  * opts->g_raw: 0 (default), g is the log-decay as in kda_decode_step; 1, g
  * holds the raw gate x of each key channel and the step takes the

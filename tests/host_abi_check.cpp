@@ -286,9 +286,14 @@ static void conv_shapes() {
   CHECK(conv_shape(KDA_F16, 17, 8, false, &s) && is_shape(s, 128, 4, KS));
   CHECK(conv_shape(KDA_F32, 4, 4, false, &s) && is_shape(s, 128, 16, M));
   CHECK(conv_shape(KDA_F32, 8, 8, false, &s) && is_shape(s, 128, 8, KS));
-  // one row: the single-row kernel over whole heads whatever the counters
+  // one row: the single-row kernel over whole heads whatever the counters;
+  // fp32 over 4 waves from 384 requests x heads
   CHECK(conv_shape(KDA_F16, 8, 1, true, &s) && is_shape(s, 128, 4, KS));
+  CHECK(conv_shape(KDA_F16, 64, 1, false, &s) && is_shape(s, 128, 4, KS));
   CHECK(conv_shape(KDA_F32, 8, 1, true, &s) && is_shape(s, 128, 2, KS));
+  CHECK(conv_shape(KDA_F32, 31, 1, false, &s) && is_shape(s, 128, 2, KS));
+  CHECK(conv_shape(KDA_F32, 32, 1, false, &s) && is_shape(s, 128, 4, KS));
+  CHECK(conv_shape(KDA_F32, 64, 1, true, &s) && is_shape(s, 128, 4, KS));
   // explicit choices
   CHECK(conv_shape(KDA_F16, 64, 8, true, &s, 0, 0, 0, M) && is_shape(s, 64, 8, M));
   CHECK(conv_shape(KDA_F16, 64, 8, false, &s, 0, 0, 0, M) && is_shape(s, 128, 16, M));
