@@ -315,9 +315,10 @@ int kda_decode_step_conv(const kda_pool* pool, const kda_conv_pool* conv,
  *  opts           as kda_decode_step_conv, plus bv 64: the halves, which
  *                 need pair_counts.  With pair_counts, chained rows take
  *                 the halves when rows_layout is KDA_ROWS_MATRIX or by
- *                 default up to 96 (fp16) requests x heads, or for fp32 up
- *                 to 48, or 96 with 6 rows or more, unless waves_per_tile or
- *                 block_rows is set; bv 128 keeps whole heads; beyond, the
+ *                 default for fp16 up to 96 requests x heads, or 240 with
+ *                 6 rows or more, and for fp32 up to 48, or 96 with 4 rows
+ *                 or more, unless waves_per_tile or block_rows is set;
+ *                 bv 128 keeps whole heads; beyond, the
  *                 defaults of kda_decode_step_conv.
  * Errors: as kda_decode_step_conv, plus KDA_ERR_NULL for NULL pair_counts
  * with n_pair_counts != 0, KDA_ERR_ARG for n_pair_counts < 0 or, with

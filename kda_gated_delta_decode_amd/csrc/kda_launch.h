@@ -244,7 +244,9 @@ inline bool resolve_conv_shape(kda_dtype dt, int32_t n_rows, int64_t units, cons
       bvm = bv != 0 ? bv : (pairs ? kMatrixBV : kHeadV);
     } else if (asked == KDA_ROWS_DEFAULT && !shaped) {
       const bool f16 = dt == KDA_F16;
-      const bool halves = pairs && bv == 0 && (f16 ? units <= 96 : units <= 48 || (units <= 96 && n_rows >= 6));
+      const bool halves = pairs && bv == 0 &&
+                          (f16 ? units <= 96 || (units <= 240 && n_rows >= 6)
+                               : units <= 48 || (units <= 96 && n_rows >= 4));
       const bool head = n_rows >= 3 && units <= (f16 ? 192 : 48);
       bvm = halves ? kMatrixBV : head ? kHeadV : 0;
     }

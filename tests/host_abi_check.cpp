@@ -269,15 +269,19 @@ static void conv_shapes() {
   using kda::Shape;
   Shape s{};
   const int32_t M = KDA_ROWS_MATRIX, KS = KDA_ROWS_K_SPLIT;
-  // halves with counters: fp16 up to 96 units, fp32 up to 48 (96 from 6 rows)
+  // halves with counters: fp16 up to 96 units (240 from 6 rows), fp32 up to
+  // 48 (96 from 4 rows)
   CHECK(conv_shape(KDA_F16, 8, 8, true, &s) && is_shape(s, 64, 8, M));
   CHECK(conv_shape(KDA_F16, 8, 2, true, &s) && is_shape(s, 64, 8, M));
-  CHECK(conv_shape(KDA_F16, 9, 8, true, &s) && is_shape(s, 128, 16, M));   // whole heads
-  CHECK(conv_shape(KDA_F16, 17, 8, true, &s) && is_shape(s, 128, 4, KS));  // K split
+  CHECK(conv_shape(KDA_F16, 9, 8, true, &s) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F16, 20, 6, true, &s) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F16, 9, 5, true, &s) && is_shape(s, 128, 16, M));   // whole heads
+  CHECK(conv_shape(KDA_F16, 21, 8, true, &s) && is_shape(s, 128, 4, KS));  // K split
   CHECK(conv_shape(KDA_F16, 9, 2, true, &s) && is_shape(s, 128, 4, KS));
   CHECK(conv_shape(KDA_F32, 4, 2, true, &s) && is_shape(s, 64, 8, M));
   CHECK(conv_shape(KDA_F32, 8, 8, true, &s) && is_shape(s, 64, 8, M));
-  CHECK(conv_shape(KDA_F32, 8, 4, true, &s) && is_shape(s, 128, 8, KS));
+  CHECK(conv_shape(KDA_F32, 8, 4, true, &s) && is_shape(s, 64, 8, M));
+  CHECK(conv_shape(KDA_F32, 8, 3, true, &s) && is_shape(s, 128, 8, KS));
   CHECK(conv_shape(KDA_F32, 9, 8, true, &s) && is_shape(s, 128, 8, KS));
   // without counters: whole heads from 3 rows, up to 192 (fp16) or 48 units
   CHECK(conv_shape(KDA_F16, 8, 8, false, &s) && is_shape(s, 128, 16, M));

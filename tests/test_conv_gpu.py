@@ -140,6 +140,17 @@ def test_fused_conv_chained_rows_in_every_layout(oracle, dtype, n_req, n_rows, l
     check(oracle, ci, waves=waves, rows_layout=rows_layout, counts=counters(ci) if pairs else None)
 
 
+@pytest.mark.parametrize("dtype,n_req,n_rows", [("f16", 20, 6), ("f16", 21, 8), ("f32", 8, 4), ("f32", 8, 3)])
+def test_fused_conv_default_layout_with_counters_at_its_bounds(oracle, dtype, n_req, n_rows):
+    """The default layout with pair counters on either side of the halves'
+    bounds (fp16: 240 requests x heads from 6 rows, then the K split; fp32:
+    96 from 4 rows, then the K split), requests in place at row 0."""
+    ci = kda_inputs.make_conv_inputs("conv bounds", n_req * n_rows + 8, n_req, n_rows, dtype,
+                                     seed=170 + n_req + n_rows)
+    init = ci.dec.slot_ids.reshape(n_req, n_rows)[:, 0].copy()
+    check(oracle, ci, init=init, counts=counters(ci))
+
+
 MATRIX_FORMS = ["matrix16", "matrix8", "halves"]
 
 
