@@ -64,10 +64,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--dtype", choices=["f32", "f16"], default="f32")
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
-    ap.add_argument("--extras", choices=["all", "copy", "probes", "pmc"], default="all",
+    ap.add_argument("--extras", choices=["all", "copy", "probes", "pmc", "layouts"], default="all",
                     help="'copy' runs only the plain-copy probe after the main workload, "
                          "'probes' only the bandwidth probes, 'pmc' the copies that calibrate "
-                         "the byte counters (plain and nontemporal) and the 8 x 8 chained rows")
+                         "the byte counters (plain and nontemporal) and the 8 x 8 chained rows, "
+                         "'layouts' only the fused step's launch shapes side by side (a few minutes)")
     ap.add_argument("--eager", action="store_true",
                     help="launch eagerly instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -363,7 +364,9 @@ def main():
         "device": dev_name,
     }
 
-    if not args.no_extras:
+    if not args.no_extras and args.extras == "layouts":
+        rec["extras"] = {"fused_layouts": fused_layouts(B, torch)}
+    if not args.no_extras and args.extras != "layouts":
         extras = {}
         # plain copies: the achievable streaming read+write bandwidth at
         # 1 GiB, and a copy moving the same bytes as one decode step; the
@@ -597,6 +600,52 @@ def fused_conv(n_req, n_rows, dtype, B, torch, steps, **launch):
     return {"workload": inp.name, "us_per_step": round(us, 3),
             "algorithmic_GB/s": round(ab / us / 1e3, 1),
             "frac_of_peak": round(ab / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def fused_layouts(B, torch):
+    """The fused step's launch shapes side by side, in us per launch (graph
+    replay, state and history pools rotated over >= 1 GiB, median of 3
+    interleaved runs): chained rows in 64-column halves (with pair counters),
+    as whole heads and in the K split; one row per request over 2, 4 and 8
+    waves per tile."""
+    import kda_inputs
+    import statistics
+    M, KS = B.KDA_ROWS_MATRIX, B.KDA_ROWS_K_SPLIT
+    chained = {"f16": [(1, 2), (8, 2), (16, 2), (48, 2), (1, 4), (8, 4), (12, 4), (16, 4), (24, 4), (8, 6),
+                       (1, 8), (8, 8), (12, 8), (16, 8), (20, 8), (32, 8)],
+               "f32": [(1, 2), (4, 2), (8, 2), (1, 4), (4, 4), (8, 4), (12, 4), (8, 6), (1, 8), (4, 8),
+                       (8, 8), (12, 8)]}
+    out = {}
+    for dt in ("f16", "f32"):
+        res = {}
+        for n_req, n_rows in chained[dt] + [(n, 1) for n in (16, 32, 64, 96)]:
+            ci = kda_inputs.make_conv_inputs("fused layouts", max(96, n_req * n_rows + 8), n_req, n_rows, dt, seed=2)
+            inp = ci.dec
+            w = Workload(inp, ROT, torch)
+            conv0 = torch.from_numpy(ci.conv).cuda().view(torch.bfloat16)
+            convs = [conv0] + [conv0.clone() for _ in range(len(w.pools) - 1)]
+            x = torch.from_numpy(ci.x).cuda()
+            cw = torch.from_numpy(ci.w).cuda()
+            if n_rows > 1:
+                counts = B.conv_pair_counts(n_req, inp.pool.shape[1], x.device)
+                forms = {"halves": dict(rows_layout=M, pair_counts=counts), "whole_heads": dict(rows_layout=M),
+                         "k_split": dict(rows_layout=KS)}
+            else:
+                forms = {"waves_%d" % nw: dict(waves_per_tile=nw) for nw in (2, 4, 8)}
+            t = {f: [] for f in forms}
+            for _ in range(3):
+                for f, o in forms.items():
+                    def step(i, o=o):
+                        B.kda_decode_step_conv(w.pools[i % len(w.pools)], convs[i % len(convs)], w.ids, x, cw,
+                                               w.g, w.b, w.out, n_rows_per_slot=n_rows, scale=inp.scale, **o)
+                    t[f].append(time_launches(step, 60, 10, torch)["launch_ms_mean"] * 1e3)
+            res["%dx%d" % (n_req, n_rows)] = {f: round(statistics.median(v), 2) for f, v in t.items()}
+            print("fused layouts %s %dx%d %s" % (dt, n_req, n_rows, res["%dx%d" % (n_req, n_rows)]),
+                  file=sys.stderr, flush=True)
+            del w, convs
+            torch.cuda.empty_cache()
+        out[dt] = res
+    return out
 
 
 MFMA_F32_PEAK_TFLOPS = 157.3  # AMD MI355X spec: dense fp32 matrix throughput
