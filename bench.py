@@ -68,7 +68,8 @@ def parse():
                     help="'copy' runs only the plain-copy probe after the main workload, "
                          "'probes' only the bandwidth probes, 'pmc' the copies that calibrate "
                          "the byte counters (plain and nontemporal) and the 8 x 8 chained rows, "
-                         "'layouts' only the fused step's launch shapes side by side (a few minutes)")
+                         "'layouts' only the launch shapes of chained rows and of the fused step side by "
+                         "side (several minutes)")
     ap.add_argument("--eager", action="store_true",
                     help="launch eagerly instead of replaying a HIP graph (for profilers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -365,7 +366,7 @@ def main():
     }
 
     if not args.no_extras and args.extras == "layouts":
-        rec["extras"] = {"fused_layouts": fused_layouts(B, torch)}
+        rec["extras"] = {"chained_layouts": chained_layouts(B, torch), "fused_layouts": fused_layouts(B, torch)}
     if not args.no_extras and args.extras != "layouts":
         extras = {}
         # plain copies: the achievable streaming read+write bandwidth at
@@ -600,6 +601,41 @@ def fused_conv(n_req, n_rows, dtype, B, torch, steps, **launch):
     return {"workload": inp.name, "us_per_step": round(us, 3),
             "algorithmic_GB/s": round(ab / us / 1e3, 1),
             "frac_of_peak": round(ab / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def chained_layouts(B, torch):
+    """Chained rows' launch shapes side by side, in us per launch (graph
+    replay, pools rotated over >= 1 GiB, median of 3 interleaved runs): the
+    matrix-core block form, the K split and (fp16) whole K per wave."""
+    import kda_inputs
+    import statistics
+    shapes = {"f16": [(1, 2), (4, 2), (8, 2), (16, 2), (48, 2), (1, 4), (4, 4), (8, 4), (16, 4), (24, 4), (8, 6),
+                      (8, 8), (12, 8), (20, 8), (24, 8), (32, 8)],
+              "f32": [(1, 2), (4, 2), (8, 2), (16, 2), (1, 4), (4, 4), (8, 4), (16, 4), (8, 6), (1, 8), (4, 8),
+                      (8, 8), (12, 8), (20, 8), (32, 8)]}
+    out = {}
+    for dt in ("f16", "f32"):
+        forms = {"block": B.KDA_ROWS_MATRIX, "k_split": B.KDA_ROWS_K_SPLIT}
+        if dt == "f16":
+            forms["whole_k"] = B.KDA_ROWS_WAVE_K
+        res = {}
+        for n_req, n_rows in shapes[dt]:
+            inp = kda_inputs.make_inputs("chained layouts", max(96, n_req * n_rows + 8), n_req, n_rows, dt, seed=1)
+            w = Workload(inp, ROT, torch)
+            t = {f: [] for f in forms}
+            for _ in range(3):
+                for f, layout in forms.items():
+                    def step(i, layout=layout):
+                        B.kda_decode_step(w.pools[i % len(w.pools)], w.ids, w.q, w.k, w.v, w.g, w.b, w.out,
+                                          n_rows_per_slot=n_rows, scale=inp.scale, rows_layout=layout)
+                    t[f].append(time_launches(step, 60, 10, torch)["launch_ms_mean"] * 1e3)
+            res["%dx%d" % (n_req, n_rows)] = {f: round(statistics.median(v), 2) for f, v in t.items()}
+            print("chained layouts %s %dx%d %s" % (dt, n_req, n_rows, res["%dx%d" % (n_req, n_rows)]),
+                  file=sys.stderr, flush=True)
+            del w
+            torch.cuda.empty_cache()
+        out[dt] = res
+    return out
 
 
 def fused_layouts(B, torch):
